@@ -1,0 +1,10 @@
+"""CPU oracle (test infrastructure only; see ttt_oracle's header)."""
+from .ttt_oracle import (  # noqa: F401
+    chunk_ranges,
+    final_state_columns,
+    gated_activation,
+    ntp_targets,
+    silu,
+    ttt_forward,
+    ttt_forward_one,
+)

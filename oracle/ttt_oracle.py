@@ -1,0 +1,157 @@
+"""CPU oracle for the chunk-wise fast-weight update of In-Place Test-Time Training.
+
+TEST INFRASTRUCTURE. Only the test suite, the smoke check and the benchmark's
+CPU-baseline leg may import or call this module. The product path (the HIP
+library and its Python binding) never does, and shares no code with it.
+
+What it computes is the plain definition, run sequentially in fp64 with NumPy.
+For each sequence b, starting from its entry state S (the initial W_down, or
+the state a previous call left):
+
+  1. Z = SiLU(x W_gate^T) * (x W_up^T): the gated MLP's intermediate activation,
+     two projections followed by a gate, with W_up and W_gate frozen
+     (paperlayer.ai summary, sec. 3 "In-Place Adaptation"; iplexlaw.co.kr
+     walkthrough, sec. 2; SwiGLU per the paperlayer summary, App. C.3).
+  2. V[t] = E_tgt[ids[t+1]]: the LM-aligned target V^ = Conv1D(X0) W_target
+     with the convolution kernel reduced to a single tap on the next token and
+     W_target folded into the target-embedding table E_tgt (paperlayer sec. 3
+     "LM-Aligned Objective"; iplexlaw sec. 4, where the kernel may pick "the
+     next token"). A row whose id lies outside [0, vocab) is zero (the causal
+     zero padding of paperlayer App. B).
+  3. For chunks i = 0 .. n-1 of C consecutive tokens (the last may be short):
+     y[chunk i] = Z[chunk i] S^T with the pre-update state (apply), then
+     S <- S + eta * V[chunk i]^T Z[chunk i] (update) (iplexlaw sec. 3,
+     apply-then-update; update rule dW_down = eta V^T Z, iplexlaw sec. 2 and
+     sec. 4; paperlayer sec. 3 "Chunk-Wise Updates").
+  4. Return y and the final S (inclusive of the last chunk's update).
+
+Readings of points the pages leave open (kept identical on both sides):
+  - the update is the sum over the chunk's tokens (no 1/C), sign "+";
+  - the one-token shift crosses chunk boundaries (the last row of chunk i takes
+    token (i+1)C, which every later chunk already sees as input);
+  - no biases, no normalisation of Z or V, no update clipping.
+
+Every function here is pinned by the CPU tests against closed forms, autograd,
+textbook special cases and invariants; none is "parity unpinned".
+"""
+from __future__ import annotations
+
+from typing import Iterable, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+
+def _f64(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64)
+
+
+def silu(g: np.ndarray) -> np.ndarray:
+    """SiLU(g) = g * sigmoid(g) = g / (1 + exp(-g)), elementwise, fp64."""
+    g = _f64(g)
+    return g / (1.0 + np.exp(-g))
+
+
+def gated_activation(x: np.ndarray, W_up: np.ndarray, W_gate: np.ndarray) -> np.ndarray:
+    """Step 1: Z = SiLU(x W_gate^T) * (x W_up^T).
+
+    x [..., d]; W_up, W_gate [f][d] (row-major, one row per hidden unit).
+    Returns Z [..., f] in fp64. The SiLU sits on the gate path.
+    """
+    x = _f64(x)
+    u = x @ _f64(W_up).T
+    g = x @ _f64(W_gate).T
+    return silu(g) * u
+
+
+def ntp_targets(ids: np.ndarray, E_tgt: np.ndarray) -> np.ndarray:
+    """Step 2: the next-token target rows.
+
+    ids [T+1] (position-aligned token ids plus one look-ahead id);
+    E_tgt [vocab][d]. Returns V [T][d] with V[t] = E_tgt[ids[t+1]], or a zero
+    row where ids[t+1] lies outside [0, vocab).
+    """
+    ids = np.asarray(ids)
+    E = _f64(E_tgt)
+    vocab, d = E.shape
+    T = ids.shape[0] - 1
+    V = np.zeros((T, d), dtype=np.float64)
+    for t in range(T):
+        tok = int(ids[t + 1])
+        if 0 <= tok < vocab:
+            V[t] = E[tok]
+    return V
+
+
+def chunk_ranges(T: int, C: int) -> List[Tuple[int, int]]:
+    """Non-overlapping chunks [start, end) of C tokens covering [0, T); the last may be short."""
+    if C < 1:
+        raise ValueError("chunk size must be >= 1")
+    return [(s, min(s + C, T)) for s in range(0, T, C)]
+
+
+def ttt_forward_one(x: np.ndarray, ids: np.ndarray, E_tgt: np.ndarray, W_up: np.ndarray,
+                    W_gate: np.ndarray, W_entry: np.ndarray, C: int, eta: float):
+    """Steps 1-4 for one sequence: x [T][d], ids [T+1], W_entry [d][f].
+
+    Returns (y [T][d], W_final [d][f]) in fp64.
+    """
+    x = _f64(x)
+    T = x.shape[0]
+    S = _f64(W_entry).copy()
+    y = np.zeros((T, S.shape[0]), dtype=np.float64)
+    if T == 0:
+        return y, S
+    Z = gated_activation(x, W_up, W_gate)
+    V = ntp_targets(ids, E_tgt)
+    for (s, e) in chunk_ranges(T, C):
+        y[s:e] = Z[s:e] @ S.T                      # apply with the pre-update state
+        S = S + eta * (V[s:e].T @ Z[s:e])          # then the chunk's rank-C update
+    return y, S
+
+
+def ttt_forward(x: np.ndarray, ids: np.ndarray, E_tgt: np.ndarray, W_up: np.ndarray,
+                W_gate: np.ndarray, W_entry: np.ndarray, C: int, eta: float):
+    """Batched form: x [B][T][d], ids [B][T+1], W_entry [d][f] (shared entry
+    state) or [B][d][f] (one state per sequence). Each sequence is independent.
+
+    Returns (y [B][T][d], W_final [B][d][f]) in fp64.
+    """
+    x = _f64(x)
+    B = x.shape[0]
+    W_entry = _f64(W_entry)
+    ys, Ws = [], []
+    for b in range(B):
+        Wb = W_entry if W_entry.ndim == 2 else W_entry[b]
+        yb, Sb = ttt_forward_one(x[b], ids[b], E_tgt, W_up, W_gate, Wb, C, eta)
+        ys.append(yb)
+        Ws.append(Sb)
+    return np.stack(ys), np.stack(Ws)
+
+
+def final_state_columns(x: np.ndarray, ids: np.ndarray, E_tgt: np.ndarray, W_up: np.ndarray,
+                        W_gate: np.ndarray, W_entry: np.ndarray, C: int, eta: float,
+                        cols: Sequence[int]) -> np.ndarray:
+    """The final state restricted to hidden units `cols`, for one sequence.
+
+    The update of column b of the state only involves column b of Z (the
+    product V^T Z is taken column by column), so the same chunk loop as in
+    ttt_forward_one, run on Z[:, cols] alone, gives W_final[:, cols] exactly.
+    This makes the full-length final state checkable at sizes where the whole
+    of Z is too costly to form on the host.
+
+    x [T][d], ids [T+1], W_entry [d][f]; returns [d][len(cols)] in fp64.
+    """
+    cols = list(cols)
+    x = _f64(x)
+    T = x.shape[0]
+    Wu = _f64(W_up)[cols]
+    Wg = _f64(W_gate)[cols]
+    S = _f64(W_entry)[:, cols].copy()
+    if T == 0:
+        return S
+    Zc = gated_activation(x, Wu, Wg)
+    V = ntp_targets(ids, E_tgt)
+    for (s, e) in chunk_ranges(T, C):
+        S = S + eta * (V[s:e].T @ Zc[s:e])
+    return S
+

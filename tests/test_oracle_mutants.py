@@ -1,0 +1,137 @@
+"""Planted mistakes in the oracle (on the CPU) must each fail at least one pin.
+
+Each mutant patches one step of oracle.ttt_oracle for the duration of a test:
+a plausible slip (a dropped term, a wrong sign, shift or index, a transposed
+operand, an off-by-one chunk). The pins must catch every one of them.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import oracle.ttt_oracle as ot
+from tests import pins
+
+
+def _loop_mutant(kind):
+    def one(x, ids, E_tgt, W_up, W_gate, W_entry, C, eta):
+        x = np.asarray(x, dtype=np.float64)
+        T = x.shape[0]
+        S = np.asarray(W_entry, dtype=np.float64).copy()
+        y = np.zeros((T, S.shape[0]))
+        if T == 0:
+            return y, S
+        Z = ot.gated_activation(x, W_up, W_gate)
+        V = ot.ntp_targets(ids, E_tgt)
+        S0 = S.copy()
+        ranges = ot.chunk_ranges(T, C)
+        for n, (s, e) in enumerate(ranges):
+            dW = eta * (V[s:e].T @ Z[s:e])
+            if kind == "update_then_apply":
+                S = S + dW
+                y[s:e] = Z[s:e] @ S.T
+                continue
+            if kind == "transposed_apply":
+                y[s:e] = Z[s:e] @ S  # only shape-valid when d == f
+            else:
+                y[s:e] = Z[s:e] @ S.T
+            if kind == "sign":
+                S = S - dW
+            elif kind == "mean":
+                S = S + dW / (e - s)
+            elif kind == "no_carry":
+                S = S0 + dW
+            elif kind == "no_eta":
+                S = S + dW / eta if eta != 0 else S
+            elif kind == "drop_last_update" and n == len(ranges) - 1:
+                pass
+            elif kind == "transposed_update":
+                S = S + eta * (Z[s:e].T @ V[s:e]).T.T if S.shape[0] == S.shape[1] else S + dW
+            else:
+                S = S + dW
+        return y, S
+    return one
+
+
+def _targets_shift(k):
+    def ntp(ids, E_tgt):
+        ids = np.asarray(ids)
+        E = np.asarray(E_tgt, dtype=np.float64)
+        T = ids.shape[0] - 1
+        V = np.zeros((T, E.shape[1]))
+        for t in range(T):
+            j = t + k
+            if 0 <= j <= T and 0 <= ids[j] < E.shape[0]:
+                V[t] = E[ids[j]]
+        return V
+    return ntp
+
+
+def _targets_clip(ids, E_tgt):
+    ids = np.asarray(ids)
+    E = np.asarray(E_tgt, dtype=np.float64)
+    nxt = np.clip(ids[1:], 0, E.shape[0] - 1)
+    return E[nxt]
+
+
+def _gate_on_up(x, W_up, W_gate):
+    x = np.asarray(x, dtype=np.float64)
+    return ot.silu(x @ np.asarray(W_up).T) * (x @ np.asarray(W_gate).T)
+
+
+def _no_silu(x, W_up, W_gate):
+    x = np.asarray(x, dtype=np.float64)
+    return (x @ np.asarray(W_gate).T) * (x @ np.asarray(W_up).T)
+
+
+def _chunks_plus_one(T, C):
+    return [(s, min(s + C + 1, T)) for s in range(0, T, C + 1)]
+
+
+def _chunks_overlap(T, C):
+    return [(max(0, s - 1), min(s + C, T)) for s in range(0, T, C)]
+
+
+def _sigmoid_wrong(g):
+    g = np.asarray(g, dtype=np.float64)
+    return g / (1.0 + np.exp(g))
+
+
+MUTANTS = {
+    "target_shift_0 (reconstruction)": ("ntp_targets", _targets_shift(0)),
+    "target_shift_2": ("ntp_targets", _targets_shift(2)),
+    "targets_clip_ids": ("ntp_targets", _targets_clip),
+    "silu_on_up_path": ("gated_activation", _gate_on_up),
+    "no_silu": ("gated_activation", _no_silu),
+    "silu_sign": ("silu", _sigmoid_wrong),
+    "chunks_of_C_plus_1": ("chunk_ranges", _chunks_plus_one),
+    "chunks_overlap": ("chunk_ranges", _chunks_overlap),
+    "update_then_apply": ("ttt_forward_one", _loop_mutant("update_then_apply")),
+    "update_sign": ("ttt_forward_one", _loop_mutant("sign")),
+    "update_mean": ("ttt_forward_one", _loop_mutant("mean")),
+    "no_state_carry": ("ttt_forward_one", _loop_mutant("no_carry")),
+    "no_eta": ("ttt_forward_one", _loop_mutant("no_eta")),
+    "drop_last_update": ("ttt_forward_one", _loop_mutant("drop_last_update")),
+    "transposed_apply": ("ttt_forward_one", _loop_mutant("transposed_apply")),
+}
+
+
+def _run_pins(fwd):
+    failures = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(fwd)
+        except (AssertionError, ValueError, IndexError) as e:
+            failures.append(str(e)[:80])
+    return failures
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    attr, repl = MUTANTS[name]
+    monkeypatch.setattr(ot, attr, repl)
+    failures = _run_pins(ot.ttt_forward)
+    assert failures, f"planted mistake '{name}' passed every pin"
+
+
+def test_unmutated_oracle_passes_all_pins():
+    assert _run_pins(oracle.ttt_forward) == []

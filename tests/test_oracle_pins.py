@@ -1,0 +1,51 @@
+"""The CPU oracle against its pins (closed forms, autograd, library special cases, invariants)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests import pins
+
+
+@pytest.mark.parametrize("pin", pins.ALL_PINS, ids=lambda p: getattr(p, "__name__", "pin"))
+def test_oracle_pin(pin):
+    pin(oracle.ttt_forward)
+
+
+def test_final_state_columns_match_full_state():
+    rng = np.random.default_rng(11)
+    x, ids, E, Wu, Wg, W0 = pins.tiny_case(rng, d=7, f=12, B=1, T=19)
+    _, W = oracle.ttt_forward(x, ids, E, Wu, Wg, W0, 4, 0.3)
+    cols = [0, 5, 11, 3]
+    Wc = oracle.final_state_columns(x[0], ids[0], E, Wu, Wg, W0, 4, 0.3, cols)
+    ref = pins.block_causal_closed_form(x[0], ids[0], E, Wu, Wg, W0, 4, 0.3)[1][:, cols]
+    assert np.max(np.abs(Wc - ref)) <= 1e-12 * np.max(np.abs(ref))
+    assert np.max(np.abs(Wc - W[0][:, cols])) <= 1e-12 * np.max(np.abs(ref))
+
+
+def test_chunk_ranges():
+    assert oracle.chunk_ranges(0, 4) == []
+    assert oracle.chunk_ranges(10, 4) == [(0, 4), (4, 8), (8, 10)]
+    assert oracle.chunk_ranges(8, 8) == [(0, 8)]
+    assert oracle.chunk_ranges(3, 100) == [(0, 3)]
+    with pytest.raises(ValueError):
+        oracle.chunk_ranges(5, 0)
+
+
+def test_empty_stream():
+    rng = np.random.default_rng(0)
+    x, ids, E, Wu, Wg, W0 = pins.tiny_case(rng, T=0)
+    y, W = oracle.ttt_forward(x, ids, E, Wu, Wg, W0, 4, 0.5)
+    assert y.shape == (1, 0, 6)
+    assert np.array_equal(W[0], W0)
+
+
+def test_silu_textbook_values():
+    # SiLU(0) = 0; SiLU(ln 3) = ln 3 * 3/4 (sigmoid(ln 3) = 3/4); odd part SiLU(g) - SiLU(-g) = g
+    g = np.array([0.0, np.log(3.0), -np.log(3.0), 2.5])
+    s = oracle.silu(g)
+    assert s[0] == 0.0
+    assert abs(s[1] - 0.75 * np.log(3.0)) < 1e-15
+    assert abs(s[2] + 0.25 * np.log(3.0)) < 1e-15
+    assert abs((oracle.silu(2.5) - oracle.silu(-2.5)) - 2.5) < 1e-14
+    assert np.allclose(s, torch.nn.functional.silu(torch.from_numpy(g)).numpy(), rtol=1e-15, atol=0)
