@@ -1,0 +1,46 @@
+// Layout and conversion helpers used at init, reset and for the eta = 0 case.
+#include "launch.h"
+
+namespace {
+
+// Wug row r: block r/64; rows 0..31 of a block are W_up rows 32*(r/64)+..., rows 32..63 the matching W_gate rows.
+__global__ __launch_bounds__(256) void k_interleave_ug(const bf16_t *Wu, const bf16_t *Wg, bf16_t *Wug, int f, int d) {
+  const int r = blockIdx.x;
+  const int blk = r >> 6, w = r & 63;
+  const bf16_t *src = (w < 32 ? Wu : Wg) + (long long)(blk * 32 + (w & 31)) * d;
+  bf16_t *dst = Wug + (long long)r * d;
+  for (int c = threadIdx.x * 8; c < d; c += 256 * 8)
+    *reinterpret_cast<uint4 *>(dst + c) = *reinterpret_cast<const uint4 *>(src + c);
+}
+
+__global__ __launch_bounds__(256) void k_bf16_to_f32(const bf16_t *src, float *dst, long long n) {
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256)
+    dst[i] = bf16_to_f32(src[i]);
+}
+
+__global__ __launch_bounds__(256) void k_f32_to_bf16(const float *src, bf16_t *dst, long long n) {
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256)
+    dst[i] = f32_to_bf16(src[i]);
+}
+
+unsigned grid_for(long long n) {
+  long long g = (n + 255) / 256;
+  return (unsigned)(g < 65536 ? (g > 0 ? g : 1) : 65536);
+}
+
+}  // namespace
+
+hipError_t launch_interleave_ug_bf16(const bf16_t *Wu, const bf16_t *Wg, bf16_t *Wug, int f, int d, hipStream_t s) {
+  hipLaunchKernelGGL(k_interleave_ug, dim3(2 * f), dim3(256), 0, s, Wu, Wg, Wug, f, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_bf16_to_f32(const bf16_t *src, float *dst, long long n, hipStream_t s) {
+  hipLaunchKernelGGL(k_bf16_to_f32, dim3(grid_for(n)), dim3(256), 0, s, src, dst, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_f32_to_bf16(const float *src, bf16_t *dst, long long n, hipStream_t s) {
+  hipLaunchKernelGGL(k_f32_to_bf16, dim3(grid_for(n)), dim3(256), 0, s, src, dst, n);
+  return hipGetLastError();
+}

@@ -1,0 +1,39 @@
+// Internal kernel launchers (host side). Not part of the C ABI.
+#pragma once
+
+#include "common.h"
+
+// ---- bf16 path: MFMA kernels (kernels_bf16.hip) ----
+// V^T[b][a][p] = E[ids[b][p+1]][a] for p < T and a valid id, else 0.     [B][d][T_pad]
+hipError_t launch_gather_vt_bf16(const int32_t *ids, const bf16_t *E, int vocab, bf16_t *VT, const Layout &lay,
+                                 hipStream_t s);
+// Z = SiLU(x W_gate^T) * (x W_up^T) -> Z [B][T_pad][f] and ZT = eta*Z^T [B][f][T_pad].
+// Wug: [2f][d], rows interleaved in blocks of 32 (32 up rows, then the matching 32 gate rows).
+hipError_t launch_a1_bf16(const bf16_t *x, const bf16_t *Wug, bf16_t *Z, bf16_t *ZT, float eta, int write_zt,
+                          const Layout &lay, hipStream_t s);
+// state[b] += sum_p ZT[b][:, p] VT[b][:, p]^T (as W[a][b] layout), snapshots snap[b][g] = bf16(state at p = g*L).
+hipError_t launch_update_bf16(const bf16_t *ZT, const bf16_t *VT, float *state, bf16_t *snap, const Layout &lay,
+                              hipStream_t s);
+// P[b][g][t][s] = eta * <Z[gL+t], Z[gL+s]> if s/C < t/C else 0, for t, s < L.
+hipError_t launch_scores_bf16(const bf16_t *Z, bf16_t *P, float eta, const Layout &lay, hipStream_t s);
+// y[b][gL+t] = Z[gL+t] snap[b][g]^T + sum_s P[b][g][t][s] V[gL+s].
+hipError_t launch_out_bf16(const bf16_t *Z, const bf16_t *P, const bf16_t *snap, const bf16_t *VT, bf16_t *y,
+                           const Layout &lay, hipStream_t s);
+
+// ---- fp32 path: FMA kernels (kernels_f32.hip), same buffers and meaning in fp32 ----
+hipError_t launch_gather_vt_f32(const int32_t *ids, const float *E, int vocab, float *VT, const Layout &lay,
+                                hipStream_t s);
+// Wug: [2][f][d] (W_up then W_gate).
+hipError_t launch_a1_f32(const float *x, const float *Wug, float *Z, float *ZT, float eta, int write_zt,
+                         const Layout &lay, hipStream_t s);
+hipError_t launch_update_f32(const float *ZT, const float *VT, float *state, float *snap, const Layout &lay,
+                             hipStream_t s);
+hipError_t launch_scores_f32(const float *Z, float *P, float eta, const Layout &lay, hipStream_t s);
+hipError_t launch_out_f32(const float *Z, const float *P, const float *snap, const float *VT, float *y,
+                          const Layout &lay, hipStream_t s);
+
+// ---- layout helpers (kernels_misc.hip) ----
+// Wug[2f][d] from W_up[f][d], W_gate[f][d]: 32-row blocks, up block then gate block.
+hipError_t launch_interleave_ug_bf16(const bf16_t *Wu, const bf16_t *Wg, bf16_t *Wug, int f, int d, hipStream_t s);
+hipError_t launch_bf16_to_f32(const bf16_t *src, float *dst, long long n, hipStream_t s);
+hipError_t launch_f32_to_bf16(const float *src, bf16_t *dst, long long n, hipStream_t s);

@@ -1,0 +1,402 @@
+// C ABI of the chunk-wise fast-weight library: handle, argument checks, the
+// token layout of a call, scratch management and the launch sequence.
+//
+// One call of ttt_forward_chunked runs, on the caller's stream:
+//   1. target gather      V^T = E_tgt[ids shifted by one]^T       (next-token target)
+//   2. up/gate GEMM       Z = SiLU(x W_gate^T) * (x W_up^T), and eta*Z^T
+//   3. state update       W += (eta Z)^T-weighted rank-C updates over the whole
+//                         block, the fp32 state resident in registers; a
+//                         snapshot of W at the start of every group of G chunks
+//   4. group scores       P = eta * (Z Z^T) masked to earlier chunks of the group
+//   5. output GEMM        y = Z snapshot^T + P V
+//   6. optional copy of the final states to W_final
+// Steps 3-5 are the exclusive prefix over chunk updates (iplexlaw.co.kr sec. 6;
+// paperlayer.ai App. B) taken at two levels: across groups through the
+// snapshots, inside a group through the block-causal term. The result equals
+// the sequential apply-then-update loop up to rounding.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <string>
+
+#include "../../include/ttt.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string &msg) {
+  g_err = msg;
+  return code;
+}
+
+#define HIP_TRY(expr)                                                                          \
+  do {                                                                                         \
+    hipError_t _e = (expr);                                                                    \
+    if (_e != hipSuccess) return fail(TTT_E_HIP, std::string(#expr) + ": " + hipGetErrorString(_e)); \
+  } while (0)
+
+constexpr int kMaxDim = 65536;
+constexpr int kMaxBatch = 4096;
+constexpr int kMaxT = 1 << 23;
+constexpr int kDefaultGroupTokens = 1024;
+
+int gcd_int(int a, int b) {
+  while (b) {
+    int t = a % b;
+    a = b;
+    b = t;
+  }
+  return a;
+}
+
+struct Plan {
+  int C;        // chunk length used for the call (C, or T when C >= T)
+  int G;        // chunks per group
+  int L;        // tokens per group
+  int ngroups;  // groups in the call
+  int T_pad;    // slots per sequence in scratch
+  int intra;    // a group holds more than one chunk
+};
+
+int make_plan(int T, int C, int G_override, Plan &p) {
+  if (T < 0 || T > kMaxT) return fail(TTT_E_SHAPE, "T out of range [0, 2^23]");
+  if (C < 1) return fail(TTT_E_SHAPE, "chunk length C must be >= 1");
+  if (G_override < 0) return fail(TTT_E_SHAPE, "group size G must be >= 0");
+  p.T_pad = (int)round_up_ll(T, 256);
+  if (T == 0) {
+    p.C = C;
+    p.G = 1;
+    p.L = 8;
+    p.ngroups = 0;
+    p.intra = 0;
+    return TTT_OK;
+  }
+  const int Ce = C < T ? C : T;
+  if (Ce == T) {  // a single chunk: one group, no within-group term
+    p.C = T;
+    p.G = 1;
+    p.L = (int)round_up_ll(T, 8);
+    p.ngroups = 1;
+    p.intra = 0;
+    return TTT_OK;
+  }
+  const int step = 8 / gcd_int(Ce, 8);
+  long long G;
+  if (G_override > 0) {
+    if (((long long)G_override * Ce) % 8 != 0)
+      return fail(TTT_E_SHAPE, "G*C must be a multiple of 8 (G=" + std::to_string(G_override) +
+                                   ", C=" + std::to_string(Ce) + ")");
+    G = G_override;
+  } else {
+    G = (kDefaultGroupTokens + Ce / 2) / Ce;
+    if (G < 1) G = 1;
+    G = round_up_ll(G, step);
+  }
+  const long long L = G * Ce;
+  p.C = Ce;
+  p.G = (int)(G < (1 << 30) ? G : (1 << 30));
+  if (L >= T) {  // one group; its length only needs to cover T
+    p.L = (int)round_up_ll(T, 8);
+    p.ngroups = 1;
+  } else {
+    p.L = (int)L;
+    p.ngroups = (int)((T + L - 1) / L);
+  }
+  p.intra = G > 1 ? 1 : 0;
+  return TTT_OK;
+}
+
+}  // namespace
+
+struct ttt_handle {
+  int d = 0, f = 0, C = 0, max_batch = 0, G_override = 0, device = 0;
+  float eta = 0.f;
+  ttt_dtype dt = TTT_BF16;
+  void *Wug = nullptr;      // bf16: [2f][d] interleaved; f32: [2][f][d]
+  float *W0 = nullptr;      // [d][f] fp32 image of W_down0
+  float *state = nullptr;   // [max_batch][d][f]
+  void *ws = nullptr;       // scratch
+  size_t ws_bytes = 0;
+  size_t fixed_bytes = 0;
+  bool profiling = false, events_made = false, timed = false;
+  hipEvent_t ev[7] = {};
+};
+
+namespace {
+
+int check_device(int *dev_out) {
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) return fail(TTT_E_NODEV, "no HIP device visible");
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  hipDeviceProp_t prop;
+  HIP_TRY(hipGetDeviceProperties(&prop, dev));
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(TTT_E_NODEV, std::string("device is ") + prop.gcnArchName + ", this library runs on gfx950 only");
+  *dev_out = dev;
+  return TTT_OK;
+}
+
+void free_handle(ttt_handle *h) {
+  if (!h) return;
+  (void)hipDeviceSynchronize();
+  if (h->Wug) (void)hipFree(h->Wug);
+  if (h->W0) (void)hipFree(h->W0);
+  if (h->state) (void)hipFree(h->state);
+  if (h->ws) (void)hipFree(h->ws);
+  if (h->events_made)
+    for (auto &e : h->ev) (void)hipEventDestroy(e);
+  delete h;
+}
+
+struct Scratch {
+  void *VT, *Z, *ZT, *snap, *P;
+  size_t total;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+Scratch scratch_layout(const ttt_handle *h, int B, const Plan &pl, bool need_zt, bool need_p) {
+  const size_t es = h->dt == TTT_BF16 ? 2 : 4;
+  const size_t vt = align256(es * (size_t)B * h->d * pl.T_pad);
+  const size_t z = align256(es * (size_t)B * pl.T_pad * h->f);
+  const size_t zt = need_zt ? z : 0;
+  const size_t sn = align256(es * (size_t)B * pl.ngroups * h->d * h->f);
+  const size_t pp = need_p ? align256(es * (size_t)B * pl.ngroups * pl.L * pl.L) : 0;
+  Scratch s;
+  size_t off = 0;
+  s.VT = (void *)off;
+  off += vt;
+  s.Z = (void *)off;
+  off += z;
+  s.ZT = (void *)off;
+  off += zt;
+  s.snap = (void *)off;
+  off += sn;
+  s.P = (void *)off;
+  off += pp;
+  s.total = off;
+  return s;
+}
+
+void *at(void *base, void *off) { return (char *)base + (size_t)off; }
+
+}  // namespace
+
+extern "C" {
+
+const char *ttt_last_error(void) { return g_err.c_str(); }
+
+int ttt_plan(int T, int C, int G_override, int *G, int *L, int *ngroups, int *T_pad) {
+  Plan p;
+  int rc = make_plan(T, C, G_override, p);
+  if (rc) return rc;
+  if (G) *G = p.G;
+  if (L) *L = p.L;
+  if (ngroups) *ngroups = p.ngroups;
+  if (T_pad) *T_pad = p.T_pad;
+  return TTT_OK;
+}
+
+int ttt_init(ttt_handle **out, const void *W_up, const void *W_gate, const void *W_down0, int d, int f, int C,
+             float eta, ttt_dtype dt, int max_batch, void *hip_stream) {
+  if (!out) return fail(TTT_E_NULL, "out is NULL");
+  *out = nullptr;
+  if (!W_up || !W_gate || !W_down0) return fail(TTT_E_NULL, "W_up, W_gate and W_down0 must be non-NULL");
+  if (dt != TTT_F32 && dt != TTT_BF16) return fail(TTT_E_DTYPE, "dtype must be TTT_F32 or TTT_BF16");
+  if (d < 64 || f < 64 || d > kMaxDim || f > kMaxDim || d % 64 || f % 64)
+    return fail(TTT_E_SHAPE, "d and f must be multiples of 64 in [64, 65536]");
+  if (dt == TTT_BF16 && (d % 256 || f % 256))
+    return fail(TTT_E_SHAPE, "the bf16 path needs d and f to be multiples of 256");
+  if (C < 1) return fail(TTT_E_SHAPE, "chunk length C must be >= 1");
+  if (!std::isfinite(eta)) return fail(TTT_E_ARG, "eta must be finite");
+  if (max_batch < 1 || max_batch > kMaxBatch) return fail(TTT_E_SHAPE, "max_batch must be in [1, 4096]");
+  int dev = 0;
+  int rc = check_device(&dev);
+  if (rc) return rc;
+
+  hipStream_t s = (hipStream_t)hip_stream;
+  ttt_handle *h = new ttt_handle();
+  h->d = d;
+  h->f = f;
+  h->C = C;
+  h->eta = eta;
+  h->dt = dt;
+  h->max_batch = max_batch;
+  h->device = dev;
+  const size_t es = dt == TTT_BF16 ? 2 : 4;
+  const size_t df = (size_t)d * f;
+  auto bail = [&](int code, const std::string &m) {
+    free_handle(h);
+    return fail(code, m);
+  };
+  if (hipMalloc(&h->Wug, 2 * df * es) != hipSuccess) return bail(TTT_E_NOMEM, "allocating W_up/W_gate copy");
+  if (hipMalloc((void **)&h->W0, df * 4) != hipSuccess) return bail(TTT_E_NOMEM, "allocating W_down0 image");
+  if (hipMalloc((void **)&h->state, df * 4 * max_batch) != hipSuccess)
+    return bail(TTT_E_NOMEM, "allocating fast-weight states");
+  h->fixed_bytes = 2 * df * es + df * 4 + df * 4 * max_batch;
+  hipError_t e = hipSuccess;
+  if (dt == TTT_BF16) {
+    e = launch_interleave_ug_bf16((const bf16_t *)W_up, (const bf16_t *)W_gate, (bf16_t *)h->Wug, f, d, s);
+    if (e == hipSuccess) e = launch_bf16_to_f32((const bf16_t *)W_down0, h->W0, (long long)df, s);
+  } else {
+    e = hipMemcpyAsync(h->Wug, W_up, df * 4, hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync((float *)h->Wug + df, W_gate, df * 4, hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(h->W0, W_down0, df * 4, hipMemcpyDeviceToDevice, s);
+  }
+  for (int b = 0; b < max_batch && e == hipSuccess; ++b)
+    e = hipMemcpyAsync(h->state + (size_t)b * df, h->W0, df * 4, hipMemcpyDeviceToDevice, s);
+  if (e != hipSuccess) return bail(TTT_E_HIP, std::string("init copies: ") + hipGetErrorString(e));
+  *out = h;
+  return TTT_OK;
+}
+
+int ttt_set_group_chunks(ttt_handle *h, int G) {
+  if (!h) return fail(TTT_E_NULL, "handle is NULL");
+  if (G < 0) return fail(TTT_E_SHAPE, "G must be >= 0");
+  if (G > 0 && ((long long)G * h->C) % 8 != 0) return fail(TTT_E_SHAPE, "G*C must be a multiple of 8");
+  h->G_override = G;
+  return TTT_OK;
+}
+
+int ttt_set_profiling(ttt_handle *h, int on) {
+  if (!h) return fail(TTT_E_NULL, "handle is NULL");
+  if (on && !h->events_made) {
+    for (auto &e : h->ev) HIP_TRY(hipEventCreate(&e));
+    h->events_made = true;
+  }
+  h->profiling = on != 0;
+  h->timed = false;
+  return TTT_OK;
+}
+
+int ttt_phase_times(ttt_handle *h, float *ms, int n) {
+  if (!h || !ms) return fail(TTT_E_NULL, "handle or ms is NULL");
+  if (n < 0 || n > 6) return fail(TTT_E_ARG, "n must be in [0, 6]");
+  if (!h->timed) return fail(TTT_E_ARG, "no profiled forward call yet (enable ttt_set_profiling first)");
+  HIP_TRY(hipEventSynchronize(h->ev[6]));
+  for (int i = 0; i < n; ++i) {
+    float t = 0.f;
+    HIP_TRY(hipEventElapsedTime(&t, h->ev[i], h->ev[i + 1]));
+    ms[i] = t;
+  }
+  return TTT_OK;
+}
+
+int ttt_workspace_bytes(ttt_handle *h, size_t *bytes) {
+  if (!h || !bytes) return fail(TTT_E_NULL, "handle or bytes is NULL");
+  *bytes = h->fixed_bytes + h->ws_bytes;
+  return TTT_OK;
+}
+
+int ttt_reset(ttt_handle *h, int b, void *hip_stream) {
+  if (!h) return fail(TTT_E_NULL, "handle is NULL");
+  if (b < -1 || b >= h->max_batch) return fail(TTT_E_ARG, "batch index out of range");
+  hipStream_t s = (hipStream_t)hip_stream;
+  const size_t df = (size_t)h->d * h->f;
+  const int lo = b < 0 ? 0 : b, hi = b < 0 ? h->max_batch : b + 1;
+  for (int i = lo; i < hi; ++i)
+    HIP_TRY(hipMemcpyAsync(h->state + (size_t)i * df, h->W0, df * 4, hipMemcpyDeviceToDevice, s));
+  return TTT_OK;
+}
+
+void ttt_destroy(ttt_handle *h) { free_handle(h); }
+
+int ttt_forward_chunked(ttt_handle *h, const void *x, const int32_t *ids, const void *E_tgt, int vocab, int B, int T,
+                        void *y, float *W_final, void *hip_stream) {
+  if (!h) return fail(TTT_E_NULL, "handle is NULL");
+  if (B < 0 || B > h->max_batch) return fail(TTT_E_SHAPE, "B must be in [0, max_batch]");
+  if (T < 0 || T > kMaxT) return fail(TTT_E_SHAPE, "T must be in [0, 2^23]");
+  if (B > 0 && T > 0 && (!x || !ids || !E_tgt || !y)) return fail(TTT_E_NULL, "x, ids, E_tgt and y must be non-NULL");
+  if (B > 0 && T > 0 && vocab < 1) return fail(TTT_E_SHAPE, "vocab must be >= 1");
+  const bool learn = h->eta != 0.f;
+  Plan pl;
+  int rc = make_plan(T, h->C, learn ? h->G_override : 0, pl);
+  if (rc) return rc;
+  if (!learn && pl.ngroups > 0) {  // no updates: one group, the entry state serves every chunk
+    pl.ngroups = 1;
+    pl.L = (int)round_up_ll(T, 8);
+    pl.intra = 0;
+  }
+  hipStream_t s = (hipStream_t)hip_stream;
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  if (dev != h->device) return fail(TTT_E_ARG, "current device differs from the handle's device");
+  const size_t df = (size_t)h->d * h->f;
+  const bool prof = h->profiling;
+  if (prof) HIP_TRY(hipEventRecord(h->ev[0], s));
+  if (B == 0 || T == 0) {
+    if (prof) {
+      for (int i = 1; i < 7; ++i) HIP_TRY(hipEventRecord(h->ev[i], s));
+      h->timed = true;
+    }
+    if (W_final && B > 0)
+      HIP_TRY(hipMemcpyAsync(W_final, h->state, (size_t)B * df * 4, hipMemcpyDeviceToDevice, s));
+    return TTT_OK;
+  }
+
+  Scratch sc = scratch_layout(h, B, pl, learn, learn && pl.intra);
+  if (sc.total > h->ws_bytes) {
+    HIP_TRY(hipStreamSynchronize(s));
+    HIP_TRY(hipDeviceSynchronize());
+    if (h->ws) HIP_TRY(hipFree(h->ws));
+    h->ws = nullptr;
+    h->ws_bytes = 0;
+    if (hipMalloc(&h->ws, sc.total) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(TTT_E_NOMEM, "allocating " + std::to_string(sc.total) + " bytes of scratch");
+    }
+    h->ws_bytes = sc.total;
+  }
+  Layout lay{B, T, pl.T_pad, pl.C, pl.L, pl.ngroups, h->d, h->f, learn ? pl.intra : 0};
+  void *VT = at(h->ws, sc.VT), *Z = at(h->ws, sc.Z), *ZT = at(h->ws, sc.ZT), *snap = at(h->ws, sc.snap),
+       *P = at(h->ws, sc.P);
+
+  if (h->dt == TTT_BF16) {
+    if (learn || lay.intra) HIP_TRY(launch_gather_vt_bf16(ids, (const bf16_t *)E_tgt, vocab, (bf16_t *)VT, lay, s));
+    if (prof) HIP_TRY(hipEventRecord(h->ev[1], s));
+    HIP_TRY(launch_a1_bf16((const bf16_t *)x, (const bf16_t *)h->Wug, (bf16_t *)Z, (bf16_t *)ZT, h->eta,
+                           learn ? 1 : 0, lay, s));
+    if (prof) HIP_TRY(hipEventRecord(h->ev[2], s));
+    if (learn) {
+      HIP_TRY(launch_update_bf16((const bf16_t *)ZT, (const bf16_t *)VT, h->state, (bf16_t *)snap, lay, s));
+    } else {
+      for (int b = 0; b < B; ++b)
+        HIP_TRY(launch_f32_to_bf16(h->state + (size_t)b * df, (bf16_t *)snap + (size_t)b * df, (long long)df, s));
+    }
+    if (prof) HIP_TRY(hipEventRecord(h->ev[3], s));
+    if (lay.intra) HIP_TRY(launch_scores_bf16((const bf16_t *)Z, (bf16_t *)P, h->eta, lay, s));
+    if (prof) HIP_TRY(hipEventRecord(h->ev[4], s));
+    HIP_TRY(launch_out_bf16((const bf16_t *)Z, (const bf16_t *)P, (const bf16_t *)snap, (const bf16_t *)VT,
+                            (bf16_t *)y, lay, s));
+  } else {
+    if (learn || lay.intra) HIP_TRY(launch_gather_vt_f32(ids, (const float *)E_tgt, vocab, (float *)VT, lay, s));
+    if (prof) HIP_TRY(hipEventRecord(h->ev[1], s));
+    HIP_TRY(launch_a1_f32((const float *)x, (const float *)h->Wug, (float *)Z, (float *)ZT, h->eta, learn ? 1 : 0,
+                          lay, s));
+    if (prof) HIP_TRY(hipEventRecord(h->ev[2], s));
+    if (learn) {
+      HIP_TRY(launch_update_f32((const float *)ZT, (const float *)VT, h->state, (float *)snap, lay, s));
+    } else {
+      HIP_TRY(hipMemcpyAsync(snap, h->state, (size_t)B * df * 4, hipMemcpyDeviceToDevice, s));
+    }
+    if (prof) HIP_TRY(hipEventRecord(h->ev[3], s));
+    if (lay.intra) HIP_TRY(launch_scores_f32((const float *)Z, (float *)P, h->eta, lay, s));
+    if (prof) HIP_TRY(hipEventRecord(h->ev[4], s));
+    HIP_TRY(launch_out_f32((const float *)Z, (const float *)P, (const float *)snap, (const float *)VT, (float *)y,
+                           lay, s));
+  }
+  if (prof) HIP_TRY(hipEventRecord(h->ev[5], s));
+  if (W_final) HIP_TRY(hipMemcpyAsync(W_final, h->state, (size_t)B * df * 4, hipMemcpyDeviceToDevice, s));
+  if (prof) {
+    HIP_TRY(hipEventRecord(h->ev[6], s));
+    h->timed = true;
+  }
+  return TTT_OK;
+}
+
+}  // extern "C"

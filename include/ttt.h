@@ -1,0 +1,165 @@
+/*
+ * ttt.h — C ABI of the MI355X (gfx950) chunk-wise fast-weight library.
+ *
+ * The library runs the hot path of In-Place Test-Time Training for one gated
+ * MLP layer whose final projection W_down is the fast weight (paperlayer.ai
+ * summary, sec. 3 "In-Place Adaptation"; iplexlaw.co.kr walkthrough, sec. 2):
+ *
+ *   Z        = SiLU(x W_gate^T) * (x W_up^T)          (W_up, W_gate frozen)
+ *   V[t]     = E_tgt[ids[t+1]]                         (next-token target row)
+ *   chunk i  : y[chunk i] = Z[chunk i] W_{i-1}^T       (apply, pre-update state)
+ *              W_i = W_{i-1} + eta V[chunk i]^T Z[chunk i]   (update)
+ *
+ * The update rule is the pages' simplified form dW_down = eta V^T Z
+ * (iplexlaw sec. 2 and sec. 4); apply-then-update over non-overlapping chunks
+ * follows iplexlaw sec. 3 and paperlayer sec. 3 "Chunk-Wise Updates"; the
+ * target is V^ = Conv1D(X0) W_target with the kernel reduced to the next-token
+ * tap and W_target folded into E_tgt (paperlayer sec. 3 "LM-Aligned
+ * Objective"); state reset at document ends follows paperlayer App. B.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers on the current HIP device,
+ *     row-major, densely packed, owned by the caller. They must stay valid
+ *     until the work queued on `hip_stream` has completed.
+ *   - `hip_stream` is a hipStream_t (NULL = the default stream). Work is
+ *     queued asynchronously; no call synchronises the host except where noted.
+ *   - Argument errors are detected before any device work is queued.
+ *   - Return value 0 = success; a negative TTT_E_* code otherwise, with a
+ *     message available from ttt_last_error() (thread-local).
+ *   - No C++ exception crosses the ABI. A handle is not thread-safe: calls on
+ *     one handle must come from one thread at a time and, when they are on
+ *     different streams, be ordered by the caller.
+ *   - Only gfx950 devices are accepted (TTT_E_NODEV otherwise).
+ */
+#ifndef TTT_H
+#define TTT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ttt_handle ttt_handle; /* opaque, owned by the library */
+
+/* Activation/weight element type. The fast-weight state is always fp32.
+ * TTT_F32:  x, W_up, W_gate, W_down0, E_tgt and y are float.
+ * TTT_BF16: they are bfloat16 (uint16 bit patterns); matrix products run on
+ *           bf16 MFMA with fp32 accumulation. */
+typedef enum { TTT_F32 = 0, TTT_BF16 = 1 } ttt_dtype;
+
+enum {
+  TTT_OK = 0,
+  TTT_E_NULL = -1,  /* a required pointer is NULL                           */
+  TTT_E_SHAPE = -2, /* a size is out of range or violates an alignment rule */
+  TTT_E_DTYPE = -3, /* unknown dtype                                         */
+  TTT_E_NOMEM = -4, /* device allocation failed                              */
+  TTT_E_HIP = -5,   /* a HIP runtime call or kernel launch failed            */
+  TTT_E_NODEV = -6, /* no device, or the current device is not gfx950        */
+  TTT_E_ARG = -7    /* other invalid argument (e.g. batch index, non-finite eta) */
+};
+
+/*
+ * ttt_init — create a handle for one layer.
+ *
+ *   W_up, W_gate : [f][d] frozen up and gate projections (dtype `dt`).
+ *   W_down0      : [d][f] initial fast weight (dtype `dt`).
+ *   d, f         : model width and hidden width, at most 65536; multiples of
+ *                  64 on the fp32 path and of 256 on the bf16 path (the MFMA
+ *                  kernels work on whole 256 x 256 tiles of the state).
+ *   C            : chunk length in tokens, C >= 1. Chunks are counted from the
+ *                  first token of each ttt_forward_chunked call.
+ *   eta          : learning rate of the update (finite).
+ *   max_batch    : number of independent sequences (fast-weight states) the
+ *                  handle holds, 1 .. 4096.
+ *
+ * The library copies the weights into buffers it owns (re-laid out for its
+ * kernels) and keeps an fp32 image of W_down0. Every state starts equal to
+ * W_down0. The caller may free its weight buffers once the queued copies have
+ * completed on `hip_stream`. On success *out receives the handle; on failure
+ * *out is set to NULL and nothing is leaked.
+ */
+int ttt_init(ttt_handle **out, const void *W_up, const void *W_gate, const void *W_down0, int d, int f,
+             int C, float eta, ttt_dtype dt, int max_batch, void *hip_stream);
+
+/*
+ * ttt_forward_chunked — run the chunk-wise apply-then-update scan over one
+ * block of tokens for sequences 0 .. B-1.
+ *
+ *   x       : [B][T][d] layer input (dtype of the handle).
+ *   ids     : [B][T+1] int32 token ids; ids[b][t] is the token at position t
+ *             and ids[b][T] the look-ahead token after the block. The target
+ *             of position t is row ids[b][t+1] of E_tgt; an id outside
+ *             [0, vocab) (e.g. -1 at a document end) gives a zero target row.
+ *   E_tgt   : [vocab][d] target-embedding table (dtype of the handle).
+ *   B       : 0 .. max_batch. T: tokens per sequence, 0 .. 2^23.
+ *   y       : [B][T][d] output (dtype of the handle), written in full.
+ *   W_final : optional [B][d][f] fp32 output; receives each sequence's state
+ *             after the block (NULL = not wanted).
+ *
+ * Each sequence starts from its current state (W_down0 after init or reset,
+ * else what the previous call left) and keeps the final state in the handle,
+ * so consecutive calls continue one stream (the last chunk of a call may be
+ * short; to continue chunking seamlessly, make T a multiple of C). Scratch
+ * memory is allocated by the library on first use and grown when B*T grows;
+ * that allocation is the only point where this call may block the host.
+ */
+int ttt_forward_chunked(ttt_handle *h, const void *x, const int32_t *ids, const void *E_tgt, int vocab, int B,
+                        int T, void *y, float *W_final, void *hip_stream);
+
+/*
+ * ttt_reset — restore the fast weight of sequence b (or of every sequence if
+ * b == -1) to W_down0: the document-boundary reset (paperlayer App. B;
+ * iplexlaw sec. 6). Queued on `hip_stream`.
+ */
+int ttt_reset(ttt_handle *h, int b, void *hip_stream);
+
+/* ttt_destroy — free the handle and everything it owns (synchronises the device). NULL is a no-op. */
+void ttt_destroy(ttt_handle *h);
+
+/* ttt_last_error — message for the last nonzero return on this thread ("" if none). */
+const char *ttt_last_error(void);
+
+/*
+ * ttt_set_group_chunks — tuning knob of the two-level scan (no effect on the
+ * result beyond rounding). The library keeps each state resident across the
+ * whole block of tokens and takes a snapshot of it (bf16 on the bf16 path,
+ * fp32 on the fp32 path) at the start of every group of G chunks; the outputs
+ * of a group are formed from its snapshot plus the block-causal term of the
+ * earlier chunks inside the group. This is the pages' exclusive prefix over
+ * chunk updates (iplexlaw sec. 6; paperlayer App. B) taken at two levels.
+ * G = 0 restores the default (about 1024 tokens per group). G*C must be a
+ * multiple of 8; TTT_E_SHAPE otherwise.
+ */
+int ttt_set_group_chunks(ttt_handle *h, int G);
+
+/*
+ * ttt_plan — host-only query of the layout a call with T tokens and chunk C
+ * would use (no device work; usable without a GPU):
+ *   *G       : chunks per snapshot group;  *L = G*C tokens per group;
+ *   *ngroups : groups in the call (ceil(T / L));
+ *   *T_pad   : token slots per sequence in the scratch buffers (T rounded up to 256).
+ * When C >= T the call is a single chunk and C is taken as T.
+ * Any output pointer may be NULL. `G_override` as in ttt_set_group_chunks.
+ */
+int ttt_plan(int T, int C, int G_override, int *G, int *L, int *ngroups, int *T_pad);
+
+/*
+ * ttt_set_profiling / ttt_phase_times — per-phase device timing of the most
+ * recent ttt_forward_chunked, from HIP events recorded on its stream.
+ * Phases: 0 target gather, 1 up/gate GEMM + SwiGLU, 2 state update with
+ * snapshots, 3 within-group scores, 4 output GEMM, 5 final-state copy.
+ * ttt_phase_times waits for the last event and writes `n` (<= 6)
+ * milliseconds to ms[]; phases that did not run read 0.
+ */
+int ttt_set_profiling(ttt_handle *h, int on);
+int ttt_phase_times(ttt_handle *h, float *ms, int n);
+
+/* ttt_workspace_bytes — device bytes the handle currently owns (weights, states, scratch). */
+int ttt_workspace_bytes(ttt_handle *h, size_t *bytes);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TTT_H */
