@@ -1,0 +1,188 @@
+"""Benchmark: chunk-wise In-Place TTT over a 128k-token stream on one MI355X.
+
+A step is one full pass of the hot path (target gather, up/gate GEMM + SwiGLU,
+state update with snapshots, within-group scores, output GEMM) over one batch
+of synthetic input, starting from a reset fast weight. Inputs are resident in
+HBM before timing starts. Prints ONE JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--chunk C] [--no-sweep] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "TTT-MLP tokens/s per layer at d=2560/ff=9728, 128k ctx; MFMA % of peak"
+WORKLOAD = "c4_4b_128k"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--chunk", type=int, default=256)
+    ap.add_argument("--seq-len", type=int, default=None, help="override T (default: the workload's 131072)")
+    ap.add_argument("--group-chunks", type=int, default=0)
+    ap.add_argument("--no-sweep", action="store_true", help="skip the C=128 leg of the chunk sweep")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-baseline duration")
+    return ap.parse_args()
+
+
+def algorithmic_flops(d, f, tokens):
+    # per token: up/gate 4df, output 2df, update 2df
+    return {"up_gate_swiglu": 4.0 * d * f * tokens, "update_snapshots": 2.0 * d * f * tokens,
+            "group_scores": 0.0, "output": 2.0 * d * f * tokens}
+
+
+def run_gpu(w, C, steps, warmup, G):
+    import numpy as np
+    import torch
+
+    import chunk_wise_weight_amd as ttt
+
+    dt = torch.bfloat16
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to("cuda", dt)
+
+    h = ttt.ttt_init(dev(w.W_up), dev(w.W_gate), dev(w.W_down0), C, w.eta, max_batch=w.B)
+    if G:
+        ttt.ttt_set_group_chunks(h, G)
+    x, E = dev(w.x), dev(w.E_tgt)
+    ids = torch.from_numpy(np.ascontiguousarray(w.ids)).cuda()
+    y = torch.empty((w.B, w.T, w.d), dtype=dt, device="cuda")
+    ttt.ttt_set_profiling(h, True)
+    for _ in range(warmup):
+        ttt.ttt_reset(h)
+        ttt.ttt_forward_chunked(h, x, ids, E, y=y)
+    torch.cuda.synchronize()
+    phase_sum = [0.0] * 6
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(steps):
+        ttt.ttt_reset(h)
+        ttt.ttt_forward_chunked(h, x, ids, E, y=y)
+        ph = ttt.ttt_phase_times(h)  # waits for this step's last event
+        phase_sum = [a + b for a, b in zip(phase_sum, ph)]
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = ev0.elapsed_time(ev1)
+    plan = ttt.ttt_plan(w.T, C, G)
+    ws = ttt.ttt_workspace_bytes(h)
+    ttt.ttt_destroy(h)
+    del x, E, ids, y
+    torch.cuda.empty_cache()
+    return {"wall_s": wall, "event_ms": ev_ms, "phase_ms": [p / steps for p in phase_sum], "plan": plan,
+            "workspace_bytes": ws}
+
+
+def cpu_baseline(w, C, target_s):
+    """The oracle as it stands, on the first S tokens of sequence 0 (a bounded sample)."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+
+    def run(S):
+        ids = w.ids[0, :S + 1]
+        uniq, inv = np.unique(ids, return_inverse=True)
+        E_s = w.E_tgt[uniq]  # the target rows this sample uses, ids remapped onto them
+        t0 = time.perf_counter()
+        oracle.ttt_forward_one(w.x[0, :S], inv.astype(np.int64), E_s, w.W_up, w.W_gate, w.W_down0, C, w.eta)
+        return time.perf_counter() - t0
+
+    S = 2 * C
+    t = run(S)
+    while t < target_s / 3 and S * 2 <= min(w.T, 16384):
+        S *= 2
+        t = run(S)
+    return {"value": S / t, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {S} tokens of sequence 0 ({S // C} chunks of {C}), full layer shape "
+                      f"d={w.d} f={w.f}, fp64 NumPy oracle, target rows gathered to the ids used; {t:.1f} s"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build runs the fast-weight path on a single MI355X "
+              "(multi-GPU sharding is a design note, not built). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from synth import make_config
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    t0 = time.perf_counter()
+    w = make_config(WORKLOAD, C=a.chunk, T=a.seq_len)
+    print(f"[bench] inputs {WORKLOAD} d={w.d} f={w.f} B={w.B} T={w.T} generated in "
+          f"{time.perf_counter() - t0:.1f}s", file=sys.stderr, flush=True)
+    tokens = w.B * w.T
+    flops = algorithmic_flops(w.d, w.f, tokens)
+    total_flops = sum(flops.values())
+
+    r = run_gpu(w, a.chunk, a.steps, a.warmup, a.group_chunks)
+    ms = r["event_ms"] / a.steps
+    names = ["gather", "up_gate_swiglu", "update_snapshots", "group_scores", "output", "final_copy"]
+    phases = dict(zip(names, r["phase_ms"]))
+    print(f"[bench] C={a.chunk}: {ms:.2f} ms/step, phases " +
+          ", ".join(f"{k} {v:.3f}" for k, v in phases.items()), file=sys.stderr, flush=True)
+    dom = max(("up_gate_swiglu", "update_snapshots", "output"), key=lambda k: phases[k])
+    achieved = flops[dom] / (phases[dom] * 1e-3) / 1e12
+    scan_ms = phases["update_snapshots"] + phases["group_scores"] + phases["output"]
+    out = {
+        "metric": METRIC,
+        "value": tokens / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{WORKLOAD}: single SwiGLU MLP layer, fast W_down, bf16 with fp32 state",
+                   "d_model": w.d, "d_ff": w.f, "batch": w.B, "seq_len": w.T, "chunk": a.chunk, "eta": w.eta,
+                   "group_chunks": r["plan"]["G"], "group_tokens": r["plan"]["L"], "parallelism": "single GPU"},
+        "mfma_frac_layer": total_flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "mfma_frac_scan_gemms": (flops["update_snapshots"] + flops["output"]) / (scan_ms * 1e-3) / 1e12
+        / PEAK_BF16_TFLOPS,
+        "phase_ms": phases,
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None},
+        "workspace_gb": r["workspace_bytes"] / 1e9,
+    }
+    if not a.no_sweep and a.chunk != 128:
+        w.C = 128
+        r2 = run_gpu(w, 128, a.steps, a.warmup, 0)
+        ms2 = r2["event_ms"] / a.steps
+        out["chunk_sweep"] = {"C128": {"tokens_per_s": tokens / (ms2 * 1e-3), "ms_per_step": ms2,
+                                       "mfma_frac_layer": total_flops / (ms2 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                                       "phase_ms": dict(zip(names, r2["phase_ms"]))}}
+        w.C = a.chunk
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, a.chunk, a.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
