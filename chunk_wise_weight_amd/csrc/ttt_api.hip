@@ -42,6 +42,8 @@ constexpr int kMaxDim = 65536;
 constexpr int kMaxBatch = 4096;
 constexpr int kMaxT = 1 << 23;
 constexpr int kDefaultGroupTokens = 1024;
+// group starts fall on the update kernel's 32-token stage boundaries
+constexpr int kGroupAlign = 32;
 
 int gcd_int(int a, int b) {
   while (b) {
@@ -83,11 +85,11 @@ int make_plan(int T, int C, int G_override, Plan &p) {
     p.intra = 0;
     return TTT_OK;
   }
-  const int step = 8 / gcd_int(Ce, 8);
+  const int step = kGroupAlign / gcd_int(Ce, kGroupAlign);
   long long G;
   if (G_override > 0) {
-    if (((long long)G_override * Ce) % 8 != 0)
-      return fail(TTT_E_SHAPE, "G*C must be a multiple of 8 (G=" + std::to_string(G_override) +
+    if (((long long)G_override * Ce) % kGroupAlign != 0)
+      return fail(TTT_E_SHAPE, "G*C must be a multiple of 32 (G=" + std::to_string(G_override) +
                                    ", C=" + std::to_string(Ce) + ")");
     G = G_override;
   } else {
@@ -258,7 +260,7 @@ int ttt_init(ttt_handle **out, const void *W_up, const void *W_gate, const void 
 int ttt_set_group_chunks(ttt_handle *h, int G) {
   if (!h) return fail(TTT_E_NULL, "handle is NULL");
   if (G < 0) return fail(TTT_E_SHAPE, "G must be >= 0");
-  if (G > 0 && ((long long)G * h->C) % 8 != 0) return fail(TTT_E_SHAPE, "G*C must be a multiple of 8");
+  if (G > 0 && ((long long)G * h->C) % kGroupAlign != 0) return fail(TTT_E_SHAPE, "G*C must be a multiple of 32");
   h->G_override = G;
   return TTT_OK;
 }

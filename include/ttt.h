@@ -129,8 +129,9 @@ const char *ttt_last_error(void);
  * of a group are formed from its snapshot plus the block-causal term of the
  * earlier chunks inside the group. This is the pages' exclusive prefix over
  * chunk updates (iplexlaw sec. 6; paperlayer App. B) taken at two levels.
- * G = 0 restores the default (about 1024 tokens per group). G*C must be a
- * multiple of 8; TTT_E_SHAPE otherwise.
+ * G = 0 restores the default (about 1024 tokens per group, rounded so that
+ * G*C is a multiple of 32). G*C must be a multiple of 32; TTT_E_SHAPE
+ * otherwise.
  */
 int ttt_set_group_chunks(ttt_handle *h, int G);
 
