@@ -1,23 +1,27 @@
 // bf16 MFMA kernels of the chunk-wise fast-weight path (gfx950).
 //
 // Every contraction is written as D[i][j] = sum_k A[i][k] * B[j][k] with both
-// operands K-contiguous ("NT" form). A block computes a 256 x 256 tile with 4
-// waves (2 x 2), each wave 128 x 128 as 4 x 4 tiles of v_mfma_f32_32x32x16_bf16
-// with fp32 accumulators (256 AGPRs per lane).
+// operands K-contiguous ("NT" form). A block has 2 x WN waves; each wave
+// computes 128 x (32*NBJ) with v_mfma_f32_32x32x16_bf16 and fp32 accumulators
+// in AGPRs. The wide GEMMs use 8 waves (WN = 4, NBJ = 2: 256 x 256 tiles, two
+// waves per SIMD so one can issue MFMAs while the other waits); the state
+// update uses 4 waves (WN = 2, NBJ = 2: 256 x 128 tiles).
 //
-// K advances in stages of 32 through a ring of 4 LDS stages (32 KB each, 128
-// KB in all): while a stage is multiplied, the next three are in flight. Tiles
-// go from HBM straight into LDS with 16-byte buffer loads (no register
-// staging); each wave waits only for the oldest stage it needs. The four
-// 16-byte chunks of each 64-byte LDS row are XOR-swizzled so that the MFMA
-// fragment reads are free of bank conflicts. Rows or columns outside an
-// operand's valid range are fetched through an out-of-range buffer offset,
-// which the hardware returns as zero.
+// K advances in stages of 32 through a ring of NS LDS stages: while a stage is
+// multiplied, the next ones are in flight. Tiles go from HBM straight into LDS
+// with 16-byte buffer loads (no register staging); each wave waits only for
+// the oldest stage it needs. Within a stage the fragment reads of the next
+// k-substep and the next stage are issued behind MFMAs already queued (a
+// software pipeline), since one wave per SIMD has no other wave to hide LDS
+// latency behind. The four 16-byte chunks of each 64-byte LDS row are
+// XOR-swizzled so that the fragment reads are free of bank conflicts. Rows or
+// columns outside an operand's valid range are fetched through an
+// out-of-range buffer offset, which the hardware returns as zero.
 //
 // Operands are either row-major (element (r, k) at r*ld + k) or K-blocked by
 // 64 (element (r, k) at (k/64)*kblk + r*64 + k%64): the token-indexed operands
 // of the update (eta Z^T and V^T) are stored K-blocked so that one stage reads
-// one contiguous slab instead of 256 rows strided by the whole stream length.
+// one contiguous slab instead of rows strided by the whole stream length.
 //
 // MFMA 32x32x16 register layout (lane l, accumulator register r):
 //   A operand: row i = l % 32, k = 8*(l/32) .. +7;  B operand: column j = l % 32, same k.
@@ -29,19 +33,23 @@
 namespace {
 
 constexpr int BM = 256;  // tile rows along i
-constexpr int BN = 256;  // tile rows along j
 constexpr int BK = 32;   // k per stage
-constexpr int NS = 4;    // stages in the LDS ring
-constexpr int NTHREADS = 256;
 constexpr uint32_t kBufferFlags = 0x00020000u;  // raw buffer descriptor word 3 on the gfx9 family
 constexpr uint32_t kOutOfRange = 0x80000000u;   // offset past num_records: the load returns zero
 
+template <int NBJ>
 struct Acc {
-  f32x16 v[4][4];
+  f32x16 v[4][NBJ];
+};
+
+// One LDS stage: the A tile (256 rows) and the B tile (32*WN*NBJ rows), 32 columns each.
+template <int WN, int NBJ>
+struct Stage {
+  bf16_t a[BM * BK];
+  bf16_t b[32 * WN * NBJ * BK];
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
-typedef bf16_t Stage[2][BM * BK];  // [operand A/B][256 rows x 32]
 
 // One K-segment of an operand, rows [0, nrows) valid, columns [0, kvalid) valid.
 struct Opnd {
@@ -60,122 +68,237 @@ __device__ __forceinline__ Opnd kblocked(const bf16_t *base, long long kblk, int
   return Opnd{base, 64, kblk, nrows, kvalid, koff};
 }
 
-__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
-// element offset of (row r, 16-byte chunk c) inside a 256 x 32 bf16 LDS tile
+__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
+// element offset of (row r, 16-byte chunk c) inside an N x 32 bf16 LDS tile
 __device__ __forceinline__ int lds_off(int r, int c) { return r * BK + ((c ^ swz(r)) << 3); }
 
-__device__ __forceinline__ void acc_zero(Acc &acc) {
+template <int NBJ>
+__device__ __forceinline__ void acc_zero(Acc<NBJ> &acc) {
 #pragma unroll
   for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
-    for (int bj = 0; bj < 4; ++bj)
+    for (int bj = 0; bj < NBJ; ++bj)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc.v[bi][bj][r] = 0.f;
 }
 
-// Queue the copy of rows [row0, row0+256) x cols [k, k+32) of one operand into
-// an LDS tile. Wave w moves rows w*64 .. w*64+63, sixteen rows per
-// instruction; lane l of an instruction fills row r0 + l/4, physical chunk
-// l%4, so it fetches the logical chunk (l%4) ^ swz(row). One descriptor per
-// call; each instruction's row offset goes in soffset.
-template <bool BLOCKED>
-__device__ __forceinline__ void issue_tile(bf16_t *lds_tile, const Opnd &s, int row0, int k, int w, int lane) {
+// Queue the copy of rows [row0, row0+ROWS) x cols [k, k+32) of one operand
+// into an LDS tile. Wave w of NW moves rows w*ROWS/NW .. +ROWS/NW, sixteen rows
+// per buffer-load instruction (instruction n of the wave); lane l of an
+// instruction fills row r0 + l/4, physical chunk l%4, so it fetches the
+// logical chunk (l%4) ^ swz(row). The instruction's row offset goes in soffset.
+template <bool BLOCKED, int ROWS, int NW>
+__device__ __forceinline__ void issue_one(bf16_t *lds_tile, const Opnd &s, int row0, int k, int w, int lane, int n) {
+  constexpr int WROWS = ROWS / NW;
   const int lr = lane >> 2;
-  const int nvw = s.nrows - row0 - w * 64;  // valid rows among this wave's 64
+  const int nvw = s.nrows - row0 - w * WROWS;  // valid rows among this wave's rows
+  const int slab = w * WROWS + n * 16;
+  const int c = (lane & 3) ^ swz(slab + lr);
   if (!BLOCKED) {
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<bf16_t *>(s.base + (long long)row0 * s.ld + k), (short)0, 0x7fffffff, kBufferFlags);
     const int ldb = (int)s.ld * 2;
-    const int kleft = s.kvalid - k;
-#pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      const int slab = w * 64 + n * 16;
-      const int c = (lane & 3) ^ swz(slab + lr);
-      const bool ok = (n * 16 + lr) < nvw && c * 8 < kleft;
-      const uint32_t voff = ok ? (uint32_t)(lr * ldb + c * 16) : kOutOfRange;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(lds_tile + slab * BK), 16, voff, slab * ldb, 0, 0);
-    }
+    const bool ok = (n * 16 + lr) < nvw && c * 8 < s.kvalid - k;
+    const uint32_t voff = ok ? (uint32_t)(lr * ldb + c * 16) : kOutOfRange;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(lds_tile + slab * BK), 16, voff, slab * ldb, 0, 0);
   } else {
     const int ka0 = s.koff + k;  // absolute column of this stage's first column
     const int kb0 = ka0 >> 6;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<bf16_t *>(s.base + (long long)kb0 * s.kblk + (long long)row0 * 64), (short)0, 0x7fffffff,
         kBufferFlags);
-    const int blkb = (int)s.kblk * 2;
-#pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      const int slab = w * 64 + n * 16;
-      const int c = (lane & 3) ^ swz(slab + lr);
-      const int ka = ka0 + c * 8;
-      const bool ok = (n * 16 + lr) < nvw && (k + c * 8) < s.kvalid;
-      const uint32_t voff =
-          ok ? (uint32_t)(((ka >> 6) - kb0) * blkb + lr * 128 + (ka & 63) * 2) : kOutOfRange;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(lds_tile + slab * BK), 16, voff, slab * 128, 0, 0);
-    }
+    const int ka = ka0 + c * 8;
+    const bool ok = (n * 16 + lr) < nvw && (k + c * 8) < s.kvalid;
+    const uint32_t voff =
+        ok ? (uint32_t)(((ka >> 6) - kb0) * (int)s.kblk * 2 + lr * 128 + (ka & 63) * 2) : kOutOfRange;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(lds_tile + slab * BK), 16, voff, slab * 128, 0, 0);
   }
 }
 
-template <bool ABLK, bool BBLK>
-__device__ __forceinline__ void issue_stage(Stage &st, const Opnd &a, const Opnd &b, int arow0, int brow0, int k,
-                                            int w, int lane) {
-  issue_tile<ABLK>(st[0], a, arow0, k, w, lane);
-  issue_tile<BBLK>(st[1], b, brow0, k, w, lane);
-}
+// buffer loads per wave per stage: A tile, then B tile
+template <int WN, int NBJ>
+constexpr int loads_a() { return BM / (2 * WN) / 16; }
+template <int WN, int NBJ>
+constexpr int loads_per_stage() { return loads_a<WN, NBJ>() + 32 * WN * NBJ / (2 * WN) / 16; }
 
-// Wait until at most `later` stages of this wave's loads (8 loads per stage)
-// are still in flight, then for every wave: their loads of the awaited stage
-// have landed too, and every wave is done with the stage computed before.
-__device__ __forceinline__ void stage_wait(int later) {
-  if (later >= 2)
-    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-  else if (later == 1)
-    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+// Load j (0 <= j < loads_per_stage) of this wave for one stage.
+template <bool ABLK, bool BBLK, int WN, int NBJ>
+__device__ __forceinline__ void issue_part(Stage<WN, NBJ> &st, const Opnd &a, const Opnd &b, int arow0, int brow0,
+                                           int k, int w, int lane, int j) {
+  constexpr int LA = loads_a<WN, NBJ>();
+  if (j < LA)
+    issue_one<ABLK, BM, 2 * WN>(st.a, a, arow0, k, w, lane, j);
   else
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
+    issue_one<BBLK, 32 * WN * NBJ, 2 * WN>(st.b, b, brow0, k, w, lane, j - LA);
 }
 
-// One 32-deep stage: 2 k-substeps of 16, 16 MFMAs each.
-__device__ __forceinline__ void mma_stage(Acc &acc, const bf16_t *lA, const bf16_t *lB, int wm, int wn, int lane) {
+// All loads of this wave for one stage.
+template <bool ABLK, bool BBLK, int WN, int NBJ>
+__device__ __forceinline__ void issue_stage(Stage<WN, NBJ> &st, const Opnd &a, const Opnd &b, int arow0, int brow0,
+                                            int k, int w, int lane) {
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    const int c = 2 * ks + (lane >> 5);
-    bf16x8 a[4], b[4];
+  for (int j = 0; j < loads_per_stage<WN, NBJ>(); ++j)
+    issue_part<ABLK, BBLK>(st, a, b, arow0, brow0, k, w, lane, j);
+}
+
+// s_waitcnt immediate (gfx9): vmcnt(n), expcnt unchanged, lgkmcnt(0).
+constexpr unsigned wait_imm(int n) { return (unsigned)((n & 15) | 0x70 | (((n >> 4) & 3) << 14)); }
+
+// Wait until at most `later` stages of this wave's loads (LPS loads per stage)
+// are still in flight and its own LDS reads are done, then meet every wave at
+// the barrier: their loads of the awaited stage have landed too, and every
+// wave is done reading the stage computed before. Only LDS is shared between
+// the waves, so no memory fence is needed (a fence would also wait for the
+// loads of the stages still in flight).
+template <int LPS>
+__device__ __forceinline__ void stage_wait(int later) {
+  switch (later) {
+    case 0: __builtin_amdgcn_s_waitcnt(wait_imm(0)); break;
+    case 1: __builtin_amdgcn_s_waitcnt(wait_imm(LPS)); break;
+    case 2: __builtin_amdgcn_s_waitcnt(wait_imm(2 * LPS)); break;
+    case 3: __builtin_amdgcn_s_waitcnt(wait_imm(3 * LPS)); break;
+    case 4: __builtin_amdgcn_s_waitcnt(wait_imm(4 * LPS)); break;
+    default: __builtin_amdgcn_s_waitcnt(wait_imm(5 * LPS)); break;
+  }
+  asm volatile("s_barrier" ::: "memory");
+}
+
+// MFMA fragments of one 16-deep k-substep: 4 A fragments (rows) and NBJ B
+// fragments (columns) of this wave's sub-tile.
+template <int NBJ>
+struct Frag {
+  bf16x8 a[4], b[NBJ];
+};
+
+// Read substep ks (0 or 1) of an LDS stage into registers.
+template <int WN, int NBJ>
+__device__ __forceinline__ void frag_read(Frag<NBJ> &fr, const Stage<WN, NBJ> &st, int ks, int wm, int wn,
+                                          int lane) {
+  const int c = 2 * ks + (lane >> 5);
 #pragma unroll
-    for (int bi = 0; bi < 4; ++bi)
-      a[bi] = *reinterpret_cast<const bf16x8 *>(lA + lds_off(wm * 128 + bi * 32 + (lane & 31), c));
+  for (int bi = 0; bi < 4; ++bi)
+    fr.a[bi] = *reinterpret_cast<const bf16x8 *>(st.a + lds_off(wm * 128 + bi * 32 + (lane & 31), c));
 #pragma unroll
-    for (int bj = 0; bj < 4; ++bj)
-      b[bj] = *reinterpret_cast<const bf16x8 *>(lB + lds_off(wn * 128 + bj * 32 + (lane & 31), c));
+  for (int bj = 0; bj < NBJ; ++bj)
+    fr.b[bj] = *reinterpret_cast<const bf16x8 *>(st.b + lds_off(wn * 32 * NBJ + bj * 32 + (lane & 31), c));
+}
+
+// MFMAs of one k-substep for fragment rows bi in [BLO, BHI).
+template <int BLO, int BHI, int NBJ>
+__device__ __forceinline__ void frag_mma(Acc<NBJ> &acc, const Frag<NBJ> &fr) {
 #pragma unroll
-    for (int bi = 0; bi < 4; ++bi)
+  for (int bi = BLO; bi < BHI; ++bi)
 #pragma unroll
-      for (int bj = 0; bj < 4; ++bj)
-        acc.v[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[bi], b[bj], acc.v[bi][bj], 0, 0, 0);
+    for (int bj = 0; bj < NBJ; ++bj)
+      acc.v[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.a[bi], fr.b[bj], acc.v[bi][bj], 0, 0, 0);
+}
+
+// Keep the compiler from moving instructions across this point.
+__device__ __forceinline__ void pin() { __builtin_amdgcn_sched_barrier(0); }
+
+// The software pipeline of one 32-deep stage kt. On entry `cur` holds (or is
+// loading) substep 0 of stage kt; on exit it holds substep 0 of stage kt+1.
+// Every LDS read and tile-load issue sits behind MFMAs already queued, so the
+// matrix cores keep running while they wait:
+//   read substep 1 of kt -> nxt | MFMAs of row 0 on cur
+//   wait for stage kt+1 + barrier
+//   MFMAs of rows 1-3 on cur and rows 0-3 on nxt, with this wave's loads of
+//   stage kt+NS (into kt's buffer) issued one at a time between them, and
+//   substep 0 of kt+1 read into cur after nxt's first row.
+// After the barrier no wave reads stage kt's buffer again (all its reads were
+// issued before, and the wait includes lgkmcnt(0)), so it can be refilled.
+// Spreading the loads keeps a burst of them from stalling the MFMA issue.
+// With AFTER, after_fn(acc) runs once all of stage kt's MFMAs are queued, and
+// the next fragments are read only then (few registers live).
+template <int WN, int NBJ, int NS, bool AFTER, class IssueFn, class AfterFn>
+__device__ __forceinline__ void pipelined_stage(Acc<NBJ> &acc, Stage<WN, NBJ> *ring, Frag<NBJ> &cur, Frag<NBJ> &nxt,
+                                                int kt, int nk, int wm, int wn, int lane, IssueFn &&issue_part,
+                                                AfterFn &&after_fn) {
+  constexpr int LPS = loads_per_stage<WN, NBJ>();
+  static_assert(LPS <= 7, "one load per MFMA row group");
+  frag_read(nxt, ring[kt % NS], 1, wm, wn, lane);
+  pin();
+  frag_mma<0, 1>(acc, cur);
+  pin();
+  const bool more = kt + 1 < nk;
+  const bool refill = kt + NS < nk;
+  if (more) {
+    const int later = (nk - 2 - kt) < (NS - 2) ? (nk - 2 - kt) : (NS - 2);
+    stage_wait<LPS>(later);
+  }
+  pin();
+  frag_mma<1, 2>(acc, cur);
+  if (refill && LPS > 0) issue_part(kt + NS, 0);
+  pin();
+  frag_mma<2, 3>(acc, cur);
+  if (refill && LPS > 1) issue_part(kt + NS, 1);
+  pin();
+  frag_mma<3, 4>(acc, cur);
+  if (refill && LPS > 2) issue_part(kt + NS, 2);
+  pin();
+  frag_mma<0, 1>(acc, nxt);
+  pin();
+  if (!AFTER && more) frag_read(cur, ring[(kt + 1) % NS], 0, wm, wn, lane);
+  if (refill && LPS > 3) issue_part(kt + NS, 3);
+  pin();
+  frag_mma<1, 2>(acc, nxt);
+  if (refill && LPS > 4) issue_part(kt + NS, 4);
+  pin();
+  frag_mma<2, 3>(acc, nxt);
+  if (refill && LPS > 5) issue_part(kt + NS, 5);
+  pin();
+  frag_mma<3, 4>(acc, nxt);
+  if (refill && LPS > 6) issue_part(kt + NS, 6);
+  pin();
+  if (AFTER) {
+    after_fn(acc);
+    if (more) frag_read(cur, ring[(kt + 1) % NS], 0, wm, wn, lane);
+    pin();
   }
 }
+
+struct NoHook {
+  template <class A>
+  __device__ void operator()(const A &) const {}
+};
+
+constexpr int WN_W = 4, NBJ_W = 2;  // wide GEMMs: 8 waves, 256 x 256 tiles
+constexpr int NS_W = 5;              // 5 x 32 KB ring (all of the LDS)
+constexpr int NT_W = 64 * 2 * WN_W;  // 512 threads
+constexpr int WN_U = 2, NBJ_U = 2;   // state update: 4 waves, 256 x 128 tiles
+constexpr int NS_U = 6;              // 6 x 24 KB ring
+constexpr int NT_U = 64 * 2 * WN_U;  // 256 threads
+
+// wave coordinates: wm selects the 128-row half along i, wn the column slice along j
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 // K loop over segment 1 (nk1 stages, both operands row-major) then segment 2
-// (nk2 stages; its A operand K-blocked when A2BLK).
+// (nk2 stages; its A operand K-blocked when A2BLK). 256 x 256 tiles.
 template <bool A2BLK>
-__device__ __forceinline__ void gemm_loop(Acc &acc, Stage *ring, const Opnd &a1, const Opnd &b1, int nk1,
-                                          const Opnd &a2, const Opnd &b2, int nk2, int arow0, int brow0) {
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), wm = w >> 1, wn = w & 1;
+__device__ __forceinline__ void gemm_loop(Acc<NBJ_W> &acc, Stage<WN_W, NBJ_W> *ring, const Opnd &a1, const Opnd &b1,
+                                          int nk1, const Opnd &a2, const Opnd &b2, int nk2, int arow0, int brow0) {
+  const int lane = threadIdx.x & 63;
+  const int w = wave_id(), wm = w & 1, wn = w >> 1;
   const int nk = nk1 + nk2;
+  if (nk <= 0) return;
   auto issue = [&](int kt) {
     if (kt < nk1)
-      issue_stage<false, false>(ring[kt % NS], a1, b1, arow0, brow0, kt * BK, w, lane);
+      issue_stage<false, false>(ring[kt % NS_W], a1, b1, arow0, brow0, kt * BK, w, lane);
     else
-      issue_stage<A2BLK, false>(ring[kt % NS], a2, b2, arow0, brow0, (kt - nk1) * BK, w, lane);
+      issue_stage<A2BLK, false>(ring[kt % NS_W], a2, b2, arow0, brow0, (kt - nk1) * BK, w, lane);
   };
-  for (int kt = 0; kt < NS - 1 && kt < nk; ++kt) issue(kt);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int later = (nk - 1 - kt) < (NS - 2) ? (nk - 1 - kt) : (NS - 2);
-    stage_wait(later);
-    if (kt + NS - 1 < nk) issue(kt + NS - 1);
-    mma_stage(acc, ring[kt % NS][0], ring[kt % NS][1], wm, wn, lane);
-  }
+  auto part = [&](int kt, int j) {
+    if (kt < nk1)
+      issue_part<false, false>(ring[kt % NS_W], a1, b1, arow0, brow0, kt * BK, w, lane, j);
+    else
+      issue_part<A2BLK, false>(ring[kt % NS_W], a2, b2, arow0, brow0, (kt - nk1) * BK, w, lane, j);
+  };
+  for (int kt = 0; kt < NS_W && kt < nk; ++kt) issue(kt);
+  Frag<NBJ_W> cur, nxt;
+  stage_wait<loads_per_stage<WN_W, NBJ_W>()>((nk - 1) < (NS_W - 1) ? (nk - 1) : (NS_W - 1));
+  frag_read(cur, ring[0], 0, wm, wn, lane);
+  for (int kt = 0; kt < nk; ++kt)
+    pipelined_stage<WN_W, NBJ_W, NS_W, false>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, part, NoHook{});
 }
 
 // ---------------------------------------------------------------------------
@@ -192,28 +315,27 @@ struct A1Args {
   int T, T_pad, d, f;
 };
 
-__global__ __launch_bounds__(NTHREADS, 1) void k_a1(A1Args p) {
-  __shared__ __attribute__((aligned(16))) Stage ring[NS];
-  const int n0 = blockIdx.x * BN;
+__global__ __launch_bounds__(NT_W, 1) void k_a1(A1Args p) {
+  __shared__ __attribute__((aligned(16))) Stage<WN_W, NBJ_W> ring[NS_W];
+  const int n0 = blockIdx.x * 256;
   const int m0 = blockIdx.y * BM;
   const int b = m0 / p.T_pad;
   const int pos0 = m0 - b * p.T_pad;
   const Opnd sa = rowmajor(p.x + ((long long)b * p.T + pos0) * p.d, p.d, p.T - pos0, p.d);
   const Opnd sb = rowmajor(p.Wug + (long long)n0 * p.d, p.d, 2 * p.f - n0, p.d);
-  Acc acc;
+  Acc<NBJ_W> acc;
   acc_zero(acc);
   gemm_loop<false>(acc, ring, sa, sb, p.d / BK, sa, sb, 0, 0, 0);
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w & 1, wn = w >> 1;
   bf16_t *ZTb = p.ZT + (long long)b * p.f * p.T_pad;
+  // the wave's two 32-column blocks are a matching (up, gate) pair of W_ug rows
+  const int feat = (n0 + wn * 64) / 2 + (lane & 31);
+  if (feat < p.f) {
 #pragma unroll
-  for (int bi = 0; bi < 4; ++bi) {
-#pragma unroll
-    for (int pr = 0; pr < 2; ++pr) {
-      const int feat = (n0 + wn * 128) / 2 + pr * 32 + (lane & 31);
-      if (feat >= p.f) continue;
-      const f32x16 &u = acc.v[bi][2 * pr];
-      const f32x16 &g = acc.v[bi][2 * pr + 1];
+    for (int bi = 0; bi < 4; ++bi) {
+      const f32x16 &u = acc.v[bi][0];
+      const f32x16 &g = acc.v[bi][1];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int pos = pos0 + wm * 128 + bi * 32 + 8 * q + 4 * (lane >> 5);
@@ -236,10 +358,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_a1(A1Args p) {
 
 // ---------------------------------------------------------------------------
 // State update with snapshots. i = hidden unit (ZT row), j = model dim (VT row),
-// k = token slot. The fp32 accumulators ARE the state W[a][i] for the tile and
-// stay in registers for the whole token stream; at each group start g*L the
-// tile is written out as a bf16 snapshot.
-// grid: (f/256, d/256, B)
+// k = token slot. The fp32 accumulators ARE the state W[a][i] for the
+// 256 (i) x 128 (a) tile and stay in registers for the whole token stream; at
+// each group start g*L the tile is written out as a bf16 snapshot.
+// grid: (f/256, d/128, B)
 struct UpdArgs {
   const bf16_t *ZT;
   const bf16_t *VT;
@@ -249,14 +371,14 @@ struct UpdArgs {
 };
 
 // Write the accumulator tile as bf16 into a snapshot W[a][i] ([d][f]).
-// `lane_ptr` points at this lane's first element (a = j0 + wn*128 + l%32,
+// `lane_ptr` points at this lane's first element (a = j0 + wn*64 + l%32,
 // i = i0 + wm*128 + 4*(l/32)); tiles are always full (d, f multiples of 256).
-__device__ __forceinline__ void dump_snapshot(const Acc &acc, bf16_t *lane_ptr, int f) {
+__device__ __forceinline__ void dump_snapshot(const Acc<NBJ_U> &acc, bf16_t *lane_ptr, int f) {
 #pragma unroll
-  for (int bj = 0; bj < 4; ++bj) {
+  for (int bj = 0; bj < NBJ_U; ++bj) {
     bf16_t *row = lane_ptr + (long long)bj * 32 * f;
 #pragma unroll
-    for (int bi = 0; bi < 4; ++bi)
+    for (int bi = 0; bi < 4; ++bi) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         uint2 pk;
@@ -264,27 +386,27 @@ __device__ __forceinline__ void dump_snapshot(const Acc &acc, bf16_t *lane_ptr, 
         pk.y = pack_bf16x2(acc.v[bi][bj][4 * q + 2], acc.v[bi][bj][4 * q + 3]);
         *reinterpret_cast<uint2 *>(row + bi * 32 + 8 * q) = pk;
       }
-    __builtin_amdgcn_sched_barrier(0);  // one column block at a time: bounded register use
+    }
   }
 }
 
-__global__ __launch_bounds__(NTHREADS, 1) void k_update(UpdArgs p) {
-  __shared__ __attribute__((aligned(16))) Stage ring[NS];
+__global__ __launch_bounds__(NT_U, 1) void k_update(UpdArgs p) {
+  __shared__ __attribute__((aligned(16))) Stage<WN_U, NBJ_U> ring[NS_U];
   const int i0 = blockIdx.x * BM;
-  const int j0 = blockIdx.y * BN;
+  const int j0 = blockIdx.y * 128;
   const int b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), wm = w >> 1, wn = w & 1;
+  const int lane = threadIdx.x & 63;
+  const int w = wave_id(), wm = w & 1, wn = w >> 1;
   const long long df = (long long)p.d * p.f;
   // this lane's first element of the tile, relative to W[0][0]
   const long long lane_off =
-      (long long)(j0 + wn * 128 + (lane & 31)) * p.f + i0 + wm * 128 + 4 * (lane >> 5);
+      (long long)(j0 + wn * 64 + (lane & 31)) * p.f + i0 + wm * 128 + 4 * (lane >> 5);
   float *st = p.state + b * df + lane_off;
   bf16_t *snap0 = p.snap + (long long)b * p.ngroups * df + lane_off;
 
-  Acc acc;
+  Acc<NBJ_U> acc;
 #pragma unroll
-  for (int bj = 0; bj < 4; ++bj) {
+  for (int bj = 0; bj < NBJ_U; ++bj) {
     const float *row = st + (long long)bj * 32 * p.f;
 #pragma unroll
     for (int bi = 0; bi < 4; ++bi)
@@ -301,24 +423,42 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_update(UpdArgs p) {
   const Opnd sa = kblocked(p.ZT + (long long)b * p.f * p.T_pad, (long long)p.f * 64, p.f, p.T_pad, 0);
   const Opnd sb = kblocked(p.VT + (long long)b * p.d * p.T_pad, (long long)p.d * 64, p.d, p.T_pad, 0);
   const int nk = p.kend / BK;
-  for (int kt = 0; kt < NS - 1 && kt < nk; ++kt)
-    issue_stage<true, true>(ring[kt % NS], sa, sb, i0, j0, kt * BK, w, lane);
-  // Group starts are multiples of the stage depth: snapshot g is written
-  // between stages, while the following stages are already in flight.
-  int kt = 0;
-  for (int g = 0; g < p.ngroups; ++g) {
-    dump_snapshot(acc, snap0 + (long long)g * df, p.f);
-    const int kt_end = (g + 1 < p.ngroups) ? (g + 1) * (p.L / BK) : nk;
-    for (; kt < kt_end; ++kt) {
-      const int later = (nk - 1 - kt) < (NS - 2) ? (nk - 1 - kt) : (NS - 2);
-      stage_wait(later);
-      if (kt + NS - 1 < nk)
-        issue_stage<true, true>(ring[(kt + NS - 1) % NS], sa, sb, i0, j0, (kt + NS - 1) * BK, w, lane);
-      mma_stage(acc, ring[kt % NS][0], ring[kt % NS][1], wm, wn, lane);
-    }
+  // Snapshot 0 is the entry state; group starts are multiples of the stage
+  // depth, so snapshot g is written right after the last stage of group g-1,
+  // while the following stages are already in flight.
+  dump_snapshot(acc, snap0, p.f);
+  int g = 1;
+  auto issue = [&](int kt2) { issue_stage<true, true>(ring[kt2 % NS_U], sa, sb, i0, j0, kt2 * BK, w, lane); };
+  auto part = [&](int kt2, int j) {
+    issue_part<true, true>(ring[kt2 % NS_U], sa, sb, i0, j0, kt2 * BK, w, lane, j);
+  };
+  for (int kt = 0; kt < NS_U && kt < nk; ++kt) issue(kt);
+  Frag<NBJ_U> cur, nxt;
+  if (nk > 0) {
+    stage_wait<loads_per_stage<WN_U, NBJ_U>()>((nk - 1) < (NS_U - 1) ? (nk - 1) : (NS_U - 1));
+    frag_read(cur, ring[0], 0, wm, wn, lane);
   }
+  auto snapshot = [&](const Acc<NBJ_U> &a) {
+    dump_snapshot(a, snap0 + (long long)g * df, p.f);
+    // Stores share the vector-memory counter with the tile loads and may
+    // complete out of order with them: drain it so the counted waits of the
+    // following stages stay exact.
+    __builtin_amdgcn_s_waitcnt(wait_imm(0));
+    ++g;
+  };
+  // Stages of group g-1 run plain; its last stage ends with snapshot g.
+  int kt = 0;
+  for (; g < p.ngroups; ) {
+    const int kt_last = g * (p.L / BK) - 1;  // last stage before group g starts
+    for (; kt < kt_last; ++kt)
+      pipelined_stage<WN_U, NBJ_U, NS_U, false>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, part, NoHook{});
+    pipelined_stage<WN_U, NBJ_U, NS_U, true>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, part, snapshot);
+    ++kt;
+  }
+  for (; kt < nk; ++kt)
+    pipelined_stage<WN_U, NBJ_U, NS_U, false>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, part, NoHook{});
 #pragma unroll
-  for (int bj = 0; bj < 4; ++bj) {
+  for (int bj = 0; bj < NBJ_U; ++bj) {
     float *row = st + (long long)bj * 32 * p.f;
 #pragma unroll
     for (int bi = 0; bi < 4; ++bi)
@@ -341,24 +481,24 @@ struct ScoreArgs {
   int T, T_pad, L, C, ngroups, f, nt;
 };
 
-__global__ __launch_bounds__(NTHREADS, 1) void k_scores(ScoreArgs p) {
-  __shared__ __attribute__((aligned(16))) Stage ring[NS];
+__global__ __launch_bounds__(NT_W, 1) void k_scores(ScoreArgs p) {
+  __shared__ __attribute__((aligned(16))) Stage<WN_W, NBJ_W> ring[NS_W];
   const int it = blockIdx.x % p.nt, jt = blockIdx.x / p.nt;
   const int g = blockIdx.y, b = blockIdx.z;
   const long long gs = (long long)g * p.L;
   const int Lg = (int)((p.T - gs) < p.L ? (p.T - gs) : p.L);
-  const int i0 = it * BM, j0 = jt * BN;
+  const int i0 = it * BM, j0 = jt * 256;
   if (it > jt || j0 >= Lg) return;
   const Opnd s = rowmajor(p.Z + ((long long)b * p.T_pad + gs) * p.f, p.f, (int)(p.T_pad - gs), p.f);
-  Acc acc;
+  Acc<NBJ_W> acc;
   acc_zero(acc);
   gemm_loop<false>(acc, ring, s, s, p.f / BK, s, s, 0, i0, j0);
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w & 1, wn = w >> 1;
   bf16_t *Pg = p.P + ((long long)b * p.ngroups + g) * p.L * p.L;
 #pragma unroll
-  for (int bj = 0; bj < 4; ++bj) {
-    const int t = j0 + wn * 128 + bj * 32 + (lane & 31);
+  for (int bj = 0; bj < NBJ_W; ++bj) {
+    const int t = j0 + wn * 64 + bj * 32 + (lane & 31);
     if (t >= p.L) continue;
     const int ct = t / p.C;
 #pragma unroll
@@ -391,10 +531,10 @@ struct OutArgs {
   int T, T_pad, L, C, ngroups, d, f, intra;
 };
 
-__global__ __launch_bounds__(NTHREADS, 1) void k_out(OutArgs p) {
-  __shared__ __attribute__((aligned(16))) Stage ring[NS];
+__global__ __launch_bounds__(NT_W, 1) void k_out(OutArgs p) {
+  __shared__ __attribute__((aligned(16))) Stage<WN_W, NBJ_W> ring[NS_W];
   const int i0 = blockIdx.x * BM;
-  const int j0 = blockIdx.y * BN;
+  const int j0 = blockIdx.y * 256;
   const int b = blockIdx.z / p.ngroups, g = blockIdx.z % p.ngroups;
   const long long gs = (long long)g * p.L;
   const int Lg = (int)((p.T - gs) < p.L ? (p.T - gs) : p.L);
@@ -404,21 +544,21 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_out(OutArgs p) {
   int nk2 = 0;
   Opnd sa2 = sa1, sb2 = sb1;
   if (p.intra) {
-    const int jl = (j0 + BN - 1 < Lg - 1) ? j0 + BN - 1 : Lg - 1;
+    const int jl = (j0 + 255 < Lg - 1) ? j0 + 255 : Lg - 1;
     const int kend = (jl / p.C) * p.C;  // start of the last row's chunk
     const int kv = (kend + 7) & ~7;
     nk2 = (kv + BK - 1) / BK;
     sa2 = kblocked(p.VT + (long long)b * p.d * p.T_pad, (long long)p.d * 64, p.d, kv, (int)gs);
     sb2 = rowmajor(p.P + ((long long)b * p.ngroups + g) * p.L * p.L, p.L, p.L, kv);
   }
-  Acc acc;
+  Acc<NBJ_W> acc;
   acc_zero(acc);
   gemm_loop<true>(acc, ring, sa1, sb1, p.f / BK, sa2, sb2, nk2, i0, j0);
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w & 1, wn = w >> 1;
 #pragma unroll
-  for (int bj = 0; bj < 4; ++bj) {
-    const int t = j0 + wn * 128 + bj * 32 + (lane & 31);
+  for (int bj = 0; bj < NBJ_W; ++bj) {
+    const int t = j0 + wn * 64 + bj * 32 + (lane & 31);
     if (t >= Lg) continue;
     bf16_t *yrow = p.y + ((long long)b * p.T + gs + t) * p.d;
 #pragma unroll
@@ -479,8 +619,8 @@ hipError_t launch_gather_vt_bf16(const int32_t *ids, const bf16_t *E, int vocab,
 hipError_t launch_a1_bf16(const bf16_t *x, const bf16_t *Wug, bf16_t *Z, bf16_t *ZT, float eta, int write_zt,
                           const Layout &lay, hipStream_t s) {
   A1Args p{x, Wug, Z, ZT, eta, write_zt, lay.T, lay.T_pad, lay.d, lay.f};
-  dim3 grid((2 * lay.f + BN - 1) / BN, (unsigned)((long long)lay.B * lay.T_pad / BM));
-  hipLaunchKernelGGL(k_a1, grid, dim3(NTHREADS), 0, s, p);
+  dim3 grid((2 * lay.f + 255) / 256, (unsigned)((long long)lay.B * lay.T_pad / BM));
+  hipLaunchKernelGGL(k_a1, grid, dim3(NT_W), 0, s, p);
   return hipGetLastError();
 }
 
@@ -488,23 +628,23 @@ hipError_t launch_update_bf16(const bf16_t *ZT, const bf16_t *VT, float *state, 
                               hipStream_t s) {
   const int kend = (int)round_up_ll(lay.T, BK);
   UpdArgs p{ZT, VT, state, snap, lay.T_pad, kend, lay.L, lay.ngroups, lay.d, lay.f};
-  dim3 grid(lay.f / BM, lay.d / BN, lay.B);
-  hipLaunchKernelGGL(k_update, grid, dim3(NTHREADS), 0, s, p);
+  dim3 grid(lay.f / BM, lay.d / 128, lay.B);
+  hipLaunchKernelGGL(k_update, grid, dim3(NT_U), 0, s, p);
   return hipGetLastError();
 }
 
 hipError_t launch_scores_bf16(const bf16_t *Z, bf16_t *P, float eta, const Layout &lay, hipStream_t s) {
-  const int nt = (lay.L + BN - 1) / BN;
+  const int nt = (lay.L + 255) / 256;
   ScoreArgs p{Z, P, eta, lay.T, lay.T_pad, lay.L, lay.C, lay.ngroups, lay.f, nt};
   dim3 grid(nt * nt, lay.ngroups, lay.B);
-  hipLaunchKernelGGL(k_scores, grid, dim3(NTHREADS), 0, s, p);
+  hipLaunchKernelGGL(k_scores, grid, dim3(NT_W), 0, s, p);
   return hipGetLastError();
 }
 
 hipError_t launch_out_bf16(const bf16_t *Z, const bf16_t *P, const bf16_t *snap, const bf16_t *VT, bf16_t *y,
                            const Layout &lay, hipStream_t s) {
   OutArgs p{Z, P, snap, VT, y, lay.T, lay.T_pad, lay.L, lay.C, lay.ngroups, lay.d, lay.f, lay.intra};
-  dim3 grid(lay.d / BM, (lay.L + BN - 1) / BN, lay.B * lay.ngroups);
-  hipLaunchKernelGGL(k_out, grid, dim3(NTHREADS), 0, s, p);
+  dim3 grid(lay.d / BM, (lay.L + 255) / 256, lay.B * lay.ngroups);
+  hipLaunchKernelGGL(k_out, grid, dim3(NT_W), 0, s, p);
   return hipGetLastError();
 }
