@@ -22,6 +22,10 @@ METRIC = "TTT-MLP tokens/s per layer at d=2560/ff=9728, 128k ctx; MFMA % of peak
 WORKLOAD = "c4_4b_128k"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
+COPY_BYTES = 1 << 30  # the calibration copy reads and writes this many bytes
+KERNEL_OF_PHASE = {"up_gate_swiglu": "k_a1", "update_snapshots": "k_update", "output": "k_out"}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_c4_4b_128k.txt")
+KERNEL_SOURCE = os.path.join(ROOT, "chunk_wise_weight_amd", "csrc", "kernels_bf16.hip")
 
 
 def parse():
@@ -35,6 +39,8 @@ def parse():
     ap.add_argument("--no-sweep", action="store_true", help="skip the C=128 leg of the chunk sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-baseline duration")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain device copy of COPY_BYTES (calibrates rocprofv3 FETCH_SIZE/WRITE_SIZE)")
     return ap.parse_args()
 
 
@@ -42,6 +48,44 @@ def algorithmic_flops(d, f, tokens):
     # per token: up/gate 4df, output 2df, update 2df
     return {"up_gate_swiglu": 4.0 * d * f * tokens, "update_snapshots": 2.0 * d * f * tokens,
             "group_scores": 0.0, "output": 2.0 * d * f * tokens}
+
+
+def measured_traffic(kernel, C):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary.
+
+    The summary holds FETCH_SIZE + WRITE_SIZE per dispatch, already scaled by
+    what the same counters read for a plain copy of known size, together with
+    the SHA-256 of the kernel source they were taken on. Returns None when the
+    summary is missing, covers another chunk size, or the source has changed.
+    """
+    import hashlib
+
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(KERNEL_SOURCE, "rb") as fh:
+        sha = hashlib.sha256(fh.read()).hexdigest()
+    fields = {}
+    for line in open(TRAFFIC_FILE):
+        parts = line.split()
+        if len(parts) >= 2 and not line.startswith("#"):
+            fields.setdefault(parts[0], parts[1:])
+    if fields.get("source_sha256", [None])[0] != sha or fields.get("chunk", [None])[0] != str(C):
+        return None
+    row = fields.get("bytes_" + kernel)
+    return float(row[0]) if row else None
+
+
+def copy_calibration():
+    """One plain device-to-device copy of COPY_BYTES, for the counter calibration."""
+    import torch
+
+    src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
 
 
 def run_gpu(w, C, steps, warmup, G):
@@ -138,6 +182,8 @@ def main():
     flops = algorithmic_flops(w.d, w.f, tokens)
     total_flops = sum(flops.values())
 
+    if a.copy_calibration:
+        copy_calibration()
     r = run_gpu(w, a.chunk, a.steps, a.warmup, a.group_chunks)
     ms = r["event_ms"] / a.steps
     names = ["gather", "up_gate_swiglu", "update_snapshots", "group_scores", "output", "final_copy"]
@@ -168,7 +214,8 @@ def main():
         / PEAK_BF16_TFLOPS,
         "phase_ms": phases,
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None},
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": measured_traffic(KERNEL_OF_PHASE[dom], a.chunk)},
         "workspace_gb": r["workspace_bytes"] / 1e9,
     }
     if not a.no_sweep and a.chunk != 128:
