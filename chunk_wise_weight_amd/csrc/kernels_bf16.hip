@@ -272,6 +272,30 @@ constexpr int NT_U = 64 * 2 * WN_U;  // 256 threads
 // wave coordinates: wm selects the 128-row half along i, wn the column slice along j
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
+// Workgroups of a launch are handed to the 8 XCDs round-robin (workgroup n to
+// XCD n % 8), and each XCD has its own L2. Renumber them so that XCD k works
+// through one contiguous range of the logical tile order: the workgroups
+// resident on an XCD at one time are then neighbours in that order and share
+// operand tiles in its L2. A bijection on [0, N).
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_tile(int n, int N) {
+  const int xcd = n % kXcds, m = n / kXcds;
+  const int q = N / kXcds, r = N % kXcds;
+  return xcd * q + (xcd < r ? xcd : r) + m;
+}
+
+// Logical tile t of an nx x ny grid, in bands of H rows along y; inside a band
+// y runs fastest, so H consecutive tiles share one x and nx*H consecutive tiles
+// cover the band. The last band may be shorter.
+__device__ __forceinline__ void band_tile(int t, int nx, int ny, int H, int &x, int &y) {
+  const int full = ny / H, per = H * nx;
+  const int band = t / per;
+  const int h = band < full ? H : ny - full * H;
+  const int r = t - band * per;
+  x = r / h;
+  y = band * H + r % h;
+}
+
 // K loop over segment 1 (nk1 stages, both operands row-major) then segment 2
 // (nk2 stages; its A operand K-blocked when A2BLK). 256 x 256 tiles.
 template <bool A2BLK>
@@ -304,7 +328,7 @@ __device__ __forceinline__ void gemm_loop(Acc<NBJ_W> &acc, Stage<WN_W, NBJ_W> *r
 // ---------------------------------------------------------------------------
 // Up/gate GEMM with SwiGLU epilogue. i = token slot, j = interleaved W_ug row.
 // Writes Z [B][T_pad][f] (row-major) and eta*Z^T K-blocked [B][T_pad/64][f][64].
-// grid: (2f/256, B*T_pad/256)
+// grid: nx * ny workgroups, nx = 2f/256, ny = B*T_pad/256
 struct A1Args {
   const bf16_t *x;
   const bf16_t *Wug;
@@ -313,12 +337,15 @@ struct A1Args {
   float eta;
   int write_zt;
   int T, T_pad, d, f;
+  int nx, ny;  // tiles along W_ug rows and along token slots
 };
 
 __global__ __launch_bounds__(NT_W, 1) void k_a1(A1Args p) {
   __shared__ __attribute__((aligned(16))) Stage<WN_W, NBJ_W> ring[NS_W];
-  const int n0 = blockIdx.x * 256;
-  const int m0 = blockIdx.y * BM;
+  int tx, ty;  // W_ug tile, token tile
+  band_tile(xcd_tile(blockIdx.x, gridDim.x), p.nx, p.ny, 8, tx, ty);
+  const int n0 = tx * 256;
+  const int m0 = ty * BM;
   const int b = m0 / p.T_pad;
   const int pos0 = m0 - b * p.T_pad;
   const Opnd sa = rowmajor(p.x + ((long long)b * p.T + pos0) * p.d, p.d, p.T - pos0, p.d);
@@ -361,7 +388,7 @@ __global__ __launch_bounds__(NT_W, 1) void k_a1(A1Args p) {
 // k = token slot. The fp32 accumulators ARE the state W[a][i] for the
 // 256 (i) x 128 (a) tile and stay in registers for the whole token stream; at
 // each group start g*L the tile is written out as a bf16 snapshot.
-// grid: (f/256, d/128, B)
+// grid: B * (f/256) * (d/128) workgroups
 struct UpdArgs {
   const bf16_t *ZT;
   const bf16_t *VT;
@@ -392,9 +419,13 @@ __device__ __forceinline__ void dump_snapshot(const Acc<NBJ_U> &acc, bf16_t *lan
 
 __global__ __launch_bounds__(NT_U, 1) void k_update(UpdArgs p) {
   __shared__ __attribute__((aligned(16))) Stage<WN_U, NBJ_U> ring[NS_U];
-  const int i0 = blockIdx.x * BM;
-  const int j0 = blockIdx.y * 128;
-  const int b = blockIdx.z;
+  const int nx = p.f / BM, ny = p.d / 128;
+  const int t = xcd_tile(blockIdx.x, gridDim.x);
+  const int b = t / (nx * ny);
+  int tx, ty;
+  band_tile(t - b * nx * ny, nx, ny, 8, tx, ty);
+  const int i0 = tx * BM;
+  const int j0 = ty * 128;
   const int lane = threadIdx.x & 63;
   const int w = wave_id(), wm = w & 1, wn = w >> 1;
   const long long df = (long long)p.d * p.f;
@@ -472,8 +503,9 @@ __global__ __launch_bounds__(NT_U, 1) void k_update(UpdArgs p) {
 
 // ---------------------------------------------------------------------------
 // Within-group scores P[t][s] = eta <z_t, z_s> for s in an earlier chunk of the
-// same group. i = s, j = t; only tiles with i-tile <= j-tile are formed.
-// grid: (nt*nt, ngroups, B), nt = ceil(L/256)
+// same group. i = s, j = t; only tiles with i-tile <= j-tile that hold an
+// unmasked entry are formed.
+// grid: B * ngroups * nt(nt+1)/2 workgroups, nt = ceil(L/256)
 struct ScoreArgs {
   const bf16_t *Z;
   bf16_t *P;
@@ -483,12 +515,21 @@ struct ScoreArgs {
 
 __global__ __launch_bounds__(NT_W, 1) void k_scores(ScoreArgs p) {
   __shared__ __attribute__((aligned(16))) Stage<WN_W, NBJ_W> ring[NS_W];
-  const int it = blockIdx.x % p.nt, jt = blockIdx.x / p.nt;
-  const int g = blockIdx.y, b = blockIdx.z;
+  const int ntri = p.nt * (p.nt + 1) / 2;
+  const int t = xcd_tile(blockIdx.x, gridDim.x);
+  const int bg = t / ntri;  // b * ngroups + g
+  int u = t - bg * ntri, jt = 0;
+  while (u > jt) u -= ++jt;  // u-th tile (it <= jt) of the lower triangle, jt-major
+  const int it = u;
+  const int g = bg % p.ngroups, b = bg / p.ngroups;
   const long long gs = (long long)g * p.L;
   const int Lg = (int)((p.T - gs) < p.L ? (p.T - gs) : p.L);
   const int i0 = it * BM, j0 = jt * 256;
-  if (it > jt || j0 >= Lg) return;
+  if (j0 >= Lg) return;
+  // A tile whose every s lies in the chunk of its last t or later is all
+  // masked; the output GEMM never reads it (it stops before that chunk).
+  const int jl = (j0 + 255 < Lg - 1) ? j0 + 255 : Lg - 1;
+  if (i0 / p.C >= jl / p.C) return;
   const Opnd s = rowmajor(p.Z + ((long long)b * p.T_pad + gs) * p.f, p.f, (int)(p.T_pad - gs), p.f);
   Acc<NBJ_W> acc;
   acc_zero(acc);
@@ -521,7 +562,7 @@ __global__ __launch_bounds__(NT_W, 1) void k_scores(ScoreArgs p) {
 // ---------------------------------------------------------------------------
 // Output GEMM: y[gL+t][a] = sum_k [snap | V^T][a][k] * [Z | P][t][k].
 // i = a (model dim), j = t (token within group).
-// grid: (d/256, ceil(L/256), B*ngroups)
+// grid: B * ngroups * (d/256) * ceil(L/256) workgroups
 struct OutArgs {
   const bf16_t *Z;
   const bf16_t *P;
@@ -533,9 +574,13 @@ struct OutArgs {
 
 __global__ __launch_bounds__(NT_W, 1) void k_out(OutArgs p) {
   __shared__ __attribute__((aligned(16))) Stage<WN_W, NBJ_W> ring[NS_W];
-  const int i0 = blockIdx.x * BM;
-  const int j0 = blockIdx.y * 256;
-  const int b = blockIdx.z / p.ngroups, g = blockIdx.z % p.ngroups;
+  // one group's tiles are consecutive, token tiles fastest
+  const int nx = p.d / BM, ny = (p.L + 255) / 256;
+  const int t = xcd_tile(blockIdx.x, gridDim.x);
+  const int bg = t / (nx * ny), r = t - bg * nx * ny;
+  const int i0 = (r / ny) * BM;
+  const int j0 = (r % ny) * 256;
+  const int b = bg / p.ngroups, g = bg % p.ngroups;
   const long long gs = (long long)g * p.L;
   const int Lg = (int)((p.T - gs) < p.L ? (p.T - gs) : p.L);
   if (j0 >= Lg) return;
@@ -618,9 +663,11 @@ hipError_t launch_gather_vt_bf16(const int32_t *ids, const bf16_t *E, int vocab,
 
 hipError_t launch_a1_bf16(const bf16_t *x, const bf16_t *Wug, bf16_t *Z, bf16_t *ZT, float eta, int write_zt,
                           const Layout &lay, hipStream_t s) {
-  A1Args p{x, Wug, Z, ZT, eta, write_zt, lay.T, lay.T_pad, lay.d, lay.f};
-  dim3 grid((2 * lay.f + 255) / 256, (unsigned)((long long)lay.B * lay.T_pad / BM));
-  hipLaunchKernelGGL(k_a1, grid, dim3(NT_W), 0, s, p);
+  const int nx = (2 * lay.f + 255) / 256;
+  const long long ny = (long long)lay.B * lay.T_pad / BM;
+  if (nx * ny >= (1LL << 31)) return hipErrorInvalidConfiguration;
+  A1Args p{x, Wug, Z, ZT, eta, write_zt, lay.T, lay.T_pad, lay.d, lay.f, nx, (int)ny};
+  hipLaunchKernelGGL(k_a1, dim3((unsigned)(nx * ny)), dim3(NT_W), 0, s, p);
   return hipGetLastError();
 }
 
@@ -628,23 +675,26 @@ hipError_t launch_update_bf16(const bf16_t *ZT, const bf16_t *VT, float *state, 
                               hipStream_t s) {
   const int kend = (int)round_up_ll(lay.T, BK);
   UpdArgs p{ZT, VT, state, snap, lay.T_pad, kend, lay.L, lay.ngroups, lay.d, lay.f};
-  dim3 grid(lay.f / BM, lay.d / 128, lay.B);
-  hipLaunchKernelGGL(k_update, grid, dim3(NT_U), 0, s, p);
+  const long long n = (long long)lay.B * (lay.f / BM) * (lay.d / 128);
+  if (n >= (1LL << 31)) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(k_update, dim3((unsigned)n), dim3(NT_U), 0, s, p);
   return hipGetLastError();
 }
 
 hipError_t launch_scores_bf16(const bf16_t *Z, bf16_t *P, float eta, const Layout &lay, hipStream_t s) {
   const int nt = (lay.L + 255) / 256;
   ScoreArgs p{Z, P, eta, lay.T, lay.T_pad, lay.L, lay.C, lay.ngroups, lay.f, nt};
-  dim3 grid(nt * nt, lay.ngroups, lay.B);
-  hipLaunchKernelGGL(k_scores, grid, dim3(NT_W), 0, s, p);
+  const long long n = (long long)lay.B * lay.ngroups * (nt * (nt + 1) / 2);
+  if (n >= (1LL << 31)) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(k_scores, dim3((unsigned)n), dim3(NT_W), 0, s, p);
   return hipGetLastError();
 }
 
 hipError_t launch_out_bf16(const bf16_t *Z, const bf16_t *P, const bf16_t *snap, const bf16_t *VT, bf16_t *y,
                            const Layout &lay, hipStream_t s) {
   OutArgs p{Z, P, snap, VT, y, lay.T, lay.T_pad, lay.L, lay.C, lay.ngroups, lay.d, lay.f, lay.intra};
-  dim3 grid(lay.d / BM, (lay.L + 255) / 256, lay.B * lay.ngroups);
-  hipLaunchKernelGGL(k_out, grid, dim3(NT_W), 0, s, p);
+  const long long n = (long long)lay.B * lay.ngroups * (lay.d / BM) * ((lay.L + 255) / 256);
+  if (n >= (1LL << 31)) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(k_out, dim3((unsigned)n), dim3(NT_W), 0, s, p);
   return hipGetLastError();
 }
