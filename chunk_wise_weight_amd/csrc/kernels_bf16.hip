@@ -7,21 +7,22 @@
 // waves per SIMD so one can issue MFMAs while the other waits); the state
 // update uses 4 waves (WN = 2, NBJ = 2: 256 x 128 tiles).
 //
-// K advances in stages of 32 through a ring of NS LDS stages: while a stage is
-// multiplied, the next ones are in flight. Tiles go from HBM straight into LDS
-// with 16-byte buffer loads (no register staging); each wave waits only for
-// the oldest stage it needs. Within a stage the fragment reads of the next
+// Tiles go from HBM straight into LDS with 16-byte buffer loads (no register
+// staging) in slabs of 64 columns, so that every row contributes one whole
+// 128-byte line: whole lines fill LDS at twice the rate of half lines. A ring
+// of NSL slabs keeps the next slabs in flight while one is multiplied, and
+// each wave waits only for the oldest slab it needs. The MFMAs run in stages
+// of 32 (two per slab); within a stage the fragment reads of the next
 // k-substep and the next stage are issued behind MFMAs already queued (a
-// software pipeline), since one wave per SIMD has no other wave to hide LDS
-// latency behind. The four 16-byte chunks of each 64-byte LDS row are
+// software pipeline). The eight 16-byte chunks of each 128-byte LDS row are
 // XOR-swizzled so that the fragment reads are free of bank conflicts. Rows or
 // columns outside an operand's valid range are fetched through an
 // out-of-range buffer offset, which the hardware returns as zero.
 //
 // Operands are either row-major (element (r, k) at r*ld + k) or K-blocked by
 // 64 (element (r, k) at (k/64)*kblk + r*64 + k%64): the token-indexed operands
-// of the update (eta Z^T and V^T) are stored K-blocked so that one stage reads
-// one contiguous slab instead of rows strided by the whole stream length.
+// of the update (eta Z^T and V^T) are stored K-blocked so that one slab is one
+// contiguous block instead of rows strided by the whole stream length.
 //
 // MFMA 32x32x16 register layout (lane l, accumulator register r):
 //   A operand: row i = l % 32, k = 8*(l/32) .. +7;  B operand: column j = l % 32, same k.
@@ -33,7 +34,8 @@
 namespace {
 
 constexpr int BM = 256;  // tile rows along i
-constexpr int BK = 32;   // k per stage
+constexpr int BK = 32;   // k per MFMA stage
+constexpr int SK = 64;   // k per load slab: one 128-byte line of every row
 constexpr uint32_t kBufferFlags = 0x00020000u;  // raw buffer descriptor word 3 on the gfx9 family
 constexpr uint32_t kOutOfRange = 0x80000000u;   // offset past num_records: the load returns zero
 
@@ -42,11 +44,11 @@ struct Acc {
   f32x16 v[4][NBJ];
 };
 
-// One LDS stage: the A tile (256 rows) and the B tile (32*WN*NBJ rows), 32 columns each.
+// One LDS slab: the A tile (256 rows) and the B tile (32*WN*NBJ rows), 64 columns each.
 template <int WN, int NBJ>
-struct Stage {
-  bf16_t a[BM * BK];
-  bf16_t b[32 * WN * NBJ * BK];
+struct Slab {
+  bf16_t a[BM * SK];
+  bf16_t b[32 * WN * NBJ * SK];
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -68,9 +70,12 @@ __device__ __forceinline__ Opnd kblocked(const bf16_t *base, long long kblk, int
   return Opnd{base, 64, kblk, nrows, kvalid, koff};
 }
 
-__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
-// element offset of (row r, 16-byte chunk c) inside an N x 32 bf16 LDS tile
-__device__ __forceinline__ int lds_off(int r, int c) { return r * BK + ((c ^ swz(r)) << 3); }
+// The eight 16-byte chunks of each 128-byte LDS row are XOR-swizzled; with
+// this pattern the fragment reads (32 consecutive rows, one chunk) are free of
+// bank conflicts, also while LDS-DMA writes land (measured with rocprofv3).
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+// element offset of (row r, logical 16-byte chunk c) inside an N x 64 bf16 LDS tile
+__device__ __forceinline__ int lds_off(int r, int c) { return r * SK + ((c ^ swz(r)) << 3); }
 
 template <int NBJ>
 __device__ __forceinline__ void acc_zero(Acc<NBJ> &acc) {
@@ -82,48 +87,49 @@ __device__ __forceinline__ void acc_zero(Acc<NBJ> &acc) {
       for (int r = 0; r < 16; ++r) acc.v[bi][bj][r] = 0.f;
 }
 
-// Queue the copy of rows [row0, row0+ROWS) x cols [k, k+32) of one operand
-// into an LDS tile. Wave w of NW moves rows w*ROWS/NW .. +ROWS/NW, sixteen rows
-// per buffer-load instruction (instruction n of the wave); lane l of an
-// instruction fills row r0 + l/4, physical chunk l%4, so it fetches the
-// logical chunk (l%4) ^ swz(row). The instruction's row offset goes in soffset.
+// Queue the copy of rows [row0, row0+ROWS) x cols [k, k+64) of one operand
+// into an LDS tile. Wave w of NW moves rows w*ROWS/NW .. +ROWS/NW, eight rows
+// per buffer-load instruction (instruction n of the wave); lanes 8r .. 8r+7 of
+// an instruction fetch the whole 128-byte line of row r (whole lines fill LDS
+// at twice the rate of half lines), lane l fills physical chunk l%8, i.e. the
+// logical chunk (l%8) ^ swz(row). The instruction's row offset goes in soffset.
 template <bool BLOCKED, int ROWS, int NW>
 __device__ __forceinline__ void issue_one(bf16_t *lds_tile, const Opnd &s, int row0, int k, int w, int lane, int n) {
   constexpr int WROWS = ROWS / NW;
-  const int lr = lane >> 2;
+  const int lr = lane >> 3;
   const int nvw = s.nrows - row0 - w * WROWS;  // valid rows among this wave's rows
-  const int slab = w * WROWS + n * 16;
-  const int c = (lane & 3) ^ swz(slab + lr);
+  const int slab = w * WROWS + n * 8;
+  const int c = (lane & 7) ^ swz(slab + lr);
   if (!BLOCKED) {
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<bf16_t *>(s.base + (long long)row0 * s.ld + k), (short)0, 0x7fffffff, kBufferFlags);
     const int ldb = (int)s.ld * 2;
-    const bool ok = (n * 16 + lr) < nvw && c * 8 < s.kvalid - k;
+    const bool ok = (n * 8 + lr) < nvw && c * 8 < s.kvalid - k;
     const uint32_t voff = ok ? (uint32_t)(lr * ldb + c * 16) : kOutOfRange;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(lds_tile + slab * BK), 16, voff, slab * ldb, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(lds_tile + slab * SK), 16, voff, slab * ldb, 0, 0);
   } else {
-    const int ka0 = s.koff + k;  // absolute column of this stage's first column
+    const int ka0 = s.koff + k;  // absolute column of this slab's first column
     const int kb0 = ka0 >> 6;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<bf16_t *>(s.base + (long long)kb0 * s.kblk + (long long)row0 * 64), (short)0, 0x7fffffff,
         kBufferFlags);
     const int ka = ka0 + c * 8;
-    const bool ok = (n * 16 + lr) < nvw && (k + c * 8) < s.kvalid;
+    const bool ok = (n * 8 + lr) < nvw && (k + c * 8) < s.kvalid;
     const uint32_t voff =
         ok ? (uint32_t)(((ka >> 6) - kb0) * (int)s.kblk * 2 + lr * 128 + (ka & 63) * 2) : kOutOfRange;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(lds_tile + slab * BK), 16, voff, slab * 128, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(lds_tile + slab * SK), 16, voff, slab * 128, 0, 0);
   }
 }
 
-// buffer loads per wave per stage: A tile, then B tile
+// buffer loads per wave per slab: A tile, then B tile
 template <int WN, int NBJ>
-constexpr int loads_a() { return BM / (2 * WN) / 16; }
+constexpr int loads_a() { return BM / (2 * WN) / 8; }
 template <int WN, int NBJ>
-constexpr int loads_per_stage() { return loads_a<WN, NBJ>() + 32 * WN * NBJ / (2 * WN) / 16; }
+constexpr int loads_per_slab() { return loads_a<WN, NBJ>() + 32 * WN * NBJ / (2 * WN) / 8; }
 
-// Load j (0 <= j < loads_per_stage) of this wave for one stage.
+// Load j (0 <= j < loads_per_slab) of this wave for one slab.
 template <bool ABLK, bool BBLK, int WN, int NBJ>
-__device__ __forceinline__ void issue_part(Stage<WN, NBJ> &st, const Opnd &a, const Opnd &b, int arow0, int brow0,
+__device__ __forceinline__ void issue_part(Slab<WN, NBJ> &st, const Opnd &a, const Opnd &b, int arow0, int brow0,
                                            int k, int w, int lane, int j) {
   constexpr int LA = loads_a<WN, NBJ>();
   if (j < LA)
@@ -132,33 +138,31 @@ __device__ __forceinline__ void issue_part(Stage<WN, NBJ> &st, const Opnd &a, co
     issue_one<BBLK, 32 * WN * NBJ, 2 * WN>(st.b, b, brow0, k, w, lane, j - LA);
 }
 
-// All loads of this wave for one stage.
+// All loads of this wave for one slab.
 template <bool ABLK, bool BBLK, int WN, int NBJ>
-__device__ __forceinline__ void issue_stage(Stage<WN, NBJ> &st, const Opnd &a, const Opnd &b, int arow0, int brow0,
-                                            int k, int w, int lane) {
+__device__ __forceinline__ void issue_slab(Slab<WN, NBJ> &st, const Opnd &a, const Opnd &b, int arow0, int brow0,
+                                           int k, int w, int lane) {
 #pragma unroll
-  for (int j = 0; j < loads_per_stage<WN, NBJ>(); ++j)
+  for (int j = 0; j < loads_per_slab<WN, NBJ>(); ++j)
     issue_part<ABLK, BBLK>(st, a, b, arow0, brow0, k, w, lane, j);
 }
 
 // s_waitcnt immediate (gfx9): vmcnt(n), expcnt unchanged, lgkmcnt(0).
 constexpr unsigned wait_imm(int n) { return (unsigned)((n & 15) | 0x70 | (((n >> 4) & 3) << 14)); }
 
-// Wait until at most `later` stages of this wave's loads (LPS loads per stage)
+// Wait until at most `later` slabs of this wave's loads (LPS loads per slab)
 // are still in flight and its own LDS reads are done, then meet every wave at
-// the barrier: their loads of the awaited stage have landed too, and every
-// wave is done reading the stage computed before. Only LDS is shared between
+// the barrier: their loads of the awaited slab have landed too, and every
+// wave is done reading the slab computed before. Only LDS is shared between
 // the waves, so no memory fence is needed (a fence would also wait for the
-// loads of the stages still in flight).
+// loads of the slabs still in flight).
 template <int LPS>
-__device__ __forceinline__ void stage_wait(int later) {
+__device__ __forceinline__ void slab_wait(int later) {
   switch (later) {
     case 0: __builtin_amdgcn_s_waitcnt(wait_imm(0)); break;
     case 1: __builtin_amdgcn_s_waitcnt(wait_imm(LPS)); break;
     case 2: __builtin_amdgcn_s_waitcnt(wait_imm(2 * LPS)); break;
-    case 3: __builtin_amdgcn_s_waitcnt(wait_imm(3 * LPS)); break;
-    case 4: __builtin_amdgcn_s_waitcnt(wait_imm(4 * LPS)); break;
-    default: __builtin_amdgcn_s_waitcnt(wait_imm(5 * LPS)); break;
+    default: __builtin_amdgcn_s_waitcnt(wait_imm(3 * LPS)); break;
   }
   asm volatile("s_barrier" ::: "memory");
 }
@@ -170,11 +174,11 @@ struct Frag {
   bf16x8 a[4], b[NBJ];
 };
 
-// Read substep ks (0 or 1) of an LDS stage into registers.
+// Read substep ks (0 or 1) of half h (0 or 1) of an LDS slab into registers.
 template <int WN, int NBJ>
-__device__ __forceinline__ void frag_read(Frag<NBJ> &fr, const Stage<WN, NBJ> &st, int ks, int wm, int wn,
+__device__ __forceinline__ void frag_read(Frag<NBJ> &fr, const Slab<WN, NBJ> &st, int h, int ks, int wm, int wn,
                                           int lane) {
-  const int c = 2 * ks + (lane >> 5);
+  const int c = 4 * h + 2 * ks + (lane >> 5);
 #pragma unroll
   for (int bi = 0; bi < 4; ++bi)
     fr.a[bi] = *reinterpret_cast<const bf16x8 *>(st.a + lds_off(wm * 128 + bi * 32 + (lane & 31), c));
@@ -196,63 +200,72 @@ __device__ __forceinline__ void frag_mma(Acc<NBJ> &acc, const Frag<NBJ> &fr) {
 // Keep the compiler from moving instructions across this point.
 __device__ __forceinline__ void pin() { __builtin_amdgcn_sched_barrier(0); }
 
-// The software pipeline of one 32-deep stage kt. On entry `cur` holds (or is
-// loading) substep 0 of stage kt; on exit it holds substep 0 of stage kt+1.
-// Every LDS read and tile-load issue sits behind MFMAs already queued, so the
-// matrix cores keep running while they wait:
+// Issue point P (0..6) of a stage that refills a slab: loads [P*LPS/7, (P+1)*LPS/7).
+template <int LPS, int P, class IssueFn>
+__device__ __forceinline__ void issue_point(IssueFn &&issue_part, int slab) {
+#pragma unroll
+  for (int j = P * LPS / 7; j < (P + 1) * LPS / 7; ++j) issue_part(slab, j);
+}
+
+// The software pipeline of one 32-deep stage kt = half kt%2 of slab kt/2. On
+// entry `cur` holds (or is loading) substep 0 of stage kt; on exit it holds
+// substep 0 of stage kt+1. Every LDS read and tile-load issue sits behind
+// MFMAs already queued, so the matrix cores keep running while they wait:
 //   read substep 1 of kt -> nxt | MFMAs of row 0 on cur
-//   wait for stage kt+1 + barrier
+//   at the end of a slab: wait for the next slab + barrier
 //   MFMAs of rows 1-3 on cur and rows 0-3 on nxt, with this wave's loads of
-//   stage kt+NS (into kt's buffer) issued one at a time between them, and
+//   slab kt/2 + NSL (into the buffer just finished) issued between them, and
 //   substep 0 of kt+1 read into cur after nxt's first row.
-// After the barrier no wave reads stage kt's buffer again (all its reads were
-// issued before, and the wait includes lgkmcnt(0)), so it can be refilled.
-// Spreading the loads keeps a burst of them from stalling the MFMA issue.
-// With AFTER, after_fn(acc) runs once all of stage kt's MFMAs are queued, and
-// the next fragments are read only then (few registers live).
-template <int WN, int NBJ, int NS, bool AFTER, class IssueFn, class AfterFn>
-__device__ __forceinline__ void pipelined_stage(Acc<NBJ> &acc, Stage<WN, NBJ> *ring, Frag<NBJ> &cur, Frag<NBJ> &nxt,
+// After the barrier no wave reads the finished slab's buffer again (all its
+// reads were issued before, and the wait includes lgkmcnt(0)), so it can be
+// refilled. Spreading the loads keeps a burst of them from stalling the MFMA
+// issue. With AFTER, after_fn(acc) runs once all of stage kt's MFMAs are
+// queued, and the next fragments are read only then (few registers live).
+template <int WN, int NBJ, int NSL, bool AFTER, class IssueFn, class AfterFn>
+__device__ __forceinline__ void pipelined_stage(Acc<NBJ> &acc, Slab<WN, NBJ> *ring, Frag<NBJ> &cur, Frag<NBJ> &nxt,
                                                 int kt, int nk, int wm, int wn, int lane, IssueFn &&issue_part,
                                                 AfterFn &&after_fn) {
-  constexpr int LPS = loads_per_stage<WN, NBJ>();
-  static_assert(LPS <= 7, "one load per MFMA row group");
-  frag_read(nxt, ring[kt % NS], 1, wm, wn, lane);
+  constexpr int LPS = loads_per_slab<WN, NBJ>();
+  const int sl = kt >> 1, h = kt & 1;
+  const int nsl = (nk + 1) >> 1;
+  frag_read(nxt, ring[sl % NSL], h, 1, wm, wn, lane);
   pin();
   frag_mma<0, 1>(acc, cur);
   pin();
   const bool more = kt + 1 < nk;
-  const bool refill = kt + NS < nk;
-  if (more) {
-    const int later = (nk - 2 - kt) < (NS - 2) ? (nk - 2 - kt) : (NS - 2);
-    stage_wait<LPS>(later);
+  const bool refill = h == 1 && sl + NSL < nsl;
+  if (more && h == 1) {
+    const int later = (nsl - 2 - sl) < (NSL - 2) ? (nsl - 2 - sl) : (NSL - 2);
+    slab_wait<LPS>(later);
   }
+  const int rs = sl + NSL;
   pin();
   frag_mma<1, 2>(acc, cur);
-  if (refill && LPS > 0) issue_part(kt + NS, 0);
+  if (refill) issue_point<LPS, 0>(issue_part, rs);
   pin();
   frag_mma<2, 3>(acc, cur);
-  if (refill && LPS > 1) issue_part(kt + NS, 1);
+  if (refill) issue_point<LPS, 1>(issue_part, rs);
   pin();
   frag_mma<3, 4>(acc, cur);
-  if (refill && LPS > 2) issue_part(kt + NS, 2);
+  if (refill) issue_point<LPS, 2>(issue_part, rs);
   pin();
   frag_mma<0, 1>(acc, nxt);
   pin();
-  if (!AFTER && more) frag_read(cur, ring[(kt + 1) % NS], 0, wm, wn, lane);
-  if (refill && LPS > 3) issue_part(kt + NS, 3);
+  if (!AFTER && more) frag_read(cur, ring[((kt + 1) >> 1) % NSL], (kt + 1) & 1, 0, wm, wn, lane);
+  if (refill) issue_point<LPS, 3>(issue_part, rs);
   pin();
   frag_mma<1, 2>(acc, nxt);
-  if (refill && LPS > 4) issue_part(kt + NS, 4);
+  if (refill) issue_point<LPS, 4>(issue_part, rs);
   pin();
   frag_mma<2, 3>(acc, nxt);
-  if (refill && LPS > 5) issue_part(kt + NS, 5);
+  if (refill) issue_point<LPS, 5>(issue_part, rs);
   pin();
   frag_mma<3, 4>(acc, nxt);
-  if (refill && LPS > 6) issue_part(kt + NS, 6);
+  if (refill) issue_point<LPS, 6>(issue_part, rs);
   pin();
   if (AFTER) {
     after_fn(acc);
-    if (more) frag_read(cur, ring[(kt + 1) % NS], 0, wm, wn, lane);
+    if (more) frag_read(cur, ring[((kt + 1) >> 1) % NSL], (kt + 1) & 1, 0, wm, wn, lane);
     pin();
   }
 }
@@ -263,10 +276,10 @@ struct NoHook {
 };
 
 constexpr int WN_W = 4, NBJ_W = 2;  // wide GEMMs: 8 waves, 256 x 256 tiles
-constexpr int NS_W = 5;              // 5 x 32 KB ring (all of the LDS)
+constexpr int NSL_W = 2;             // 2 x 64 KB slabs
 constexpr int NT_W = 64 * 2 * WN_W;  // 512 threads
 constexpr int WN_U = 2, NBJ_U = 2;   // state update: 4 waves, 256 x 128 tiles
-constexpr int NS_U = 6;              // 6 x 24 KB ring
+constexpr int NSL_U = 3;             // 3 x 48 KB slabs
 constexpr int NT_U = 64 * 2 * WN_U;  // 256 threads
 
 // wave coordinates: wm selects the 128-row half along i, wn the column slice along j
@@ -297,32 +310,30 @@ __device__ __forceinline__ void band_tile(int t, int nx, int ny, int H, int &x, 
 }
 
 // K loop over segment 1 (nk1 stages, both operands row-major) then segment 2
-// (nk2 stages; its A operand K-blocked when A2BLK). 256 x 256 tiles.
+// (nk2 stages; its A operand K-blocked when A2BLK). nk1 is even, so no slab
+// straddles the two segments. 256 x 256 tiles.
 template <bool A2BLK>
-__device__ __forceinline__ void gemm_loop(Acc<NBJ_W> &acc, Stage<WN_W, NBJ_W> *ring, const Opnd &a1, const Opnd &b1,
+__device__ __forceinline__ void gemm_loop(Acc<NBJ_W> &acc, Slab<WN_W, NBJ_W> *ring, const Opnd &a1, const Opnd &b1,
                                           int nk1, const Opnd &a2, const Opnd &b2, int nk2, int arow0, int brow0) {
   const int lane = threadIdx.x & 63;
   const int w = wave_id(), wm = w & 1, wn = w >> 1;
   const int nk = nk1 + nk2;
   if (nk <= 0) return;
-  auto issue = [&](int kt) {
-    if (kt < nk1)
-      issue_stage<false, false>(ring[kt % NS_W], a1, b1, arow0, brow0, kt * BK, w, lane);
+  const int ns1 = nk1 >> 1, nsl = (nk + 1) >> 1;
+  auto part = [&](int sl, int j) {
+    if (sl < ns1)
+      issue_part<false, false>(ring[sl % NSL_W], a1, b1, arow0, brow0, sl * SK, w, lane, j);
     else
-      issue_stage<A2BLK, false>(ring[kt % NS_W], a2, b2, arow0, brow0, (kt - nk1) * BK, w, lane);
+      issue_part<A2BLK, false>(ring[sl % NSL_W], a2, b2, arow0, brow0, (sl - ns1) * SK, w, lane, j);
   };
-  auto part = [&](int kt, int j) {
-    if (kt < nk1)
-      issue_part<false, false>(ring[kt % NS_W], a1, b1, arow0, brow0, kt * BK, w, lane, j);
-    else
-      issue_part<A2BLK, false>(ring[kt % NS_W], a2, b2, arow0, brow0, (kt - nk1) * BK, w, lane, j);
-  };
-  for (int kt = 0; kt < NS_W && kt < nk; ++kt) issue(kt);
+  for (int sl = 0; sl < NSL_W && sl < nsl; ++sl)
+#pragma unroll
+    for (int j = 0; j < loads_per_slab<WN_W, NBJ_W>(); ++j) part(sl, j);
   Frag<NBJ_W> cur, nxt;
-  stage_wait<loads_per_stage<WN_W, NBJ_W>()>((nk - 1) < (NS_W - 1) ? (nk - 1) : (NS_W - 1));
-  frag_read(cur, ring[0], 0, wm, wn, lane);
+  slab_wait<loads_per_slab<WN_W, NBJ_W>()>((nsl - 1) < (NSL_W - 1) ? (nsl - 1) : (NSL_W - 1));
+  frag_read(cur, ring[0], 0, 0, wm, wn, lane);
   for (int kt = 0; kt < nk; ++kt)
-    pipelined_stage<WN_W, NBJ_W, NS_W, false>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, part, NoHook{});
+    pipelined_stage<WN_W, NBJ_W, NSL_W, false>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, part, NoHook{});
 }
 
 // ---------------------------------------------------------------------------
@@ -341,7 +352,7 @@ struct A1Args {
 };
 
 __global__ __launch_bounds__(NT_W, 1) void k_a1(A1Args p) {
-  __shared__ __attribute__((aligned(16))) Stage<WN_W, NBJ_W> ring[NS_W];
+  __shared__ __attribute__((aligned(16))) Slab<WN_W, NBJ_W> ring[NSL_W];
   int tx, ty;  // W_ug tile, token tile
   band_tile(xcd_tile(blockIdx.x, gridDim.x), p.nx, p.ny, 8, tx, ty);
   const int n0 = tx * 256;
@@ -418,7 +429,7 @@ __device__ __forceinline__ void dump_snapshot(const Acc<NBJ_U> &acc, bf16_t *lan
 }
 
 __global__ __launch_bounds__(NT_U, 1) void k_update(UpdArgs p) {
-  __shared__ __attribute__((aligned(16))) Stage<WN_U, NBJ_U> ring[NS_U];
+  __shared__ __attribute__((aligned(16))) Slab<WN_U, NBJ_U> ring[NSL_U];
   const int nx = p.f / BM, ny = p.d / 128;
   const int t = xcd_tile(blockIdx.x, gridDim.x);
   const int b = t / (nx * ny);
@@ -456,18 +467,20 @@ __global__ __launch_bounds__(NT_U, 1) void k_update(UpdArgs p) {
   const int nk = p.kend / BK;
   // Snapshot 0 is the entry state; group starts are multiples of the stage
   // depth, so snapshot g is written right after the last stage of group g-1,
-  // while the following stages are already in flight.
+  // while the following slabs are already in flight.
   dump_snapshot(acc, snap0, p.f);
   int g = 1;
-  auto issue = [&](int kt2) { issue_stage<true, true>(ring[kt2 % NS_U], sa, sb, i0, j0, kt2 * BK, w, lane); };
-  auto part = [&](int kt2, int j) {
-    issue_part<true, true>(ring[kt2 % NS_U], sa, sb, i0, j0, kt2 * BK, w, lane, j);
+  auto part = [&](int sl, int j) {
+    issue_part<true, true>(ring[sl % NSL_U], sa, sb, i0, j0, sl * SK, w, lane, j);
   };
-  for (int kt = 0; kt < NS_U && kt < nk; ++kt) issue(kt);
+  const int nsl = (nk + 1) >> 1;
+  for (int sl = 0; sl < NSL_U && sl < nsl; ++sl)
+#pragma unroll
+    for (int j = 0; j < loads_per_slab<WN_U, NBJ_U>(); ++j) part(sl, j);
   Frag<NBJ_U> cur, nxt;
   if (nk > 0) {
-    stage_wait<loads_per_stage<WN_U, NBJ_U>()>((nk - 1) < (NS_U - 1) ? (nk - 1) : (NS_U - 1));
-    frag_read(cur, ring[0], 0, wm, wn, lane);
+    slab_wait<loads_per_slab<WN_U, NBJ_U>()>((nsl - 1) < (NSL_U - 1) ? (nsl - 1) : (NSL_U - 1));
+    frag_read(cur, ring[0], 0, 0, wm, wn, lane);
   }
   auto snapshot = [&](const Acc<NBJ_U> &a) {
     dump_snapshot(a, snap0 + (long long)g * df, p.f);
@@ -482,12 +495,12 @@ __global__ __launch_bounds__(NT_U, 1) void k_update(UpdArgs p) {
   for (; g < p.ngroups; ) {
     const int kt_last = g * (p.L / BK) - 1;  // last stage before group g starts
     for (; kt < kt_last; ++kt)
-      pipelined_stage<WN_U, NBJ_U, NS_U, false>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, part, NoHook{});
-    pipelined_stage<WN_U, NBJ_U, NS_U, true>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, part, snapshot);
+      pipelined_stage<WN_U, NBJ_U, NSL_U, false>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, part, NoHook{});
+    pipelined_stage<WN_U, NBJ_U, NSL_U, true>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, part, snapshot);
     ++kt;
   }
   for (; kt < nk; ++kt)
-    pipelined_stage<WN_U, NBJ_U, NS_U, false>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, part, NoHook{});
+    pipelined_stage<WN_U, NBJ_U, NSL_U, false>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, part, NoHook{});
 #pragma unroll
   for (int bj = 0; bj < NBJ_U; ++bj) {
     float *row = st + (long long)bj * 32 * p.f;
@@ -514,7 +527,7 @@ struct ScoreArgs {
 };
 
 __global__ __launch_bounds__(NT_W, 1) void k_scores(ScoreArgs p) {
-  __shared__ __attribute__((aligned(16))) Stage<WN_W, NBJ_W> ring[NS_W];
+  __shared__ __attribute__((aligned(16))) Slab<WN_W, NBJ_W> ring[NSL_W];
   const int ntri = p.nt * (p.nt + 1) / 2;
   const int t = xcd_tile(blockIdx.x, gridDim.x);
   const int bg = t / ntri;  // b * ngroups + g
@@ -573,7 +586,7 @@ struct OutArgs {
 };
 
 __global__ __launch_bounds__(NT_W, 1) void k_out(OutArgs p) {
-  __shared__ __attribute__((aligned(16))) Stage<WN_W, NBJ_W> ring[NS_W];
+  __shared__ __attribute__((aligned(16))) Slab<WN_W, NBJ_W> ring[NSL_W];
   // one group's tiles are consecutive, token tiles fastest
   const int nx = p.d / BM, ny = (p.L + 255) / 256;
   const int t = xcd_tile(blockIdx.x, gridDim.x);
