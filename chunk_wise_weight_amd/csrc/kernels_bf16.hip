@@ -278,9 +278,17 @@ struct NoHook {
 constexpr int WN_W = 4, NBJ_W = 2;  // wide GEMMs: 8 waves, 256 x 256 tiles
 constexpr int NSL_W = 2;             // 2 x 64 KB slabs
 constexpr int NT_W = 64 * 2 * WN_W;  // 512 threads
+constexpr int WC_W = 32 * NBJ_W;     // columns per wave
 constexpr int WN_U = 2, NBJ_U = 2;   // state update: 4 waves, 256 x 128 tiles
 constexpr int NSL_U = 3;             // 3 x 48 KB slabs
 constexpr int NT_U = 64 * 2 * WN_U;  // 256 threads
+
+// LDS of the output GEMM: the K-loop ring, reused by the epilogue to turn the
+// MFMA register layout into whole-line stores of y.
+constexpr int LY_P = 264;  // [256 tokens][256 model dims + pad]: y
+constexpr int kRingBytes = (int)sizeof(Slab<WN_W, NBJ_W>) * NSL_W;
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+constexpr int kSmemOut = cmax(kRingBytes, 256 * LY_P * 2);
 
 // wave coordinates: wm selects the 128-row half along i, wn the column slice along j
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
@@ -396,24 +404,31 @@ __global__ __launch_bounds__(NT_W, 1) void k_a1(A1Args p) {
 
 // ---------------------------------------------------------------------------
 // State update with snapshots. i = hidden unit (ZT row), j = model dim (VT row),
-// k = token slot. The fp32 accumulators ARE the state W[a][i] for the
-// 256 (i) x 128 (a) tile and stay in registers for the whole token stream; at
-// each group start g*L the tile is written out as a bf16 snapshot.
-// grid: B * (f/256) * (d/128) workgroups
+// k = token slot. The fp32 accumulators ARE the state W[a][i] of one tile and
+// stay in registers for the whole token stream; at each group start g*L the
+// tile is written out as a bf16 snapshot.
+//
+// The state is cut into 256 x 256 tiles (i x a), numbered per sequence in
+// bands of 8 along a (see band_tile) and then across sequences. Whole rounds
+// of them (one per CU) run on the 8-wave configuration; a last partial round
+// of at most 128 tiles is split into 256 x 128 halves that run as one round
+// on the 4-wave configuration, so no CU idles for a whole round.
 struct UpdArgs {
   const bf16_t *ZT;
   const bf16_t *VT;
   float *state;
   bf16_t *snap;
   int T_pad, kend, L, ngroups, d, f;
+  int tile0;  // first 256 x 256 tile of this launch
 };
 
 // Write the accumulator tile as bf16 into a snapshot W[a][i] ([d][f]).
-// `lane_ptr` points at this lane's first element (a = j0 + wn*64 + l%32,
+// `lane_ptr` points at this lane's first element (a = j0 + wn*32*NBJ + l%32,
 // i = i0 + wm*128 + 4*(l/32)); tiles are always full (d, f multiples of 256).
-__device__ __forceinline__ void dump_snapshot(const Acc<NBJ_U> &acc, bf16_t *lane_ptr, int f) {
+template <int NBJ>
+__device__ __forceinline__ void dump_snapshot(const Acc<NBJ> &acc, bf16_t *lane_ptr, int f) {
 #pragma unroll
-  for (int bj = 0; bj < NBJ_U; ++bj) {
+  for (int bj = 0; bj < NBJ; ++bj) {
     bf16_t *row = lane_ptr + (long long)bj * 32 * f;
 #pragma unroll
     for (int bi = 0; bi < 4; ++bi) {
@@ -428,27 +443,32 @@ __device__ __forceinline__ void dump_snapshot(const Acc<NBJ_U> &acc, bf16_t *lan
   }
 }
 
-__global__ __launch_bounds__(NT_U, 1) void k_update(UpdArgs p) {
-  __shared__ __attribute__((aligned(16))) Slab<WN_U, NBJ_U> ring[NSL_U];
-  const int nx = p.f / BM, ny = p.d / 128;
-  const int t = xcd_tile(blockIdx.x, gridDim.x);
+// WN = 4: workgroup n of the launch is tile tile0 + n (a 256 x 256 tile);
+// WN = 2: workgroup n is half n%2 (128 columns of a) of tile tile0 + n/2.
+template <int WN, int NBJ, int NSL>
+__global__ __launch_bounds__(128 * WN, 1) void k_update(UpdArgs p) {
+  __shared__ __attribute__((aligned(16))) Slab<WN, NBJ> ring[NSL];
+  constexpr int BN = 32 * WN * NBJ;  // columns of a per workgroup
+  const int nx = p.f / BM, ny = p.d / 256;
+  const int n = xcd_tile(blockIdx.x, gridDim.x);
+  const int t = p.tile0 + n / (256 / BN);
   const int b = t / (nx * ny);
   int tx, ty;
   band_tile(t - b * nx * ny, nx, ny, 8, tx, ty);
   const int i0 = tx * BM;
-  const int j0 = ty * 128;
+  const int j0 = ty * 256 + (n % (256 / BN)) * BN;
   const int lane = threadIdx.x & 63;
   const int w = wave_id(), wm = w & 1, wn = w >> 1;
   const long long df = (long long)p.d * p.f;
   // this lane's first element of the tile, relative to W[0][0]
   const long long lane_off =
-      (long long)(j0 + wn * 64 + (lane & 31)) * p.f + i0 + wm * 128 + 4 * (lane >> 5);
+      (long long)(j0 + wn * 32 * NBJ + (lane & 31)) * p.f + i0 + wm * 128 + 4 * (lane >> 5);
   float *st = p.state + b * df + lane_off;
   bf16_t *snap0 = p.snap + (long long)b * p.ngroups * df + lane_off;
 
-  Acc<NBJ_U> acc;
+  Acc<NBJ> acc;
 #pragma unroll
-  for (int bj = 0; bj < NBJ_U; ++bj) {
+  for (int bj = 0; bj < NBJ; ++bj) {
     const float *row = st + (long long)bj * 32 * p.f;
 #pragma unroll
     for (int bi = 0; bi < 4; ++bi)
@@ -471,23 +491,24 @@ __global__ __launch_bounds__(NT_U, 1) void k_update(UpdArgs p) {
   dump_snapshot(acc, snap0, p.f);
   int g = 1;
   auto part = [&](int sl, int j) {
-    issue_part<true, true>(ring[sl % NSL_U], sa, sb, i0, j0, sl * SK, w, lane, j);
+    issue_part<true, true>(ring[sl % NSL], sa, sb, i0, j0, sl * SK, w, lane, j);
   };
   const int nsl = (nk + 1) >> 1;
-  for (int sl = 0; sl < NSL_U && sl < nsl; ++sl)
+  for (int sl = 0; sl < NSL && sl < nsl; ++sl)
 #pragma unroll
-    for (int j = 0; j < loads_per_slab<WN_U, NBJ_U>(); ++j) part(sl, j);
-  Frag<NBJ_U> cur, nxt;
+    for (int j = 0; j < loads_per_slab<WN, NBJ>(); ++j) part(sl, j);
+  Frag<NBJ> cur, nxt;
   if (nk > 0) {
-    slab_wait<loads_per_slab<WN_U, NBJ_U>()>((nsl - 1) < (NSL_U - 1) ? (nsl - 1) : (NSL_U - 1));
+    slab_wait<loads_per_slab<WN, NBJ>()>((nsl - 1) < (NSL - 1) ? (nsl - 1) : (NSL - 1));
     frag_read(cur, ring[0], 0, 0, wm, wn, lane);
   }
-  auto snapshot = [&](const Acc<NBJ_U> &a) {
+  // The snapshot stores share the vector-memory counter with the tile loads.
+  // The counted waits stay exact for the loads: loads complete in issue
+  // order among themselves, so while a load is outstanding every later load
+  // is too, and the count exceeds the number allowed; a store in flight can
+  // only make a wait last longer.
+  auto snapshot = [&](const Acc<NBJ> &a) {
     dump_snapshot(a, snap0 + (long long)g * df, p.f);
-    // Stores share the vector-memory counter with the tile loads and may
-    // complete out of order with them: drain it so the counted waits of the
-    // following stages stay exact.
-    __builtin_amdgcn_s_waitcnt(wait_imm(0));
     ++g;
   };
   // Stages of group g-1 run plain; its last stage ends with snapshot g.
@@ -495,14 +516,14 @@ __global__ __launch_bounds__(NT_U, 1) void k_update(UpdArgs p) {
   for (; g < p.ngroups; ) {
     const int kt_last = g * (p.L / BK) - 1;  // last stage before group g starts
     for (; kt < kt_last; ++kt)
-      pipelined_stage<WN_U, NBJ_U, NSL_U, false>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, part, NoHook{});
-    pipelined_stage<WN_U, NBJ_U, NSL_U, true>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, part, snapshot);
+      pipelined_stage<WN, NBJ, NSL, false>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, part, NoHook{});
+    pipelined_stage<WN, NBJ, NSL, true>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, part, snapshot);
     ++kt;
   }
   for (; kt < nk; ++kt)
-    pipelined_stage<WN_U, NBJ_U, NSL_U, false>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, part, NoHook{});
+    pipelined_stage<WN, NBJ, NSL, false>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, part, NoHook{});
 #pragma unroll
-  for (int bj = 0; bj < NBJ_U; ++bj) {
+  for (int bj = 0; bj < NBJ; ++bj) {
     float *row = st + (long long)bj * 32 * p.f;
 #pragma unroll
     for (int bi = 0; bi < 4; ++bi)
@@ -552,7 +573,7 @@ __global__ __launch_bounds__(NT_W, 1) void k_scores(ScoreArgs p) {
   bf16_t *Pg = p.P + ((long long)b * p.ngroups + g) * p.L * p.L;
 #pragma unroll
   for (int bj = 0; bj < NBJ_W; ++bj) {
-    const int t = j0 + wn * 64 + bj * 32 + (lane & 31);
+    const int t = j0 + wn * WC_W + bj * 32 + (lane & 31);
     if (t >= p.L) continue;
     const int ct = t / p.C;
 #pragma unroll
@@ -586,7 +607,8 @@ struct OutArgs {
 };
 
 __global__ __launch_bounds__(NT_W, 1) void k_out(OutArgs p) {
-  __shared__ __attribute__((aligned(16))) Slab<WN_W, NBJ_W> ring[NSL_W];
+  __shared__ __attribute__((aligned(16))) bf16_t smem[kSmemOut / 2];
+  Slab<WN_W, NBJ_W> *ring = reinterpret_cast<Slab<WN_W, NBJ_W> *>(smem);
   // one group's tiles are consecutive, token tiles fastest
   const int nx = p.d / BM, ny = (p.L + 255) / 256;
   const int t = xcd_tile(blockIdx.x, gridDim.x);
@@ -613,22 +635,33 @@ __global__ __launch_bounds__(NT_W, 1) void k_out(OutArgs p) {
   acc_zero(acc);
   gemm_loop<true>(acc, ring, sa1, sb1, p.f / BK, sa2, sb2, nk2, i0, j0);
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w & 1, wn = w >> 1;
+  // Epilogue through LDS ([token][model dim]) so y rows leave in whole lines.
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), wm = w & 1, wn = w >> 1;
+  bf16_t *ly = smem;
+  __syncthreads();  // every wave is done with the ring
 #pragma unroll
   for (int bj = 0; bj < NBJ_W; ++bj) {
-    const int t = j0 + wn * 64 + bj * 32 + (lane & 31);
-    if (t >= Lg) continue;
-    bf16_t *yrow = p.y + ((long long)b * p.T + gs + t) * p.d;
+    const int tl = wn * WC_W + bj * 32 + (lane & 31);
 #pragma unroll
     for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int a = i0 + wm * 128 + bi * 32 + 8 * q + 4 * (lane >> 5);
+        const int al = wm * 128 + bi * 32 + 8 * q + 4 * (lane >> 5);
         uint2 pk;
         pk.x = pack_bf16x2(acc.v[bi][bj][4 * q + 0], acc.v[bi][bj][4 * q + 1]);
         pk.y = pack_bf16x2(acc.v[bi][bj][4 * q + 2], acc.v[bi][bj][4 * q + 3]);
-        *reinterpret_cast<uint2 *>(yrow + a) = pk;
+        *reinterpret_cast<uint2 *>(ly + tl * LY_P + al) = pk;
       }
+  }
+  __syncthreads();
+  // 256 token rows x 512 bytes; rows past the group's end are not written
+#pragma unroll
+  for (int it = 0; it < 8192 / NT_W; ++it) {
+    const int idx = it * NT_W + tid;
+    const int tr = idx >> 5, ch = idx & 31;
+    if (j0 + tr < Lg)
+      *reinterpret_cast<uint4 *>(p.y + ((long long)b * p.T + gs + j0 + tr) * p.d + i0 + ch * 8) =
+          *reinterpret_cast<const uint4 *>(ly + tr * LY_P + ch * 8);
   }
 }
 
@@ -687,10 +720,18 @@ hipError_t launch_a1_bf16(const bf16_t *x, const bf16_t *Wug, bf16_t *Z, bf16_t 
 hipError_t launch_update_bf16(const bf16_t *ZT, const bf16_t *VT, float *state, bf16_t *snap, const Layout &lay,
                               hipStream_t s) {
   const int kend = (int)round_up_ll(lay.T, BK);
-  UpdArgs p{ZT, VT, state, snap, lay.T_pad, kend, lay.L, lay.ngroups, lay.d, lay.f};
-  const long long n = (long long)lay.B * (lay.f / BM) * (lay.d / 128);
-  if (n >= (1LL << 31)) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(k_update, dim3((unsigned)n), dim3(NT_U), 0, s, p);
+  const long long tiles = (long long)lay.B * (lay.f / BM) * (lay.d / 256);
+  if (tiles * 2 >= (1LL << 31)) return hipErrorInvalidConfiguration;
+  // whole rounds on the wide configuration, a last round of <= 128 tiles as halves
+  const int cus = 256;
+  const long long rem = tiles % cus;
+  const long long whole = rem <= cus / 2 ? tiles - rem : tiles;
+  UpdArgs p{ZT, VT, state, snap, lay.T_pad, kend, lay.L, lay.ngroups, lay.d, lay.f, 0};
+  if (whole > 0) hipLaunchKernelGGL((k_update<WN_W, NBJ_W, NSL_W>), dim3((unsigned)whole), dim3(NT_W), 0, s, p);
+  if (tiles > whole) {
+    p.tile0 = (int)whole;
+    hipLaunchKernelGGL((k_update<WN_U, NBJ_U, NSL_U>), dim3((unsigned)(2 * (tiles - whole))), dim3(NT_U), 0, s, p);
+  }
   return hipGetLastError();
 }
 

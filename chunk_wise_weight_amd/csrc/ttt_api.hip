@@ -159,6 +159,9 @@ struct Scratch {
   size_t total;
 };
 
+// Kernels move 16-byte vectors: device pointers handed in must be 16-byte aligned.
+bool misaligned(const void *p) { return ((uintptr_t)p & 15) != 0; }
+
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 Scratch scratch_layout(const ttt_handle *h, int B, const Plan &pl, bool need_zt, bool need_p) {
@@ -208,6 +211,8 @@ int ttt_init(ttt_handle **out, const void *W_up, const void *W_gate, const void 
   if (!out) return fail(TTT_E_NULL, "out is NULL");
   *out = nullptr;
   if (!W_up || !W_gate || !W_down0) return fail(TTT_E_NULL, "W_up, W_gate and W_down0 must be non-NULL");
+  if (misaligned(W_up) || misaligned(W_gate) || misaligned(W_down0))
+    return fail(TTT_E_ARG, "W_up, W_gate and W_down0 must be 16-byte aligned");
   if (dt != TTT_F32 && dt != TTT_BF16) return fail(TTT_E_DTYPE, "dtype must be TTT_F32 or TTT_BF16");
   if (d < 64 || f < 64 || d > kMaxDim || f > kMaxDim || d % 64 || f % 64)
     return fail(TTT_E_SHAPE, "d and f must be multiples of 64 in [64, 65536]");
@@ -315,6 +320,8 @@ int ttt_forward_chunked(ttt_handle *h, const void *x, const int32_t *ids, const 
   if (T < 0 || T > kMaxT) return fail(TTT_E_SHAPE, "T must be in [0, 2^23]");
   if (B > 0 && T > 0 && (!x || !ids || !E_tgt || !y)) return fail(TTT_E_NULL, "x, ids, E_tgt and y must be non-NULL");
   if (B > 0 && T > 0 && vocab < 1) return fail(TTT_E_SHAPE, "vocab must be >= 1");
+  if (B > 0 && T > 0 && (misaligned(x) || misaligned(E_tgt) || misaligned(y)))
+    return fail(TTT_E_ARG, "x, E_tgt and y must be 16-byte aligned");
   const bool learn = h->eta != 0.f;
   Plan pl;
   int rc = make_plan(T, h->C, learn ? h->G_override : 0, pl);

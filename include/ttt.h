@@ -64,7 +64,8 @@ enum {
  * ttt_init — create a handle for one layer.
  *
  *   W_up, W_gate : [f][d] frozen up and gate projections (dtype `dt`).
- *   W_down0      : [d][f] initial fast weight (dtype `dt`).
+ *   W_down0      : [d][f] initial fast weight (dtype `dt`). The three
+ *                  weight pointers must be 16-byte aligned.
  *   d, f         : model width and hidden width, at most 65536; multiples of
  *                  64 on the fp32 path and of 256 on the bf16 path (the MFMA
  *                  kernels work on whole 256 x 256 tiles of the state).
@@ -97,6 +98,8 @@ int ttt_init(ttt_handle **out, const void *W_up, const void *W_gate, const void 
  *   y       : [B][T][d] output (dtype of the handle), written in full.
  *   W_final : optional [B][d][f] fp32 output; receives each sequence's state
  *             after the block (NULL = not wanted).
+ *
+ * x, E_tgt and y must be 16-byte aligned (TTT_E_ARG otherwise).
  *
  * Each sequence starts from its current state (W_down0 after init or reset,
  * else what the previous call left) and keeps the final state in the handle,

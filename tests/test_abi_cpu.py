@@ -80,7 +80,7 @@ def test_plan_errors():
     assert "multiple of 32" in ttt.ttt_last_error()
 
 
-def _raw_init(W=(1, 1, 1), d=64, f=64, C=8, eta=0.1, dt=0, mb=1):
+def _raw_init(W=(16, 32, 48), d=64, f=64, C=8, eta=0.1, dt=0, mb=1):
     L = ttt.lib()
     h = ctypes.c_void_p(123)
     ptrs = [ctypes.c_void_p(v) for v in W]
@@ -101,6 +101,8 @@ def test_init_argument_errors():
     assert _raw_init(mb=0)[0] == -2
     assert _raw_init(eta=float("nan"))[0] == -7
     assert _raw_init(eta=float("inf"))[0] == -7
+    assert _raw_init(W=(16, 34, 48))[0] == -7  # weights must be 16-byte aligned
+    assert "aligned" in ttt.ttt_last_error()
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path")
