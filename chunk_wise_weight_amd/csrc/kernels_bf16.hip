@@ -251,7 +251,9 @@ __device__ __forceinline__ void pipelined_stage(Acc<NBJ> &acc, Slab<WN, NBJ> *ri
   pin();
   frag_mma<0, 1>(acc, nxt);
   pin();
-  if (!AFTER && more) frag_read(cur, ring[((kt + 1) >> 1) % NSL], (kt + 1) & 1, 0, wm, wn, lane);
+  // unconditional (past the end it reads a stale buffer of the ring): no
+  // branch, so the compiler can count the reads and wait for each exactly
+  if (!AFTER) frag_read(cur, ring[((kt + 1) >> 1) % NSL], (kt + 1) & 1, 0, wm, wn, lane);
   if (refill) issue_point<LPS, 3>(issue_part, rs);
   pin();
   frag_mma<1, 2>(acc, nxt);
@@ -265,7 +267,7 @@ __device__ __forceinline__ void pipelined_stage(Acc<NBJ> &acc, Slab<WN, NBJ> *ri
   pin();
   if (AFTER) {
     after_fn(acc);
-    if (more) frag_read(cur, ring[((kt + 1) >> 1) % NSL], (kt + 1) & 1, 0, wm, wn, lane);
+    frag_read(cur, ring[((kt + 1) >> 1) % NSL], (kt + 1) & 1, 0, wm, wn, lane);
     pin();
   }
 }
