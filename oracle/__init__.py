@@ -1,6 +1,7 @@
 """CPU oracle (test infrastructure only; see ttt_oracle's header)."""
 from .ttt_oracle import (  # noqa: F401
     chunk_ranges,
+    clip_update,
     final_state_columns,
     gated_activation,
     ntp_targets,

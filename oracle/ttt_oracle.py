@@ -25,11 +25,20 @@ the state a previous call left):
      sec. 4; paperlayer sec. 3 "Chunk-Wise Updates").
   4. Return y and the final S (inclusive of the last chunk's update).
 
+Optional update clipping (clip_tau): before a chunk's update is applied it is
+rescaled to Frobenius norm tau when its norm exceeds tau, i.e.
+dW <- dW * min(1, tau / ||dW||_F), with dW = eta V[chunk]^T Z[chunk] the
+whole chunk update (paperlayer App. C.2 "Inference Stability", where the
+threshold for the reported long-context evaluations is 1e-5; iplexlaw sec. 6,
+the closing implementation notes). Off by default.
+
 Readings of points the pages leave open (kept identical on both sides):
   - the update is the sum over the chunk's tokens (no 1/C), sign "+";
   - the one-token shift crosses chunk boundaries (the last row of chunk i takes
     token (i+1)C, which every later chunk already sees as input);
-  - no biases, no normalisation of Z or V, no update clipping.
+  - no biases, no normalisation of Z or V;
+  - clipping, when on, acts on each chunk's update as a whole (the "delta" of
+    the pages), after the learning rate is applied.
 
 Every function here is pinned by the CPU tests against closed forms, autograd,
 textbook special cases and invariants; none is "parity unpinned".
@@ -89,10 +98,23 @@ def chunk_ranges(T: int, C: int) -> List[Tuple[int, int]]:
     return [(s, min(s + C, T)) for s in range(0, T, C)]
 
 
+def clip_update(dW: np.ndarray, clip_tau: Optional[float]) -> np.ndarray:
+    """Rescale one chunk update to Frobenius norm clip_tau if it is larger
+    (paperlayer App. C.2; iplexlaw sec. 6). clip_tau None: unchanged."""
+    if clip_tau is None:
+        return dW
+    n = float(np.linalg.norm(dW))  # Frobenius norm of the whole matrix
+    if n > clip_tau:
+        return dW * (clip_tau / n)
+    return dW
+
+
 def ttt_forward_one(x: np.ndarray, ids: np.ndarray, E_tgt: np.ndarray, W_up: np.ndarray,
-                    W_gate: np.ndarray, W_entry: np.ndarray, C: int, eta: float):
+                    W_gate: np.ndarray, W_entry: np.ndarray, C: int, eta: float,
+                    clip_tau: Optional[float] = None):
     """Steps 1-4 for one sequence: x [T][d], ids [T+1], W_entry [d][f].
 
+    clip_tau: None, or the Frobenius threshold of each chunk update.
     Returns (y [T][d], W_final [d][f]) in fp64.
     """
     x = _f64(x)
@@ -105,12 +127,14 @@ def ttt_forward_one(x: np.ndarray, ids: np.ndarray, E_tgt: np.ndarray, W_up: np.
     V = ntp_targets(ids, E_tgt)
     for (s, e) in chunk_ranges(T, C):
         y[s:e] = Z[s:e] @ S.T                      # apply with the pre-update state
-        S = S + eta * (V[s:e].T @ Z[s:e])          # then the chunk's rank-C update
+        dW = eta * (V[s:e].T @ Z[s:e])             # the chunk's rank-C update
+        S = S + clip_update(dW, clip_tau)          # then applied (clipped if asked)
     return y, S
 
 
 def ttt_forward(x: np.ndarray, ids: np.ndarray, E_tgt: np.ndarray, W_up: np.ndarray,
-                W_gate: np.ndarray, W_entry: np.ndarray, C: int, eta: float):
+                W_gate: np.ndarray, W_entry: np.ndarray, C: int, eta: float,
+                clip_tau: Optional[float] = None):
     """Batched form: x [B][T][d], ids [B][T+1], W_entry [d][f] (shared entry
     state) or [B][d][f] (one state per sequence). Each sequence is independent.
 
@@ -122,7 +146,7 @@ def ttt_forward(x: np.ndarray, ids: np.ndarray, E_tgt: np.ndarray, W_up: np.ndar
     ys, Ws = [], []
     for b in range(B):
         Wb = W_entry if W_entry.ndim == 2 else W_entry[b]
-        yb, Sb = ttt_forward_one(x[b], ids[b], E_tgt, W_up, W_gate, Wb, C, eta)
+        yb, Sb = ttt_forward_one(x[b], ids[b], E_tgt, W_up, W_gate, Wb, C, eta, clip_tau)
         ys.append(yb)
         Ws.append(Sb)
     return np.stack(ys), np.stack(Ws)
@@ -140,6 +164,7 @@ def final_state_columns(x: np.ndarray, ids: np.ndarray, E_tgt: np.ndarray, W_up:
     of Z is too costly to form on the host.
 
     x [T][d], ids [T+1], W_entry [d][f]; returns [d][len(cols)] in fp64.
+    Unclipped updates only: a clipped update's scale depends on every column.
     """
     cols = list(cols)
     x = _f64(x)

@@ -1,7 +1,8 @@
 """Pins for the CPU oracle: checks against things other than the oracle itself.
 
 Each check takes `fwd`, a callable with the signature of oracle.ttt_forward
-(x [B][T][d], ids [B][T+1], E, W_up, W_gate, W_entry, C, eta) -> (y, W_final),
+(x [B][T][d], ids [B][T+1], E, W_up, W_gate, W_entry, C, eta, clip_tau=None)
+-> (y, W_final),
 and raises AssertionError when the callable disagrees with what the pages and
 the mathematics fix. The planted-mistake tests run the same checks against
 deliberately broken copies of the oracle and require each copy to fail one.
@@ -248,6 +249,81 @@ def check_zero_targets(fwd, seed=9):
     _close(W2[0], W0 + 0.7 * V.T @ Z, 1e-9, what="zero look-ahead W_final")
 
 
+# P11: update clipping (paperlayer App. C.2 "Inference Stability"; iplexlaw
+# sec. 6). The reference takes each chunk's norm through the chunk Grams,
+# ||V_i^T Z_i||_F^2 = sum((V_i V_i^T) * (Z_i Z_i^T)), not through the update
+# matrix itself, and applies the factors in the block-causal closed form.
+def clipped_closed_form(x, ids_row, E, Wu, Wg, W0, C, eta, tau):
+    Z = _torch_z(x, Wu, Wg).numpy()
+    V = _torch_v(ids_row, E).numpy()
+    T = Z.shape[0]
+    cidx = np.arange(T) // C
+    n_chunks = int(cidx.max()) + 1
+    c = np.ones(n_chunks)
+    norms = np.zeros(n_chunks)
+    for i in range(n_chunks):
+        sel = cidx == i
+        Zi, Vi = Z[sel], V[sel]
+        norms[i] = eta * np.sqrt(max(float(np.sum((Vi @ Vi.T) * (Zi @ Zi.T))), 0.0))
+        if norms[i] > tau:
+            c[i] = tau / norms[i]
+    M = (cidx[None, :] < cidx[:, None]) * c[cidx][None, :]
+    y = Z @ W0.T + eta * ((M * (Z @ Z.T)) @ V)
+    W = W0 + eta * (V * c[cidx][:, None]).T @ Z
+    return y, W, c, norms
+
+
+def check_clip_closed_form(fwd, seed=12):
+    rng = np.random.default_rng(seed)
+    x, ids, E, Wu, Wg, W0 = tiny_case(rng, d=6, f=10, B=2, T=23)
+    eta = 0.21
+    clipped = kept = 0
+    for C in (1, 3, 5, 23):
+        norms = np.concatenate([clipped_closed_form(x[b], ids[b], E, Wu, Wg, W0, C, eta, np.inf)[3]
+                                for b in range(2)])
+        tau = float(np.median(norms)) if len(norms) > 2 else 0.5 * float(norms.min())
+        y, W = fwd(x, ids, E, Wu, Wg, W0, C, eta, clip_tau=tau)
+        for b in range(2):
+            y_ref, W_ref, c, _ = clipped_closed_form(x[b], ids[b], E, Wu, Wg, W0, C, eta, tau)
+            clipped += int(np.sum(c < 1))
+            kept += int(np.sum(c == 1))
+            _close(y[b], y_ref, 1e-9, what=f"P11 C={C} b={b} y")
+            _close(W[b], W_ref, 1e-9, what=f"P11 C={C} b={b} W_final")
+    assert clipped > 0 and kept > 0
+
+
+def check_clip_limits(fwd, seed=13):
+    rng = np.random.default_rng(seed)
+    x, ids, E, Wu, Wg, W0 = tiny_case(rng, d=5, f=8, B=1, T=16)
+    eta = 0.4
+    # an infinite threshold never clips
+    y0, W0_ = fwd(x, ids, E, Wu, Wg, W0, 4, eta)
+    y1, W1 = fwd(x, ids, E, Wu, Wg, W0, 4, eta, clip_tau=np.inf)
+    assert np.array_equal(y0, y1) and np.array_equal(W0_, W1), "P11 tau=inf changed the result"
+    # a vanishing threshold leaves the textbook static MLP
+    y2, W2 = fwd(x, ids, E, Wu, Wg, W0, 4, eta, clip_tau=1e-300)
+    Z = _torch_z(x[0], Wu, Wg).numpy()
+    _close(y2[0], Z @ W0.T, 1e-12, what="P11 tau->0 y")
+    assert np.max(np.abs(W2[0] - W0)) <= 1e-290
+    # chunk by chunk: each applied update is the raw update scaled to norm min(norm, tau)
+    tau = 0.8 * float(np.min(clipped_closed_form(x[0], ids[0], E, Wu, Wg, W0, 4, eta, np.inf)[3]))
+    tau = max(tau, 1e-3)
+    W = W0.copy()
+    n_clipped = 0
+    for s in range(0, 16, 4):
+        xs, ids_s = x[:, s:s + 4], ids[:, s:s + 5]
+        _, Wn = fwd(xs, ids_s, E, Wu, Wg, W, 4, eta, clip_tau=tau)
+        _, Wr = fwd(xs, ids_s, E, Wu, Wg, W, 4, eta)
+        d_app, d_raw = Wn[0] - W, Wr[0] - W
+        n_raw = np.linalg.norm(d_raw)
+        _close(d_app, d_raw * (min(1.0, tau / n_raw) if n_raw > 0 else 1.0), 1e-9,
+               what=f"P11 chunk at {s} applied update")
+        assert abs(np.linalg.norm(d_app) - min(n_raw, tau)) <= 1e-9 * max(n_raw, tau)
+        n_clipped += int(n_raw > tau)
+        W = Wn[0]
+    assert n_clipped > 0
+
+
 ALL_PINS = [
     check_static_mlp,
     lambda fwd: check_static_mlp(fwd, square=True),
@@ -260,4 +336,6 @@ ALL_PINS = [
     check_batch_independence,
     check_induction,
     check_zero_targets,
+    check_clip_closed_form,
+    check_clip_limits,
 ]

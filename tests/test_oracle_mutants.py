@@ -13,7 +13,7 @@ from tests import pins
 
 
 def _loop_mutant(kind):
-    def one(x, ids, E_tgt, W_up, W_gate, W_entry, C, eta):
+    def one(x, ids, E_tgt, W_up, W_gate, W_entry, C, eta, clip_tau=None):
         x = np.asarray(x, dtype=np.float64)
         T = x.shape[0]
         S = np.asarray(W_entry, dtype=np.float64).copy()
@@ -25,7 +25,16 @@ def _loop_mutant(kind):
         S0 = S.copy()
         ranges = ot.chunk_ranges(T, C)
         for n, (s, e) in enumerate(ranges):
-            dW = eta * (V[s:e].T @ Z[s:e])
+            dW = ot.clip_update(eta * (V[s:e].T @ Z[s:e]), clip_tau)
+            if kind == "clip_accumulated":
+                # clips the change accumulated since the entry state, not the chunk update
+                y[s:e] = Z[s:e] @ S.T
+                S = S0 + ot.clip_update(S - S0 + eta * (V[s:e].T @ Z[s:e]), clip_tau)
+                continue
+            if kind == "clip_before_eta" and clip_tau is not None:
+                raw = V[s:e].T @ Z[s:e]
+                n = np.linalg.norm(raw)
+                dW = eta * raw * (min(1.0, clip_tau / n) if n > 0 else 1.0)
             if kind == "update_then_apply":
                 S = S + dW
                 y[s:e] = Z[s:e] @ S.T
@@ -91,6 +100,32 @@ def _chunks_overlap(T, C):
     return [(max(0, s - 1), min(s + C, T)) for s in range(0, T, C)]
 
 
+def _clip_always(dW, tau):
+    # rescales every update to norm tau (a normalisation, not a clip)
+    return dW if tau is None else dW * (tau / np.linalg.norm(dW))
+
+
+def _clip_maxabs(dW, tau):
+    if tau is None:
+        return dW
+    n = np.max(np.abs(dW))
+    return dW * (tau / n) if n > tau else dW
+
+
+def _clip_spectral(dW, tau):
+    if tau is None:
+        return dW
+    n = np.linalg.norm(dW, 2)
+    return dW * (tau / n) if n > tau else dW
+
+
+def _clip_squared(dW, tau):
+    if tau is None:
+        return dW
+    n2 = float(np.sum(dW * dW))
+    return dW * (tau / n2) if n2 > tau else dW
+
+
 def _sigmoid_wrong(g):
     g = np.asarray(g, dtype=np.float64)
     return g / (1.0 + np.exp(g))
@@ -112,6 +147,12 @@ MUTANTS = {
     "no_eta": ("ttt_forward_one", _loop_mutant("no_eta")),
     "drop_last_update": ("ttt_forward_one", _loop_mutant("drop_last_update")),
     "transposed_apply": ("ttt_forward_one", _loop_mutant("transposed_apply")),
+    "clip_always_to_tau": ("clip_update", _clip_always),
+    "clip_max_abs_norm": ("clip_update", _clip_maxabs),
+    "clip_spectral_norm": ("clip_update", _clip_spectral),
+    "clip_squared_norm": ("clip_update", _clip_squared),
+    "clip_accumulated_change": ("ttt_forward_one", _loop_mutant("clip_accumulated")),
+    "clip_before_eta": ("ttt_forward_one", _loop_mutant("clip_before_eta")),
 }
 
 
