@@ -36,7 +36,8 @@ def parse():
     ap.add_argument("--chunk", type=int, default=256)
     ap.add_argument("--seq-len", type=int, default=None, help="override T (default: the workload's 131072)")
     ap.add_argument("--group-chunks", type=int, default=0)
-    ap.add_argument("--no-sweep", action="store_true", help="skip the C=128 leg of the chunk sweep")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the extra legs: C=128, and update clipping at tau=1e-5")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-baseline duration")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -44,10 +45,15 @@ def parse():
     return ap.parse_args()
 
 
+def ttt_phases():
+    import chunk_wise_weight_amd as ttt
+    return ttt.PHASES
+
+
 def algorithmic_flops(d, f, tokens):
     # per token: up/gate 4df, output 2df, update 2df
     return {"up_gate_swiglu": 4.0 * d * f * tokens, "update_snapshots": 2.0 * d * f * tokens,
-            "group_scores": 0.0, "output": 2.0 * d * f * tokens}
+            "group_scores": 0.0, "output": 2.0 * d * f * tokens, "clip_factors": 0.0}
 
 
 def measured_traffic(kernel, C):
@@ -88,7 +94,7 @@ def copy_calibration():
     torch.cuda.empty_cache()
 
 
-def run_gpu(w, C, steps, warmup, G):
+def run_gpu(w, C, steps, warmup, G, clip_tau=0.0):
     import numpy as np
     import torch
 
@@ -102,6 +108,8 @@ def run_gpu(w, C, steps, warmup, G):
     h = ttt.ttt_init(dev(w.W_up), dev(w.W_gate), dev(w.W_down0), C, w.eta, max_batch=w.B)
     if G:
         ttt.ttt_set_group_chunks(h, G)
+    if clip_tau:
+        ttt.ttt_set_clip(h, clip_tau)
     x, E = dev(w.x), dev(w.E_tgt)
     ids = torch.from_numpy(np.ascontiguousarray(w.ids)).cuda()
     y = torch.empty((w.B, w.T, w.d), dtype=dt, device="cuda")
@@ -110,7 +118,7 @@ def run_gpu(w, C, steps, warmup, G):
         ttt.ttt_reset(h)
         ttt.ttt_forward_chunked(h, x, ids, E, y=y)
     torch.cuda.synchronize()
-    phase_sum = [0.0] * 6
+    phase_sum = [0.0] * len(ttt.PHASES)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -186,7 +194,7 @@ def main():
         copy_calibration()
     r = run_gpu(w, a.chunk, a.steps, a.warmup, a.group_chunks)
     ms = r["event_ms"] / a.steps
-    names = ["gather", "up_gate_swiglu", "update_snapshots", "group_scores", "output", "final_copy"]
+    names = list(ttt_phases())
     phases = dict(zip(names, r["phase_ms"]))
     print(f"[bench] C={a.chunk}: {ms:.2f} ms/step, phases " +
           ", ".join(f"{k} {v:.3f}" for k, v in phases.items()), file=sys.stderr, flush=True)
@@ -226,6 +234,12 @@ def main():
                                        "mfma_frac_layer": total_flops / (ms2 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                                        "phase_ms": dict(zip(names, r2["phase_ms"]))}}
         w.C = a.chunk
+    if not a.no_sweep:
+        # the pages' long-context setting: Frobenius clipping of each chunk update at 1e-5
+        r3 = run_gpu(w, a.chunk, a.steps, a.warmup, a.group_chunks, clip_tau=1e-5)
+        ms3 = r3["event_ms"] / a.steps
+        out["clip_leg"] = {"clip_tau": 1e-5, "tokens_per_s": tokens / (ms3 * 1e-3), "ms_per_step": ms3,
+                           "phase_ms": dict(zip(names, r3["phase_ms"]))}
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, a.chunk, a.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -20,7 +20,8 @@ TTT_F32, TTT_BF16 = 0, 1
 ERRORS = {-1: "TTT_E_NULL", -2: "TTT_E_SHAPE", -3: "TTT_E_DTYPE", -4: "TTT_E_NOMEM", -5: "TTT_E_HIP",
           -6: "TTT_E_NODEV", -7: "TTT_E_ARG"}
 EXPORTS = ("ttt_init", "ttt_forward_chunked", "ttt_reset", "ttt_destroy", "ttt_last_error",
-           "ttt_set_group_chunks", "ttt_plan", "ttt_set_profiling", "ttt_phase_times", "ttt_workspace_bytes")
+           "ttt_set_group_chunks", "ttt_set_clip", "ttt_plan", "ttt_set_profiling", "ttt_phase_times",
+           "ttt_workspace_bytes")
 
 _lib = None
 
@@ -52,6 +53,8 @@ def lib() -> ctypes.CDLL:
     L.ttt_last_error.restype = ctypes.c_char_p
     L.ttt_set_group_chunks.argtypes = [vp, i32]
     L.ttt_set_group_chunks.restype = i32
+    L.ttt_set_clip.argtypes = [vp, f32]
+    L.ttt_set_clip.restype = i32
     ip = ctypes.POINTER(i32)
     L.ttt_plan.argtypes = [i32, i32, i32, ip, ip, ip, ip]
     L.ttt_plan.restype = i32
@@ -178,6 +181,11 @@ def ttt_set_group_chunks(h: Handle, G: int) -> None:
     _check(lib().ttt_set_group_chunks(h.ptr, int(G)), "ttt_set_group_chunks")
 
 
+def ttt_set_clip(h: Handle, tau: float) -> None:
+    """Frobenius clipping of each chunk update at threshold tau (0 or inf: off)."""
+    _check(lib().ttt_set_clip(h.ptr, float(tau)), "ttt_set_clip")
+
+
 def ttt_plan(T: int, C: int, G: int = 0) -> Dict[str, int]:
     """Host-only: the group layout a call with T tokens and chunk C uses."""
     g, L, n, tp = (ctypes.c_int() for _ in range(4))
@@ -190,13 +198,13 @@ def ttt_set_profiling(h: Handle, on: bool = True) -> None:
     _check(lib().ttt_set_profiling(h.ptr, 1 if on else 0), "ttt_set_profiling")
 
 
-PHASES = ("gather", "up_gate_swiglu", "update_snapshots", "group_scores", "output", "final_copy")
+PHASES = ("gather", "up_gate_swiglu", "clip_factors", "update_snapshots", "group_scores", "output", "final_copy")
 
 
 def ttt_phase_times(h: Handle) -> List[float]:
     """Milliseconds per phase of the most recent profiled forward (waits for it)."""
-    buf = (ctypes.c_float * 6)()
-    _check(lib().ttt_phase_times(h.ptr, buf, 6), "ttt_phase_times")
+    buf = (ctypes.c_float * len(PHASES))()
+    _check(lib().ttt_phase_times(h.ptr, buf, len(PHASES)), "ttt_phase_times")
     return list(buf)
 
 

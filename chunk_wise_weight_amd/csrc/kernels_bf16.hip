@@ -346,6 +346,27 @@ __device__ __forceinline__ void gemm_loop(Acc<NBJ_W> &acc, Slab<WN_W, NBJ_W> *ri
     pipelined_stage<WN_W, NBJ_W, NSL_W, false>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, part, NoHook{});
 }
 
+// K loop over one row-major segment of nk stages for any configuration.
+template <int WN, int NBJ, int NSL>
+__device__ __forceinline__ void gemm_rows(Acc<NBJ> &acc, Slab<WN, NBJ> *ring, const Opnd &a, const Opnd &b, int nk,
+                                          int arow0, int brow0) {
+  const int lane = threadIdx.x & 63;
+  const int w = wave_id(), wm = w & 1, wn = w >> 1;
+  if (nk <= 0) return;
+  const int nsl = (nk + 1) >> 1;
+  auto part = [&](int sl, int j) {
+    issue_part<false, false>(ring[sl % NSL], a, b, arow0, brow0, sl * SK, w, lane, j);
+  };
+  for (int sl = 0; sl < NSL && sl < nsl; ++sl)
+#pragma unroll
+    for (int j = 0; j < loads_per_slab<WN, NBJ>(); ++j) part(sl, j);
+  Frag<NBJ> cur, nxt;
+  slab_wait<loads_per_slab<WN, NBJ>()>((nsl - 1) < (NSL - 1) ? (nsl - 1) : (NSL - 1));
+  frag_read(cur, ring[0], 0, 0, wm, wn, lane);
+  for (int kt = 0; kt < nk; ++kt)
+    pipelined_stage<WN, NBJ, NSL, false>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, part, NoHook{});
+}
+
 // ---------------------------------------------------------------------------
 // Up/gate GEMM with SwiGLU epilogue. i = token slot, j = interleaved W_ug row.
 // Writes Z [B][T_pad][f] (row-major) and eta*Z^T K-blocked [B][T_pad/64][f][64].
@@ -668,12 +689,81 @@ __global__ __launch_bounds__(NT_W, 1) void k_out(OutArgs p) {
 }
 
 // ---------------------------------------------------------------------------
+// Chunk Gram products for update clipping: ||V_i^T Z_i||_F^2 equals the sum of
+// (V_i V_i^T) * (Z_i Z_i^T) over the chunk's token pairs. For s-tile u (256
+// tokens) and t-tile w (128 tokens) of one sequence, G_Z = Z_s Z_t^T (K = f)
+// and G_V = V_s V_t^T (K = d) go into two sets of accumulators; the entries
+// with s and t in the same chunk contribute G_V * G_Z, summed per row s into
+// rowpart[b][u][wr][s % 256] (wr = w - first t-tile that can share a chunk
+// with the s-tile). Summing a chunk's rows over every wr gives its squared
+// norm; the sums run in a fixed order, so results are deterministic.
+// grid: B * (T_pad/256) * wspan workgroups of 256 threads
+struct GramArgs {
+  const bf16_t *Z;  // [B][T_pad][f]
+  const bf16_t *V;  // [B][T_pad][d], rows past T zero
+  float *rowpart;   // [B][T_pad/256][wspan][256]
+  int T, T_pad, C, d, f, wspan;
+};
+
+constexpr int GR_P = 129;  // fp32 pitch of the [256][128] product tile in LDS (conflict-free row sums)
+
+__global__ __launch_bounds__(NT_U, 1) void k_chunk_gram(GramArgs p) {
+  __shared__ __attribute__((aligned(16))) Slab<WN_U, NBJ_U> ring[NSL_U];
+  static_assert(sizeof(ring) >= sizeof(float) * 256 * GR_P, "the product tile reuses the ring");
+  const int nu = p.T_pad / 256;
+  const int wr = blockIdx.x % p.wspan;
+  const int u = (blockIdx.x / p.wspan) % nu;
+  const int b = blockIdx.x / (p.wspan * nu);
+  const int s0 = u * 256;
+  float *out = p.rowpart + (((long long)b * nu + u) * p.wspan + wr) * 256;
+  const int s_last = (s0 + 255 < p.T - 1) ? s0 + 255 : p.T - 1;
+  const int w = (int)((long long)(s0 / p.C) * p.C / 128) + wr;
+  const long long w_end = (((long long)(s_last / p.C) + 1) * p.C - 1) / 128;
+  const int w_hi = (int)(w_end < p.T_pad / 128 - 1 ? w_end : p.T_pad / 128 - 1);
+  if (s0 >= p.T || w > w_hi) {  // no token pair of this tile shares a chunk
+    out[threadIdx.x] = 0.f;
+    return;
+  }
+  const int t0 = w * 128;
+  const bf16_t *Zb = p.Z + (long long)b * p.T_pad * p.f;
+  const bf16_t *Vb = p.V + (long long)b * p.T_pad * p.d;
+  Acc<NBJ_U> az, av;
+  acc_zero(az);
+  acc_zero(av);
+  const Opnd oz = rowmajor(Zb, p.f, p.T_pad, p.f), ov = rowmajor(Vb, p.d, p.T_pad, p.d);
+  gemm_rows<WN_U, NBJ_U, NSL_U>(az, ring, oz, oz, p.f / BK, s0, t0);
+  __syncthreads();  // the second pass refills the ring
+  gemm_rows<WN_U, NBJ_U, NSL_U>(av, ring, ov, ov, p.d / BK, s0, t0);
+  __syncthreads();  // the product tile reuses the ring
+  float *tile = reinterpret_cast<float *>(ring);
+  const int lane = threadIdx.x & 63, wv = wave_id(), wm = wv & 1, wn = wv >> 1;
+#pragma unroll
+  for (int bj = 0; bj < NBJ_U; ++bj) {
+    const int tl = wn * 32 * NBJ_U + bj * 32 + (lane & 31);
+    const int ct = (t0 + tl) / p.C;
+#pragma unroll
+    for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int sl = wm * 128 + bi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const bool same = (s0 + sl) / p.C == ct;
+        tile[sl * GR_P + tl] = same ? az.v[bi][bj][r] * av.v[bi][bj][r] : 0.f;
+      }
+  }
+  __syncthreads();
+  float sum = 0.f;
+  for (int t = 0; t < 128; ++t) sum += tile[threadIdx.x * GR_P + t];
+  out[threadIdx.x] = sum;
+}
+
+// ---------------------------------------------------------------------------
 // Target gather, transposed and K-blocked: V^T[b][p/64][a][p%64] = E[ids[b][p+1]][a].
 // A 64-slot x 64-feature tile passes through LDS so both the row reads of E and
-// the writes (one contiguous 8 KB block) are 16 B per lane.
+// the writes (one contiguous 8 KB block) are 16 B per lane. With Vrow non-null
+// the rows are also written row-major, Vrow[b][p][a] (used by update clipping).
 // grid: (T_pad/64, d/64, B)
-__global__ __launch_bounds__(256) void k_gather_vt(const int32_t *ids, const bf16_t *E, int vocab, bf16_t *VT, int T,
-                                                   int T_pad, int d) {
+__global__ __launch_bounds__(256) void k_gather_vt(const int32_t *ids, const bf16_t *E, int vocab, bf16_t *VT,
+                                                   bf16_t *Vrow, int T, int T_pad, int d) {
   __shared__ __attribute__((aligned(16))) bf16_t tile[64][72];
   const int p0 = blockIdx.x * 64, a0 = blockIdx.y * 64, b = blockIdx.z;
   const int tid = threadIdx.x, seg = tid & 7;
@@ -686,6 +776,7 @@ __global__ __launch_bounds__(256) void k_gather_vt(const int32_t *ids, const bf1
     uint4 v = make_uint4(0u, 0u, 0u, 0u);
     if (id >= 0 && id < vocab) v = *reinterpret_cast<const uint4 *>(E + (long long)id * d + a0 + seg * 8);
     *reinterpret_cast<uint4 *>(&tile[pl][seg * 8]) = v;
+    if (Vrow) *reinterpret_cast<uint4 *>(Vrow + ((long long)b * T_pad + pos) * d + a0 + seg * 8) = v;
   }
   __syncthreads();
   bf16_t *blk = VT + ((long long)b * (T_pad / 64) + blockIdx.x) * d * 64;
@@ -702,10 +793,19 @@ __global__ __launch_bounds__(256) void k_gather_vt(const int32_t *ids, const bf1
 
 }  // namespace
 
-hipError_t launch_gather_vt_bf16(const int32_t *ids, const bf16_t *E, int vocab, bf16_t *VT, const Layout &lay,
-                                 hipStream_t s) {
+hipError_t launch_gather_vt_bf16(const int32_t *ids, const bf16_t *E, int vocab, bf16_t *VT, bf16_t *Vrow,
+                                 const Layout &lay, hipStream_t s) {
   dim3 grid(lay.T_pad / 64, lay.d / 64, lay.B);
-  hipLaunchKernelGGL(k_gather_vt, grid, dim3(256), 0, s, ids, E, vocab, VT, lay.T, lay.T_pad, lay.d);
+  hipLaunchKernelGGL(k_gather_vt, grid, dim3(256), 0, s, ids, E, vocab, VT, Vrow, lay.T, lay.T_pad, lay.d);
+  return hipGetLastError();
+}
+
+hipError_t launch_chunk_gram_bf16(const bf16_t *Z, const bf16_t *Vrow, float *rowpart, int wspan, const Layout &lay,
+                                  hipStream_t s) {
+  const long long n = (long long)lay.B * (lay.T_pad / 256) * wspan;
+  if (n >= (1LL << 31)) return hipErrorInvalidConfiguration;
+  GramArgs p{Z, Vrow, rowpart, lay.T, lay.T_pad, lay.C, lay.d, lay.f, wspan};
+  hipLaunchKernelGGL(k_chunk_gram, dim3((unsigned)n), dim3(NT_U), 0, s, p);
   return hipGetLastError();
 }
 

@@ -223,8 +223,8 @@ __global__ __launch_bounds__(NT) void k_out_f32(const float *Z, const float *P, 
 }
 
 // V^T[b][a][p] = E[ids[b][p+1]][a]. grid (T_pad/64, d/64, B)
-__global__ __launch_bounds__(256) void k_gather_vt_f32(const int32_t *ids, const float *E, int vocab, float *VT, int T,
-                                                       int T_pad, int d) {
+__global__ __launch_bounds__(256) void k_gather_vt_f32(const int32_t *ids, const float *E, int vocab, float *VT,
+                                                       float *Vrow, int T, int T_pad, int d) {
   __shared__ float tile[64][65];
   __shared__ int tok[64];
   const int p0 = blockIdx.x * 64, a0 = blockIdx.y * 64, b = blockIdx.z;
@@ -237,7 +237,9 @@ __global__ __launch_bounds__(256) void k_gather_vt_f32(const int32_t *ids, const
   for (int idx = tid; idx < 64 * 64; idx += 256) {
     const int pl = idx >> 6, a = idx & 63;
     const int id = tok[pl];
-    tile[pl][a] = (id >= 0 && id < vocab) ? E[(long long)id * d + a0 + a] : 0.f;
+    const float v = (id >= 0 && id < vocab) ? E[(long long)id * d + a0 + a] : 0.f;
+    tile[pl][a] = v;
+    if (Vrow) Vrow[((long long)b * T_pad + p0 + pl) * d + a0 + a] = v;
   }
   __syncthreads();
   for (int idx = tid; idx < 64 * 64; idx += 256) {
@@ -248,10 +250,10 @@ __global__ __launch_bounds__(256) void k_gather_vt_f32(const int32_t *ids, const
 
 }  // namespace
 
-hipError_t launch_gather_vt_f32(const int32_t *ids, const float *E, int vocab, float *VT, const Layout &lay,
-                                hipStream_t s) {
+hipError_t launch_gather_vt_f32(const int32_t *ids, const float *E, int vocab, float *VT, float *Vrow,
+                                const Layout &lay, hipStream_t s) {
   dim3 grid(lay.T_pad / 64, lay.d / 64, lay.B);
-  hipLaunchKernelGGL(k_gather_vt_f32, grid, dim3(256), 0, s, ids, E, vocab, VT, lay.T, lay.T_pad, lay.d);
+  hipLaunchKernelGGL(k_gather_vt_f32, grid, dim3(256), 0, s, ids, E, vocab, VT, Vrow, lay.T, lay.T_pad, lay.d);
   return hipGetLastError();
 }
 

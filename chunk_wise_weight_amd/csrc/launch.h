@@ -4,9 +4,10 @@
 #include "common.h"
 
 // ---- bf16 path: MFMA kernels (kernels_bf16.hip) ----
-// V^T[b][a][p] = E[ids[b][p+1]][a] for p < T and a valid id, else 0.     [B][d][T_pad]
-hipError_t launch_gather_vt_bf16(const int32_t *ids, const bf16_t *E, int vocab, bf16_t *VT, const Layout &lay,
-                                 hipStream_t s);
+// V^T[b][a][p] = E[ids[b][p+1]][a] for p < T and a valid id, else 0; K-blocked [B][T_pad/64][d][64].
+// Vrow (nullable): the same rows row-major, [B][T_pad][d].
+hipError_t launch_gather_vt_bf16(const int32_t *ids, const bf16_t *E, int vocab, bf16_t *VT, bf16_t *Vrow,
+                                 const Layout &lay, hipStream_t s);
 // Z = SiLU(x W_gate^T) * (x W_up^T) -> Z [B][T_pad][f] and ZT = eta*Z^T [B][f][T_pad].
 // Wug: [2f][d], rows interleaved in blocks of 32 (32 up rows, then the matching 32 gate rows).
 hipError_t launch_a1_bf16(const bf16_t *x, const bf16_t *Wug, bf16_t *Z, bf16_t *ZT, float eta, int write_zt,
@@ -19,10 +20,13 @@ hipError_t launch_scores_bf16(const bf16_t *Z, bf16_t *P, float eta, const Layou
 // y[b][gL+t] = Z[gL+t] snap[b][g]^T + sum_s P[b][g][t][s] V[gL+s].
 hipError_t launch_out_bf16(const bf16_t *Z, const bf16_t *P, const bf16_t *snap, const bf16_t *VT, bf16_t *y,
                            const Layout &lay, hipStream_t s);
+// Per-row chunk Gram sums for clipping: rowpart [B][T_pad/256][wspan][256] fp32.
+hipError_t launch_chunk_gram_bf16(const bf16_t *Z, const bf16_t *Vrow, float *rowpart, int wspan, const Layout &lay,
+                                  hipStream_t s);
 
 // ---- fp32 path: FMA kernels (kernels_f32.hip), same buffers and meaning in fp32 ----
-hipError_t launch_gather_vt_f32(const int32_t *ids, const float *E, int vocab, float *VT, const Layout &lay,
-                                hipStream_t s);
+hipError_t launch_gather_vt_f32(const int32_t *ids, const float *E, int vocab, float *VT, float *Vrow,
+                                const Layout &lay, hipStream_t s);
 // Wug: [2][f][d] (W_up then W_gate).
 hipError_t launch_a1_f32(const float *x, const float *Wug, float *Z, float *ZT, float eta, int write_zt,
                          const Layout &lay, hipStream_t s);
@@ -31,6 +35,19 @@ hipError_t launch_update_f32(const float *ZT, const float *VT, float *state, flo
 hipError_t launch_scores_f32(const float *Z, float *P, float eta, const Layout &lay, hipStream_t s);
 hipError_t launch_out_f32(const float *Z, const float *P, const float *snap, const float *VT, float *y,
                           const Layout &lay, hipStream_t s);
+
+// ---- update clipping (kernels_clip.hip) ----
+// t-tiles per s-tile in rowpart (1 on the fp32 path) and chunks per sequence of a call.
+int clip_wspan(const Layout &lay, bool bf16);
+int clip_chunks(const Layout &lay);
+// fp32 path: rowpart [B][T_pad] (wspan 1).
+hipError_t launch_chunk_gram_f32(const float *Z, const float *Vrow, float *rowpart, const Layout &lay, hipStream_t s);
+// c[b][i] = min(1, tau / (|eta| sqrt(sum of chunk i's rows of rowpart))).
+hipError_t launch_chunk_factors(const float *rowpart, float *cfac, int wspan, float eta, float tau, const Layout &lay,
+                                hipStream_t s);
+// Scale slot t of V^T by c[b][t / C] (K-blocked bf16 / row-major fp32 layouts).
+hipError_t launch_scale_vt_bf16(bf16_t *VT, const float *cfac, const Layout &lay, hipStream_t s);
+hipError_t launch_scale_vt_f32(float *VT, const float *cfac, const Layout &lay, hipStream_t s);
 
 // ---- layout helpers (kernels_misc.hip) ----
 // Wug[2f][d] from W_up[f][d], W_gate[f][d]: 32-row blocks, up block then gate block.

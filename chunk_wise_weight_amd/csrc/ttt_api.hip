@@ -4,6 +4,8 @@
 // One call of ttt_forward_chunked runs, on the caller's stream:
 //   1. target gather      V^T = E_tgt[ids shifted by one]^T       (next-token target)
 //   2. up/gate GEMM       Z = SiLU(x W_gate^T) * (x W_up^T), and eta*Z^T
+//   2b. optional clipping per-chunk factors c_i = min(1, tau/||eta V_i^T Z_i||_F)
+//                         from chunk Grams; V^T's rows of chunk i scaled by c_i
 //   3. state update       W += (eta Z)^T-weighted rank-C updates over the whole
 //                         block, the fp32 state resident in registers; a
 //                         snapshot of W at the start of every group of G chunks
@@ -44,6 +46,8 @@ constexpr int kMaxT = 1 << 23;
 constexpr int kDefaultGroupTokens = 1024;
 // group starts fall on the update kernel's 32-token stage boundaries
 constexpr int kGroupAlign = 32;
+// profiled phases: gather, up/gate, clip factors, update, scores, output, final copy
+constexpr int kPhases = 7;
 
 int gcd_int(int a, int b) {
   while (b) {
@@ -116,6 +120,7 @@ int make_plan(int T, int C, int G_override, Plan &p) {
 struct ttt_handle {
   int d = 0, f = 0, C = 0, max_batch = 0, G_override = 0, device = 0;
   float eta = 0.f;
+  float clip_tau = 0.f;     // > 0: Frobenius clipping of each chunk update
   ttt_dtype dt = TTT_BF16;
   void *Wug = nullptr;      // bf16: [2f][d] interleaved; f32: [2][f][d]
   float *W0 = nullptr;      // [d][f] fp32 image of W_down0
@@ -124,7 +129,7 @@ struct ttt_handle {
   size_t ws_bytes = 0;
   size_t fixed_bytes = 0;
   bool profiling = false, events_made = false, timed = false;
-  hipEvent_t ev[7] = {};
+  hipEvent_t ev[kPhases + 1] = {};
 };
 
 namespace {
@@ -155,7 +160,7 @@ void free_handle(ttt_handle *h) {
 }
 
 struct Scratch {
-  void *VT, *Z, *ZT, *snap, *P;
+  void *VT, *Z, *ZT, *snap, *P, *Vrow, *rowpart, *cfac;
   size_t total;
 };
 
@@ -164,13 +169,17 @@ bool misaligned(const void *p) { return ((uintptr_t)p & 15) != 0; }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-Scratch scratch_layout(const ttt_handle *h, int B, const Plan &pl, bool need_zt, bool need_p) {
+Scratch scratch_layout(const ttt_handle *h, int B, const Plan &pl, bool need_zt, bool need_p, bool clip,
+                       int wspan) {
   const size_t es = h->dt == TTT_BF16 ? 2 : 4;
   const size_t vt = align256(es * (size_t)B * h->d * pl.T_pad);
   const size_t z = align256(es * (size_t)B * pl.T_pad * h->f);
   const size_t zt = need_zt ? z : 0;
   const size_t sn = align256(es * (size_t)B * pl.ngroups * h->d * h->f);
   const size_t pp = need_p ? align256(es * (size_t)B * pl.ngroups * pl.L * pl.L) : 0;
+  const size_t vr = clip ? align256(es * (size_t)B * pl.T_pad * h->d) : 0;
+  const size_t rp = clip ? align256(4 * (size_t)B * (pl.T_pad / 256) * wspan * 256) : 0;
+  const size_t cf = clip ? align256(4 * (size_t)B * ((pl.T_pad + pl.C - 1) / pl.C)) : 0;
   Scratch s;
   size_t off = 0;
   s.VT = (void *)off;
@@ -183,6 +192,12 @@ Scratch scratch_layout(const ttt_handle *h, int B, const Plan &pl, bool need_zt,
   off += sn;
   s.P = (void *)off;
   off += pp;
+  s.Vrow = (void *)off;
+  off += vr;
+  s.rowpart = (void *)off;
+  off += rp;
+  s.cfac = (void *)off;
+  off += cf;
   s.total = off;
   return s;
 }
@@ -270,6 +285,13 @@ int ttt_set_group_chunks(ttt_handle *h, int G) {
   return TTT_OK;
 }
 
+int ttt_set_clip(ttt_handle *h, float tau) {
+  if (!h) return fail(TTT_E_NULL, "handle is NULL");
+  if (!(tau >= 0.f)) return fail(TTT_E_ARG, "tau must be >= 0 (0 or +inf: no clipping)");
+  h->clip_tau = std::isinf(tau) ? 0.f : tau;
+  return TTT_OK;
+}
+
 int ttt_set_profiling(ttt_handle *h, int on) {
   if (!h) return fail(TTT_E_NULL, "handle is NULL");
   if (on && !h->events_made) {
@@ -283,9 +305,9 @@ int ttt_set_profiling(ttt_handle *h, int on) {
 
 int ttt_phase_times(ttt_handle *h, float *ms, int n) {
   if (!h || !ms) return fail(TTT_E_NULL, "handle or ms is NULL");
-  if (n < 0 || n > 6) return fail(TTT_E_ARG, "n must be in [0, 6]");
+  if (n < 0 || n > kPhases) return fail(TTT_E_ARG, "n must be in [0, 7]");
   if (!h->timed) return fail(TTT_E_ARG, "no profiled forward call yet (enable ttt_set_profiling first)");
-  HIP_TRY(hipEventSynchronize(h->ev[6]));
+  HIP_TRY(hipEventSynchronize(h->ev[kPhases]));
   for (int i = 0; i < n; ++i) {
     float t = 0.f;
     HIP_TRY(hipEventElapsedTime(&t, h->ev[i], h->ev[i + 1]));
@@ -340,7 +362,7 @@ int ttt_forward_chunked(ttt_handle *h, const void *x, const int32_t *ids, const 
   if (prof) HIP_TRY(hipEventRecord(h->ev[0], s));
   if (B == 0 || T == 0) {
     if (prof) {
-      for (int i = 1; i < 7; ++i) HIP_TRY(hipEventRecord(h->ev[i], s));
+      for (int i = 1; i <= kPhases; ++i) HIP_TRY(hipEventRecord(h->ev[i], s));
       h->timed = true;
     }
     if (W_final && B > 0)
@@ -348,7 +370,10 @@ int ttt_forward_chunked(ttt_handle *h, const void *x, const int32_t *ids, const 
     return TTT_OK;
   }
 
-  Scratch sc = scratch_layout(h, B, pl, learn, learn && pl.intra);
+  const bool clip = learn && h->clip_tau > 0.f;
+  Layout lay{B, T, pl.T_pad, pl.C, pl.L, pl.ngroups, h->d, h->f, learn ? pl.intra : 0};
+  const int wspan = clip_wspan(lay, h->dt == TTT_BF16);
+  Scratch sc = scratch_layout(h, B, pl, learn, learn && pl.intra, clip, wspan);
   if (sc.total > h->ws_bytes) {
     HIP_TRY(hipStreamSynchronize(s));
     HIP_TRY(hipDeviceSynchronize());
@@ -361,48 +386,63 @@ int ttt_forward_chunked(ttt_handle *h, const void *x, const int32_t *ids, const 
     }
     h->ws_bytes = sc.total;
   }
-  Layout lay{B, T, pl.T_pad, pl.C, pl.L, pl.ngroups, h->d, h->f, learn ? pl.intra : 0};
   void *VT = at(h->ws, sc.VT), *Z = at(h->ws, sc.Z), *ZT = at(h->ws, sc.ZT), *snap = at(h->ws, sc.snap),
        *P = at(h->ws, sc.P);
+  void *Vrow = clip ? at(h->ws, sc.Vrow) : nullptr;
+  float *rowpart = (float *)at(h->ws, sc.rowpart), *cfac = (float *)at(h->ws, sc.cfac);
 
   if (h->dt == TTT_BF16) {
-    if (learn || lay.intra) HIP_TRY(launch_gather_vt_bf16(ids, (const bf16_t *)E_tgt, vocab, (bf16_t *)VT, lay, s));
+    if (learn || lay.intra)
+      HIP_TRY(launch_gather_vt_bf16(ids, (const bf16_t *)E_tgt, vocab, (bf16_t *)VT, (bf16_t *)Vrow, lay, s));
     if (prof) HIP_TRY(hipEventRecord(h->ev[1], s));
     HIP_TRY(launch_a1_bf16((const bf16_t *)x, (const bf16_t *)h->Wug, (bf16_t *)Z, (bf16_t *)ZT, h->eta,
                            learn ? 1 : 0, lay, s));
     if (prof) HIP_TRY(hipEventRecord(h->ev[2], s));
+    if (clip) {
+      HIP_TRY(launch_chunk_gram_bf16((const bf16_t *)Z, (const bf16_t *)Vrow, rowpart, wspan, lay, s));
+      HIP_TRY(launch_chunk_factors(rowpart, cfac, wspan, h->eta, h->clip_tau, lay, s));
+      HIP_TRY(launch_scale_vt_bf16((bf16_t *)VT, cfac, lay, s));
+    }
+    if (prof) HIP_TRY(hipEventRecord(h->ev[3], s));
     if (learn) {
       HIP_TRY(launch_update_bf16((const bf16_t *)ZT, (const bf16_t *)VT, h->state, (bf16_t *)snap, lay, s));
     } else {
       for (int b = 0; b < B; ++b)
         HIP_TRY(launch_f32_to_bf16(h->state + (size_t)b * df, (bf16_t *)snap + (size_t)b * df, (long long)df, s));
     }
-    if (prof) HIP_TRY(hipEventRecord(h->ev[3], s));
-    if (lay.intra) HIP_TRY(launch_scores_bf16((const bf16_t *)Z, (bf16_t *)P, h->eta, lay, s));
     if (prof) HIP_TRY(hipEventRecord(h->ev[4], s));
+    if (lay.intra) HIP_TRY(launch_scores_bf16((const bf16_t *)Z, (bf16_t *)P, h->eta, lay, s));
+    if (prof) HIP_TRY(hipEventRecord(h->ev[5], s));
     HIP_TRY(launch_out_bf16((const bf16_t *)Z, (const bf16_t *)P, (const bf16_t *)snap, (const bf16_t *)VT,
                             (bf16_t *)y, lay, s));
   } else {
-    if (learn || lay.intra) HIP_TRY(launch_gather_vt_f32(ids, (const float *)E_tgt, vocab, (float *)VT, lay, s));
+    if (learn || lay.intra)
+      HIP_TRY(launch_gather_vt_f32(ids, (const float *)E_tgt, vocab, (float *)VT, (float *)Vrow, lay, s));
     if (prof) HIP_TRY(hipEventRecord(h->ev[1], s));
     HIP_TRY(launch_a1_f32((const float *)x, (const float *)h->Wug, (float *)Z, (float *)ZT, h->eta, learn ? 1 : 0,
                           lay, s));
     if (prof) HIP_TRY(hipEventRecord(h->ev[2], s));
+    if (clip) {
+      HIP_TRY(launch_chunk_gram_f32((const float *)Z, (const float *)Vrow, rowpart, lay, s));
+      HIP_TRY(launch_chunk_factors(rowpart, cfac, wspan, h->eta, h->clip_tau, lay, s));
+      HIP_TRY(launch_scale_vt_f32((float *)VT, cfac, lay, s));
+    }
+    if (prof) HIP_TRY(hipEventRecord(h->ev[3], s));
     if (learn) {
       HIP_TRY(launch_update_f32((const float *)ZT, (const float *)VT, h->state, (float *)snap, lay, s));
     } else {
       HIP_TRY(hipMemcpyAsync(snap, h->state, (size_t)B * df * 4, hipMemcpyDeviceToDevice, s));
     }
-    if (prof) HIP_TRY(hipEventRecord(h->ev[3], s));
-    if (lay.intra) HIP_TRY(launch_scores_f32((const float *)Z, (float *)P, h->eta, lay, s));
     if (prof) HIP_TRY(hipEventRecord(h->ev[4], s));
+    if (lay.intra) HIP_TRY(launch_scores_f32((const float *)Z, (float *)P, h->eta, lay, s));
+    if (prof) HIP_TRY(hipEventRecord(h->ev[5], s));
     HIP_TRY(launch_out_f32((const float *)Z, (const float *)P, (const float *)snap, (const float *)VT, (float *)y,
                            lay, s));
   }
-  if (prof) HIP_TRY(hipEventRecord(h->ev[5], s));
+  if (prof) HIP_TRY(hipEventRecord(h->ev[6], s));
   if (W_final) HIP_TRY(hipMemcpyAsync(W_final, h->state, (size_t)B * df * 4, hipMemcpyDeviceToDevice, s));
   if (prof) {
-    HIP_TRY(hipEventRecord(h->ev[6], s));
+    HIP_TRY(hipEventRecord(h->ev[7], s));
     h->timed = true;
   }
   return TTT_OK;

@@ -150,11 +150,25 @@ int ttt_set_group_chunks(ttt_handle *h, int G);
 int ttt_plan(int T, int C, int G_override, int *G, int *L, int *ngroups, int *T_pad);
 
 /*
+ * ttt_set_clip — Frobenius-norm clipping of each chunk update (paperlayer
+ * App. C.2 "Inference Stability", threshold 1e-5 in the reported long-context
+ * evaluations; iplexlaw sec. 6): with tau > 0, chunk i's update
+ * dW_i = eta V_i^T Z_i is applied as dW_i * min(1, tau / ||dW_i||_F), in the
+ * state and in the outputs of later chunks alike. tau = 0 or +inf turns it
+ * off (the default); tau < 0 or NaN returns TTT_E_ARG. The norm is taken from
+ * the chunk Grams, ||V_i^T Z_i||_F^2 = sum_{s,t in chunk i} <v_s,v_t><z_s,z_t>,
+ * in fp32. Applies to later ttt_forward_chunked calls; needs extra scratch
+ * ([B][T][d] target rows in the handle's dtype plus small fp32 buffers).
+ */
+int ttt_set_clip(ttt_handle *h, float tau);
+
+/*
  * ttt_set_profiling / ttt_phase_times — per-phase device timing of the most
  * recent ttt_forward_chunked, from HIP events recorded on its stream.
- * Phases: 0 target gather, 1 up/gate GEMM + SwiGLU, 2 state update with
- * snapshots, 3 within-group scores, 4 output GEMM, 5 final-state copy.
- * ttt_phase_times waits for the last event and writes `n` (<= 6)
+ * Phases: 0 target gather, 1 up/gate GEMM + SwiGLU, 2 clipping factors
+ * (0 when clipping is off), 3 state update with snapshots, 4 within-group
+ * scores, 5 output GEMM, 6 final-state copy.
+ * ttt_phase_times waits for the last event and writes `n` (<= 7)
  * milliseconds to ms[]; phases that did not run read 0.
  */
 int ttt_set_profiling(ttt_handle *h, int on);
