@@ -2,6 +2,7 @@
 from .ttt_oracle import (  # noqa: F401
     chunk_ranges,
     clip_update,
+    conv_targets,
     final_state_columns,
     gated_activation,
     ntp_targets,

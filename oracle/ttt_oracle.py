@@ -25,6 +25,18 @@ the state a previous call left):
      sec. 4; paperlayer sec. 3 "Chunk-Wise Updates").
   4. Return y and the final S (inclusive of the last chunk's update).
 
+Optional general target (conv_w, W_target): V^ = Conv1D(X0) W_target with
+a depthwise kernel of K taps over the token embeddings X0 (rows of the table
+passed as E_tgt), on the tokens after position t (paperlayer sec. 3
+"LM-Aligned Objective"; iplexlaw sec. 4 and sec. 6, kernel size 5, "nearby
+future tokens"). The chunk boundary pads the convolution: row t of chunk i
+uses the embedding at position t+1+k only up to position (i+1)C (and T), the
+first token of the next chunk, which that chunk already holds as its input;
+anything further would let chunk i+1's first outputs see later tokens
+(iplexlaw sec. 6, padding at chunk boundaries; paperlayer App. B, causal
+padding). With K = 1, conv_w = 1 and W_target = I it is the next-token target
+of step 2.
+
 Optional update clipping (clip_tau): before a chunk's update is applied it is
 rescaled to Frobenius norm tau when its norm exceeds tau, i.e.
 dW <- dW * min(1, tau / ||dW||_F), with dW = eta V[chunk]^T Z[chunk] the
@@ -91,6 +103,32 @@ def ntp_targets(ids: np.ndarray, E_tgt: np.ndarray) -> np.ndarray:
     return V
 
 
+def conv_targets(ids: np.ndarray, E_in: np.ndarray, conv_w: np.ndarray, W_target: np.ndarray, C: int) -> np.ndarray:
+    """The general target rows V^ = Conv1D(X0) W_target of one sequence.
+
+    ids [T+1]; E_in [vocab][d] (token embeddings X0); conv_w [K][d] (depthwise,
+    tap k on position t+1+k); W_target [d][d]. Tap k of row t is used when
+    t+1+k <= min((t//C + 1) * C, T) and the id is in [0, vocab); otherwise that
+    tap is zero padding. Returns V [T][d] = U W_target with U the tap sums.
+    """
+    ids = np.asarray(ids)
+    E = _f64(E_in)
+    cw = _f64(conv_w)
+    vocab, d = E.shape
+    T = ids.shape[0] - 1
+    U = np.zeros((T, d), dtype=np.float64)
+    for t in range(T):
+        limit = min((t // C + 1) * C, T)  # last embedding position row t may read
+        for k in range(cw.shape[0]):
+            p = t + 1 + k
+            if p > limit:
+                break
+            tok = int(ids[p])
+            if 0 <= tok < vocab:
+                U[t] += cw[k] * E[tok]
+    return U @ _f64(W_target)
+
+
 def chunk_ranges(T: int, C: int) -> List[Tuple[int, int]]:
     """Non-overlapping chunks [start, end) of C tokens covering [0, T); the last may be short."""
     if C < 1:
@@ -111,10 +149,13 @@ def clip_update(dW: np.ndarray, clip_tau: Optional[float]) -> np.ndarray:
 
 def ttt_forward_one(x: np.ndarray, ids: np.ndarray, E_tgt: np.ndarray, W_up: np.ndarray,
                     W_gate: np.ndarray, W_entry: np.ndarray, C: int, eta: float,
-                    clip_tau: Optional[float] = None):
+                    clip_tau: Optional[float] = None, conv_w: Optional[np.ndarray] = None,
+                    W_target: Optional[np.ndarray] = None):
     """Steps 1-4 for one sequence: x [T][d], ids [T+1], W_entry [d][f].
 
     clip_tau: None, or the Frobenius threshold of each chunk update.
+    conv_w [K][d], W_target [d][d]: the general target (E_tgt then holds the
+    token embeddings X0); None: the next-token target rows of E_tgt.
     Returns (y [T][d], W_final [d][f]) in fp64.
     """
     x = _f64(x)
@@ -124,7 +165,10 @@ def ttt_forward_one(x: np.ndarray, ids: np.ndarray, E_tgt: np.ndarray, W_up: np.
     if T == 0:
         return y, S
     Z = gated_activation(x, W_up, W_gate)
-    V = ntp_targets(ids, E_tgt)
+    if conv_w is None:
+        V = ntp_targets(ids, E_tgt)
+    else:
+        V = conv_targets(ids, E_tgt, conv_w, W_target, C)
     for (s, e) in chunk_ranges(T, C):
         y[s:e] = Z[s:e] @ S.T                      # apply with the pre-update state
         dW = eta * (V[s:e].T @ Z[s:e])             # the chunk's rank-C update
@@ -134,7 +178,8 @@ def ttt_forward_one(x: np.ndarray, ids: np.ndarray, E_tgt: np.ndarray, W_up: np.
 
 def ttt_forward(x: np.ndarray, ids: np.ndarray, E_tgt: np.ndarray, W_up: np.ndarray,
                 W_gate: np.ndarray, W_entry: np.ndarray, C: int, eta: float,
-                clip_tau: Optional[float] = None):
+                clip_tau: Optional[float] = None, conv_w: Optional[np.ndarray] = None,
+                W_target: Optional[np.ndarray] = None):
     """Batched form: x [B][T][d], ids [B][T+1], W_entry [d][f] (shared entry
     state) or [B][d][f] (one state per sequence). Each sequence is independent.
 
@@ -146,7 +191,7 @@ def ttt_forward(x: np.ndarray, ids: np.ndarray, E_tgt: np.ndarray, W_up: np.ndar
     ys, Ws = [], []
     for b in range(B):
         Wb = W_entry if W_entry.ndim == 2 else W_entry[b]
-        yb, Sb = ttt_forward_one(x[b], ids[b], E_tgt, W_up, W_gate, Wb, C, eta, clip_tau)
+        yb, Sb = ttt_forward_one(x[b], ids[b], E_tgt, W_up, W_gate, Wb, C, eta, clip_tau, conv_w, W_target)
         ys.append(yb)
         Ws.append(Sb)
     return np.stack(ys), np.stack(Ws)

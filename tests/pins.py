@@ -324,6 +324,76 @@ def check_clip_limits(fwd, seed=13):
     assert n_clipped > 0
 
 
+# P12: the general target V^ = Conv1D(X0) W_target (paperlayer sec. 3
+# "LM-Aligned Objective"; iplexlaw sec. 4 and sec. 6). The reference builds it
+# as banded shift matrices acting on the embedded token rows, not with a loop.
+def conv_target_matrix_form(ids_row, E, conv_w, W_target, C):
+    ids_row = np.asarray(ids_row)
+    T = ids_row.shape[0] - 1
+    X = _torch_v(np.concatenate([[-1], ids_row[1:]]), E).numpy()  # X[p-1] = embedding of ids[p]
+    X = np.concatenate([np.zeros((1, E.shape[1])), X])              # X[p] = embedding of ids[p], X[0] unused
+    t = np.arange(T)
+    limit = np.minimum((t // C + 1) * C, T)
+    U = np.zeros((T, E.shape[1]))
+    for k in range(conv_w.shape[0]):
+        Sk = np.zeros((T, T + 1))
+        ok = t + 1 + k <= limit
+        Sk[t[ok], (t + 1 + k)[ok]] = 1.0
+        U += (Sk @ X) * conv_w[k][None, :]
+    return U @ W_target
+
+
+def _conv_case(rng, d=6, f=10, B=1, T=23, K=5):
+    x, ids, E, Wu, Wg, W0 = tiny_case(rng, d=d, f=f, B=B, T=T)
+    cw = rng.standard_normal((K, d))
+    Wt = rng.standard_normal((d, d)) / np.sqrt(d)
+    return x, ids, E, Wu, Wg, W0, cw, Wt
+
+
+def check_conv_target(fwd, seed=14):
+    rng = np.random.default_rng(seed)
+    x, ids, E, Wu, Wg, W0, cw, Wt = _conv_case(rng, B=2)
+    eta = 0.17
+    # one tap of weight 1 and W_target = I: the next-token target
+    y1, W1 = fwd(x, ids, E, Wu, Wg, W0, 5, eta, conv_w=np.ones((1, 6)), W_target=np.eye(6))
+    y0, W0_ = fwd(x, ids, E, Wu, Wg, W0, 5, eta)
+    _close(y1, y0, 1e-13, what="P12 one tap = next-token y")
+    _close(W1, W0_, 1e-13, what="P12 one tap = next-token W_final")
+    # one tap with per-channel weights folds into the table: E' = E diag(w) W_target
+    w1 = cw[:1]
+    y2, W2 = fwd(x, ids, E, Wu, Wg, W0, 5, eta, conv_w=w1, W_target=Wt)
+    y3, W3 = fwd(x, ids, (E * w1) @ Wt, Wu, Wg, W0, 5, eta)
+    _close(y2, y3, 1e-11, what="P12 folded table y")
+    _close(W2, W3, 1e-11, what="P12 folded table W_final")
+    # five taps, several chunk sizes: block-causal closed form on the banded-matrix target
+    for C in (1, 2, 3, 5, 8, 23):
+        y, W = fwd(x, ids, E, Wu, Wg, W0, C, eta, conv_w=cw, W_target=Wt)
+        for b in range(2):
+            Z = _torch_z(x[b], Wu, Wg).numpy()
+            V = conv_target_matrix_form(ids[b], E, cw, Wt, C)
+            T = Z.shape[0]
+            tt = np.arange(T)
+            M = (tt[None, :] // C) < (tt[:, None] // C)
+            _close(y[b], Z @ W0.T + eta * ((M * (Z @ Z.T)) @ V), 1e-9, what=f"P12 C={C} b={b} y")
+            _close(W[b], W0 + eta * V.T @ Z, 1e-9, what=f"P12 C={C} b={b} W_final")
+
+
+def check_conv_causality(fwd, seed=15):
+    # brute force: changing the token at position q leaves every output before q unchanged
+    rng = np.random.default_rng(seed)
+    x, ids, E, Wu, Wg, W0, cw, Wt = _conv_case(rng, T=16)
+    C, eta = 4, 0.3
+    y, _ = fwd(x, ids, E, Wu, Wg, W0, C, eta, conv_w=cw, W_target=Wt)
+    for q in range(1, 17):
+        ids2 = ids.copy()
+        ids2[0, q] = (ids2[0, q] + 1) % E.shape[0]
+        y2, _ = fwd(x, ids2, E, Wu, Wg, W0, C, eta, conv_w=cw, W_target=Wt)
+        assert np.array_equal(y2[0, :q], y[0, :q]), f"P12 causality: token {q} reached an earlier output"
+        if q % C == 0 and q < 16:
+            # the first token of a chunk is tapped by the previous chunk's targets
+            assert not np.array_equal(y2[0, q:], y[0, q:])
+
+
 ALL_PINS = [
     check_static_mlp,
     lambda fwd: check_static_mlp(fwd, square=True),
@@ -338,4 +408,6 @@ ALL_PINS = [
     check_zero_targets,
     check_clip_closed_form,
     check_clip_limits,
+    check_conv_target,
+    check_conv_causality,
 ]

@@ -13,7 +13,7 @@ from tests import pins
 
 
 def _loop_mutant(kind):
-    def one(x, ids, E_tgt, W_up, W_gate, W_entry, C, eta, clip_tau=None):
+    def one(x, ids, E_tgt, W_up, W_gate, W_entry, C, eta, clip_tau=None, conv_w=None, W_target=None):
         x = np.asarray(x, dtype=np.float64)
         T = x.shape[0]
         S = np.asarray(W_entry, dtype=np.float64).copy()
@@ -21,7 +21,7 @@ def _loop_mutant(kind):
         if T == 0:
             return y, S
         Z = ot.gated_activation(x, W_up, W_gate)
-        V = ot.ntp_targets(ids, E_tgt)
+        V = ot.ntp_targets(ids, E_tgt) if conv_w is None else ot.conv_targets(ids, E_tgt, conv_w, W_target, C)
         S0 = S.copy()
         ranges = ot.chunk_ranges(T, C)
         for n, (s, e) in enumerate(ranges):
@@ -126,6 +126,31 @@ def _clip_squared(dW, tau):
     return dW * (tau / n2) if n2 > tau else dW
 
 
+def _conv_mutant(kind):
+    def conv(ids, E_in, conv_w, W_target, C):
+        ids = np.asarray(ids)
+        E = np.asarray(E_in, dtype=np.float64)
+        cw = np.asarray(conv_w, dtype=np.float64)
+        T = ids.shape[0] - 1
+        U = np.zeros((T, E.shape[1]))
+        for t in range(T):
+            limit = min((t // C + 1) * C, T)
+            if kind == "no_padding":
+                limit = T
+            elif kind == "strict_padding":
+                limit = min((t // C + 1) * C - 1, T)
+            for k in range(cw.shape[0]):
+                p = t + k if kind == "offset_0" else t + 1 + k
+                if p > limit:
+                    break
+                tok = int(ids[p])
+                if 0 <= tok < E.shape[0]:
+                    U[t] += (cw[cw.shape[0] - 1 - k] if kind == "reversed_taps" else cw[k]) * E[tok]
+        Wt = np.asarray(W_target, dtype=np.float64)
+        return U @ (Wt.T if kind == "transposed_W_target" else Wt)
+    return conv
+
+
 def _sigmoid_wrong(g):
     g = np.asarray(g, dtype=np.float64)
     return g / (1.0 + np.exp(g))
@@ -153,6 +178,11 @@ MUTANTS = {
     "clip_squared_norm": ("clip_update", _clip_squared),
     "clip_accumulated_change": ("ttt_forward_one", _loop_mutant("clip_accumulated")),
     "clip_before_eta": ("ttt_forward_one", _loop_mutant("clip_before_eta")),
+    "conv_taps_from_current_token": ("conv_targets", _conv_mutant("offset_0")),
+    "conv_no_chunk_padding": ("conv_targets", _conv_mutant("no_padding")),
+    "conv_no_crossing_at_all": ("conv_targets", _conv_mutant("strict_padding")),
+    "conv_reversed_taps": ("conv_targets", _conv_mutant("reversed_taps")),
+    "conv_transposed_W_target": ("conv_targets", _conv_mutant("transposed_W_target")),
 }
 
 
