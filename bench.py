@@ -37,7 +37,7 @@ def parse():
     ap.add_argument("--seq-len", type=int, default=None, help="override T (default: the workload's 131072)")
     ap.add_argument("--group-chunks", type=int, default=0)
     ap.add_argument("--no-sweep", action="store_true",
-                    help="skip the extra legs: C=128, and update clipping at tau=1e-5")
+                    help="skip the extra legs: C=128, update clipping at tau=1e-5, the general K=5 target")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-baseline duration")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -94,7 +94,7 @@ def copy_calibration():
     torch.cuda.empty_cache()
 
 
-def run_gpu(w, C, steps, warmup, G, clip_tau=0.0):
+def run_gpu(w, C, steps, warmup, G, clip_tau=0.0, target_conv=None):
     import numpy as np
     import torch
 
@@ -110,6 +110,8 @@ def run_gpu(w, C, steps, warmup, G, clip_tau=0.0):
         ttt.ttt_set_group_chunks(h, G)
     if clip_tau:
         ttt.ttt_set_clip(h, clip_tau)
+    if target_conv is not None:
+        ttt.ttt_set_target_conv(h, dev(target_conv[0]), dev(target_conv[1]))
     x, E = dev(w.x), dev(w.E_tgt)
     ids = torch.from_numpy(np.ascontiguousarray(w.ids)).cuda()
     y = torch.empty((w.B, w.T, w.d), dtype=dt, device="cuda")
@@ -240,6 +242,13 @@ def main():
         ms3 = r3["event_ms"] / a.steps
         out["clip_leg"] = {"clip_tau": 1e-5, "tokens_per_s": tokens / (ms3 * 1e-3), "ms_per_step": ms3,
                            "phase_ms": dict(zip(names, r3["phase_ms"]))}
+        # the general target Conv1D(X0) W_target with a kernel of 5 taps (E_tgt as X0)
+        from synth import make_target_conv
+        r4 = run_gpu(w, a.chunk, a.steps, a.warmup, a.group_chunks,
+                     target_conv=make_target_conv(w.d, 5, "bf16", seed=4))
+        ms4 = r4["event_ms"] / a.steps
+        out["target_conv_leg"] = {"K": 5, "tokens_per_s": tokens / (ms4 * 1e-3), "ms_per_step": ms4,
+                                  "phase_ms": dict(zip(names, r4["phase_ms"]))}
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, a.chunk, a.cpu_seconds)
     print(json.dumps(out), flush=True)

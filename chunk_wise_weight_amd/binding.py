@@ -20,7 +20,7 @@ TTT_F32, TTT_BF16 = 0, 1
 ERRORS = {-1: "TTT_E_NULL", -2: "TTT_E_SHAPE", -3: "TTT_E_DTYPE", -4: "TTT_E_NOMEM", -5: "TTT_E_HIP",
           -6: "TTT_E_NODEV", -7: "TTT_E_ARG"}
 EXPORTS = ("ttt_init", "ttt_forward_chunked", "ttt_reset", "ttt_destroy", "ttt_last_error",
-           "ttt_set_group_chunks", "ttt_set_clip", "ttt_plan", "ttt_set_profiling", "ttt_phase_times",
+           "ttt_set_group_chunks", "ttt_set_clip", "ttt_set_target_conv", "ttt_plan", "ttt_set_profiling", "ttt_phase_times",
            "ttt_workspace_bytes")
 
 _lib = None
@@ -55,6 +55,8 @@ def lib() -> ctypes.CDLL:
     L.ttt_set_group_chunks.restype = i32
     L.ttt_set_clip.argtypes = [vp, f32]
     L.ttt_set_clip.restype = i32
+    L.ttt_set_target_conv.argtypes = [vp, vp, i32, vp, vp]
+    L.ttt_set_target_conv.restype = i32
     ip = ctypes.POINTER(i32)
     L.ttt_plan.argtypes = [i32, i32, i32, ip, ip, ip, ip]
     L.ttt_plan.restype = i32
@@ -184,6 +186,22 @@ def ttt_set_group_chunks(h: Handle, G: int) -> None:
 def ttt_set_clip(h: Handle, tau: float) -> None:
     """Frobenius clipping of each chunk update at threshold tau (0 or inf: off)."""
     _check(lib().ttt_set_clip(h.ptr, float(tau)), "ttt_set_clip")
+
+
+def ttt_set_target_conv(h: Handle, conv_w=None, W_target=None, stream=None) -> None:
+    """The general target Conv1D(X0) W_target: conv_w [K][d], W_target [d][d]
+    (device tensors of the handle's dtype). conv_w None restores the next-token target."""
+    if conv_w is None:
+        _check(lib().ttt_set_target_conv(h.ptr, None, 0, None, _stream(stream)), "ttt_set_target_conv")
+        return
+    cw = conv_w.contiguous()
+    wt = W_target.contiguous()
+    _dev(cw, "conv_w", h.dtype)
+    _dev(wt, "W_target", h.dtype)
+    if cw.dim() != 2 or cw.shape[1] != h.d or tuple(wt.shape) != (h.d, h.d):
+        raise ValueError("shapes must be conv_w [K][d] and W_target [d][d]")
+    _check(lib().ttt_set_target_conv(h.ptr, _ptr(cw), int(cw.shape[0]), _ptr(wt), _stream(stream)),
+           "ttt_set_target_conv")
 
 
 def ttt_plan(T: int, C: int, G: int = 0) -> Dict[str, int]:

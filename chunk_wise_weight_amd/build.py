@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libttt.so")
-SOURCES = ["ttt_api.hip", "kernels_bf16.hip", "kernels_f32.hip", "kernels_clip.hip", "kernels_misc.hip"]
+SOURCES = ["ttt_api.hip", "kernels_bf16.hip", "kernels_f32.hip", "kernels_clip.hip", "kernels_target.hip", "kernels_misc.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -426,6 +426,61 @@ __global__ __launch_bounds__(NT_W, 1) void k_a1(A1Args p) {
 }
 
 // ---------------------------------------------------------------------------
+// General target rows V = U W_target (U: tap sums of the token embeddings),
+// written straight into the layouts the scan reads: V^T K-blocked
+// [B][T_pad/64][d][64] and, when clipping needs it, V row-major [B][T_pad][d].
+// i = token slot, j = model dim a; the B operand is W_target^T [d][d] (row a
+// holds column a of W_target). U rows past T are zero, so are those of V.
+// grid: nx * ny workgroups, nx = d/256, ny = B*T_pad/256
+struct TgtArgs {
+  const bf16_t *U;
+  const bf16_t *WtT;
+  bf16_t *VT;
+  bf16_t *Vrow;
+  int T_pad, d, nx, ny;
+};
+
+__global__ __launch_bounds__(NT_W, 1) void k_target_gemm(TgtArgs p) {
+  __shared__ __attribute__((aligned(16))) Slab<WN_W, NBJ_W> ring[NSL_W];
+  int tx, ty;  // model-dim tile, token tile
+  band_tile(xcd_tile(blockIdx.x, gridDim.x), p.nx, p.ny, 8, tx, ty);
+  const int n0 = tx * 256;
+  const int m0 = ty * BM;
+  const int b = m0 / p.T_pad;
+  const int pos0 = m0 - b * p.T_pad;
+  const Opnd sa = rowmajor(p.U + (long long)m0 * p.d, p.d, BM, p.d);
+  const Opnd sb = rowmajor(p.WtT + (long long)n0 * p.d, p.d, 256, p.d);
+  Acc<NBJ_W> acc;
+  acc_zero(acc);
+  gemm_loop<false>(acc, ring, sa, sb, p.d / BK, sa, sb, 0, 0, 0);
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w & 1, wn = w >> 1;
+  bf16_t *VTb = p.VT + (long long)b * p.d * p.T_pad;
+#pragma unroll
+  for (int bj = 0; bj < NBJ_W; ++bj) {
+    const int a = n0 + wn * WC_W + bj * 32 + (lane & 31);
+#pragma unroll
+    for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int pos = pos0 + wm * 128 + bi * 32 + 8 * q + 4 * (lane >> 5);
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = acc.v[bi][bj][4 * q + r];
+        uint2 pk;
+        pk.x = pack_bf16x2(v[0], v[1]);
+        pk.y = pack_bf16x2(v[2], v[3]);
+        *reinterpret_cast<uint2 *>(VTb + ((long long)(pos >> 6) * p.d + a) * 64 + (pos & 63)) = pk;
+        if (p.Vrow) {
+          bf16_t *vr = p.Vrow + ((long long)b * p.T_pad + pos) * p.d + a;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) vr[(long long)r * p.d] = f32_to_bf16(v[r]);
+        }
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // State update with snapshots. i = hidden unit (ZT row), j = model dim (VT row),
 // k = token slot. The fp32 accumulators ARE the state W[a][i] of one tile and
 // stay in registers for the whole token stream; at each group start g*L the
@@ -816,6 +871,16 @@ hipError_t launch_a1_bf16(const bf16_t *x, const bf16_t *Wug, bf16_t *Z, bf16_t 
   if (nx * ny >= (1LL << 31)) return hipErrorInvalidConfiguration;
   A1Args p{x, Wug, Z, ZT, eta, write_zt, lay.T, lay.T_pad, lay.d, lay.f, nx, (int)ny};
   hipLaunchKernelGGL(k_a1, dim3((unsigned)(nx * ny)), dim3(NT_W), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_target_gemm_bf16(const bf16_t *U, const bf16_t *WtT, bf16_t *VT, bf16_t *Vrow, const Layout &lay,
+                                  hipStream_t s) {
+  const int nx = lay.d / 256;
+  const long long ny = (long long)lay.B * lay.T_pad / BM;
+  if (nx * ny >= (1LL << 31)) return hipErrorInvalidConfiguration;
+  TgtArgs p{U, WtT, VT, Vrow, lay.T_pad, lay.d, nx, (int)ny};
+  hipLaunchKernelGGL(k_target_gemm, dim3((unsigned)(nx * ny)), dim3(NT_W), 0, s, p);
   return hipGetLastError();
 }
 

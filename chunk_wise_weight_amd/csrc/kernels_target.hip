@@ -1,0 +1,124 @@
+// The general LM-aligned target V^ = Conv1D(X0) W_target (paperlayer.ai
+// summary, sec. 3 "LM-Aligned Objective"; iplexlaw.co.kr walkthrough, sec. 4
+// and sec. 6): a depthwise convolution of K taps over the token embeddings on
+// the tokens after each position, then a d x d projection.
+//
+// Row t of chunk i (chunks of C counted from the call's first token) sums
+// tap k on the embedding of the token at position t+1+k only while that
+// position is at most min((i+1)C, T): the chunk boundary pads the
+// convolution, except for the first token of the next chunk, which that chunk
+// already holds as its input. With K = 1, weight 1 and W_target = I this is
+// the next-token gather.
+#include "launch.h"
+
+namespace {
+
+template <typename Tin>
+__device__ __forceinline__ float to_f32(Tin v);
+template <>
+__device__ __forceinline__ float to_f32<float>(float v) { return v; }
+template <>
+__device__ __forceinline__ float to_f32<bf16_t>(bf16_t v) { return bf16_to_f32(v); }
+
+__device__ __forceinline__ void store_out(float *p, float v) { *p = v; }
+__device__ __forceinline__ void store_out(bf16_t *p, float v) { *p = f32_to_bf16(v); }
+
+// U[b][t][a] = sum_k cw[k][a] * E[ids[b][t+1+k]][a] (fp32 sums), rows t >= T zero.
+// One thread per (b, t, group of 8 model dims).
+template <typename Tv>
+__global__ __launch_bounds__(256) void k_conv_taps(const int32_t *ids, const Tv *E, int vocab, const float *cw, int K,
+                                                   Tv *U, int T, int T_pad, int C, int d, long long ngroups8) {
+  for (long long g = (long long)blockIdx.x * 256 + threadIdx.x; g < ngroups8; g += (long long)gridDim.x * 256) {
+    const int a0 = (int)(g % (d / 8)) * 8;
+    const long long bt = g / (d / 8);
+    const int t = (int)(bt % T_pad);
+    const int b = (int)(bt / T_pad);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (t < T) {
+      const long long chunk_end = ((long long)(t / C) + 1) * C;
+      const int limit = (int)(chunk_end < T ? chunk_end : T);
+      for (int k = 0; k < K; ++k) {
+        const int p = t + 1 + k;
+        if (p > limit) break;
+        const int tok = ids[(long long)b * (T + 1) + p];
+        if (tok < 0 || tok >= vocab) continue;
+        const Tv *e = E + (long long)tok * d + a0;
+        const float *w = cw + (long long)k * d + a0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] += w[j] * to_f32(e[j]);
+      }
+    }
+    Tv *u = U + ((long long)b * T_pad + t) * d + a0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) store_out(u + j, acc[j]);
+  }
+}
+
+// fp32 path: VT[b][a][t] = sum_c U[b][t][c] W[c][a]; Vrow[b][t][a] the same value (optional).
+__global__ __launch_bounds__(256) void k_target_gemm_f32(const float *U, const float *W, float *VT, float *Vrow,
+                                                         int T_pad, int d, long long n) {
+  for (long long e = (long long)blockIdx.x * 256 + threadIdx.x; e < n; e += (long long)gridDim.x * 256) {
+    const int t = (int)(e % T_pad);
+    const long long ba = e / T_pad;
+    const int a = (int)(ba % d);
+    const int b = (int)(ba / d);
+    const float *u = U + ((long long)b * T_pad + t) * d;
+    float s = 0.f;
+    for (int c = 0; c < d; ++c) s += u[c] * W[(long long)c * d + a];
+    VT[e] = s;
+    if (Vrow) Vrow[((long long)b * T_pad + t) * d + a] = s;
+  }
+}
+
+// dst[j][i] = src[i][j] for an n x n matrix (set-up only).
+template <typename Tv>
+__global__ __launch_bounds__(256) void k_transpose(const Tv *src, Tv *dst, int n) {
+  for (long long e = (long long)blockIdx.x * 256 + threadIdx.x; e < (long long)n * n; e += (long long)gridDim.x * 256) {
+    const int i = (int)(e / n), j = (int)(e % n);
+    dst[(long long)j * n + i] = src[e];
+  }
+}
+
+__global__ __launch_bounds__(256) void k_copy_f32(const float *src, float *dst, long long n) {
+  for (long long e = (long long)blockIdx.x * 256 + threadIdx.x; e < n; e += (long long)gridDim.x * 256) dst[e] = src[e];
+}
+
+unsigned grid_for(long long n) {
+  long long g = (n + 255) / 256;
+  return (unsigned)(g < 65536 ? (g > 0 ? g : 1) : 65536);
+}
+
+}  // namespace
+
+hipError_t launch_conv_taps_bf16(const int32_t *ids, const bf16_t *E, int vocab, const float *cw, int K, bf16_t *U,
+                                 const Layout &lay, hipStream_t s) {
+  const long long n = (long long)lay.B * lay.T_pad * (lay.d / 8);
+  hipLaunchKernelGGL((k_conv_taps<bf16_t>), dim3(grid_for(n)), dim3(256), 0, s, ids, E, vocab, cw, K, U, lay.T,
+                     lay.T_pad, lay.C, lay.d, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_conv_taps_f32(const int32_t *ids, const float *E, int vocab, const float *cw, int K, float *U,
+                                const Layout &lay, hipStream_t s) {
+  const long long n = (long long)lay.B * lay.T_pad * (lay.d / 8);
+  hipLaunchKernelGGL((k_conv_taps<float>), dim3(grid_for(n)), dim3(256), 0, s, ids, E, vocab, cw, K, U, lay.T,
+                     lay.T_pad, lay.C, lay.d, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_target_gemm_f32(const float *U, const float *W, float *VT, float *Vrow, const Layout &lay,
+                                  hipStream_t s) {
+  const long long n = (long long)lay.B * lay.d * lay.T_pad;
+  hipLaunchKernelGGL(k_target_gemm_f32, dim3(grid_for(n)), dim3(256), 0, s, U, W, VT, Vrow, lay.T_pad, lay.d, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_bf16(const bf16_t *src, bf16_t *dst, int n, hipStream_t s) {
+  hipLaunchKernelGGL((k_transpose<bf16_t>), dim3(grid_for((long long)n * n)), dim3(256), 0, s, src, dst, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_f32(const float *src, float *dst, long long n, hipStream_t s) {
+  hipLaunchKernelGGL(k_copy_f32, dim3(grid_for(n)), dim3(256), 0, s, src, dst, n);
+  return hipGetLastError();
+}

@@ -49,6 +49,21 @@ hipError_t launch_chunk_factors(const float *rowpart, float *cfac, int wspan, fl
 hipError_t launch_scale_vt_bf16(bf16_t *VT, const float *cfac, const Layout &lay, hipStream_t s);
 hipError_t launch_scale_vt_f32(float *VT, const float *cfac, const Layout &lay, hipStream_t s);
 
+// ---- general target Conv1D(X0) W_target (kernels_target.hip; GEMM in kernels_bf16.hip) ----
+// U[b][t] = sum_k cw[k] * E[ids[b][t+1+k]] with the chunk-boundary limit; [B][T_pad][d], rows >= T zero.
+hipError_t launch_conv_taps_bf16(const int32_t *ids, const bf16_t *E, int vocab, const float *cw, int K, bf16_t *U,
+                                 const Layout &lay, hipStream_t s);
+hipError_t launch_conv_taps_f32(const int32_t *ids, const float *E, int vocab, const float *cw, int K, float *U,
+                                const Layout &lay, hipStream_t s);
+// V = U W_target into V^T (K-blocked bf16 / row-major [B][d][T_pad] fp32) and, if Vrow, row-major V.
+// bf16 takes W_target^T [d][d]; fp32 takes W_target [d][d].
+hipError_t launch_target_gemm_bf16(const bf16_t *U, const bf16_t *WtT, bf16_t *VT, bf16_t *Vrow, const Layout &lay,
+                                   hipStream_t s);
+hipError_t launch_target_gemm_f32(const float *U, const float *W, float *VT, float *Vrow, const Layout &lay,
+                                  hipStream_t s);
+hipError_t launch_transpose_bf16(const bf16_t *src, bf16_t *dst, int n, hipStream_t s);
+hipError_t launch_copy_f32(const float *src, float *dst, long long n, hipStream_t s);
+
 // ---- layout helpers (kernels_misc.hip) ----
 // Wug[2f][d] from W_up[f][d], W_gate[f][d]: 32-row blocks, up block then gate block.
 hipError_t launch_interleave_ug_bf16(const bf16_t *Wu, const bf16_t *Wg, bf16_t *Wug, int f, int d, hipStream_t s);

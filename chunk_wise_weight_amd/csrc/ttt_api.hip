@@ -2,7 +2,9 @@
 // token layout of a call, scratch management and the launch sequence.
 //
 // One call of ttt_forward_chunked runs, on the caller's stream:
-//   1. target gather      V^T = E_tgt[ids shifted by one]^T       (next-token target)
+//   1. target gather      V^T = E_tgt[ids shifted by one]^T       (next-token target), or
+//                         the general target Conv1D(X0) W_target: tap sums of the
+//                         token embeddings, then one GEMM into V^T
 //   2. up/gate GEMM       Z = SiLU(x W_gate^T) * (x W_up^T), and eta*Z^T
 //   2b. optional clipping per-chunk factors c_i = min(1, tau/||eta V_i^T Z_i||_F)
 //                         from chunk Grams; V^T's rows of chunk i scaled by c_i
@@ -48,6 +50,7 @@ constexpr int kDefaultGroupTokens = 1024;
 constexpr int kGroupAlign = 32;
 // profiled phases: gather, up/gate, clip factors, update, scores, output, final copy
 constexpr int kPhases = 7;
+constexpr int kMaxTaps = 64;
 
 int gcd_int(int a, int b) {
   while (b) {
@@ -121,6 +124,9 @@ struct ttt_handle {
   int d = 0, f = 0, C = 0, max_batch = 0, G_override = 0, device = 0;
   float eta = 0.f;
   float clip_tau = 0.f;     // > 0: Frobenius clipping of each chunk update
+  int conv_K = 0;           // > 0: general target with K taps
+  float *conv_w = nullptr;  // [K][d] fp32 tap weights
+  void *Wt = nullptr;       // bf16: W_target^T [d][d]; f32: W_target [d][d]
   ttt_dtype dt = TTT_BF16;
   void *Wug = nullptr;      // bf16: [2f][d] interleaved; f32: [2][f][d]
   float *W0 = nullptr;      // [d][f] fp32 image of W_down0
@@ -153,6 +159,8 @@ void free_handle(ttt_handle *h) {
   if (h->Wug) (void)hipFree(h->Wug);
   if (h->W0) (void)hipFree(h->W0);
   if (h->state) (void)hipFree(h->state);
+  if (h->conv_w) (void)hipFree(h->conv_w);
+  if (h->Wt) (void)hipFree(h->Wt);
   if (h->ws) (void)hipFree(h->ws);
   if (h->events_made)
     for (auto &e : h->ev) (void)hipEventDestroy(e);
@@ -160,7 +168,7 @@ void free_handle(ttt_handle *h) {
 }
 
 struct Scratch {
-  void *VT, *Z, *ZT, *snap, *P, *Vrow, *rowpart, *cfac;
+  void *VT, *Z, *ZT, *snap, *P, *Vrow, *rowpart, *cfac, *U;
   size_t total;
 };
 
@@ -170,7 +178,7 @@ bool misaligned(const void *p) { return ((uintptr_t)p & 15) != 0; }
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 Scratch scratch_layout(const ttt_handle *h, int B, const Plan &pl, bool need_zt, bool need_p, bool clip,
-                       int wspan) {
+                       int wspan, bool conv) {
   const size_t es = h->dt == TTT_BF16 ? 2 : 4;
   const size_t vt = align256(es * (size_t)B * h->d * pl.T_pad);
   const size_t z = align256(es * (size_t)B * pl.T_pad * h->f);
@@ -180,6 +188,7 @@ Scratch scratch_layout(const ttt_handle *h, int B, const Plan &pl, bool need_zt,
   const size_t vr = clip ? align256(es * (size_t)B * pl.T_pad * h->d) : 0;
   const size_t rp = clip ? align256(4 * (size_t)B * (pl.T_pad / 256) * wspan * 256) : 0;
   const size_t cf = clip ? align256(4 * (size_t)B * ((pl.T_pad + pl.C - 1) / pl.C)) : 0;
+  const size_t uu = conv ? align256(es * (size_t)B * pl.T_pad * h->d) : 0;
   Scratch s;
   size_t off = 0;
   s.VT = (void *)off;
@@ -198,6 +207,8 @@ Scratch scratch_layout(const ttt_handle *h, int B, const Plan &pl, bool need_zt,
   off += rp;
   s.cfac = (void *)off;
   off += cf;
+  s.U = (void *)off;
+  off += uu;
   s.total = off;
   return s;
 }
@@ -292,6 +303,45 @@ int ttt_set_clip(ttt_handle *h, float tau) {
   return TTT_OK;
 }
 
+int ttt_set_target_conv(ttt_handle *h, const void *conv_w, int K, const void *W_target, void *hip_stream) {
+  if (!h) return fail(TTT_E_NULL, "handle is NULL");
+  if (K < 0 || K > kMaxTaps) return fail(TTT_E_ARG, "K must be in [0, 64]");
+  hipStream_t s = (hipStream_t)hip_stream;
+  if (K == 0) {
+    HIP_TRY(hipStreamSynchronize(s));
+    if (h->conv_w) HIP_TRY(hipFree(h->conv_w));
+    if (h->Wt) HIP_TRY(hipFree(h->Wt));
+    h->conv_w = nullptr;
+    h->Wt = nullptr;
+    h->conv_K = 0;
+    return TTT_OK;
+  }
+  if (!conv_w || !W_target) return fail(TTT_E_NULL, "conv_w and W_target must be non-NULL");
+  if (misaligned(conv_w) || misaligned(W_target)) return fail(TTT_E_ARG, "conv_w and W_target must be 16-byte aligned");
+  const size_t es = h->dt == TTT_BF16 ? 2 : 4;
+  const size_t dd = (size_t)h->d * h->d;
+  HIP_TRY(hipStreamSynchronize(s));
+  if (h->conv_w) HIP_TRY(hipFree(h->conv_w));
+  if (h->Wt) HIP_TRY(hipFree(h->Wt));
+  h->conv_w = nullptr;
+  h->Wt = nullptr;
+  h->conv_K = 0;
+  if (hipMalloc((void **)&h->conv_w, (size_t)K * h->d * 4) != hipSuccess ||
+      hipMalloc(&h->Wt, dd * es) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(TTT_E_NOMEM, "allocating the target convolution weights");
+  }
+  if (h->dt == TTT_BF16) {
+    HIP_TRY(launch_bf16_to_f32((const bf16_t *)conv_w, h->conv_w, (long long)K * h->d, s));
+    HIP_TRY(launch_transpose_bf16((const bf16_t *)W_target, (bf16_t *)h->Wt, h->d, s));
+  } else {
+    HIP_TRY(launch_copy_f32((const float *)conv_w, h->conv_w, (long long)K * h->d, s));
+    HIP_TRY(hipMemcpyAsync(h->Wt, W_target, dd * 4, hipMemcpyDeviceToDevice, s));
+  }
+  h->conv_K = K;
+  return TTT_OK;
+}
+
 int ttt_set_profiling(ttt_handle *h, int on) {
   if (!h) return fail(TTT_E_NULL, "handle is NULL");
   if (on && !h->events_made) {
@@ -373,7 +423,8 @@ int ttt_forward_chunked(ttt_handle *h, const void *x, const int32_t *ids, const 
   const bool clip = learn && h->clip_tau > 0.f;
   Layout lay{B, T, pl.T_pad, pl.C, pl.L, pl.ngroups, h->d, h->f, learn ? pl.intra : 0};
   const int wspan = clip_wspan(lay, h->dt == TTT_BF16);
-  Scratch sc = scratch_layout(h, B, pl, learn, learn && pl.intra, clip, wspan);
+  const bool conv = h->conv_K > 0 && (learn || lay.intra);
+  Scratch sc = scratch_layout(h, B, pl, learn, learn && pl.intra, clip, wspan, conv);
   if (sc.total > h->ws_bytes) {
     HIP_TRY(hipStreamSynchronize(s));
     HIP_TRY(hipDeviceSynchronize());
@@ -390,10 +441,15 @@ int ttt_forward_chunked(ttt_handle *h, const void *x, const int32_t *ids, const 
        *P = at(h->ws, sc.P);
   void *Vrow = clip ? at(h->ws, sc.Vrow) : nullptr;
   float *rowpart = (float *)at(h->ws, sc.rowpart), *cfac = (float *)at(h->ws, sc.cfac);
+  void *U = at(h->ws, sc.U);
 
   if (h->dt == TTT_BF16) {
-    if (learn || lay.intra)
+    if (conv) {
+      HIP_TRY(launch_conv_taps_bf16(ids, (const bf16_t *)E_tgt, vocab, h->conv_w, h->conv_K, (bf16_t *)U, lay, s));
+      HIP_TRY(launch_target_gemm_bf16((const bf16_t *)U, (const bf16_t *)h->Wt, (bf16_t *)VT, (bf16_t *)Vrow, lay, s));
+    } else if (learn || lay.intra) {
       HIP_TRY(launch_gather_vt_bf16(ids, (const bf16_t *)E_tgt, vocab, (bf16_t *)VT, (bf16_t *)Vrow, lay, s));
+    }
     if (prof) HIP_TRY(hipEventRecord(h->ev[1], s));
     HIP_TRY(launch_a1_bf16((const bf16_t *)x, (const bf16_t *)h->Wug, (bf16_t *)Z, (bf16_t *)ZT, h->eta,
                            learn ? 1 : 0, lay, s));
@@ -416,8 +472,12 @@ int ttt_forward_chunked(ttt_handle *h, const void *x, const int32_t *ids, const 
     HIP_TRY(launch_out_bf16((const bf16_t *)Z, (const bf16_t *)P, (const bf16_t *)snap, (const bf16_t *)VT,
                             (bf16_t *)y, lay, s));
   } else {
-    if (learn || lay.intra)
+    if (conv) {
+      HIP_TRY(launch_conv_taps_f32(ids, (const float *)E_tgt, vocab, h->conv_w, h->conv_K, (float *)U, lay, s));
+      HIP_TRY(launch_target_gemm_f32((const float *)U, (const float *)h->Wt, (float *)VT, (float *)Vrow, lay, s));
+    } else if (learn || lay.intra) {
       HIP_TRY(launch_gather_vt_f32(ids, (const float *)E_tgt, vocab, (float *)VT, (float *)Vrow, lay, s));
+    }
     if (prof) HIP_TRY(hipEventRecord(h->ev[1], s));
     HIP_TRY(launch_a1_f32((const float *)x, (const float *)h->Wug, (float *)Z, (float *)ZT, h->eta, learn ? 1 : 0,
                           lay, s));

@@ -150,6 +150,28 @@ int ttt_set_group_chunks(ttt_handle *h, int G);
 int ttt_plan(int T, int C, int G_override, int *G, int *L, int *ngroups, int *T_pad);
 
 /*
+ * ttt_set_target_conv — the general LM-aligned target V^ = Conv1D(X0) W_target
+ * (paperlayer sec. 3 "LM-Aligned Objective"; iplexlaw sec. 4 and sec. 6, a
+ * depthwise kernel of size 5 over the token embeddings and a learnable
+ * projection) in place of the next-token rows of E_tgt.
+ *   conv_w   : [K][d] depthwise tap weights (dtype of the handle); tap k of
+ *              target row t reads the embedding of the token at position
+ *              t+1+k (ids[b][t+1+k]).
+ *   K        : 1 .. 64 taps; K = 0 restores the next-token target (the other
+ *              arguments are then ignored).
+ *   W_target : [d][d] projection (dtype of the handle): V^[t] = U[t] W_target.
+ * After this call the E_tgt argument of ttt_forward_chunked is the token
+ * embedding table X0 [vocab][d]. The chunk boundary pads the convolution: row t
+ * of chunk i uses tap positions only up to min((i+1)C, T), the first token of
+ * the next chunk (already that chunk's input); later taps are zero, so no output
+ * depends on a later token. With K = 1, conv_w = 1 and W_target = I the result
+ * equals the next-token target. Both arrays are copied (the caller may free
+ * them once the stream has run the copy); they must be 16-byte aligned.
+ * Synchronises `hip_stream`. Adds [B][T][d] of scratch per forward.
+ */
+int ttt_set_target_conv(ttt_handle *h, const void *conv_w, int K, const void *W_target, void *hip_stream);
+
+/*
  * ttt_set_clip — Frobenius-norm clipping of each chunk update (paperlayer
  * App. C.2 "Inference Stability", threshold 1e-5 in the reported long-context
  * evaluations; iplexlaw sec. 6): with tau > 0, chunk i's update

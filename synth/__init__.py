@@ -11,4 +11,5 @@ from .workloads import (  # noqa: F401
     bf16_bits,
     make_inputs,
     make_config,
+    make_target_conv,
 )

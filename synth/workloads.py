@@ -143,6 +143,19 @@ def make_config(name: str, *, T: Optional[int] = None, C: Optional[int] = None, 
     return make_inputs(name=name, **cfg)
 
 
+def make_target_conv(d: int, K: int = 5, dtype: str = "bf16", seed=0) -> Tuple[np.ndarray, np.ndarray]:
+    """Weights of the general target: conv_w [K][d] depthwise taps with std
+    1/sqrt(K), and W_target [d][d] = I + N(0, 1/d) (a diagonal-dominant
+    projection, as the pages start it from a diagonal form). Drawn in fp32 and,
+    for bf16, rounded once (RNE)."""
+    rng = np.random.default_rng(seed)
+    cw = _normal(rng, (K, d), 1.0 / np.sqrt(K))
+    Wt = np.eye(d, dtype=np.float32) + _normal(rng, (d, d), 1.0 / np.sqrt(d))
+    if dtype == "bf16":
+        cw, Wt = bf16_round(cw), bf16_round(Wt)
+    return cw.astype(np.float32), Wt.astype(np.float32)
+
+
 def shape_of(name: str) -> Tuple[int, int, int, int, int]:
     c = CONFIGS[name]
     return c["d"], c["f"], c["B"], c["T"], c["C"]
