@@ -8,5 +8,6 @@ from .ttt_oracle import (  # noqa: F401
     ntp_targets,
     silu,
     ttt_forward,
+    ttt_forward_docs,
     ttt_forward_one,
 )

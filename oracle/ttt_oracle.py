@@ -197,6 +197,45 @@ def ttt_forward(x: np.ndarray, ids: np.ndarray, E_tgt: np.ndarray, W_up: np.ndar
     return np.stack(ys), np.stack(Ws)
 
 
+def ttt_forward_docs(x: np.ndarray, ids: np.ndarray, E_tgt: np.ndarray, W_up: np.ndarray, W_gate: np.ndarray,
+                     W_entry: np.ndarray, W_reset: np.ndarray, C: int, eta: float,
+                     doc_starts: Sequence[Sequence[int]], clip_tau: Optional[float] = None,
+                     conv_w: Optional[np.ndarray] = None, W_target: Optional[np.ndarray] = None):
+    """Packed documents: the stream of sequence b holds several documents, a new
+    one starting at each position of doc_starts[b] (strictly increasing, inside
+    (0, T)). At each document start the fast weight returns to W_reset (the
+    initial W_down) and chunking restarts from that token; the last token of a
+    document has no look-ahead (its target is zero), while the call's last
+    document keeps ids[T], the stream continuing into the next call
+    (paperlayer App. B and iplexlaw sec. 6: reset at document boundaries so no
+    state crosses between independent documents).
+
+    x [B][T][d], ids [B][T+1], W_entry [d][f] or [B][d][f] (state at the call's
+    first token). Returns (y [B][T][d], W_final [B][d][f]) in fp64.
+    """
+    x = _f64(x)
+    B, T = x.shape[0], x.shape[1]
+    W_entry = _f64(W_entry)
+    ys, Ws = [], []
+    for b in range(B):
+        S = (W_entry if W_entry.ndim == 2 else W_entry[b]).copy()
+        starts = list(doc_starts[b])
+        bounds = [0] + starts + [T]
+        yb = np.zeros((T, S.shape[0]))
+        for j in range(len(bounds) - 1):
+            s0, s1 = bounds[j], bounds[j + 1]
+            if j > 0:
+                S = _f64(W_reset).copy()        # a new document starts from the initial weight
+            ids_seg = np.array(ids[b][s0:s1 + 1], copy=True)
+            if j < len(bounds) - 2:
+                ids_seg[-1] = -1                 # no look-ahead past a document's end
+            yb[s0:s1], S = ttt_forward_one(x[b, s0:s1], ids_seg, E_tgt, W_up, W_gate, S, C, eta,
+                                           clip_tau, conv_w, W_target)
+        ys.append(yb)
+        Ws.append(S)
+    return np.stack(ys), np.stack(Ws)
+
+
 def final_state_columns(x: np.ndarray, ids: np.ndarray, E_tgt: np.ndarray, W_up: np.ndarray,
                         W_gate: np.ndarray, W_entry: np.ndarray, C: int, eta: float,
                         cols: Sequence[int]) -> np.ndarray:

@@ -48,8 +48,11 @@ def _torch_z(x, Wu, Wg):
 
 
 def _torch_v(ids_row, E):
+    """Next-token rows by torch embedding; ids outside [0, vocab) give zero rows."""
     idx = torch.from_numpy(np.asarray(ids_row[1:], dtype=np.int64))
-    return F.embedding(idx, torch.from_numpy(np.asarray(E, dtype=np.float64)))
+    Et = torch.from_numpy(np.asarray(E, dtype=np.float64))
+    ok = (idx >= 0) & (idx < Et.shape[0])
+    return F.embedding(torch.where(ok, idx, torch.zeros_like(idx)), Et) * ok[:, None].to(Et.dtype)
 
 
 # P1: eta = 0 (any C) or C >= T (any eta, for y) reduces to the textbook gated MLP.
@@ -394,6 +397,48 @@ def check_conv_causality(fwd, seed=15):
             assert not np.array_equal(y2[0, q:], y[0, q:])
 
 
+# P13: packed documents (paperlayer App. B; iplexlaw sec. 6). Checked through
+# the plain forward (no boundaries), the block-causal closed form on one
+# document from the initial weight, and brute-force independence.
+def check_documents(fwd, seed=16):
+    import oracle.ttt_oracle as _ot
+
+    def fdocs(*a, **k):
+        return _ot.ttt_forward_docs(*a, **k)
+    rng = np.random.default_rng(seed)
+    x, ids, E, Wu, Wg, W0 = tiny_case(rng, d=5, f=8, B=2, T=22)
+    Wentry = W0 + 0.1 * rng.standard_normal(W0.shape)  # a carried state, not the reset value
+    C, eta = 4, 0.3
+    # no boundaries: the plain forward
+    y, W = fdocs(x, ids, E, Wu, Wg, Wentry, W0, C, eta, [[], []])
+    y_ref, W_ref = fwd(x, ids, E, Wu, Wg, Wentry, C, eta)
+    _close(y, y_ref, 1e-12, what="P13 no boundary y")
+    _close(W, W_ref, 1e-12, what="P13 no boundary W_final")
+    # a boundary at 9 (not a multiple of C): the last document alone from W0,
+    # chunked from its own first token (closed form), its look-ahead kept
+    y, W = fdocs(x, ids, E, Wu, Wg, Wentry, W0, C, eta, [[9], [6, 15]])
+    for b, r in ((0, 9), (1, 15)):
+        y_cf, W_cf = block_causal_closed_form(x[b, r:], ids[b, r:], E, Wu, Wg, W0, C, eta)
+        _close(y[b, r:], y_cf, 1e-9, what=f"P13 last document b={b} y")
+        _close(W[b], W_cf, 1e-9, what=f"P13 last document b={b} W_final")
+    # the first document: from the carried state, its last target zero
+    ids_z = ids.copy()
+    ids_z[0, 9] = -1
+    y_cf, _ = block_causal_closed_form(x[0, :9], ids_z[0, :10], E, Wu, Wg, Wentry, C, eta)
+    _close(y[0, :9], y_cf, 1e-9, what="P13 first document y")
+    # brute force: nothing before a boundary reaches the outputs after it, and the
+    # first token of a document is no target of the one before
+    for q in range(0, 9):
+        x2 = x.copy()
+        x2[0, q] += 1.0
+        y2, W2 = fdocs(x2, ids, E, Wu, Wg, Wentry, W0, C, eta, [[9], [6, 15]])
+        assert np.array_equal(y2[0, 9:], y[0, 9:]) and np.array_equal(W2[0], W[0])
+    ids2 = ids.copy()
+    ids2[0, 9] = (ids2[0, 9] + 1) % E.shape[0]
+    y2, W2 = fdocs(x, ids2, E, Wu, Wg, Wentry, W0, C, eta, [[9], [6, 15]])
+    assert np.array_equal(y2[0], y[0]) and np.array_equal(W2[0], W[0]), "P13 look-ahead crossed a document end"
+
+
 ALL_PINS = [
     check_static_mlp,
     lambda fwd: check_static_mlp(fwd, square=True),
@@ -410,4 +455,5 @@ ALL_PINS = [
     check_clip_limits,
     check_conv_target,
     check_conv_causality,
+    check_documents,
 ]

@@ -151,6 +151,33 @@ def _conv_mutant(kind):
     return conv
 
 
+def _docs_mutant(kind):
+    def docs(x, ids, E_tgt, W_up, W_gate, W_entry, W_reset, C, eta, doc_starts, clip_tau=None, conv_w=None,
+             W_target=None):
+        x = np.asarray(x, dtype=np.float64)
+        B, T = x.shape[0], x.shape[1]
+        W_entry = np.asarray(W_entry, dtype=np.float64)
+        ys, Ws = [], []
+        for b in range(B):
+            S = (W_entry if W_entry.ndim == 2 else W_entry[b]).copy()
+            starts = [r + 1 if kind == "late_reset" else r for r in doc_starts[b]]
+            bounds = [0] + starts + [T]
+            yb = np.zeros((T, S.shape[0]))
+            for j in range(len(bounds) - 1):
+                s0, s1 = bounds[j], bounds[j + 1]
+                if j > 0 and kind != "no_reset":
+                    S = (W_entry if kind == "reset_to_entry" else np.asarray(W_reset, dtype=np.float64)).copy()
+                ids_seg = np.array(ids[b][s0:s1 + 1], copy=True)
+                if j < len(bounds) - 2 and kind != "lookahead_kept":
+                    ids_seg[-1] = -1
+                yb[s0:s1], S = ot.ttt_forward_one(x[b, s0:s1], ids_seg, E_tgt, W_up, W_gate, S, C, eta,
+                                                  clip_tau, conv_w, W_target)
+            ys.append(yb)
+            Ws.append(S)
+        return np.stack(ys), np.stack(Ws)
+    return docs
+
+
 def _sigmoid_wrong(g):
     g = np.asarray(g, dtype=np.float64)
     return g / (1.0 + np.exp(g))
@@ -183,6 +210,10 @@ MUTANTS = {
     "conv_no_crossing_at_all": ("conv_targets", _conv_mutant("strict_padding")),
     "conv_reversed_taps": ("conv_targets", _conv_mutant("reversed_taps")),
     "conv_transposed_W_target": ("conv_targets", _conv_mutant("transposed_W_target")),
+    "docs_no_reset": ("ttt_forward_docs", _docs_mutant("no_reset")),
+    "docs_reset_to_carried_state": ("ttt_forward_docs", _docs_mutant("reset_to_entry")),
+    "docs_lookahead_across_end": ("ttt_forward_docs", _docs_mutant("lookahead_kept")),
+    "docs_reset_one_token_late": ("ttt_forward_docs", _docs_mutant("late_reset")),
 }
 
 
