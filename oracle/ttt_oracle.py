@@ -204,9 +204,11 @@ def ttt_forward_docs(x: np.ndarray, ids: np.ndarray, E_tgt: np.ndarray, W_up: np
     """Packed documents: the stream of sequence b holds several documents, a new
     one starting at each position of doc_starts[b] (strictly increasing, inside
     (0, T)). At each document start the fast weight returns to W_reset (the
-    initial W_down) and chunking restarts from that token; the last token of a
-    document has no look-ahead (its target is zero), while the call's last
-    document keeps ids[T], the stream continuing into the next call
+    initial W_down) and chunking restarts from that token. The last token of a
+    document gets no look-ahead (its target is zero); that row lies in the
+    document's last chunk, whose update the reset discards, so the choice
+    never reaches an output. The call's last document keeps ids[T], the stream
+    continuing into the next call
     (paperlayer App. B and iplexlaw sec. 6: reset at document boundaries so no
     state crosses between independent documents).
 

@@ -426,17 +426,18 @@ def check_documents(fwd, seed=16):
     ids_z[0, 9] = -1
     y_cf, _ = block_causal_closed_form(x[0, :9], ids_z[0, :10], E, Wu, Wg, Wentry, C, eta)
     _close(y[0, :9], y_cf, 1e-9, what="P13 first document y")
-    # brute force: nothing before a boundary reaches the outputs after it, and the
-    # first token of a document is no target of the one before
+    # brute force: nothing before a boundary reaches the outputs after it
     for q in range(0, 9):
         x2 = x.copy()
         x2[0, q] += 1.0
         y2, W2 = fdocs(x2, ids, E, Wu, Wg, Wentry, W0, C, eta, [[9], [6, 15]])
         assert np.array_equal(y2[0, 9:], y[0, 9:]) and np.array_equal(W2[0], W[0])
+    # the first token of the next document is no target of this one's outputs (the
+    # last chunk's update, the only one it could enter, is discarded by the reset)
     ids2 = ids.copy()
     ids2[0, 9] = (ids2[0, 9] + 1) % E.shape[0]
     y2, W2 = fdocs(x, ids2, E, Wu, Wg, Wentry, W0, C, eta, [[9], [6, 15]])
-    assert np.array_equal(y2[0], y[0]) and np.array_equal(W2[0], W[0]), "P13 look-ahead crossed a document end"
+    assert np.array_equal(y2[0, :9], y[0, :9]), "P13 look-ahead crossed a document end"
 
 
 ALL_PINS = [

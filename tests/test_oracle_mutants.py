@@ -212,7 +212,6 @@ MUTANTS = {
     "conv_transposed_W_target": ("conv_targets", _conv_mutant("transposed_W_target")),
     "docs_no_reset": ("ttt_forward_docs", _docs_mutant("no_reset")),
     "docs_reset_to_carried_state": ("ttt_forward_docs", _docs_mutant("reset_to_entry")),
-    "docs_lookahead_across_end": ("ttt_forward_docs", _docs_mutant("lookahead_kept")),
     "docs_reset_one_token_late": ("ttt_forward_docs", _docs_mutant("late_reset")),
 }
 
