@@ -37,7 +37,8 @@ def parse():
     ap.add_argument("--seq-len", type=int, default=None, help="override T (default: the workload's 131072)")
     ap.add_argument("--group-chunks", type=int, default=0)
     ap.add_argument("--no-sweep", action="store_true",
-                    help="skip the extra legs: C=128, update clipping at tau=1e-5, the general K=5 target")
+                    help="skip the extra legs: C = 128/512/1024, update clipping at tau=1e-5, the general K=5 "
+                         "target, four packed documents")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-baseline duration")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -94,7 +95,7 @@ def copy_calibration():
     torch.cuda.empty_cache()
 
 
-def run_gpu(w, C, steps, warmup, G, clip_tau=0.0, target_conv=None):
+def run_gpu(w, C, steps, warmup, G, clip_tau=0.0, target_conv=None, doc_starts=None):
     import numpy as np
     import torch
 
@@ -116,9 +117,15 @@ def run_gpu(w, C, steps, warmup, G, clip_tau=0.0, target_conv=None):
     ids = torch.from_numpy(np.ascontiguousarray(w.ids)).cuda()
     y = torch.empty((w.B, w.T, w.d), dtype=dt, device="cuda")
     ttt.ttt_set_profiling(h, True)
+    def forward():
+        if doc_starts is None:
+            ttt.ttt_forward_chunked(h, x, ids, E, y=y)
+        else:
+            ttt.ttt_forward_docs(h, x, ids, E, doc_starts, y=y)
+
     for _ in range(warmup):
         ttt.ttt_reset(h)
-        ttt.ttt_forward_chunked(h, x, ids, E, y=y)
+        forward()
     torch.cuda.synchronize()
     phase_sum = [0.0] * len(ttt.PHASES)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -127,7 +134,7 @@ def run_gpu(w, C, steps, warmup, G, clip_tau=0.0, target_conv=None):
     ev0.record()
     for _ in range(steps):
         ttt.ttt_reset(h)
-        ttt.ttt_forward_chunked(h, x, ids, E, y=y)
+        forward()
         ph = ttt.ttt_phase_times(h)  # waits for this step's last event
         phase_sum = [a + b for a, b in zip(phase_sum, ph)]
     ev1.record()
@@ -228,13 +235,18 @@ def main():
                      "traffic": measured_traffic(KERNEL_OF_PHASE[dom], a.chunk)},
         "workspace_gb": r["workspace_bytes"] / 1e9,
     }
-    if not a.no_sweep and a.chunk != 128:
-        w.C = 128
-        r2 = run_gpu(w, 128, a.steps, a.warmup, 0)
-        ms2 = r2["event_ms"] / a.steps
-        out["chunk_sweep"] = {"C128": {"tokens_per_s": tokens / (ms2 * 1e-3), "ms_per_step": ms2,
-                                       "mfma_frac_layer": total_flops / (ms2 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-                                       "phase_ms": dict(zip(names, r2["phase_ms"]))}}
+    if not a.no_sweep:
+        out["chunk_sweep"] = {}
+        for Cs in (128, 512, 1024):
+            if Cs == a.chunk:
+                continue
+            w.C = Cs
+            r2 = run_gpu(w, Cs, a.steps, a.warmup, 0)
+            ms2 = r2["event_ms"] / a.steps
+            out["chunk_sweep"][f"C{Cs}"] = {
+                "tokens_per_s": tokens / (ms2 * 1e-3), "ms_per_step": ms2,
+                "mfma_frac_layer": total_flops / (ms2 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                "group_tokens": r2["plan"]["L"], "phase_ms": dict(zip(names, r2["phase_ms"]))}
         w.C = a.chunk
     if not a.no_sweep:
         # the pages' long-context setting: Frobenius clipping of each chunk update at 1e-5
@@ -249,6 +261,11 @@ def main():
         ms4 = r4["event_ms"] / a.steps
         out["target_conv_leg"] = {"K": 5, "tokens_per_s": tokens / (ms4 * 1e-3), "ms_per_step": ms4,
                                   "phase_ms": dict(zip(names, r4["phase_ms"]))}
+        # packed documents: four documents of T/4 tokens, the state reset at each start
+        starts = [[w.T // 4 * k for k in (1, 2, 3)] for _ in range(w.B)]
+        r5 = run_gpu(w, a.chunk, a.steps, a.warmup, a.group_chunks, doc_starts=starts)
+        ms5 = r5["event_ms"] / a.steps
+        out["docs_leg"] = {"documents_per_sequence": 4, "tokens_per_s": tokens / (ms5 * 1e-3), "ms_per_step": ms5}
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, a.chunk, a.cpu_seconds)
     print(json.dumps(out), flush=True)

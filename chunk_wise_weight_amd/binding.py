@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libttt.so")
 TTT_F32, TTT_BF16 = 0, 1
 ERRORS = {-1: "TTT_E_NULL", -2: "TTT_E_SHAPE", -3: "TTT_E_DTYPE", -4: "TTT_E_NOMEM", -5: "TTT_E_HIP",
           -6: "TTT_E_NODEV", -7: "TTT_E_ARG"}
-EXPORTS = ("ttt_init", "ttt_forward_chunked", "ttt_reset", "ttt_destroy", "ttt_last_error",
+EXPORTS = ("ttt_init", "ttt_forward_chunked", "ttt_forward_docs", "ttt_reset", "ttt_destroy", "ttt_last_error",
            "ttt_set_group_chunks", "ttt_set_clip", "ttt_set_target_conv", "ttt_plan", "ttt_set_profiling", "ttt_phase_times",
            "ttt_workspace_bytes")
 
@@ -58,6 +58,8 @@ def lib() -> ctypes.CDLL:
     L.ttt_set_target_conv.argtypes = [vp, vp, i32, vp, vp]
     L.ttt_set_target_conv.restype = i32
     ip = ctypes.POINTER(i32)
+    L.ttt_forward_docs.argtypes = [vp, vp, vp, vp, i32, i32, i32, ip, ip, vp, vp, vp]
+    L.ttt_forward_docs.restype = i32
     L.ttt_plan.argtypes = [i32, i32, i32, ip, ip, ip, ip]
     L.ttt_plan.restype = i32
     L.ttt_set_profiling.argtypes = [vp, i32]
@@ -140,10 +142,7 @@ def ttt_init(W_up: torch.Tensor, W_gate: torch.Tensor, W_down0: torch.Tensor, C:
     return Handle(h, d, f, int(C), float(eta), dt, int(max_batch))
 
 
-def ttt_forward_chunked(h: Handle, x: torch.Tensor, ids: torch.Tensor, E_tgt: torch.Tensor,
-                        y: Optional[torch.Tensor] = None, W_final: Optional[torch.Tensor] = None,
-                        want_W_final: bool = False, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """x [B][T][d], ids [B][T+1] int32, E_tgt [vocab][d] -> (y [B][T][d], W_final [B][d][f] fp32 or None)."""
+def _forward_args(h, x, ids, E_tgt, y, W_final, want_W_final):
     _dev(x, "x", h.dtype)
     _dev(ids, "ids", torch.int32)
     _dev(E_tgt, "E_tgt", h.dtype)
@@ -164,10 +163,34 @@ def ttt_forward_chunked(h: Handle, x: torch.Tensor, ids: torch.Tensor, E_tgt: to
         _dev(W_final, "W_final", torch.float32)
         if tuple(W_final.shape) != (B, h.d, h.f):
             raise ValueError("W_final must be [B][d][f]")
+    return B, T, y, W_final
+
+
+
+def ttt_forward_chunked(h: Handle, x: torch.Tensor, ids: torch.Tensor, E_tgt: torch.Tensor,
+                        y: Optional[torch.Tensor] = None, W_final: Optional[torch.Tensor] = None,
+                        want_W_final: bool = False, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """x [B][T][d], ids [B][T+1] int32, E_tgt [vocab][d] -> (y [B][T][d], W_final [B][d][f] fp32 or None)."""
+    B, T, y, W_final = _forward_args(h, x, ids, E_tgt, y, W_final, want_W_final)
     _check(lib().ttt_forward_chunked(h.ptr, _ptr(x), _ptr(ids), _ptr(E_tgt), int(E_tgt.shape[0]), int(B), int(T),
                                      _ptr(y), _ptr(W_final), _stream(stream)), "ttt_forward_chunked")
     return y, W_final
 
+
+def ttt_forward_docs(h: Handle, x: torch.Tensor, ids: torch.Tensor, E_tgt: torch.Tensor, doc_starts,
+                     y: Optional[torch.Tensor] = None, W_final: Optional[torch.Tensor] = None,
+                     want_W_final: bool = False, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Packed documents: doc_starts[b] lists the positions in (0, T) where a new
+    document starts in sequence b (the state returns to W_down0 there)."""
+    B, T, y, W_final = _forward_args(h, x, ids, E_tgt, y, W_final, want_W_final)
+    if len(doc_starts) != B:
+        raise ValueError("doc_starts needs one list per sequence")
+    counts = (ctypes.c_int32 * max(B, 1))(*[len(s) for s in doc_starts])
+    flat = [int(p) for s in doc_starts for p in s]
+    starts = (ctypes.c_int32 * max(len(flat), 1))(*flat)
+    _check(lib().ttt_forward_docs(h.ptr, _ptr(x), _ptr(ids), _ptr(E_tgt), int(E_tgt.shape[0]), int(B), int(T),
+                                  starts, counts, _ptr(y), _ptr(W_final), _stream(stream)), "ttt_forward_docs")
+    return y, W_final
 
 def ttt_reset(h: Handle, b: int = -1, stream=None) -> None:
     _check(lib().ttt_reset(h.ptr, int(b), _stream(stream)), "ttt_reset")

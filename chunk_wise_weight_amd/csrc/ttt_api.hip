@@ -217,6 +217,128 @@ void *at(void *base, void *off) { return (char *)base + (size_t)off; }
 
 }  // namespace
 
+namespace {
+
+// One forward over B sequences of T tokens whose states are state[0 .. B).
+int forward_impl(ttt_handle *h, const void *x, const int32_t *ids, const void *E_tgt, int vocab, int B, int T,
+                 void *y, float *state, float *W_final, hipStream_t s_in) {
+  const bool learn = h->eta != 0.f;
+  Plan pl;
+  int rc = make_plan(T, h->C, learn ? h->G_override : 0, pl);
+  if (rc) return rc;
+  if (!learn && pl.ngroups > 0) {  // no updates: one group, the entry state serves every chunk
+    pl.ngroups = 1;
+    pl.L = (int)round_up_ll(T, 8);
+    pl.intra = 0;
+  }
+  hipStream_t s = s_in;
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  if (dev != h->device) return fail(TTT_E_ARG, "current device differs from the handle's device");
+  const size_t df = (size_t)h->d * h->f;
+  const bool prof = h->profiling;
+  if (prof) HIP_TRY(hipEventRecord(h->ev[0], s));
+  if (B == 0 || T == 0) {
+    if (prof) {
+      for (int i = 1; i <= kPhases; ++i) HIP_TRY(hipEventRecord(h->ev[i], s));
+      h->timed = true;
+    }
+    if (W_final && B > 0)
+      HIP_TRY(hipMemcpyAsync(W_final, state, (size_t)B * df * 4, hipMemcpyDeviceToDevice, s));
+    return TTT_OK;
+  }
+
+  const bool clip = learn && h->clip_tau > 0.f;
+  Layout lay{B, T, pl.T_pad, pl.C, pl.L, pl.ngroups, h->d, h->f, learn ? pl.intra : 0};
+  const int wspan = clip_wspan(lay, h->dt == TTT_BF16);
+  const bool conv = h->conv_K > 0 && (learn || lay.intra);
+  Scratch sc = scratch_layout(h, B, pl, learn, learn && pl.intra, clip, wspan, conv);
+  if (sc.total > h->ws_bytes) {
+    HIP_TRY(hipStreamSynchronize(s));
+    HIP_TRY(hipDeviceSynchronize());
+    if (h->ws) HIP_TRY(hipFree(h->ws));
+    h->ws = nullptr;
+    h->ws_bytes = 0;
+    if (hipMalloc(&h->ws, sc.total) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(TTT_E_NOMEM, "allocating " + std::to_string(sc.total) + " bytes of scratch");
+    }
+    h->ws_bytes = sc.total;
+  }
+  void *VT = at(h->ws, sc.VT), *Z = at(h->ws, sc.Z), *ZT = at(h->ws, sc.ZT), *snap = at(h->ws, sc.snap),
+       *P = at(h->ws, sc.P);
+  void *Vrow = clip ? at(h->ws, sc.Vrow) : nullptr;
+  float *rowpart = (float *)at(h->ws, sc.rowpart), *cfac = (float *)at(h->ws, sc.cfac);
+  void *U = at(h->ws, sc.U);
+
+  if (h->dt == TTT_BF16) {
+    if (conv) {
+      HIP_TRY(launch_conv_taps_bf16(ids, (const bf16_t *)E_tgt, vocab, h->conv_w, h->conv_K, (bf16_t *)U, lay, s));
+      HIP_TRY(launch_target_gemm_bf16((const bf16_t *)U, (const bf16_t *)h->Wt, (bf16_t *)VT, (bf16_t *)Vrow, lay, s));
+    } else if (learn || lay.intra) {
+      HIP_TRY(launch_gather_vt_bf16(ids, (const bf16_t *)E_tgt, vocab, (bf16_t *)VT, (bf16_t *)Vrow, lay, s));
+    }
+    if (prof) HIP_TRY(hipEventRecord(h->ev[1], s));
+    HIP_TRY(launch_a1_bf16((const bf16_t *)x, (const bf16_t *)h->Wug, (bf16_t *)Z, (bf16_t *)ZT, h->eta,
+                           learn ? 1 : 0, lay, s));
+    if (prof) HIP_TRY(hipEventRecord(h->ev[2], s));
+    if (clip) {
+      HIP_TRY(launch_chunk_gram_bf16((const bf16_t *)Z, (const bf16_t *)Vrow, rowpart, wspan, lay, s));
+      HIP_TRY(launch_chunk_factors(rowpart, cfac, wspan, h->eta, h->clip_tau, lay, s));
+      HIP_TRY(launch_scale_vt_bf16((bf16_t *)VT, cfac, lay, s));
+    }
+    if (prof) HIP_TRY(hipEventRecord(h->ev[3], s));
+    if (learn) {
+      HIP_TRY(launch_update_bf16((const bf16_t *)ZT, (const bf16_t *)VT, state, (bf16_t *)snap, lay, s));
+    } else {
+      for (int b = 0; b < B; ++b)
+        HIP_TRY(launch_f32_to_bf16(state + (size_t)b * df, (bf16_t *)snap + (size_t)b * df, (long long)df, s));
+    }
+    if (prof) HIP_TRY(hipEventRecord(h->ev[4], s));
+    if (lay.intra) HIP_TRY(launch_scores_bf16((const bf16_t *)Z, (bf16_t *)P, h->eta, lay, s));
+    if (prof) HIP_TRY(hipEventRecord(h->ev[5], s));
+    HIP_TRY(launch_out_bf16((const bf16_t *)Z, (const bf16_t *)P, (const bf16_t *)snap, (const bf16_t *)VT,
+                            (bf16_t *)y, lay, s));
+  } else {
+    if (conv) {
+      HIP_TRY(launch_conv_taps_f32(ids, (const float *)E_tgt, vocab, h->conv_w, h->conv_K, (float *)U, lay, s));
+      HIP_TRY(launch_target_gemm_f32((const float *)U, (const float *)h->Wt, (float *)VT, (float *)Vrow, lay, s));
+    } else if (learn || lay.intra) {
+      HIP_TRY(launch_gather_vt_f32(ids, (const float *)E_tgt, vocab, (float *)VT, (float *)Vrow, lay, s));
+    }
+    if (prof) HIP_TRY(hipEventRecord(h->ev[1], s));
+    HIP_TRY(launch_a1_f32((const float *)x, (const float *)h->Wug, (float *)Z, (float *)ZT, h->eta, learn ? 1 : 0,
+                          lay, s));
+    if (prof) HIP_TRY(hipEventRecord(h->ev[2], s));
+    if (clip) {
+      HIP_TRY(launch_chunk_gram_f32((const float *)Z, (const float *)Vrow, rowpart, lay, s));
+      HIP_TRY(launch_chunk_factors(rowpart, cfac, wspan, h->eta, h->clip_tau, lay, s));
+      HIP_TRY(launch_scale_vt_f32((float *)VT, cfac, lay, s));
+    }
+    if (prof) HIP_TRY(hipEventRecord(h->ev[3], s));
+    if (learn) {
+      HIP_TRY(launch_update_f32((const float *)ZT, (const float *)VT, state, (float *)snap, lay, s));
+    } else {
+      HIP_TRY(hipMemcpyAsync(snap, state, (size_t)B * df * 4, hipMemcpyDeviceToDevice, s));
+    }
+    if (prof) HIP_TRY(hipEventRecord(h->ev[4], s));
+    if (lay.intra) HIP_TRY(launch_scores_f32((const float *)Z, (float *)P, h->eta, lay, s));
+    if (prof) HIP_TRY(hipEventRecord(h->ev[5], s));
+    HIP_TRY(launch_out_f32((const float *)Z, (const float *)P, (const float *)snap, (const float *)VT, (float *)y,
+                           lay, s));
+  }
+  if (prof) HIP_TRY(hipEventRecord(h->ev[6], s));
+  if (W_final) HIP_TRY(hipMemcpyAsync(W_final, state, (size_t)B * df * 4, hipMemcpyDeviceToDevice, s));
+  if (prof) {
+    HIP_TRY(hipEventRecord(h->ev[7], s));
+    h->timed = true;
+  }
+  return TTT_OK;
+}
+
+
+}  // namespace
+
 extern "C" {
 
 const char *ttt_last_error(void) { return g_err.c_str(); }
@@ -394,117 +516,57 @@ int ttt_forward_chunked(ttt_handle *h, const void *x, const int32_t *ids, const 
   if (B > 0 && T > 0 && vocab < 1) return fail(TTT_E_SHAPE, "vocab must be >= 1");
   if (B > 0 && T > 0 && (misaligned(x) || misaligned(E_tgt) || misaligned(y)))
     return fail(TTT_E_ARG, "x, E_tgt and y must be 16-byte aligned");
-  const bool learn = h->eta != 0.f;
-  Plan pl;
-  int rc = make_plan(T, h->C, learn ? h->G_override : 0, pl);
-  if (rc) return rc;
-  if (!learn && pl.ngroups > 0) {  // no updates: one group, the entry state serves every chunk
-    pl.ngroups = 1;
-    pl.L = (int)round_up_ll(T, 8);
-    pl.intra = 0;
+  return forward_impl(h, x, ids, E_tgt, vocab, B, T, y, h->state, W_final, (hipStream_t)hip_stream);
+}
+
+int ttt_forward_docs(ttt_handle *h, const void *x, const int32_t *ids, const void *E_tgt, int vocab, int B, int T,
+                     const int32_t *doc_starts, const int32_t *doc_counts, void *y, float *W_final,
+                     void *hip_stream) {
+  if (!h) return fail(TTT_E_NULL, "handle is NULL");
+  if (B < 0 || B > h->max_batch) return fail(TTT_E_SHAPE, "B must be in [0, max_batch]");
+  if (T < 0 || T > kMaxT) return fail(TTT_E_SHAPE, "T must be in [0, 2^23]");
+  if (B > 0 && T > 0 && (!x || !ids || !E_tgt || !y)) return fail(TTT_E_NULL, "x, ids, E_tgt and y must be non-NULL");
+  if (B > 0 && T > 0 && vocab < 1) return fail(TTT_E_SHAPE, "vocab must be >= 1");
+  if (B > 0 && T > 0 && (misaligned(x) || misaligned(E_tgt) || misaligned(y)))
+    return fail(TTT_E_ARG, "x, E_tgt and y must be 16-byte aligned");
+  if (B > 0 && T > 0 && !doc_counts) return fail(TTT_E_NULL, "doc_counts must be non-NULL");
+  long long total = 0;
+  for (int b = 0; b < B && T > 0; ++b) {
+    if (doc_counts[b] < 0 || doc_counts[b] >= T) return fail(TTT_E_ARG, "doc_counts[b] must be in [0, T)");
+    total += doc_counts[b];
+  }
+  if (total > 0 && !doc_starts) return fail(TTT_E_NULL, "doc_starts must be non-NULL");
+  for (int b = 0, k = 0; b < B && T > 0; ++b) {
+    int prev = 0;
+    for (int j = 0; j < doc_counts[b]; ++j, ++k) {
+      if (doc_starts[k] <= prev || doc_starts[k] >= T)
+        return fail(TTT_E_ARG, "document starts must increase strictly inside (0, T)");
+      prev = doc_starts[k];
+    }
   }
   hipStream_t s = (hipStream_t)hip_stream;
-  int dev = 0;
-  HIP_TRY(hipGetDevice(&dev));
-  if (dev != h->device) return fail(TTT_E_ARG, "current device differs from the handle's device");
+  if (B == 0 || T == 0 || total == 0) return forward_impl(h, x, ids, E_tgt, vocab, B, T, y, h->state, W_final, s);
+  const size_t es = h->dt == TTT_BF16 ? 2 : 4;
   const size_t df = (size_t)h->d * h->f;
-  const bool prof = h->profiling;
-  if (prof) HIP_TRY(hipEventRecord(h->ev[0], s));
-  if (B == 0 || T == 0) {
-    if (prof) {
-      for (int i = 1; i <= kPhases; ++i) HIP_TRY(hipEventRecord(h->ev[i], s));
-      h->timed = true;
+  // Each document runs on its own slice: the state of sequence b returns to
+  // W_down0 at every document start, and chunking restarts there. The ids
+  // slice keeps the next document's first token as its look-ahead; that
+  // target only enters the document's last chunk update, which the reset
+  // discards.
+  for (int b = 0, k = 0; b < B; ++b) {
+    int s0 = 0;
+    for (int j = 0; j <= doc_counts[b]; ++j) {
+      const int s1 = j < doc_counts[b] ? doc_starts[k + j] : T;
+      if (j > 0) HIP_TRY(hipMemcpyAsync(h->state + (size_t)b * df, h->W0, df * 4, hipMemcpyDeviceToDevice, s));
+      const size_t off = ((size_t)b * T + s0) * h->d * es;
+      const int rc = forward_impl(h, (const char *)x + off, ids + (size_t)b * (T + 1) + s0, E_tgt, vocab, 1, s1 - s0,
+                                  (char *)y + off, h->state + (size_t)b * df, nullptr, s);
+      if (rc) return rc;
+      s0 = s1;
     }
-    if (W_final && B > 0)
-      HIP_TRY(hipMemcpyAsync(W_final, h->state, (size_t)B * df * 4, hipMemcpyDeviceToDevice, s));
-    return TTT_OK;
+    k += doc_counts[b];
   }
-
-  const bool clip = learn && h->clip_tau > 0.f;
-  Layout lay{B, T, pl.T_pad, pl.C, pl.L, pl.ngroups, h->d, h->f, learn ? pl.intra : 0};
-  const int wspan = clip_wspan(lay, h->dt == TTT_BF16);
-  const bool conv = h->conv_K > 0 && (learn || lay.intra);
-  Scratch sc = scratch_layout(h, B, pl, learn, learn && pl.intra, clip, wspan, conv);
-  if (sc.total > h->ws_bytes) {
-    HIP_TRY(hipStreamSynchronize(s));
-    HIP_TRY(hipDeviceSynchronize());
-    if (h->ws) HIP_TRY(hipFree(h->ws));
-    h->ws = nullptr;
-    h->ws_bytes = 0;
-    if (hipMalloc(&h->ws, sc.total) != hipSuccess) {
-      (void)hipGetLastError();
-      return fail(TTT_E_NOMEM, "allocating " + std::to_string(sc.total) + " bytes of scratch");
-    }
-    h->ws_bytes = sc.total;
-  }
-  void *VT = at(h->ws, sc.VT), *Z = at(h->ws, sc.Z), *ZT = at(h->ws, sc.ZT), *snap = at(h->ws, sc.snap),
-       *P = at(h->ws, sc.P);
-  void *Vrow = clip ? at(h->ws, sc.Vrow) : nullptr;
-  float *rowpart = (float *)at(h->ws, sc.rowpart), *cfac = (float *)at(h->ws, sc.cfac);
-  void *U = at(h->ws, sc.U);
-
-  if (h->dt == TTT_BF16) {
-    if (conv) {
-      HIP_TRY(launch_conv_taps_bf16(ids, (const bf16_t *)E_tgt, vocab, h->conv_w, h->conv_K, (bf16_t *)U, lay, s));
-      HIP_TRY(launch_target_gemm_bf16((const bf16_t *)U, (const bf16_t *)h->Wt, (bf16_t *)VT, (bf16_t *)Vrow, lay, s));
-    } else if (learn || lay.intra) {
-      HIP_TRY(launch_gather_vt_bf16(ids, (const bf16_t *)E_tgt, vocab, (bf16_t *)VT, (bf16_t *)Vrow, lay, s));
-    }
-    if (prof) HIP_TRY(hipEventRecord(h->ev[1], s));
-    HIP_TRY(launch_a1_bf16((const bf16_t *)x, (const bf16_t *)h->Wug, (bf16_t *)Z, (bf16_t *)ZT, h->eta,
-                           learn ? 1 : 0, lay, s));
-    if (prof) HIP_TRY(hipEventRecord(h->ev[2], s));
-    if (clip) {
-      HIP_TRY(launch_chunk_gram_bf16((const bf16_t *)Z, (const bf16_t *)Vrow, rowpart, wspan, lay, s));
-      HIP_TRY(launch_chunk_factors(rowpart, cfac, wspan, h->eta, h->clip_tau, lay, s));
-      HIP_TRY(launch_scale_vt_bf16((bf16_t *)VT, cfac, lay, s));
-    }
-    if (prof) HIP_TRY(hipEventRecord(h->ev[3], s));
-    if (learn) {
-      HIP_TRY(launch_update_bf16((const bf16_t *)ZT, (const bf16_t *)VT, h->state, (bf16_t *)snap, lay, s));
-    } else {
-      for (int b = 0; b < B; ++b)
-        HIP_TRY(launch_f32_to_bf16(h->state + (size_t)b * df, (bf16_t *)snap + (size_t)b * df, (long long)df, s));
-    }
-    if (prof) HIP_TRY(hipEventRecord(h->ev[4], s));
-    if (lay.intra) HIP_TRY(launch_scores_bf16((const bf16_t *)Z, (bf16_t *)P, h->eta, lay, s));
-    if (prof) HIP_TRY(hipEventRecord(h->ev[5], s));
-    HIP_TRY(launch_out_bf16((const bf16_t *)Z, (const bf16_t *)P, (const bf16_t *)snap, (const bf16_t *)VT,
-                            (bf16_t *)y, lay, s));
-  } else {
-    if (conv) {
-      HIP_TRY(launch_conv_taps_f32(ids, (const float *)E_tgt, vocab, h->conv_w, h->conv_K, (float *)U, lay, s));
-      HIP_TRY(launch_target_gemm_f32((const float *)U, (const float *)h->Wt, (float *)VT, (float *)Vrow, lay, s));
-    } else if (learn || lay.intra) {
-      HIP_TRY(launch_gather_vt_f32(ids, (const float *)E_tgt, vocab, (float *)VT, (float *)Vrow, lay, s));
-    }
-    if (prof) HIP_TRY(hipEventRecord(h->ev[1], s));
-    HIP_TRY(launch_a1_f32((const float *)x, (const float *)h->Wug, (float *)Z, (float *)ZT, h->eta, learn ? 1 : 0,
-                          lay, s));
-    if (prof) HIP_TRY(hipEventRecord(h->ev[2], s));
-    if (clip) {
-      HIP_TRY(launch_chunk_gram_f32((const float *)Z, (const float *)Vrow, rowpart, lay, s));
-      HIP_TRY(launch_chunk_factors(rowpart, cfac, wspan, h->eta, h->clip_tau, lay, s));
-      HIP_TRY(launch_scale_vt_f32((float *)VT, cfac, lay, s));
-    }
-    if (prof) HIP_TRY(hipEventRecord(h->ev[3], s));
-    if (learn) {
-      HIP_TRY(launch_update_f32((const float *)ZT, (const float *)VT, h->state, (float *)snap, lay, s));
-    } else {
-      HIP_TRY(hipMemcpyAsync(snap, h->state, (size_t)B * df * 4, hipMemcpyDeviceToDevice, s));
-    }
-    if (prof) HIP_TRY(hipEventRecord(h->ev[4], s));
-    if (lay.intra) HIP_TRY(launch_scores_f32((const float *)Z, (float *)P, h->eta, lay, s));
-    if (prof) HIP_TRY(hipEventRecord(h->ev[5], s));
-    HIP_TRY(launch_out_f32((const float *)Z, (const float *)P, (const float *)snap, (const float *)VT, (float *)y,
-                           lay, s));
-  }
-  if (prof) HIP_TRY(hipEventRecord(h->ev[6], s));
   if (W_final) HIP_TRY(hipMemcpyAsync(W_final, h->state, (size_t)B * df * 4, hipMemcpyDeviceToDevice, s));
-  if (prof) {
-    HIP_TRY(hipEventRecord(h->ev[7], s));
-    h->timed = true;
-  }
   return TTT_OK;
 }
 

@@ -112,6 +112,29 @@ int ttt_forward_chunked(ttt_handle *h, const void *x, const int32_t *ids, const 
                         int T, void *y, float *W_final, void *hip_stream);
 
 /*
+ * ttt_forward_docs — ttt_forward_chunked over streams that pack several
+ * documents (paperlayer App. B; iplexlaw sec. 6: the fast weight returns to its
+ * initial value at document boundaries, so no state crosses between
+ * independent documents).
+ *   doc_counts : host array [B]; doc_counts[b] documents start inside
+ *                sequence b's block besides the one it opens with (0 .. T-1).
+ *   doc_starts : host array, the concatenated start positions: sequence b's
+ *                are the next doc_counts[b] entries, strictly increasing inside
+ *                (0, T). NULL allowed when every count is 0.
+ * The first document continues the sequence's current state (like
+ * ttt_forward_chunked); at every listed start the state returns to W_down0 and
+ * chunking restarts from that token. A document's last target row lies in its
+ * last chunk, whose update the reset discards, so no target crosses a
+ * document end. The final state is the last document's, kept in the handle as
+ * usual. Documents run one after the other on the stream (B = 1 launches per
+ * document); with profiling on, ttt_phase_times reports the last document's
+ * phases. Other arguments, ownership and errors as ttt_forward_chunked.
+ */
+int ttt_forward_docs(ttt_handle *h, const void *x, const int32_t *ids, const void *E_tgt, int vocab, int B, int T,
+                     const int32_t *doc_starts, const int32_t *doc_counts, void *y, float *W_final,
+                     void *hip_stream);
+
+/*
  * ttt_reset — restore the fast weight of sequence b (or of every sequence if
  * b == -1) to W_down0: the document-boundary reset (paperlayer App. B;
  * iplexlaw sec. 6). Queued on `hip_stream`.

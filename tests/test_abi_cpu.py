@@ -118,6 +118,8 @@ def test_null_handle_paths():
     assert L.ttt_reset(None, -1, None) == -1
     assert L.ttt_set_group_chunks(None, 2) == -1
     assert L.ttt_set_clip(None, 1.0) == -1
+    assert L.ttt_set_target_conv(None, None, 0, None, None) == -1
+    assert L.ttt_forward_docs(None, None, None, None, 1, 1, 1, None, None, None, None, None) == -1
     assert L.ttt_set_profiling(None, 1) == -1
     buf = (ctypes.c_float * 6)()
     assert L.ttt_phase_times(None, buf, 6) == -1
