@@ -57,6 +57,6 @@ def c4_inputs():
     return make_config("c4_4b_128k")
 
 
-@pytest.mark.parametrize("C", [256, 128])
+@pytest.mark.parametrize("C", [256, 128, 512, 1024])
 def test_c4_4b_128k(c4_inputs, C):
     _check(c4_inputs, C)
