@@ -41,6 +41,8 @@ def parse():
                          "target, four packed documents")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-baseline duration")
+    ap.add_argument("--stack", action="store_true",
+                    help="measure the 36-layer stack (B=2 x 16384 tokens, C=256) instead of the single layer")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain device copy of COPY_BYTES (calibrates rocprofv3 FETCH_SIZE/WRITE_SIZE)")
     return ap.parse_args()
@@ -180,6 +182,72 @@ def cpu_baseline(w, C, target_s):
                       f"d={w.d} f={w.f}, fp64 NumPy oracle, target rows gathered to the ids used; {t:.1f} s"}
 
 
+def run_stack(a):
+    """36 independent 4B-class layers, each with its own weights, fast weights and
+    synthetic input; the sequences' token stream and the target-embedding table
+    are the model's, shared by every layer. One step runs all 36 layers."""
+    import numpy as np
+    import torch
+
+    import chunk_wise_weight_amd as ttt
+    from synth import make_config, make_inputs
+    from synth.workloads import C5_LAYERS
+
+    t0 = time.perf_counter()
+    base = make_config("c5_4b_stack36")
+    dt = torch.bfloat16
+
+    def dev(arr):
+        return torch.from_numpy(np.ascontiguousarray(arr)).to("cuda", dt)
+
+    E = dev(base.E_tgt)
+    ids = torch.from_numpy(np.ascontiguousarray(base.ids)).cuda()
+    layers = []
+    for l in range(C5_LAYERS):
+        w = base if l == 0 else make_inputs(d=base.d, f=base.f, B=base.B, T=base.T, C=base.C, eta=base.eta,
+                                            dtype="bf16", vocab=1, e_std=0.02, seed=(5, l))
+        h = ttt.ttt_init(dev(w.W_up), dev(w.W_gate), dev(w.W_down0), base.C, base.eta, max_batch=base.B)
+        layers.append((h, dev(w.x)))
+    print(f"[bench] stack of {C5_LAYERS} layers d={base.d} f={base.f} B={base.B} T={base.T} ready in "
+          f"{time.perf_counter() - t0:.1f}s", file=sys.stderr, flush=True)
+    y = torch.empty((base.B, base.T, base.d), dtype=dt, device="cuda")
+
+    def step():
+        for h, x in layers:
+            ttt.ttt_reset(h)
+            ttt.ttt_forward_chunked(h, x, ids, E, y=y)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(a.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / a.steps
+    tokens = base.B * base.T
+    flops = 8.0 * base.d * base.f * tokens * C5_LAYERS
+    ws = sum(ttt.ttt_workspace_bytes(h) for h, _ in layers)
+    out = {
+        "metric": "TTT-MLP stack tokens/s, 36 layers of d=2560/ff=9728, B=2 x 16384",
+        "value": tokens / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "c5_4b_stack36: 36 SwiGLU MLP layers, own weights and fast W_down per sequence, "
+                               "shared token stream and target table", "layers": C5_LAYERS, "d_model": base.d,
+                   "d_ff": base.f, "batch": base.B, "seq_len": base.T, "chunk": base.C, "eta": base.eta,
+                   "parallelism": "single GPU"},
+        "layer_tokens_per_s": tokens * C5_LAYERS / (ms * 1e-3),
+        "mfma_frac_stack": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "memory_gb": ws / 1e9,
+    }
+    for h, _ in layers:
+        ttt.ttt_destroy(h)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     a = parse()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -191,6 +259,9 @@ def main():
     from synth import make_config
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if a.stack:
+        run_stack(a)
+        return
     t0 = time.perf_counter()
     w = make_config(WORKLOAD, C=a.chunk, T=a.seq_len)
     print(f"[bench] inputs {WORKLOAD} d={w.d} f={w.f} B={w.B} T={w.T} generated in "
