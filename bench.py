@@ -172,11 +172,11 @@ def cpu_baseline(w, C, target_s):
         oracle.ttt_forward_one(w.x[0, :S], inv.astype(np.int64), E_s, w.W_up, w.W_gate, w.W_down0, C, w.eta)
         return time.perf_counter() - t0
 
-    S = 2 * C
+    # a short run gives the rate; the timed sample is then sized to about target_s seconds
+    S = min(w.T, 4 * C)
     t = run(S)
-    while t < target_s / 3 and S * 2 <= min(w.T, 16384):
-        S *= 2
-        t = run(S)
+    S = max(S, min(w.T, int(S / t * target_s) // C * C))
+    t = run(S)
     return {"value": S / t, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"first {S} tokens of sequence 0 ({S // C} chunks of {C}), full layer shape "
                       f"d={w.d} f={w.f}, fp64 NumPy oracle, target rows gathered to the ids used; {t:.1f} s"}
