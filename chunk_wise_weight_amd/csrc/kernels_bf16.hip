@@ -175,13 +175,16 @@ struct Frag {
 };
 
 // Read substep ks (0 or 1) of half h (0 or 1) of an LDS slab into registers.
-template <int WN, int NBJ>
+// APLANE: the A tile is held as 8 planes of [256 rows][8 columns] (column
+// chunk c of row r at (c*256 + r)*8) instead of swizzled 128-byte rows.
+template <int WN, int NBJ, bool APLANE = false>
 __device__ __forceinline__ void frag_read(Frag<NBJ> &fr, const Slab<WN, NBJ> &st, int h, int ks, int wm, int wn,
                                           int lane) {
   const int c = 4 * h + 2 * ks + (lane >> 5);
 #pragma unroll
   for (int bi = 0; bi < 4; ++bi)
-    fr.a[bi] = *reinterpret_cast<const bf16x8 *>(st.a + lds_off(wm * 128 + bi * 32 + (lane & 31), c));
+    fr.a[bi] = *reinterpret_cast<const bf16x8 *>(
+        st.a + (APLANE ? (c * BM + wm * 128 + bi * 32 + (lane & 31)) * 8 : lds_off(wm * 128 + bi * 32 + (lane & 31), c)));
 #pragma unroll
   for (int bj = 0; bj < NBJ; ++bj)
     fr.b[bj] = *reinterpret_cast<const bf16x8 *>(st.b + lds_off(wn * 32 * NBJ + bj * 32 + (lane & 31), c));
@@ -221,14 +224,14 @@ __device__ __forceinline__ void issue_point(IssueFn &&issue_part, int slab) {
 // refilled. Spreading the loads keeps a burst of them from stalling the MFMA
 // issue. With AFTER, after_fn(acc) runs once all of stage kt's MFMAs are
 // queued, and the next fragments are read only then (few registers live).
-template <int WN, int NBJ, int NSL, bool AFTER, class IssueFn, class AfterFn>
+template <int WN, int NBJ, int NSL, bool AFTER, bool APLANE = false, class IssueFn, class AfterFn>
 __device__ __forceinline__ void pipelined_stage(Acc<NBJ> &acc, Slab<WN, NBJ> *ring, Frag<NBJ> &cur, Frag<NBJ> &nxt,
                                                 int kt, int nk, int wm, int wn, int lane, IssueFn &&issue_part,
                                                 AfterFn &&after_fn) {
   constexpr int LPS = loads_per_slab<WN, NBJ>();
   const int sl = kt >> 1, h = kt & 1;
   const int nsl = (nk + 1) >> 1;
-  frag_read(nxt, ring[sl % NSL], h, 1, wm, wn, lane);
+  frag_read<WN, NBJ, APLANE>(nxt, ring[sl % NSL], h, 1, wm, wn, lane);
   pin();
   frag_mma<0, 1>(acc, cur);
   pin();
@@ -253,7 +256,7 @@ __device__ __forceinline__ void pipelined_stage(Acc<NBJ> &acc, Slab<WN, NBJ> *ri
   pin();
   // unconditional (past the end it reads a stale buffer of the ring): no
   // branch, so the compiler can count the reads and wait for each exactly
-  if (!AFTER) frag_read(cur, ring[((kt + 1) >> 1) % NSL], (kt + 1) & 1, 0, wm, wn, lane);
+  if (!AFTER) frag_read<WN, NBJ, APLANE>(cur, ring[((kt + 1) >> 1) % NSL], (kt + 1) & 1, 0, wm, wn, lane);
   if (refill) issue_point<LPS, 3>(issue_part, rs);
   pin();
   frag_mma<1, 2>(acc, nxt);
@@ -267,7 +270,7 @@ __device__ __forceinline__ void pipelined_stage(Acc<NBJ> &acc, Slab<WN, NBJ> *ri
   pin();
   if (AFTER) {
     after_fn(acc);
-    frag_read(cur, ring[((kt + 1) >> 1) % NSL], (kt + 1) & 1, 0, wm, wn, lane);
+    frag_read<WN, NBJ, APLANE>(cur, ring[((kt + 1) >> 1) % NSL], (kt + 1) & 1, 0, wm, wn, lane);
     pin();
   }
 }
@@ -365,6 +368,50 @@ __device__ __forceinline__ void gemm_rows(Acc<NBJ> &acc, Slab<WN, NBJ> *ring, co
   frag_read(cur, ring[0], 0, 0, wm, wn, lane);
   for (int kt = 0; kt < nk; ++kt)
     pipelined_stage<WN, NBJ, NSL, false>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, part, NoHook{});
+}
+
+// A "plane" operand holds column chunk c (8 columns) of every row contiguously:
+// element (r, k) at (k/8)*pstride + r*8 + k%8. Load n (0..LA-1) of wave w of a
+// 256-row x 64-column A tile moves 64 rows of one plane: 1 KB contiguous in
+// memory, landing as 1 KB contiguous in LDS ([8 planes][256 rows][8]).
+template <int NW>
+__device__ __forceinline__ void issue_plane(bf16_t *lds_tile, const bf16_t *base, long long pstride, int nrows,
+                                            int kvalid, int row0, int k, int w, int lane, int n) {
+  const int q = w * (32 / NW) + n;  // 1 KB piece 0..31 of the tile
+  const int pl = q >> 2, rb = (q & 3) * 64;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t *>(base + ((long long)(k >> 3) + pl) * pstride + (long long)row0 * 8), (short)0, 0x7fffffff,
+      kBufferFlags);
+  const bool ok = row0 + rb + lane < nrows && k + pl * 8 < kvalid;
+  const uint32_t voff = ok ? (uint32_t)((rb + lane) * 16) : kOutOfRange;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(lds_tile + (pl * BM + rb) * 8), 16, voff, 0, 0, 0);
+}
+
+// K loop over nk stages, A a plane operand (rows row0.., pstride elements per
+// plane, nrows rows valid, kvalid columns) and B row-major. 256 x 256 tiles.
+__device__ __forceinline__ void gemm_plane_a(Acc<NBJ_W> &acc, Slab<WN_W, NBJ_W> *ring, const bf16_t *abase,
+                                             long long pstride, int anrows, int akvalid, const Opnd &b, int nk,
+                                             int arow0, int brow0) {
+  const int lane = threadIdx.x & 63;
+  const int w = wave_id(), wm = w & 1, wn = w >> 1;
+  if (nk <= 0) return;
+  constexpr int LA = loads_a<WN_W, NBJ_W>();
+  static_assert(LA * 2 * WN_W == 32, "one A tile is 32 pieces of 1 KB");
+  const int nsl = (nk + 1) >> 1;
+  auto part = [&](int sl, int j) {
+    if (j < LA)
+      issue_plane<2 * WN_W>(ring[sl % NSL_W].a, abase, pstride, anrows, akvalid, arow0, sl * SK, w, lane, j);
+    else
+      issue_one<false, 32 * WN_W * NBJ_W, 2 * WN_W>(ring[sl % NSL_W].b, b, brow0, sl * SK, w, lane, j - LA);
+  };
+  for (int sl = 0; sl < NSL_W && sl < nsl; ++sl)
+#pragma unroll
+    for (int j = 0; j < loads_per_slab<WN_W, NBJ_W>(); ++j) part(sl, j);
+  Frag<NBJ_W> cur, nxt;
+  slab_wait<loads_per_slab<WN_W, NBJ_W>()>((nsl - 1) < (NSL_W - 1) ? (nsl - 1) : (NSL_W - 1));
+  frag_read<WN_W, NBJ_W, true>(cur, ring[0], 0, 0, wm, wn, lane);
+  for (int kt = 0; kt < nk; ++kt)
+    pipelined_stage<WN_W, NBJ_W, NSL_W, false, true>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, part, NoHook{});
 }
 
 // ---------------------------------------------------------------------------
@@ -500,25 +547,27 @@ struct UpdArgs {
   int tile0;  // first 256 x 256 tile of this launch
 };
 
-// Write the accumulator tile as bf16 into a snapshot W[a][i] ([d][f]).
-// `lane_ptr` points at this lane's first element (a = j0 + wn*32*NBJ + l%32,
-// i = i0 + wm*128 + 4*(l/32)); tiles are always full (d, f multiples of 256).
+// Write the accumulator tile as bf16 into a snapshot W[a][i], held as planes
+// of 8 columns ([f/8][d][8]: element (a, i) at ((i/8)*d + a)*8 + i%8). Lane l
+// holds, per group of 4 accumulator registers, four consecutive i of one a;
+// lanes l and l+32 hold the two halves of one 16-byte chunk, and the 32 lanes
+// of a half walk 32 consecutive a: each store instruction writes 512
+// contiguous bytes. `lane_ptr` points at this lane's element for (bi, bj, q) =
+// (0, 0, 0): a = j0 + wn*32*NBJ + l%32, i = i0 + wm*128 + 4*(l/32); tiles are
+// always full (d, f multiples of 256).
 template <int NBJ>
-__device__ __forceinline__ void dump_snapshot(const Acc<NBJ> &acc, bf16_t *lane_ptr, int f) {
+__device__ __forceinline__ void dump_snapshot(const Acc<NBJ> &acc, bf16_t *lane_ptr, int d) {
 #pragma unroll
-  for (int bj = 0; bj < NBJ; ++bj) {
-    bf16_t *row = lane_ptr + (long long)bj * 32 * f;
+  for (int bj = 0; bj < NBJ; ++bj)
 #pragma unroll
-    for (int bi = 0; bi < 4; ++bi) {
+    for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         uint2 pk;
         pk.x = pack_bf16x2(acc.v[bi][bj][4 * q + 0], acc.v[bi][bj][4 * q + 1]);
         pk.y = pack_bf16x2(acc.v[bi][bj][4 * q + 2], acc.v[bi][bj][4 * q + 3]);
-        *reinterpret_cast<uint2 *>(row + bi * 32 + 8 * q) = pk;
+        *reinterpret_cast<uint2 *>(lane_ptr + (long long)(bi * 4 + q) * 8 * d + bj * 256) = pk;
       }
-    }
-  }
 }
 
 // WN = 4: workgroup n of the launch is tile tile0 + n (a 256 x 256 tile);
@@ -538,11 +587,13 @@ __global__ __launch_bounds__(128 * WN, 1) void k_update(UpdArgs p) {
   const int lane = threadIdx.x & 63;
   const int w = wave_id(), wm = w & 1, wn = w >> 1;
   const long long df = (long long)p.d * p.f;
-  // this lane's first element of the tile, relative to W[0][0]
+  // this lane's first element of the tile in the state ([d][f]) and in a snapshot ([f/8][d][8])
   const long long lane_off =
       (long long)(j0 + wn * 32 * NBJ + (lane & 31)) * p.f + i0 + wm * 128 + 4 * (lane >> 5);
+  const long long lane_snap =
+      (long long)((i0 + wm * 128) / 8) * 8 * p.d + (j0 + wn * 32 * NBJ + (lane & 31)) * 8 + 4 * (lane >> 5);
   float *st = p.state + b * df + lane_off;
-  bf16_t *snap0 = p.snap + (long long)b * p.ngroups * df + lane_off;
+  bf16_t *snap0 = p.snap + (long long)b * p.ngroups * df + lane_snap;
 
   Acc<NBJ> acc;
 #pragma unroll
@@ -566,7 +617,7 @@ __global__ __launch_bounds__(128 * WN, 1) void k_update(UpdArgs p) {
   // Snapshot 0 is the entry state; group starts are multiples of the stage
   // depth, so snapshot g is written right after the last stage of group g-1,
   // while the following slabs are already in flight.
-  dump_snapshot(acc, snap0, p.f);
+  dump_snapshot(acc, snap0, p.d);
   int g = 1;
   auto part = [&](int sl, int j) {
     issue_part<true, true>(ring[sl % NSL], sa, sb, i0, j0, sl * SK, w, lane, j);
@@ -586,7 +637,7 @@ __global__ __launch_bounds__(128 * WN, 1) void k_update(UpdArgs p) {
   // is too, and the count exceeds the number allowed; a store in flight can
   // only make a wait last longer.
   auto snapshot = [&](const Acc<NBJ> &a) {
-    dump_snapshot(a, snap0 + (long long)g * df, p.f);
+    dump_snapshot(a, snap0 + (long long)g * df, p.d);
     ++g;
   };
   // Stages of group g-1 run plain; its last stage ends with snapshot g.
@@ -672,6 +723,25 @@ __global__ __launch_bounds__(NT_W, 1) void k_scores(ScoreArgs p) {
 }
 
 // ---------------------------------------------------------------------------
+// Snapshot from an fp32 state with no update: snap[((i/8)*d + a)*8 + i%8] =
+// bf16(state[a][i]). Thread (plane, a) converts one 8-column chunk.
+__global__ __launch_bounds__(256) void k_state_to_snap(const float *state, bf16_t *snap, int d, int f) {
+  const long long n = (long long)d * (f / 8);
+  for (long long t = blockIdx.x * 256LL + threadIdx.x; t < n; t += (long long)gridDim.x * 256) {
+    const int a = (int)(t % d);
+    const long long pl = t / d;
+    const float4 lo = *reinterpret_cast<const float4 *>(state + (long long)a * f + pl * 8);
+    const float4 hi = *reinterpret_cast<const float4 *>(state + (long long)a * f + pl * 8 + 4);
+    uint4 pk;
+    pk.x = pack_bf16x2(lo.x, lo.y);
+    pk.y = pack_bf16x2(lo.z, lo.w);
+    pk.z = pack_bf16x2(hi.x, hi.y);
+    pk.w = pack_bf16x2(hi.z, hi.w);
+    *reinterpret_cast<uint4 *>(snap + t * 8) = pk;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Output GEMM: y[gL+t][a] = sum_k [snap | V^T][a][k] * [Z | P][t][k].
 // i = a (model dim), j = t (token within group).
 // grid: B * ngroups * (d/256) * ceil(L/256) workgroups
@@ -697,10 +767,10 @@ __global__ __launch_bounds__(NT_W, 1) void k_out(OutArgs p) {
   const long long gs = (long long)g * p.L;
   const int Lg = (int)((p.T - gs) < p.L ? (p.T - gs) : p.L);
   if (j0 >= Lg) return;
-  const Opnd sa1 = rowmajor(p.snap + ((long long)b * p.ngroups + g) * p.d * p.f, p.f, p.d, p.f);
+  const bf16_t *snap_g = p.snap + ((long long)b * p.ngroups + g) * p.d * p.f;  // [f/8][d][8]
   const Opnd sb1 = rowmajor(p.Z + ((long long)b * p.T_pad + gs) * p.f, p.f, (int)(p.T_pad - gs), p.f);
   int nk2 = 0;
-  Opnd sa2 = sa1, sb2 = sb1;
+  Opnd sa2 = sb1, sb2 = sb1;
   if (p.intra) {
     const int jl = (j0 + 255 < Lg - 1) ? j0 + 255 : Lg - 1;
     const int kend = (jl / p.C) * p.C;  // start of the last row's chunk
@@ -711,7 +781,11 @@ __global__ __launch_bounds__(NT_W, 1) void k_out(OutArgs p) {
   }
   Acc<NBJ_W> acc;
   acc_zero(acc);
-  gemm_loop<true>(acc, ring, sa1, sb1, p.f / BK, sa2, sb2, nk2, i0, j0);
+  gemm_plane_a(acc, ring, snap_g, (long long)p.d * 8, p.d, p.f, sb1, p.f / BK, i0, j0);
+  if (nk2 > 0) {
+    __syncthreads();  // every wave is done reading the ring before it is refilled
+    gemm_loop<true>(acc, ring, sa2, sb2, 0, sa2, sb2, nk2, i0, j0);
+  }
 
   // Epilogue through LDS ([token][model dim]) so y rows leave in whole lines.
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), wm = w & 1, wn = w >> 1;
@@ -908,6 +982,15 @@ hipError_t launch_scores_bf16(const bf16_t *Z, bf16_t *P, float eta, const Layou
   const long long n = (long long)lay.B * lay.ngroups * (nt * (nt + 1) / 2);
   if (n >= (1LL << 31)) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(k_scores, dim3((unsigned)n), dim3(NT_W), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_state_to_snap_bf16(const float *state, bf16_t *snap, int d, int f, hipStream_t s) {
+  if (d <= 0 || f <= 0 || f % 8) return hipErrorInvalidValue;
+  const long long n = (long long)d * (f / 8);
+  const long long blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(k_state_to_snap, dim3((unsigned)(blocks < 65536 ? blocks : 65536)), dim3(256), 0, s, state, snap, d,
+                     f);
   return hipGetLastError();
 }
 

@@ -13,10 +13,13 @@ hipError_t launch_gather_vt_bf16(const int32_t *ids, const bf16_t *E, int vocab,
 hipError_t launch_a1_bf16(const bf16_t *x, const bf16_t *Wug, bf16_t *Z, bf16_t *ZT, float eta, int write_zt,
                           const Layout &lay, hipStream_t s);
 // state[b] += sum_p ZT[b][:, p] VT[b][:, p]^T (as W[a][b] layout), snapshots snap[b][g] = bf16(state at p = g*L).
+// Snapshots are held as planes of 8 columns: [B][ngroups][f/8][d][8].
 hipError_t launch_update_bf16(const bf16_t *ZT, const bf16_t *VT, float *state, bf16_t *snap, const Layout &lay,
                               hipStream_t s);
 // P[b][g][t][s] = eta * <Z[gL+t], Z[gL+s]> if s/C < t/C else 0, for t, s < L.
 hipError_t launch_scores_bf16(const bf16_t *Z, bf16_t *P, float eta, const Layout &lay, hipStream_t s);
+// One snapshot [f/8][d][8] = bf16 of one fp32 state [d][f] (no update).
+hipError_t launch_state_to_snap_bf16(const float *state, bf16_t *snap, int d, int f, hipStream_t s);
 // y[b][gL+t] = Z[gL+t] snap[b][g]^T + sum_s P[b][g][t][s] V[gL+s].
 hipError_t launch_out_bf16(const bf16_t *Z, const bf16_t *P, const bf16_t *snap, const bf16_t *VT, bf16_t *y,
                            const Layout &lay, hipStream_t s);

@@ -292,7 +292,7 @@ int forward_impl(ttt_handle *h, const void *x, const int32_t *ids, const void *E
       HIP_TRY(launch_update_bf16((const bf16_t *)ZT, (const bf16_t *)VT, state, (bf16_t *)snap, lay, s));
     } else {
       for (int b = 0; b < B; ++b)
-        HIP_TRY(launch_f32_to_bf16(state + (size_t)b * df, (bf16_t *)snap + (size_t)b * df, (long long)df, s));
+        HIP_TRY(launch_state_to_snap_bf16(state + (size_t)b * df, (bf16_t *)snap + (size_t)b * df, h->d, h->f, s));
     }
     if (prof) HIP_TRY(hipEventRecord(h->ev[4], s));
     if (lay.intra) HIP_TRY(launch_scores_bf16((const bf16_t *)Z, (bf16_t *)P, h->eta, lay, s));
