@@ -19,10 +19,15 @@
 // columns outside an operand's valid range are fetched through an
 // out-of-range buffer offset, which the hardware returns as zero.
 //
-// Operands are either row-major (element (r, k) at r*ld + k) or K-blocked by
-// 64 (element (r, k) at (k/64)*kblk + r*64 + k%64): the token-indexed operands
-// of the update (eta Z^T and V^T) are stored K-blocked so that one slab is one
-// contiguous block instead of rows strided by the whole stream length.
+// Operands are row-major (element (r, k) at r*ld + k), K-blocked by 64
+// (element (r, k) at (k/64)*kblk + r*64 + k%64), or held in planes of 8
+// columns (element (r, k) at (k/8)*pstride + r*8 + k%8). V^T is K-blocked, so
+// one slab is one contiguous block instead of rows strided by the whole stream
+// length. eta*Z^T and the snapshots are planes: the MFMA register layout holds
+// four consecutive k of one row per lane, so a store instruction of 32 rows x
+// 16 bytes is 512 contiguous bytes in a plane (in row-major or K-blocked form
+// it would touch 32 lines); a plane slab loads as 1 KB contiguous pieces into
+// an LDS tile of [8][256][8], whose fragment reads need no swizzle.
 //
 // MFMA 32x32x16 register layout (lane l, accumulator register r):
 //   A operand: row i = l % 32, k = 8*(l/32) .. +7;  B operand: column j = l % 32, same k.
@@ -416,7 +421,7 @@ __device__ __forceinline__ void gemm_plane_a(Acc<NBJ_W> &acc, Slab<WN_W, NBJ_W> 
 
 // ---------------------------------------------------------------------------
 // Up/gate GEMM with SwiGLU epilogue. i = token slot, j = interleaved W_ug row.
-// Writes Z [B][T_pad][f] (row-major) and eta*Z^T K-blocked [B][T_pad/64][f][64].
+// Writes Z [B][T_pad][f] (row-major) and eta*Z^T in planes of 8 tokens [B][T_pad/8][f][8].
 // grid: nx * ny workgroups, nx = 2f/256, ny = B*T_pad/256
 struct A1Args {
   const bf16_t *x;
@@ -462,7 +467,7 @@ __global__ __launch_bounds__(NT_W, 1) void k_a1(A1Args p) {
           uint2 pk;
           pk.x = pack_bf16x2(p.eta * z[0], p.eta * z[1]);
           pk.y = pack_bf16x2(p.eta * z[2], p.eta * z[3]);
-          *reinterpret_cast<uint2 *>(ZTb + ((long long)(pos >> 6) * p.f + feat) * 64 + (pos & 63)) = pk;
+          *reinterpret_cast<uint2 *>(ZTb + ((long long)(pos >> 3) * p.f + feat) * 8 + (pos & 7)) = pk;
         }
         bf16_t *zrow = p.Z + ((long long)b * p.T_pad + pos) * p.f + feat;
 #pragma unroll
@@ -611,7 +616,7 @@ __global__ __launch_bounds__(128 * WN, 1) void k_update(UpdArgs p) {
       }
   }
 
-  const Opnd sa = kblocked(p.ZT + (long long)b * p.f * p.T_pad, (long long)p.f * 64, p.f, p.T_pad, 0);
+  const bf16_t *za = p.ZT + (long long)b * p.f * p.T_pad;  // eta Z^T in planes of 8 tokens: [T_pad/8][f][8]
   const Opnd sb = kblocked(p.VT + (long long)b * p.d * p.T_pad, (long long)p.d * 64, p.d, p.T_pad, 0);
   const int nk = p.kend / BK;
   // Snapshot 0 is the entry state; group starts are multiples of the stage
@@ -619,8 +624,12 @@ __global__ __launch_bounds__(128 * WN, 1) void k_update(UpdArgs p) {
   // while the following slabs are already in flight.
   dump_snapshot(acc, snap0, p.d);
   int g = 1;
+  constexpr int LA = loads_a<WN, NBJ>();
   auto part = [&](int sl, int j) {
-    issue_part<true, true>(ring[sl % NSL], sa, sb, i0, j0, sl * SK, w, lane, j);
+    if (j < LA)
+      issue_plane<2 * WN>(ring[sl % NSL].a, za, (long long)p.f * 8, p.f, p.T_pad, i0, sl * SK, w, lane, j);
+    else
+      issue_one<true, BN, 2 * WN>(ring[sl % NSL].b, sb, j0, sl * SK, w, lane, j - LA);
   };
   const int nsl = (nk + 1) >> 1;
   for (int sl = 0; sl < NSL && sl < nsl; ++sl)
@@ -629,7 +638,7 @@ __global__ __launch_bounds__(128 * WN, 1) void k_update(UpdArgs p) {
   Frag<NBJ> cur, nxt;
   if (nk > 0) {
     slab_wait<loads_per_slab<WN, NBJ>()>((nsl - 1) < (NSL - 1) ? (nsl - 1) : (NSL - 1));
-    frag_read(cur, ring[0], 0, 0, wm, wn, lane);
+    frag_read<WN, NBJ, true>(cur, ring[0], 0, 0, wm, wn, lane);
   }
   // The snapshot stores share the vector-memory counter with the tile loads.
   // The counted waits stay exact for the loads: loads complete in issue
@@ -645,12 +654,12 @@ __global__ __launch_bounds__(128 * WN, 1) void k_update(UpdArgs p) {
   for (; g < p.ngroups; ) {
     const int kt_last = g * (p.L / BK) - 1;  // last stage before group g starts
     for (; kt < kt_last; ++kt)
-      pipelined_stage<WN, NBJ, NSL, false>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, part, NoHook{});
-    pipelined_stage<WN, NBJ, NSL, true>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, part, snapshot);
+      pipelined_stage<WN, NBJ, NSL, false, true>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, part, NoHook{});
+    pipelined_stage<WN, NBJ, NSL, true, true>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, part, snapshot);
     ++kt;
   }
   for (; kt < nk; ++kt)
-    pipelined_stage<WN, NBJ, NSL, false>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, part, NoHook{});
+    pipelined_stage<WN, NBJ, NSL, false, true>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, part, NoHook{});
 #pragma unroll
   for (int bj = 0; bj < NBJ; ++bj) {
     float *row = st + (long long)bj * 32 * p.f;

@@ -8,7 +8,7 @@
 // Vrow (nullable): the same rows row-major, [B][T_pad][d].
 hipError_t launch_gather_vt_bf16(const int32_t *ids, const bf16_t *E, int vocab, bf16_t *VT, bf16_t *Vrow,
                                  const Layout &lay, hipStream_t s);
-// Z = SiLU(x W_gate^T) * (x W_up^T) -> Z [B][T_pad][f] and ZT = eta*Z^T [B][f][T_pad].
+// Z = SiLU(x W_gate^T) * (x W_up^T) -> Z [B][T_pad][f] and ZT = eta*Z^T in planes of 8 tokens [B][T_pad/8][f][8].
 // Wug: [2f][d], rows interleaved in blocks of 32 (32 up rows, then the matching 32 gate rows).
 hipError_t launch_a1_bf16(const bf16_t *x, const bf16_t *Wug, bf16_t *Z, bf16_t *ZT, float eta, int write_zt,
                           const Layout &lay, hipStream_t s);
