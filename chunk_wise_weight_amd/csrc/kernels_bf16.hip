@@ -143,15 +143,6 @@ __device__ __forceinline__ void issue_part(Slab<WN, NBJ> &st, const Opnd &a, con
     issue_one<BBLK, 32 * WN * NBJ, 2 * WN>(st.b, b, brow0, k, w, lane, j - LA);
 }
 
-// All loads of this wave for one slab.
-template <bool ABLK, bool BBLK, int WN, int NBJ>
-__device__ __forceinline__ void issue_slab(Slab<WN, NBJ> &st, const Opnd &a, const Opnd &b, int arow0, int brow0,
-                                           int k, int w, int lane) {
-#pragma unroll
-  for (int j = 0; j < loads_per_slab<WN, NBJ>(); ++j)
-    issue_part<ABLK, BBLK>(st, a, b, arow0, brow0, k, w, lane, j);
-}
-
 // s_waitcnt immediate (gfx9): vmcnt(n), expcnt unchanged, lgkmcnt(0).
 constexpr unsigned wait_imm(int n) { return (unsigned)((n & 15) | 0x70 | (((n >> 4) & 3) << 14)); }
 

@@ -18,11 +18,6 @@ __global__ __launch_bounds__(256) void k_bf16_to_f32(const bf16_t *src, float *d
     dst[i] = bf16_to_f32(src[i]);
 }
 
-__global__ __launch_bounds__(256) void k_f32_to_bf16(const float *src, bf16_t *dst, long long n) {
-  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256)
-    dst[i] = f32_to_bf16(src[i]);
-}
-
 unsigned grid_for(long long n) {
   long long g = (n + 255) / 256;
   return (unsigned)(g < 65536 ? (g > 0 ? g : 1) : 65536);
@@ -40,7 +35,3 @@ hipError_t launch_bf16_to_f32(const bf16_t *src, float *dst, long long n, hipStr
   return hipGetLastError();
 }
 
-hipError_t launch_f32_to_bf16(const float *src, bf16_t *dst, long long n, hipStream_t s) {
-  hipLaunchKernelGGL(k_f32_to_bf16, dim3(grid_for(n)), dim3(256), 0, s, src, dst, n);
-  return hipGetLastError();
-}

@@ -71,4 +71,3 @@ hipError_t launch_copy_f32(const float *src, float *dst, long long n, hipStream_
 // Wug[2f][d] from W_up[f][d], W_gate[f][d]: 32-row blocks, up block then gate block.
 hipError_t launch_interleave_ug_bf16(const bf16_t *Wu, const bf16_t *Wg, bf16_t *Wug, int f, int d, hipStream_t s);
 hipError_t launch_bf16_to_f32(const bf16_t *src, float *dst, long long n, hipStream_t s);
-hipError_t launch_f32_to_bf16(const float *src, bf16_t *dst, long long n, hipStream_t s);
