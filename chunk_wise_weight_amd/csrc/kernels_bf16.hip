@@ -58,23 +58,6 @@ struct Slab {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// One K-segment of an operand, rows [0, nrows) valid, columns [0, kvalid) valid.
-struct Opnd {
-  const bf16_t *base;
-  long long ld;    // row-major: row pitch in elements
-  long long kblk;  // K-blocked: elements per 64-column block (0 = row-major)
-  int nrows;
-  int kvalid;
-  int koff;        // K-blocked: absolute column of segment column 0
-};
-
-__device__ __forceinline__ Opnd rowmajor(const bf16_t *base, long long ld, int nrows, int kvalid) {
-  return Opnd{base, ld, 0, nrows, kvalid, 0};
-}
-__device__ __forceinline__ Opnd kblocked(const bf16_t *base, long long kblk, int nrows, int kvalid, int koff) {
-  return Opnd{base, 64, kblk, nrows, kvalid, koff};
-}
-
 // The eight 16-byte chunks of each 128-byte LDS row are XOR-swizzled; with
 // this pattern the fragment reads (32 consecutive rows, one chunk) are free of
 // bank conflicts, also while LDS-DMA writes land (measured with rocprofv3).
@@ -92,56 +75,136 @@ __device__ __forceinline__ void acc_zero(Acc<NBJ> &acc) {
       for (int r = 0; r < 16; ++r) acc.v[bi][bj][r] = 0.f;
 }
 
-// Queue the copy of rows [row0, row0+ROWS) x cols [k, k+64) of one operand
-// into an LDS tile. Wave w of NW moves rows w*ROWS/NW .. +ROWS/NW, eight rows
-// per buffer-load instruction (instruction n of the wave); lanes 8r .. 8r+7 of
-// an instruction fetch the whole 128-byte line of row r (whole lines fill LDS
-// at twice the rate of half lines), lane l fills physical chunk l%8, i.e. the
-// logical chunk (l%8) ^ swz(row). The instruction's row offset goes in soffset.
-template <bool BLOCKED, int ROWS, int NW>
-__device__ __forceinline__ void issue_one(bf16_t *lds_tile, const Opnd &s, int row0, int k, int w, int lane, int n) {
-  constexpr int WROWS = ROWS / NW;
-  const int lr = lane >> 3;
-  const int nvw = s.nrows - row0 - w * WROWS;  // valid rows among this wave's rows
-  const int slab = w * WROWS + n * 8;
-  const int c = (lane & 7) ^ swz(slab + lr);
-  if (!BLOCKED) {
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<bf16_t *>(s.base + (long long)row0 * s.ld + k), (short)0, 0x7fffffff, kBufferFlags);
-    const int ldb = (int)s.ld * 2;
-    const bool ok = (n * 8 + lr) < nvw && c * 8 < s.kvalid - k;
-    const uint32_t voff = ok ? (uint32_t)(lr * ldb + c * 16) : kOutOfRange;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(lds_tile + slab * SK), 16, voff, slab * ldb, 0, 0);
-  } else {
-    const int ka0 = s.koff + k;  // absolute column of this slab's first column
-    const int kb0 = ka0 >> 6;
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<bf16_t *>(s.base + (long long)kb0 * s.kblk + (long long)row0 * 64), (short)0, 0x7fffffff,
-        kBufferFlags);
-    const int ka = ka0 + c * 8;
-    const bool ok = (n * 8 + lr) < nvw && (k + c * 8) < s.kvalid;
-    const uint32_t voff =
-        ok ? (uint32_t)(((ka >> 6) - kb0) * (int)s.kblk * 2 + lr * 128 + (ka & 63) * 2) : kOutOfRange;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(lds_tile + slab * SK), 16, voff, slab * 128, 0, 0);
-  }
-}
-
 // buffer loads per wave per slab: A tile, then B tile
 template <int WN, int NBJ>
 constexpr int loads_a() { return BM / (2 * WN) / 8; }
 template <int WN, int NBJ>
 constexpr int loads_per_slab() { return loads_a<WN, NBJ>() + 32 * WN * NBJ / (2 * WN) / 8; }
 
-// Load j (0 <= j < loads_per_slab) of this wave for one slab.
-template <bool ABLK, bool BBLK, int WN, int NBJ>
-__device__ __forceinline__ void issue_part(Slab<WN, NBJ> &st, const Opnd &a, const Opnd &b, int arow0, int brow0,
-                                           int k, int w, int lane, int j) {
-  constexpr int LA = loads_a<WN, NBJ>();
-  if (j < LA)
-    issue_one<ABLK, BM, 2 * WN>(st.a, a, arow0, k, w, lane, j);
-  else
-    issue_one<BBLK, 32 * WN * NBJ, 2 * WN>(st.b, b, brow0, k, w, lane, j - LA);
-}
+// ---- Tile loads ----
+// A load instruction moves 1 KB from memory straight into LDS: 16 bytes per
+// lane, lane l landing at the instruction's LDS base + 16 l. Descriptors and
+// per-lane offsets are prepared once (per tile, or per slab where the slab
+// moves the base), so each load costs one instruction and a scalar offset.
+//
+// Row-major and K-blocked tiles load 8 rows per instruction: lanes 8r .. 8r+7
+// fetch the whole 128-byte line of row r (whole lines fill LDS at twice the
+// rate of half lines), and lane l fills physical chunk l%8, i.e. the logical
+// chunk (l%8) ^ swz(row). Load n of wave w (of NW) moves rows
+// w*ROWS/NW + 8n .. +8.
+
+// Row-major operand: element (r, k) at base[r*ld + k], base at the tile's
+// first row. Rows r >= nrows read zero: the lane offset holds the whole row
+// offset and passes num_records. COLS: columns >= kvalid read zero too.
+template <int ROWS, int NW, bool COLS = false>
+struct RmLoad {
+  static constexpr int WR = ROWS / NW, N = WR / 8;
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t vo[N];
+  int kvalid;
+  __device__ __forceinline__ void init(const bf16_t *base, long long ld, int nrows, int kvalid_, int w, int lane) {
+    const long long bytes = (long long)(nrows > 0 ? nrows : 0) * ld * 2;
+    rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t *>(base), (short)0,
+                                           (int)(bytes < 0x7fffffffLL ? bytes : 0x7fffffffLL), kBufferFlags);
+    kvalid = kvalid_;
+    const int lr = lane >> 3;
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      const int row = w * WR + 8 * n + lr;
+      vo[n] = (uint32_t)((long long)row * ld * 2 + (((lane & 7) ^ swz(row)) << 4));
+    }
+  }
+  struct Pre {};
+  __device__ __forceinline__ Pre prep(int) const { return Pre{}; }
+  __device__ __forceinline__ void issue(const Pre &, bf16_t *tile, int sl, int w, int lane, int n) const {
+    uint32_t v = vo[n];
+    if (COLS) {
+      const int c = (lane & 7) ^ swz(w * WR + 8 * n + (lane >> 3));
+      if (sl * SK + c * 8 >= kvalid) v = kOutOfRange;
+    }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(tile + (w * WR + 8 * n) * SK), 16, v, sl * SK * 2, 0,
+                                             0);
+  }
+};
+
+// K-blocked operand: element (r, k) at base[(k/64)*kblk + r*64 + k%64], base
+// at the tile's first row in block 0; every row of the tile is valid. The
+// descriptor follows the slab's block. The swizzle depends on n only through
+// its parity (WR is a multiple of 16), so two lane offsets serve every load.
+template <int ROWS, int NW>
+struct KbLoad {
+  static constexpr int WR = ROWS / NW, N = WR / 8;
+  static_assert(WR % 16 == 0, "two lane offsets need WR a multiple of 16");
+  const bf16_t *base;
+  long long kblk;
+  uint32_t ve, vd;  // lane offsets for even / odd n
+  __device__ __forceinline__ void init(const bf16_t *base_, long long kblk_, int w, int lane) {
+    base = base_;
+    kblk = kblk_;
+    const int lr = lane >> 3;
+    ve = (uint32_t)(lr * 128 + (((lane & 7) ^ swz(w * WR + lr)) << 4));
+    vd = (uint32_t)(lr * 128 + (((lane & 7) ^ swz(w * WR + 8 + lr)) << 4));
+  }
+  using Pre = __amdgpu_buffer_rsrc_t;
+  __device__ __forceinline__ Pre prep(int sl) const {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t *>(base + (long long)sl * kblk), (short)0, 0x7fffffff,
+                                             kBufferFlags);
+  }
+  __device__ __forceinline__ void issue(const Pre &rs, bf16_t *tile, int, int w, int, int n) const {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(tile + (w * WR + 8 * n) * SK), 16, (n & 1) ? vd : ve,
+                                             (w * WR + 8 * n) * 128, 0, 0);
+  }
+};
+
+// Plane operand (planes of 8 columns): element (r, k) at base[(k/8)*pstride +
+// r*8 + k%8], base at the tile's first row in plane 0; 256-row tiles, every
+// row valid. Load n of wave w moves 1 KB piece q = w*(32/NW) + n of the slab:
+// rows (q%4)*64 .. +64 of plane q/4, contiguous in memory and in the LDS tile
+// [8 planes][256 rows][8].
+template <int NW>
+struct PlLoad {
+  static constexpr int N = 32 / NW;
+  const bf16_t *base;
+  long long pstride;
+  uint32_t vl;  // lane * 16
+  __device__ __forceinline__ void init(const bf16_t *base_, long long pstride_, int lane) {
+    base = base_;
+    pstride = pstride_;
+    vl = (uint32_t)(lane * 16);
+  }
+  using Pre = __amdgpu_buffer_rsrc_t;
+  __device__ __forceinline__ Pre prep(int sl) const {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t *>(base + (long long)sl * 8 * pstride), (short)0,
+                                             0x7fffffff, kBufferFlags);
+  }
+  // N is a multiple of 4, so the row block is q%4 = n%4
+  __device__ __forceinline__ void issue(const Pre &rs, bf16_t *tile, int, int w, int, int n) const {
+    static_assert(N % 4 == 0, "row block from n alone");
+    const int pl = w * (N / 4) + (n >> 2);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(tile + (pl * BM + (n & 3) * 64) * 8), 16, vl,
+                                             (int)(pl * pstride * 2) + (n & 3) * 1024, 0, 0);
+  }
+};
+
+// The loads of one slab: the A tile's, then the B tile's.
+template <class LA, class LB>
+struct SlabLoads {
+  LA a;
+  LB b;
+  static constexpr int N = LA::N + LB::N;
+  struct Pre {
+    typename LA::Pre a;
+    typename LB::Pre b;
+  };
+  __device__ __forceinline__ Pre prep(int sl) const { return Pre{a.prep(sl), b.prep(sl)}; }
+  template <class S>
+  __device__ __forceinline__ void issue(const Pre &p, S &slab, int sl, int w, int lane, int j) const {
+    if (j < LA::N)
+      a.issue(p.a, slab.a, sl, w, lane, j);
+    else
+      b.issue(p.b, slab.b, sl, w, lane, j - LA::N);
+  }
+};
 
 // s_waitcnt immediate (gfx9): vmcnt(n), expcnt unchanged, lgkmcnt(0).
 constexpr unsigned wait_imm(int n) { return (unsigned)((n & 15) | 0x70 | (((n >> 4) & 3) << 14)); }
@@ -200,10 +263,11 @@ __device__ __forceinline__ void frag_mma(Acc<NBJ> &acc, const Frag<NBJ> &fr) {
 __device__ __forceinline__ void pin() { __builtin_amdgcn_sched_barrier(0); }
 
 // Issue point P (0..6) of a stage that refills a slab: loads [P*LPS/7, (P+1)*LPS/7).
-template <int LPS, int P, class IssueFn>
-__device__ __forceinline__ void issue_point(IssueFn &&issue_part, int slab) {
+template <int LPS, int P, class SL, class S>
+__device__ __forceinline__ void issue_point(const SL &ld, const typename SL::Pre &pre, S &slab, int sl, int w,
+                                            int lane) {
 #pragma unroll
-  for (int j = P * LPS / 7; j < (P + 1) * LPS / 7; ++j) issue_part(slab, j);
+  for (int j = P * LPS / 7; j < (P + 1) * LPS / 7; ++j) ld.issue(pre, slab, sl, w, lane, j);
 }
 
 // The software pipeline of one 32-deep stage kt = half kt%2 of slab kt/2. On
@@ -220,11 +284,12 @@ __device__ __forceinline__ void issue_point(IssueFn &&issue_part, int slab) {
 // refilled. Spreading the loads keeps a burst of them from stalling the MFMA
 // issue. With AFTER, after_fn(acc) runs once all of stage kt's MFMAs are
 // queued, and the next fragments are read only then (few registers live).
-template <int WN, int NBJ, int NSL, bool AFTER, bool APLANE = false, class IssueFn, class AfterFn>
+template <int WN, int NBJ, int NSL, bool AFTER, bool APLANE = false, class SL, class AfterFn>
 __device__ __forceinline__ void pipelined_stage(Acc<NBJ> &acc, Slab<WN, NBJ> *ring, Frag<NBJ> &cur, Frag<NBJ> &nxt,
-                                                int kt, int nk, int wm, int wn, int lane, IssueFn &&issue_part,
+                                                int kt, int nk, int wm, int wn, int lane, int w, const SL &ld,
                                                 AfterFn &&after_fn) {
   constexpr int LPS = loads_per_slab<WN, NBJ>();
+  static_assert(SL::N == LPS, "the slab loads match the tile configuration");
   const int sl = kt >> 1, h = kt & 1;
   const int nsl = (nk + 1) >> 1;
   frag_read<WN, NBJ, APLANE>(nxt, ring[sl % NSL], h, 1, wm, wn, lane);
@@ -238,31 +303,34 @@ __device__ __forceinline__ void pipelined_stage(Acc<NBJ> &acc, Slab<WN, NBJ> *ri
     slab_wait<LPS>(later);
   }
   const int rs = sl + NSL;
+  Slab<WN, NBJ> &dst = ring[sl % NSL];  // the buffer just finished refills with slab rs
+  typename SL::Pre pre{};
+  if (refill) pre = ld.prep(rs);
   pin();
   frag_mma<1, 2>(acc, cur);
-  if (refill) issue_point<LPS, 0>(issue_part, rs);
+  if (refill) issue_point<LPS, 0>(ld, pre, dst, rs, w, lane);
   pin();
   frag_mma<2, 3>(acc, cur);
-  if (refill) issue_point<LPS, 1>(issue_part, rs);
+  if (refill) issue_point<LPS, 1>(ld, pre, dst, rs, w, lane);
   pin();
   frag_mma<3, 4>(acc, cur);
-  if (refill) issue_point<LPS, 2>(issue_part, rs);
+  if (refill) issue_point<LPS, 2>(ld, pre, dst, rs, w, lane);
   pin();
   frag_mma<0, 1>(acc, nxt);
   pin();
   // unconditional (past the end it reads a stale buffer of the ring): no
   // branch, so the compiler can count the reads and wait for each exactly
   if (!AFTER) frag_read<WN, NBJ, APLANE>(cur, ring[((kt + 1) >> 1) % NSL], (kt + 1) & 1, 0, wm, wn, lane);
-  if (refill) issue_point<LPS, 3>(issue_part, rs);
+  if (refill) issue_point<LPS, 3>(ld, pre, dst, rs, w, lane);
   pin();
   frag_mma<1, 2>(acc, nxt);
-  if (refill) issue_point<LPS, 4>(issue_part, rs);
+  if (refill) issue_point<LPS, 4>(ld, pre, dst, rs, w, lane);
   pin();
   frag_mma<2, 3>(acc, nxt);
-  if (refill) issue_point<LPS, 5>(issue_part, rs);
+  if (refill) issue_point<LPS, 5>(ld, pre, dst, rs, w, lane);
   pin();
   frag_mma<3, 4>(acc, nxt);
-  if (refill) issue_point<LPS, 6>(issue_part, rs);
+  if (refill) issue_point<LPS, 6>(ld, pre, dst, rs, w, lane);
   pin();
   if (AFTER) {
     after_fn(acc);
@@ -318,97 +386,28 @@ __device__ __forceinline__ void band_tile(int t, int nx, int ny, int H, int &x, 
   y = band * H + r % h;
 }
 
-// K loop over segment 1 (nk1 stages, both operands row-major) then segment 2
-// (nk2 stages; its A operand K-blocked when A2BLK). nk1 is even, so no slab
-// straddles the two segments. 256 x 256 tiles.
-template <bool A2BLK>
-__device__ __forceinline__ void gemm_loop(Acc<NBJ_W> &acc, Slab<WN_W, NBJ_W> *ring, const Opnd &a1, const Opnd &b1,
-                                          int nk1, const Opnd &a2, const Opnd &b2, int nk2, int arow0, int brow0) {
-  const int lane = threadIdx.x & 63;
-  const int w = wave_id(), wm = w & 1, wn = w >> 1;
-  const int nk = nk1 + nk2;
-  if (nk <= 0) return;
-  const int ns1 = nk1 >> 1, nsl = (nk + 1) >> 1;
-  auto part = [&](int sl, int j) {
-    if (sl < ns1)
-      issue_part<false, false>(ring[sl % NSL_W], a1, b1, arow0, brow0, sl * SK, w, lane, j);
-    else
-      issue_part<A2BLK, false>(ring[sl % NSL_W], a2, b2, arow0, brow0, (sl - ns1) * SK, w, lane, j);
-  };
-  for (int sl = 0; sl < NSL_W && sl < nsl; ++sl)
-#pragma unroll
-    for (int j = 0; j < loads_per_slab<WN_W, NBJ_W>(); ++j) part(sl, j);
-  Frag<NBJ_W> cur, nxt;
-  slab_wait<loads_per_slab<WN_W, NBJ_W>()>((nsl - 1) < (NSL_W - 1) ? (nsl - 1) : (NSL_W - 1));
-  frag_read(cur, ring[0], 0, 0, wm, wn, lane);
-  for (int kt = 0; kt < nk; ++kt)
-    pipelined_stage<WN_W, NBJ_W, NSL_W, false>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, part, NoHook{});
-}
-
-// K loop over one row-major segment of nk stages for any configuration.
-template <int WN, int NBJ, int NSL>
-__device__ __forceinline__ void gemm_rows(Acc<NBJ> &acc, Slab<WN, NBJ> *ring, const Opnd &a, const Opnd &b, int nk,
-                                          int arow0, int brow0) {
+// K loop of nk stages over the slab loads `ld` (tiles of 256 x 32*WN*NBJ,
+// NSL slabs in the ring). APLANE: the A tile is a plane operand.
+template <int WN, int NBJ, int NSL, bool APLANE, class SL>
+__device__ __forceinline__ void gemm_k(Acc<NBJ> &acc, Slab<WN, NBJ> *ring, const SL &ld, int nk) {
   const int lane = threadIdx.x & 63;
   const int w = wave_id(), wm = w & 1, wn = w >> 1;
   if (nk <= 0) return;
   const int nsl = (nk + 1) >> 1;
-  auto part = [&](int sl, int j) {
-    issue_part<false, false>(ring[sl % NSL], a, b, arow0, brow0, sl * SK, w, lane, j);
-  };
-  for (int sl = 0; sl < NSL && sl < nsl; ++sl)
+  for (int sl = 0; sl < NSL && sl < nsl; ++sl) {
+    const typename SL::Pre pre = ld.prep(sl);
 #pragma unroll
-    for (int j = 0; j < loads_per_slab<WN, NBJ>(); ++j) part(sl, j);
+    for (int j = 0; j < SL::N; ++j) ld.issue(pre, ring[sl], sl, w, lane, j);
+  }
   Frag<NBJ> cur, nxt;
   slab_wait<loads_per_slab<WN, NBJ>()>((nsl - 1) < (NSL - 1) ? (nsl - 1) : (NSL - 1));
-  frag_read(cur, ring[0], 0, 0, wm, wn, lane);
+  frag_read<WN, NBJ, APLANE>(cur, ring[0], 0, 0, wm, wn, lane);
   for (int kt = 0; kt < nk; ++kt)
-    pipelined_stage<WN, NBJ, NSL, false>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, part, NoHook{});
+    pipelined_stage<WN, NBJ, NSL, false, APLANE>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, w, ld, NoHook{});
 }
 
-// A "plane" operand holds column chunk c (8 columns) of every row contiguously:
-// element (r, k) at (k/8)*pstride + r*8 + k%8. Load n (0..LA-1) of wave w of a
-// 256-row x 64-column A tile moves 64 rows of one plane: 1 KB contiguous in
-// memory, landing as 1 KB contiguous in LDS ([8 planes][256 rows][8]).
-template <int NW>
-__device__ __forceinline__ void issue_plane(bf16_t *lds_tile, const bf16_t *base, long long pstride, int nrows,
-                                            int kvalid, int row0, int k, int w, int lane, int n) {
-  const int q = w * (32 / NW) + n;  // 1 KB piece 0..31 of the tile
-  const int pl = q >> 2, rb = (q & 3) * 64;
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<bf16_t *>(base + ((long long)(k >> 3) + pl) * pstride + (long long)row0 * 8), (short)0, 0x7fffffff,
-      kBufferFlags);
-  const bool ok = row0 + rb + lane < nrows && k + pl * 8 < kvalid;
-  const uint32_t voff = ok ? (uint32_t)((rb + lane) * 16) : kOutOfRange;
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(lds_tile + (pl * BM + rb) * 8), 16, voff, 0, 0, 0);
-}
-
-// K loop over nk stages, A a plane operand (rows row0.., pstride elements per
-// plane, nrows rows valid, kvalid columns) and B row-major. 256 x 256 tiles.
-__device__ __forceinline__ void gemm_plane_a(Acc<NBJ_W> &acc, Slab<WN_W, NBJ_W> *ring, const bf16_t *abase,
-                                             long long pstride, int anrows, int akvalid, const Opnd &b, int nk,
-                                             int arow0, int brow0) {
-  const int lane = threadIdx.x & 63;
-  const int w = wave_id(), wm = w & 1, wn = w >> 1;
-  if (nk <= 0) return;
-  constexpr int LA = loads_a<WN_W, NBJ_W>();
-  static_assert(LA * 2 * WN_W == 32, "one A tile is 32 pieces of 1 KB");
-  const int nsl = (nk + 1) >> 1;
-  auto part = [&](int sl, int j) {
-    if (j < LA)
-      issue_plane<2 * WN_W>(ring[sl % NSL_W].a, abase, pstride, anrows, akvalid, arow0, sl * SK, w, lane, j);
-    else
-      issue_one<false, 32 * WN_W * NBJ_W, 2 * WN_W>(ring[sl % NSL_W].b, b, brow0, sl * SK, w, lane, j - LA);
-  };
-  for (int sl = 0; sl < NSL_W && sl < nsl; ++sl)
-#pragma unroll
-    for (int j = 0; j < loads_per_slab<WN_W, NBJ_W>(); ++j) part(sl, j);
-  Frag<NBJ_W> cur, nxt;
-  slab_wait<loads_per_slab<WN_W, NBJ_W>()>((nsl - 1) < (NSL_W - 1) ? (nsl - 1) : (NSL_W - 1));
-  frag_read<WN_W, NBJ_W, true>(cur, ring[0], 0, 0, wm, wn, lane);
-  for (int kt = 0; kt < nk; ++kt)
-    pipelined_stage<WN_W, NBJ_W, NSL_W, false, true>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, part, NoHook{});
-}
+// The wide GEMMs' loaders: 8 waves, 256 x 256 tiles.
+using RmW = RmLoad<BM, 2 * WN_W>;
 
 // ---------------------------------------------------------------------------
 // Up/gate GEMM with SwiGLU epilogue. i = token slot, j = interleaved W_ug row.
@@ -433,11 +432,12 @@ __global__ __launch_bounds__(NT_W, 1) void k_a1(A1Args p) {
   const int m0 = ty * BM;
   const int b = m0 / p.T_pad;
   const int pos0 = m0 - b * p.T_pad;
-  const Opnd sa = rowmajor(p.x + ((long long)b * p.T + pos0) * p.d, p.d, p.T - pos0, p.d);
-  const Opnd sb = rowmajor(p.Wug + (long long)n0 * p.d, p.d, 2 * p.f - n0, p.d);
+  SlabLoads<RmW, RmW> ld;
+  ld.a.init(p.x + ((long long)b * p.T + pos0) * p.d, p.d, p.T - pos0, p.d, wave_id(), threadIdx.x & 63);
+  ld.b.init(p.Wug + (long long)n0 * p.d, p.d, 2 * p.f - n0, p.d, wave_id(), threadIdx.x & 63);
   Acc<NBJ_W> acc;
   acc_zero(acc);
-  gemm_loop<false>(acc, ring, sa, sb, p.d / BK, sa, sb, 0, 0, 0);
+  gemm_k<WN_W, NBJ_W, NSL_W, false>(acc, ring, ld, p.d / BK);
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w & 1, wn = w >> 1;
   bf16_t *ZTb = p.ZT + (long long)b * p.f * p.T_pad;
@@ -491,11 +491,12 @@ __global__ __launch_bounds__(NT_W, 1) void k_target_gemm(TgtArgs p) {
   const int m0 = ty * BM;
   const int b = m0 / p.T_pad;
   const int pos0 = m0 - b * p.T_pad;
-  const Opnd sa = rowmajor(p.U + (long long)m0 * p.d, p.d, BM, p.d);
-  const Opnd sb = rowmajor(p.WtT + (long long)n0 * p.d, p.d, 256, p.d);
+  SlabLoads<RmW, RmW> ld;
+  ld.a.init(p.U + (long long)m0 * p.d, p.d, BM, p.d, wave_id(), threadIdx.x & 63);
+  ld.b.init(p.WtT + (long long)n0 * p.d, p.d, 256, p.d, wave_id(), threadIdx.x & 63);
   Acc<NBJ_W> acc;
   acc_zero(acc);
-  gemm_loop<false>(acc, ring, sa, sb, p.d / BK, sa, sb, 0, 0, 0);
+  gemm_k<WN_W, NBJ_W, NSL_W, false>(acc, ring, ld, p.d / BK);
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w & 1, wn = w >> 1;
   bf16_t *VTb = p.VT + (long long)b * p.d * p.T_pad;
@@ -607,25 +608,22 @@ __global__ __launch_bounds__(128 * WN, 1) void k_update(UpdArgs p) {
       }
   }
 
-  const bf16_t *za = p.ZT + (long long)b * p.f * p.T_pad;  // eta Z^T in planes of 8 tokens: [T_pad/8][f][8]
-  const Opnd sb = kblocked(p.VT + (long long)b * p.d * p.T_pad, (long long)p.d * 64, p.d, p.T_pad, 0);
+  // A: eta Z^T in planes of 8 tokens [T_pad/8][f][8]; B: V^T K-blocked [T_pad/64][d][64]
+  SlabLoads<PlLoad<2 * WN>, KbLoad<BN, 2 * WN>> ld;
+  ld.a.init(p.ZT + (long long)b * p.f * p.T_pad + (long long)i0 * 8, (long long)p.f * 8, lane);
+  ld.b.init(p.VT + (long long)b * p.d * p.T_pad + (long long)j0 * 64, (long long)p.d * 64, w, lane);
   const int nk = p.kend / BK;
   // Snapshot 0 is the entry state; group starts are multiples of the stage
   // depth, so snapshot g is written right after the last stage of group g-1,
   // while the following slabs are already in flight.
   dump_snapshot(acc, snap0, p.d);
   int g = 1;
-  constexpr int LA = loads_a<WN, NBJ>();
-  auto part = [&](int sl, int j) {
-    if (j < LA)
-      issue_plane<2 * WN>(ring[sl % NSL].a, za, (long long)p.f * 8, p.f, p.T_pad, i0, sl * SK, w, lane, j);
-    else
-      issue_one<true, BN, 2 * WN>(ring[sl % NSL].b, sb, j0, sl * SK, w, lane, j - LA);
-  };
   const int nsl = (nk + 1) >> 1;
-  for (int sl = 0; sl < NSL && sl < nsl; ++sl)
+  for (int sl = 0; sl < NSL && sl < nsl; ++sl) {
+    const auto pre = ld.prep(sl);
 #pragma unroll
-    for (int j = 0; j < loads_per_slab<WN, NBJ>(); ++j) part(sl, j);
+    for (int j = 0; j < ld.N; ++j) ld.issue(pre, ring[sl], sl, w, lane, j);
+  }
   Frag<NBJ> cur, nxt;
   if (nk > 0) {
     slab_wait<loads_per_slab<WN, NBJ>()>((nsl - 1) < (NSL - 1) ? (nsl - 1) : (NSL - 1));
@@ -645,12 +643,12 @@ __global__ __launch_bounds__(128 * WN, 1) void k_update(UpdArgs p) {
   for (; g < p.ngroups; ) {
     const int kt_last = g * (p.L / BK) - 1;  // last stage before group g starts
     for (; kt < kt_last; ++kt)
-      pipelined_stage<WN, NBJ, NSL, false, true>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, part, NoHook{});
-    pipelined_stage<WN, NBJ, NSL, true, true>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, part, snapshot);
+      pipelined_stage<WN, NBJ, NSL, false, true>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, w, ld, NoHook{});
+    pipelined_stage<WN, NBJ, NSL, true, true>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, w, ld, snapshot);
     ++kt;
   }
   for (; kt < nk; ++kt)
-    pipelined_stage<WN, NBJ, NSL, false, true>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, part, NoHook{});
+    pipelined_stage<WN, NBJ, NSL, false, true>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, w, ld, NoHook{});
 #pragma unroll
   for (int bj = 0; bj < NBJ; ++bj) {
     float *row = st + (long long)bj * 32 * p.f;
@@ -693,10 +691,13 @@ __global__ __launch_bounds__(NT_W, 1) void k_scores(ScoreArgs p) {
   // masked; the output GEMM never reads it (it stops before that chunk).
   const int jl = (j0 + 255 < Lg - 1) ? j0 + 255 : Lg - 1;
   if (i0 / p.C >= jl / p.C) return;
-  const Opnd s = rowmajor(p.Z + ((long long)b * p.T_pad + gs) * p.f, p.f, (int)(p.T_pad - gs), p.f);
+  const bf16_t *Zg = p.Z + ((long long)b * p.T_pad + gs) * p.f;
+  SlabLoads<RmW, RmW> ld;
+  ld.a.init(Zg + (long long)i0 * p.f, p.f, (int)(p.T_pad - gs - i0), p.f, wave_id(), threadIdx.x & 63);
+  ld.b.init(Zg + (long long)j0 * p.f, p.f, (int)(p.T_pad - gs - j0), p.f, wave_id(), threadIdx.x & 63);
   Acc<NBJ_W> acc;
   acc_zero(acc);
-  gemm_loop<false>(acc, ring, s, s, p.f / BK, s, s, 0, i0, j0);
+  gemm_k<WN_W, NBJ_W, NSL_W, false>(acc, ring, ld, p.f / BK);
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w & 1, wn = w >> 1;
   bf16_t *Pg = p.P + ((long long)b * p.ngroups + g) * p.L * p.L;
@@ -767,24 +768,30 @@ __global__ __launch_bounds__(NT_W, 1) void k_out(OutArgs p) {
   const long long gs = (long long)g * p.L;
   const int Lg = (int)((p.T - gs) < p.L ? (p.T - gs) : p.L);
   if (j0 >= Lg) return;
-  const bf16_t *snap_g = p.snap + ((long long)b * p.ngroups + g) * p.d * p.f;  // [f/8][d][8]
-  const Opnd sb1 = rowmajor(p.Z + ((long long)b * p.T_pad + gs) * p.f, p.f, (int)(p.T_pad - gs), p.f);
-  int nk2 = 0;
-  Opnd sa2 = sb1, sb2 = sb1;
-  if (p.intra) {
+  const int w8 = wave_id(), l8 = threadIdx.x & 63;
+  Acc<NBJ_W> acc;
+  acc_zero(acc);
+  {  // segment 1: the group's snapshot ([f/8][d][8] planes) against Z, K = f
+    SlabLoads<PlLoad<2 * WN_W>, RmW> ld;
+    ld.a.init(p.snap + ((long long)b * p.ngroups + g) * p.d * p.f + (long long)i0 * 8, (long long)p.d * 8, l8);
+    ld.b.init(p.Z + ((long long)b * p.T_pad + gs + j0) * p.f, p.f, (int)(p.T_pad - gs - j0), p.f, w8, l8);
+    gemm_k<WN_W, NBJ_W, NSL_W, true>(acc, ring, ld, p.f / BK);
+  }
+  if (p.intra) {  // segment 2: V^T against P over the tokens before the last row's chunk
     const int jl = (j0 + 255 < Lg - 1) ? j0 + 255 : Lg - 1;
     const int kend = (jl / p.C) * p.C;  // start of the last row's chunk
     const int kv = (kend + 7) & ~7;
-    nk2 = (kv + BK - 1) / BK;
-    sa2 = kblocked(p.VT + (long long)b * p.d * p.T_pad, (long long)p.d * 64, p.d, kv, (int)gs);
-    sb2 = rowmajor(p.P + ((long long)b * p.ngroups + g) * p.L * p.L, p.L, p.L, kv);
-  }
-  Acc<NBJ_W> acc;
-  acc_zero(acc);
-  gemm_plane_a(acc, ring, snap_g, (long long)p.d * 8, p.d, p.f, sb1, p.f / BK, i0, j0);
-  if (nk2 > 0) {
-    __syncthreads();  // every wave is done reading the ring before it is refilled
-    gemm_loop<true>(acc, ring, sa2, sb2, 0, sa2, sb2, nk2, i0, j0);
+    const int nk2 = (kv + BK - 1) / BK;
+    if (nk2 > 0) {
+      // gs is a multiple of 64 (the plan's group length is), so V^T's slabs are whole blocks; columns of P
+      // at or past kv read zero, so the V^T columns they meet contribute nothing
+      SlabLoads<KbLoad<BM, 2 * WN_W>, RmLoad<BM, 2 * WN_W, true>> ld;
+      ld.a.init(p.VT + (long long)b * p.d * p.T_pad + (gs >> 6) * ((long long)p.d * 64) + (long long)i0 * 64,
+                (long long)p.d * 64, w8, l8);
+      ld.b.init(p.P + ((long long)b * p.ngroups + g) * p.L * p.L + (long long)j0 * p.L, p.L, p.L - j0, kv, w8, l8);
+      __syncthreads();  // every wave is done reading the ring before it is refilled
+      gemm_k<WN_W, NBJ_W, NSL_W, false>(acc, ring, ld, nk2);
+    }
   }
 
   // Epilogue through LDS ([token][model dim]) so y rows leave in whole lines.
@@ -859,10 +866,20 @@ __global__ __launch_bounds__(NT_U, 1) void k_chunk_gram(GramArgs p) {
   Acc<NBJ_U> az, av;
   acc_zero(az);
   acc_zero(av);
-  const Opnd oz = rowmajor(Zb, p.f, p.T_pad, p.f), ov = rowmajor(Vb, p.d, p.T_pad, p.d);
-  gemm_rows<WN_U, NBJ_U, NSL_U>(az, ring, oz, oz, p.f / BK, s0, t0);
+  const int wg = wave_id(), lg = threadIdx.x & 63;
+  {
+    SlabLoads<RmLoad<BM, 2 * WN_U>, RmLoad<32 * WN_U * NBJ_U, 2 * WN_U>> ld;
+    ld.a.init(Zb + (long long)s0 * p.f, p.f, p.T_pad - s0, p.f, wg, lg);
+    ld.b.init(Zb + (long long)t0 * p.f, p.f, p.T_pad - t0, p.f, wg, lg);
+    gemm_k<WN_U, NBJ_U, NSL_U, false>(az, ring, ld, p.f / BK);
+  }
   __syncthreads();  // the second pass refills the ring
-  gemm_rows<WN_U, NBJ_U, NSL_U>(av, ring, ov, ov, p.d / BK, s0, t0);
+  {
+    SlabLoads<RmLoad<BM, 2 * WN_U>, RmLoad<32 * WN_U * NBJ_U, 2 * WN_U>> ld;
+    ld.a.init(Vb + (long long)s0 * p.d, p.d, p.T_pad - s0, p.d, wg, lg);
+    ld.b.init(Vb + (long long)t0 * p.d, p.d, p.T_pad - t0, p.d, wg, lg);
+    gemm_k<WN_U, NBJ_U, NSL_U, false>(av, ring, ld, p.d / BK);
+  }
   __syncthreads();  // the product tile reuses the ring
   float *tile = reinterpret_cast<float *>(ring);
   const int lane = threadIdx.x & 63, wv = wave_id(), wm = wv & 1, wn = wv >> 1;

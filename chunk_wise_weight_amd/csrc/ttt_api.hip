@@ -47,7 +47,7 @@ constexpr int kMaxBatch = 4096;
 constexpr int kMaxT = 1 << 23;
 constexpr int kDefaultGroupTokens = 1024;
 // group starts fall on the update kernel's 32-token stage boundaries
-constexpr int kGroupAlign = 32;
+constexpr int kGroupAlign = 64;  // a group starts on a 64-token block of the K-blocked V^T
 // profiled phases: gather, up/gate, clip factors, update, scores, output, final copy
 constexpr int kPhases = 7;
 constexpr int kMaxTaps = 64;
@@ -96,7 +96,7 @@ int make_plan(int T, int C, int G_override, Plan &p) {
   long long G;
   if (G_override > 0) {
     if (((long long)G_override * Ce) % kGroupAlign != 0)
-      return fail(TTT_E_SHAPE, "G*C must be a multiple of 32 (G=" + std::to_string(G_override) +
+      return fail(TTT_E_SHAPE, "G*C must be a multiple of 64 (G=" + std::to_string(G_override) +
                                    ", C=" + std::to_string(Ce) + ")");
     G = G_override;
   } else {
@@ -413,7 +413,7 @@ int ttt_init(ttt_handle **out, const void *W_up, const void *W_gate, const void 
 int ttt_set_group_chunks(ttt_handle *h, int G) {
   if (!h) return fail(TTT_E_NULL, "handle is NULL");
   if (G < 0) return fail(TTT_E_SHAPE, "G must be >= 0");
-  if (G > 0 && ((long long)G * h->C) % kGroupAlign != 0) return fail(TTT_E_SHAPE, "G*C must be a multiple of 32");
+  if (G > 0 && ((long long)G * h->C) % kGroupAlign != 0) return fail(TTT_E_SHAPE, "G*C must be a multiple of 64");
   h->G_override = G;
   return TTT_OK;
 }

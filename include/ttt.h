@@ -156,7 +156,7 @@ const char *ttt_last_error(void);
  * earlier chunks inside the group. This is the pages' exclusive prefix over
  * chunk updates (iplexlaw sec. 6; paperlayer App. B) taken at two levels.
  * G = 0 restores the default (about 1024 tokens per group, rounded so that
- * G*C is a multiple of 32). G*C must be a multiple of 32; TTT_E_SHAPE
+ * G*C is a multiple of 64). G*C must be a multiple of 64; TTT_E_SHAPE
  * otherwise.
  */
 int ttt_set_group_chunks(ttt_handle *h, int G);

@@ -45,13 +45,13 @@ def test_error_codes_match_header():
     (131072, 128, 0, dict(G=8, L=1024, ngroups=128, T_pad=131072)),
     (32768, 256, 0, dict(G=4, L=1024, ngroups=32, T_pad=32768)),
     (3000, 100, 0, dict(G=16, L=1600, ngroups=2, T_pad=3072)),
-    (1000, 3, 0, dict(G=352, L=1000, ngroups=1, T_pad=1024)),  # one group covers T
-    (5000, 3, 0, dict(G=352, L=1056, ngroups=5, T_pad=5120)),
+    (1000, 3, 0, dict(G=384, L=1000, ngroups=1, T_pad=1024)),  # one group covers T
+    (5000, 3, 0, dict(G=384, L=1152, ngroups=5, T_pad=5120)),
     (5000, 1, 0, dict(G=1024, L=1024, ngroups=5, T_pad=5120)),
     (300, 4096, 0, dict(G=1, L=304, ngroups=1, T_pad=512)),   # single chunk
     (4096, 4096, 0, dict(G=1, L=4096, ngroups=1, T_pad=4096)),
-    (10000, 3000, 0, dict(G=4, L=10000, ngroups=1, T_pad=10240)),
-    (30000, 3000, 0, dict(G=4, L=12000, ngroups=3, T_pad=30208)),
+    (10000, 3000, 0, dict(G=8, L=10000, ngroups=1, T_pad=10240)),
+    (30000, 3000, 0, dict(G=8, L=24000, ngroups=2, T_pad=30208)),
     (2048, 128, 2, dict(G=2, L=256, ngroups=8, T_pad=2048)),
     (0, 128, 0, dict(ngroups=0, T_pad=0)),
 ])
@@ -62,7 +62,7 @@ def test_plan(T, C, G, exp):
     if T > 0:
         assert p["L"] % 8 == 0
         if p["ngroups"] > 1:
-            assert p["L"] % 32 == 0
+            assert p["L"] % 64 == 0
         assert p["ngroups"] * p["L"] >= T and (p["ngroups"] - 1) * p["L"] < T
         assert p["T_pad"] % 256 == 0 and p["T_pad"] >= T
 
@@ -75,9 +75,9 @@ def test_plan_errors():
         ttt.ttt_plan(1 << 24, 128)
     assert e.value.code == -2
     with pytest.raises(ttt.TTTError) as e:
-        ttt.ttt_plan(1000, 3, 8)  # 24 is not a multiple of 32
+        ttt.ttt_plan(1000, 3, 8)  # 24 is not a multiple of 64
     assert e.value.code == -2
-    assert "multiple of 32" in ttt.ttt_last_error()
+    assert "multiple of 64" in ttt.ttt_last_error()
 
 
 def _raw_init(W=(16, 32, 48), d=64, f=64, C=8, eta=0.1, dt=0, mb=1):

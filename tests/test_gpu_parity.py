@@ -63,7 +63,7 @@ def test_fp32_variants(T, C, G, B):
 BF16_CASES = [  # (T, C, G, B)
     (3000, 128, 0, 2),
     (3000, 256, 0, 1),
-    (3000, 100, 0, 1),   # group length 1000: snapshots fall inside a 64-token stage
+    (3000, 100, 0, 1),   # chunks of 100 cross the 64-token slabs; groups of 1600
     (1500, 1, 0, 1),     # per-token updates, causal within-group term
     (700, 1024, 0, 1),   # one chunk
     (4096, 128, 2, 1),   # groups of 256 tokens
