@@ -22,8 +22,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ bf16_t f32_to_bf16(float x) { return __builtin_bit_cast(bf16_t, (__bf16)x); }
 
-// SiLU(g) = g / (1 + e^-g), fp32.
-__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
+// SiLU(g) = g / (1 + e^-g) in fp32 with the hardware reciprocal (v_rcp_f32,
+// within 1 ulp) in place of an IEEE division: within a few fp32 ulp of the
+// division form, far below the bf16 rounding of the values it feeds, at a
+// third of the instructions.
+__device__ __forceinline__ float silu_fast(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
 // One K-segment of a GEMM operand: row r, column k (segment-local) lives at
 // base[r * ld + k]. Rows >= nrows and columns >= kvalid read as zero.

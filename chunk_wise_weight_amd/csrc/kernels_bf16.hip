@@ -453,7 +453,7 @@ __global__ __launch_bounds__(NT_W, 1) void k_a1(A1Args p) {
         const int pos = pos0 + wm * 128 + bi * 32 + 8 * q + 4 * (lane >> 5);
         float z[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) z[r] = silu_f32(g[4 * q + r]) * u[4 * q + r];
+        for (int r = 0; r < 4; ++r) z[r] = silu_fast(g[4 * q + r]) * u[4 * q + r];
         if (p.write_zt) {
           uint2 pk;
           pk.x = pack_bf16x2(p.eta * z[0], p.eta * z[1]);
