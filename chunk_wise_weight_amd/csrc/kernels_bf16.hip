@@ -284,21 +284,25 @@ __device__ __forceinline__ void issue_point(const SL &ld, const typename SL::Pre
 // refilled. Spreading the loads keeps a burst of them from stalling the MFMA
 // issue. With AFTER, after_fn(acc) runs once all of stage kt's MFMAs are
 // queued, and the next fragments are read only then (few registers live).
-template <int WN, int NBJ, int NSL, bool AFTER, bool APLANE = false, class SL, class AfterFn>
-__device__ __forceinline__ void pipelined_stage(Acc<NBJ> &acc, Slab<WN, NBJ> *ring, Frag<NBJ> &cur, Frag<NBJ> &nxt,
-                                                int kt, int nk, int wm, int wn, int lane, int w, const SL &ld,
-                                                AfterFn &&after_fn) {
+// H (= kt % 2) and REFILL (this stage refills the buffer it finished: 1/0)
+// are fixed at compile time where the caller knows them, else -1 (decided
+// here at run time).
+template <int WN, int NBJ, int NSL, bool AFTER, bool APLANE, int H, int REFILL, class SL, class AfterFn>
+__device__ __forceinline__ void stage_body(Acc<NBJ> &acc, Slab<WN, NBJ> *ring, Frag<NBJ> &cur, Frag<NBJ> &nxt,
+                                           int kt, int nk, int wm, int wn, int lane, int w, const SL &ld,
+                                           AfterFn &&after_fn) {
   constexpr int LPS = loads_per_slab<WN, NBJ>();
   static_assert(SL::N == LPS, "the slab loads match the tile configuration");
-  const int sl = kt >> 1, h = kt & 1;
+  const int sl = kt >> 1;
   const int nsl = (nk + 1) >> 1;
+  const int h = H >= 0 ? H : (kt & 1);
+  const bool refill = REFILL >= 0 ? REFILL == 1 : (h == 1 && sl + NSL < nsl);
   frag_read<WN, NBJ, APLANE>(nxt, ring[sl % NSL], h, 1, wm, wn, lane);
   pin();
   frag_mma<0, 1>(acc, cur);
   pin();
-  const bool more = kt + 1 < nk;
-  const bool refill = h == 1 && sl + NSL < nsl;
-  if (more && h == 1) {
+  const bool more = kt + 1 < nk;  // always true when refilling
+  if (h == 1 && (refill || more)) {
     const int later = (nsl - 2 - sl) < (NSL - 2) ? (nsl - 2 - sl) : (NSL - 2);
     slab_wait<LPS>(later);
   }
@@ -337,6 +341,13 @@ __device__ __forceinline__ void pipelined_stage(Acc<NBJ> &acc, Slab<WN, NBJ> *ri
     frag_read<WN, NBJ, APLANE>(cur, ring[((kt + 1) >> 1) % NSL], (kt + 1) & 1, 0, wm, wn, lane);
     pin();
   }
+}
+
+template <int WN, int NBJ, int NSL, bool AFTER, bool APLANE = false, class SL, class AfterFn>
+__device__ __forceinline__ void pipelined_stage(Acc<NBJ> &acc, Slab<WN, NBJ> *ring, Frag<NBJ> &cur, Frag<NBJ> &nxt,
+                                                int kt, int nk, int wm, int wn, int lane, int w, const SL &ld,
+                                                AfterFn &&after_fn) {
+  stage_body<WN, NBJ, NSL, AFTER, APLANE, -1, -1>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, w, ld, after_fn);
 }
 
 struct NoHook {
@@ -402,8 +413,20 @@ __device__ __forceinline__ void gemm_k(Acc<NBJ> &acc, Slab<WN, NBJ> *ring, const
   Frag<NBJ> cur, nxt;
   slab_wait<loads_per_slab<WN, NBJ>()>((nsl - 1) < (NSL - 1) ? (nsl - 1) : (NSL - 1));
   frag_read<WN, NBJ, APLANE>(cur, ring[0], 0, 0, wm, wn, lane);
-  for (int kt = 0; kt < nk; ++kt)
-    pipelined_stage<WN, NBJ, NSL, false, APLANE>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, w, ld, NoHook{});
+  // slabs 0 .. nsl-NSL-1 refill their buffer; the rest drain the ring; an odd
+  // nk ends on a lone even stage
+  const int nref = nsl > NSL ? nsl - NSL : 0;
+  int kt = 0;
+  for (int s = 0; s < nref; ++s, kt += 2) {
+    stage_body<WN, NBJ, NSL, false, APLANE, 0, 0>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, w, ld, NoHook{});
+    stage_body<WN, NBJ, NSL, false, APLANE, 1, 1>(acc, ring, cur, nxt, kt + 1, nk, wm, wn, lane, w, ld, NoHook{});
+  }
+  for (; kt + 1 < nk; kt += 2) {
+    stage_body<WN, NBJ, NSL, false, APLANE, 0, 0>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, w, ld, NoHook{});
+    stage_body<WN, NBJ, NSL, false, APLANE, 1, 0>(acc, ring, cur, nxt, kt + 1, nk, wm, wn, lane, w, ld, NoHook{});
+  }
+  if (kt < nk)
+    stage_body<WN, NBJ, NSL, false, APLANE, 0, 0>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, w, ld, NoHook{});
 }
 
 // The wide GEMMs' loaders: 8 waves, 256 x 256 tiles.
