@@ -397,6 +397,31 @@ __device__ __forceinline__ void band_tile(int t, int nx, int ny, int H, int &x, 
   y = band * H + r % h;
 }
 
+// Stages kt .. kt_end-1 of an nk-stage K loop without hooks (kt even), with
+// each stage's parity and refill fixed at compile time: the stages of slabs
+// 0 .. nsl-NSL-1 refill their buffer, the rest drain the ring, and an odd
+// count of stages ends on a lone even stage. Leaves kt = kt_end.
+template <int WN, int NBJ, int NSL, bool APLANE, class SL>
+__device__ __forceinline__ void stage_run(Acc<NBJ> &acc, Slab<WN, NBJ> *ring, Frag<NBJ> &cur, Frag<NBJ> &nxt,
+                                          int &kt, int kt_end, int nk, int wm, int wn, int lane, int w,
+                                          const SL &ld) {
+  const int nsl = (nk + 1) >> 1;
+  const int kref = nsl > NSL ? 2 * (nsl - NSL) : 0;  // first stage past the refilling slabs
+  const int k1 = kref < kt_end ? kref : kt_end;
+  for (; kt + 1 < k1; kt += 2) {
+    stage_body<WN, NBJ, NSL, false, APLANE, 0, 0>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, w, ld, NoHook{});
+    stage_body<WN, NBJ, NSL, false, APLANE, 1, 1>(acc, ring, cur, nxt, kt + 1, nk, wm, wn, lane, w, ld, NoHook{});
+  }
+  for (; kt + 1 < kt_end; kt += 2) {
+    stage_body<WN, NBJ, NSL, false, APLANE, 0, 0>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, w, ld, NoHook{});
+    stage_body<WN, NBJ, NSL, false, APLANE, 1, 0>(acc, ring, cur, nxt, kt + 1, nk, wm, wn, lane, w, ld, NoHook{});
+  }
+  if (kt < kt_end) {
+    stage_body<WN, NBJ, NSL, false, APLANE, 0, 0>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, w, ld, NoHook{});
+    ++kt;
+  }
+}
+
 // K loop of nk stages over the slab loads `ld` (tiles of 256 x 32*WN*NBJ,
 // NSL slabs in the ring). APLANE: the A tile is a plane operand.
 template <int WN, int NBJ, int NSL, bool APLANE, class SL>
@@ -413,20 +438,8 @@ __device__ __forceinline__ void gemm_k(Acc<NBJ> &acc, Slab<WN, NBJ> *ring, const
   Frag<NBJ> cur, nxt;
   slab_wait<loads_per_slab<WN, NBJ>()>((nsl - 1) < (NSL - 1) ? (nsl - 1) : (NSL - 1));
   frag_read<WN, NBJ, APLANE>(cur, ring[0], 0, 0, wm, wn, lane);
-  // slabs 0 .. nsl-NSL-1 refill their buffer; the rest drain the ring; an odd
-  // nk ends on a lone even stage
-  const int nref = nsl > NSL ? nsl - NSL : 0;
   int kt = 0;
-  for (int s = 0; s < nref; ++s, kt += 2) {
-    stage_body<WN, NBJ, NSL, false, APLANE, 0, 0>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, w, ld, NoHook{});
-    stage_body<WN, NBJ, NSL, false, APLANE, 1, 1>(acc, ring, cur, nxt, kt + 1, nk, wm, wn, lane, w, ld, NoHook{});
-  }
-  for (; kt + 1 < nk; kt += 2) {
-    stage_body<WN, NBJ, NSL, false, APLANE, 0, 0>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, w, ld, NoHook{});
-    stage_body<WN, NBJ, NSL, false, APLANE, 1, 0>(acc, ring, cur, nxt, kt + 1, nk, wm, wn, lane, w, ld, NoHook{});
-  }
-  if (kt < nk)
-    stage_body<WN, NBJ, NSL, false, APLANE, 0, 0>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, w, ld, NoHook{});
+  stage_run<WN, NBJ, NSL, APLANE>(acc, ring, cur, nxt, kt, nk, nk, wm, wn, lane, w, ld);
 }
 
 // The wide GEMMs' loaders: 8 waves, 256 x 256 tiles.
@@ -662,16 +675,16 @@ __global__ __launch_bounds__(128 * WN, 1) void k_update(UpdArgs p) {
     ++g;
   };
   // Stages of group g-1 run plain; its last stage ends with snapshot g.
+  // A group spans L/BK stages, an even number (L is a multiple of 64), so
+  // every group ends on an odd stage.
   int kt = 0;
   for (; g < p.ngroups; ) {
     const int kt_last = g * (p.L / BK) - 1;  // last stage before group g starts
-    for (; kt < kt_last; ++kt)
-      pipelined_stage<WN, NBJ, NSL, false, true>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, w, ld, NoHook{});
+    stage_run<WN, NBJ, NSL, true>(acc, ring, cur, nxt, kt, kt_last, nk, wm, wn, lane, w, ld);
     pipelined_stage<WN, NBJ, NSL, true, true>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, w, ld, snapshot);
     ++kt;
   }
-  for (; kt < nk; ++kt)
-    pipelined_stage<WN, NBJ, NSL, false, true>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, w, ld, NoHook{});
+  stage_run<WN, NBJ, NSL, true>(acc, ring, cur, nxt, kt, nk, nk, wm, wn, lane, w, ld);
 #pragma unroll
   for (int bj = 0; bj < NBJ; ++bj) {
     float *row = st + (long long)bj * 32 * p.f;
