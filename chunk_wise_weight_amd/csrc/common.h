@@ -22,6 +22,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ bf16_t f32_to_bf16(float x) { return __builtin_bit_cast(bf16_t, (__bf16)x); }
 
+// Non-temporal stores (the `nt` bit): for results no later instruction of
+// the same kernel reads, so that they do not push the operand tiles other
+// workgroups are still reading out of L2.
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void store_nt(void *p, uint32_t lo, uint32_t hi) {
+  __builtin_nontemporal_store(u32x2_t{lo, hi}, reinterpret_cast<u32x2_t *>(p));
+}
+__device__ __forceinline__ void store_nt(bf16_t *p, bf16_t v) { __builtin_nontemporal_store(v, p); }
+
 // SiLU(g) = g / (1 + e^-g) in fp32 with the hardware reciprocal (v_rcp_f32,
 // within 1 ulp) in place of an IEEE division: within a few fp32 ulp of the
 // division form, far below the bf16 rounding of the values it feeds, at a

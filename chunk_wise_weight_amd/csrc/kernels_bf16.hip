@@ -490,15 +490,12 @@ __global__ __launch_bounds__(NT_W, 1) void k_a1(A1Args p) {
         float z[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) z[r] = silu_fast(g[4 * q + r]) * u[4 * q + r];
-        if (p.write_zt) {
-          uint2 pk;
-          pk.x = pack_bf16x2(p.eta * z[0], p.eta * z[1]);
-          pk.y = pack_bf16x2(p.eta * z[2], p.eta * z[3]);
-          *reinterpret_cast<uint2 *>(ZTb + ((long long)(pos >> 3) * p.f + feat) * 8 + (pos & 7)) = pk;
-        }
+        if (p.write_zt)
+          store_nt(ZTb + ((long long)(pos >> 3) * p.f + feat) * 8 + (pos & 7), pack_bf16x2(p.eta * z[0], p.eta * z[1]),
+                   pack_bf16x2(p.eta * z[2], p.eta * z[3]));
         bf16_t *zrow = p.Z + ((long long)b * p.T_pad + pos) * p.f + feat;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) zrow[(long long)r * p.f] = f32_to_bf16(z[r]);
+        for (int r = 0; r < 4; ++r) store_nt(zrow + (long long)r * p.f, f32_to_bf16(z[r]));
       }
     }
   }
