@@ -25,7 +25,8 @@ PEAK_HBM_GBS = 8000.0
 COPY_BYTES = 1 << 30  # the calibration copy reads and writes this many bytes
 KERNEL_OF_PHASE = {"up_gate_swiglu": "k_a1", "update_snapshots": "k_update", "output": "k_out"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_c4_4b_128k.txt")
-KERNEL_SOURCE = os.path.join(ROOT, "chunk_wise_weight_amd", "csrc", "kernels_bf16.hip")
+# the sources the bf16 kernels are compiled from; the traffic summary is keyed to their hash
+KERNEL_SOURCES = [os.path.join(ROOT, "chunk_wise_weight_amd", "csrc", n) for n in ("kernels_bf16.hip", "common.h")]
 
 
 def parse():
@@ -64,15 +65,18 @@ def measured_traffic(kernel, C):
 
     The summary holds FETCH_SIZE + WRITE_SIZE per dispatch, already scaled by
     what the same counters read for a plain copy of known size, together with
-    the SHA-256 of the kernel source they were taken on. Returns None when the
+    the SHA-256 of the kernel sources they were taken on. Returns None when the
     summary is missing, covers another chunk size, or the source has changed.
     """
     import hashlib
 
     if not os.path.exists(TRAFFIC_FILE):
         return None
-    with open(KERNEL_SOURCE, "rb") as fh:
-        sha = hashlib.sha256(fh.read()).hexdigest()
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as fh:
+            h.update(fh.read())
+    sha = h.hexdigest()
     fields = {}
     for line in open(TRAFFIC_FILE):
         parts = line.split()
