@@ -34,6 +34,8 @@
 //   D: j = l % 32, i = 8*(r/4) + 4*(l/32) + r%4.
 // So each lane holds, per group of 4 registers, four consecutive i for one j:
 // epilogues store 4 consecutive elements along i.
+#include <type_traits>
+
 #include "launch.h"
 
 namespace {
@@ -192,6 +194,7 @@ struct SlabLoads {
   LA a;
   LB b;
   static constexpr int N = LA::N + LB::N;
+  static constexpr bool kPf = false;  // no prefetch
   struct Pre {
     typename LA::Pre a;
     typename LB::Pre b;
@@ -214,15 +217,18 @@ constexpr unsigned wait_imm(int n) { return (unsigned)((n & 15) | 0x70 | (((n >>
 // the barrier: their loads of the awaited slab have landed too, and every
 // wave is done reading the slab computed before. Only LDS is shared between
 // the waves, so no memory fence is needed (a fence would also wait for the
-// loads of the slabs still in flight).
-template <int LPS>
+// loads of the slabs still in flight). `later` is at most MAXL. EXTRA more
+// operations issued after the awaited slab's loads (prefetches) may stay in
+// flight too: the counter is decremented in issue order.
+template <int LPS, int MAXL, int EXTRA = 0>
 __device__ __forceinline__ void slab_wait(int later) {
-  switch (later) {
-    case 0: __builtin_amdgcn_s_waitcnt(wait_imm(0)); break;
-    case 1: __builtin_amdgcn_s_waitcnt(wait_imm(LPS)); break;
-    case 2: __builtin_amdgcn_s_waitcnt(wait_imm(2 * LPS)); break;
-    default: __builtin_amdgcn_s_waitcnt(wait_imm(3 * LPS)); break;
-  }
+  static_assert(MAXL >= 0 && MAXL <= 2 && MAXL * LPS + EXTRA <= 63, "vmcnt holds 6 bits");
+  if (MAXL == 0 || later <= 0)
+    __builtin_amdgcn_s_waitcnt(wait_imm(EXTRA));
+  else if (MAXL == 1 || later == 1)
+    __builtin_amdgcn_s_waitcnt(wait_imm((MAXL >= 1 ? LPS : 0) + EXTRA));
+  else
+    __builtin_amdgcn_s_waitcnt(wait_imm(MAXL * LPS + EXTRA));
   asm volatile("s_barrier" ::: "memory");
 }
 
@@ -284,6 +290,9 @@ __device__ __forceinline__ void issue_point(const SL &ld, const typename SL::Pre
 // refilled. Spreading the loads keeps a burst of them from stalling the MFMA
 // issue. With AFTER, after_fn(acc) runs once all of stage kt's MFMAs are
 // queued, and the next fragments are read only then (few registers live).
+// Loads with a prefetch (SL::kPf) also touch, in every odd stage, this
+// workgroup's share of slab kt/2 + NSL + 2, so that the slab's own loads two
+// stages later find it in L2.
 // H (= kt % 2) and REFILL (this stage refills the buffer it finished: 1/0)
 // are fixed at compile time where the caller knows them, else -1 (decided
 // here at run time).
@@ -304,7 +313,7 @@ __device__ __forceinline__ void stage_body(Acc<NBJ> &acc, Slab<WN, NBJ> *ring, F
   const bool more = kt + 1 < nk;  // always true when refilling
   if (h == 1 && (refill || more)) {
     const int later = (nsl - 2 - sl) < (NSL - 2) ? (nsl - 2 - sl) : (NSL - 2);
-    slab_wait<LPS>(later);
+    slab_wait<LPS, NSL - 2, SL::kPf ? 1 : 0>(later);
   }
   const int rs = sl + NSL;
   Slab<WN, NBJ> &dst = ring[sl % NSL];  // the buffer just finished refills with slab rs
@@ -335,6 +344,10 @@ __device__ __forceinline__ void stage_body(Acc<NBJ> &acc, Slab<WN, NBJ> *ring, F
   pin();
   frag_mma<3, 4>(acc, nxt);
   if (refill) issue_point<LPS, 6>(ld, pre, dst, rs, w, lane);
+  // one prefetch per odd stage, always issued, so every slab wait counts one
+  if constexpr (SL::kPf) {
+    if (h == 1) ld.prefetch((sl + NSL + 2) < (nsl - 1) ? (sl + NSL + 2) : (nsl - 1), w, lane);
+  }
   pin();
   if (AFTER) {
     after_fn(acc);
@@ -424,19 +437,28 @@ __device__ __forceinline__ void stage_run(Acc<NBJ> &acc, Slab<WN, NBJ> *ring, Fr
 
 // K loop of nk stages over the slab loads `ld` (tiles of 256 x 32*WN*NBJ,
 // NSL slabs in the ring). APLANE: the A tile is a plane operand.
+// Start of a K loop of nsl >= 1 slabs: the loads of the first min(NSL, nsl)
+// slabs and, with a prefetch, the first prefetch (slab NSL + 1); then the
+// wait for slab 0.
+template <int WN, int NBJ, int NSL, class SL>
+__device__ __forceinline__ void ring_prologue(const SL &ld, Slab<WN, NBJ> *ring, int nsl, int w, int lane) {
+  for (int sl = 0; sl < NSL && sl < nsl; ++sl) {
+    const typename SL::Pre pre = ld.prep(sl);
+#pragma unroll
+    for (int j = 0; j < SL::N; ++j) ld.issue(pre, ring[sl], sl, w, lane, j);
+  }
+  if constexpr (SL::kPf) ld.prefetch((NSL + 1) < (nsl - 1) ? (NSL + 1) : (nsl - 1), w, lane);
+  slab_wait<loads_per_slab<WN, NBJ>(), NSL - 1, SL::kPf ? 1 : 0>((nsl - 1) < (NSL - 1) ? (nsl - 1) : (NSL - 1));
+}
+
 template <int WN, int NBJ, int NSL, bool APLANE, class SL>
 __device__ __forceinline__ void gemm_k(Acc<NBJ> &acc, Slab<WN, NBJ> *ring, const SL &ld, int nk) {
   const int lane = threadIdx.x & 63;
   const int w = wave_id(), wm = w & 1, wn = w >> 1;
   if (nk <= 0) return;
   const int nsl = (nk + 1) >> 1;
-  for (int sl = 0; sl < NSL && sl < nsl; ++sl) {
-    const typename SL::Pre pre = ld.prep(sl);
-#pragma unroll
-    for (int j = 0; j < SL::N; ++j) ld.issue(pre, ring[sl], sl, w, lane, j);
-  }
+  ring_prologue<WN, NBJ, NSL>(ld, ring, nsl, w, lane);
   Frag<NBJ> cur, nxt;
-  slab_wait<loads_per_slab<WN, NBJ>()>((nsl - 1) < (NSL - 1) ? (nsl - 1) : (NSL - 1));
   frag_read<WN, NBJ, APLANE>(cur, ring[0], 0, 0, wm, wn, lane);
   int kt = 0;
   stage_run<WN, NBJ, NSL, APLANE>(acc, ring, cur, nxt, kt, nk, nk, wm, wn, lane, w, ld);
@@ -568,6 +590,45 @@ __global__ __launch_bounds__(NT_W, 1) void k_target_gemm(TgtArgs p) {
 // of them (one per CU) run on the 8-wave configuration; a last partial round
 // of at most 128 tiles is split into 256 x 128 halves that run as one round
 // on the 4-wave configuration, so no CU idles for a whole round.
+// Tile loads of the update's whole rounds (8 waves, 256 x 256 tiles) with an
+// L2 prefetch. Every eta Z^T tile is read by one XCD only, so its slabs come
+// from HBM, one slab ahead of use without the prefetch. The workgroups that
+// share an operand tile split its prefetch: the 8 along a band of the tile
+// order take plane pa = ty % 8 of an eta Z^T slab (8 planes of 32 lines of
+// 128 bytes), the 4 along x take row quarter qb = tx % 4 of a V^T slab (256
+// rows of one line). Waves 0-3 touch 8 lines of the plane each, waves 4-7 16
+// lines of the quarter, with one 4-byte DMA per wave into a 256-byte LDS sink
+// that nothing reads. (In the half-tile round an eta Z^T tile has as few as 4
+// sharers, and the prefetch measured slower there.)
+struct UpdLoads : SlabLoads<PlLoad<8>, KbLoad<256, 8>> {
+  static constexpr bool kPf = true;
+  uint32_t *sink;
+  int pa, qb;
+  __device__ __forceinline__ void prefetch(int sl, int w, int lane) const {
+    __amdgpu_buffer_rsrc_t rs;
+    uint32_t vo;
+    if (w < 4) {
+      rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t *>(a.base + ((long long)sl * 8 + pa) * a.pstride),
+                                             (short)0, 0x7fffffff, kBufferFlags);
+      vo = (uint32_t)((8 * w + (lane & 7)) * 128);
+    } else {
+      rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t *>(b.base + (long long)sl * b.kblk), (short)0,
+                                             0x7fffffff, kBufferFlags);
+      vo = (uint32_t)((64 * qb + 16 * (w - 4) + (lane & 15)) * 128);
+    }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)sink, 4, vo, 0, 0, 0);
+  }
+};
+
+// LDS of the update: the ring and the prefetch sink in one object. (With the
+// sink in an object of its own, the compiler cannot tell the prefetch DMA from
+// the ring's, and waits for it before every fragment read.)
+template <int WN, int NBJ, int NSL>
+struct UpdLds {
+  Slab<WN, NBJ> ring[NSL];
+  uint32_t sink[64];
+};
+
 struct UpdArgs {
   const bf16_t *ZT;
   const bf16_t *VT;
@@ -604,7 +665,8 @@ __device__ __forceinline__ void dump_snapshot(const Acc<NBJ> &acc, bf16_t *lane_
 // WN = 2: workgroup n is half n%2 (128 columns of a) of tile tile0 + n/2.
 template <int WN, int NBJ, int NSL>
 __global__ __launch_bounds__(128 * WN, 1) void k_update(UpdArgs p) {
-  __shared__ __attribute__((aligned(16))) Slab<WN, NBJ> ring[NSL];
+  __shared__ __attribute__((aligned(16))) UpdLds<WN, NBJ, NSL> lds;
+  Slab<WN, NBJ> *ring = lds.ring;
   constexpr int BN = 32 * WN * NBJ;  // columns of a per workgroup
   const int nx = p.f / BM, ny = p.d / 256;
   const int n = xcd_tile(blockIdx.x, gridDim.x);
@@ -642,7 +704,12 @@ __global__ __launch_bounds__(128 * WN, 1) void k_update(UpdArgs p) {
   }
 
   // A: eta Z^T in planes of 8 tokens [T_pad/8][f][8]; B: V^T K-blocked [T_pad/64][d][64]
-  SlabLoads<PlLoad<2 * WN>, KbLoad<BN, 2 * WN>> ld;
+  std::conditional_t<WN == 4, UpdLoads, SlabLoads<PlLoad<2 * WN>, KbLoad<BN, 2 * WN>>> ld;
+  if constexpr (WN == 4) {
+    ld.sink = lds.sink;
+    ld.pa = ty & 7;
+    ld.qb = tx & 3;
+  }
   ld.a.init(p.ZT + (long long)b * p.f * p.T_pad + (long long)i0 * 8, (long long)p.f * 8, lane);
   ld.b.init(p.VT + (long long)b * p.d * p.T_pad + (long long)j0 * 64, (long long)p.d * 64, w, lane);
   const int nk = p.kend / BK;
@@ -652,14 +719,9 @@ __global__ __launch_bounds__(128 * WN, 1) void k_update(UpdArgs p) {
   dump_snapshot(acc, snap0, p.d);
   int g = 1;
   const int nsl = (nk + 1) >> 1;
-  for (int sl = 0; sl < NSL && sl < nsl; ++sl) {
-    const auto pre = ld.prep(sl);
-#pragma unroll
-    for (int j = 0; j < ld.N; ++j) ld.issue(pre, ring[sl], sl, w, lane, j);
-  }
   Frag<NBJ> cur, nxt;
   if (nk > 0) {
-    slab_wait<loads_per_slab<WN, NBJ>()>((nsl - 1) < (NSL - 1) ? (nsl - 1) : (NSL - 1));
+    ring_prologue<WN, NBJ, NSL>(ld, ring, nsl, w, lane);
     frag_read<WN, NBJ, true>(cur, ring[0], 0, 0, wm, wn, lane);
   }
   // The snapshot stores share the vector-memory counter with the tile loads.
