@@ -91,6 +91,31 @@ def test_bf16_variants(T, C, G, B):
     assert np.array_equal(Wf0, np.broadcast_to(W0, Wf0.shape))
 
 
+SHORT_4B_CASES = [  # (T, C, G, B) at d = 2560, f = 9728
+    (64, 64, 0, 1),     # one slab
+    (200, 64, 2, 1),    # odd stage count, groups of 128 tokens
+    (333, 64, 1, 2),    # a snapshot every 64 tokens; 760 tiles, all on the 256 x 256 shape
+    (333, 100, 0, 1),   # 380 tiles: whole round and half-tile round
+]
+
+
+@pytest.mark.parametrize("T,C,G,B", SHORT_4B_CASES)
+def test_bf16_4b_shape_short_streams(T, C, G, B):
+    # At the 4B layer width the state has 380 tiles per sequence, so the update
+    # runs its 256 x 256 kernel (with the L2 prefetch two slabs ahead, clamped
+    # to the last slab) on streams of only a few slabs.
+    w = make_inputs(d=2560, f=9728, B=B, T=T, C=C, eta=1e-3, dtype="bf16", vocab=509, e_std=0.5, seed=70 + T + G)
+    print(f"[bf16 4b short] T={T} C={C} G={G} B={B}", flush=True)
+    y, Wf = Layer(w, G=G).forward_np()
+    y0, _ = Layer(w, G=G, eta=0.0).forward_np()
+    y_ref, W_ref = _oracle(w)
+    y0_ref, _ = _oracle(w, eta=0.0)
+    W0 = w.W_down0.astype(np.float64)
+    assert rel_fro(y, y_ref) <= BF16_TOL, rel_fro(y, y_ref)
+    assert rel_fro(y - y0, y_ref - y0_ref) <= BF16_TOL, rel_fro(y - y0, y_ref - y0_ref)
+    assert rel_fro(Wf - W0, W_ref - W0) <= BF16_TOL, rel_fro(Wf - W0, W_ref - W0)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_static_and_empty(dtype):
     d, f = (64, 128) if dtype == "f32" else (256, 256)
