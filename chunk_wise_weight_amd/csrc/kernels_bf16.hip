@@ -942,9 +942,10 @@ __global__ __launch_bounds__(NT_U, 1) void k_chunk_gram(GramArgs p) {
   __shared__ __attribute__((aligned(16))) Slab<WN_U, NBJ_U> ring[NSL_U];
   static_assert(sizeof(ring) >= sizeof(float) * 256 * GR_P, "the product tile reuses the ring");
   const int nu = p.T_pad / 256;
-  const int wr = blockIdx.x % p.wspan;
-  const int u = (blockIdx.x / p.wspan) % nu;
-  const int b = blockIdx.x / (p.wspan * nu);
+  const int id = xcd_tile(blockIdx.x, gridDim.x);  // the t-tiles of an s-tile share an XCD
+  const int wr = id % p.wspan;
+  const int u = (id / p.wspan) % nu;
+  const int b = id / (p.wspan * nu);
   const int s0 = u * 256;
   float *out = p.rowpart + (((long long)b * nu + u) * p.wspan + wr) * 256;
   const int s_last = (s0 + 255 < p.T - 1) ? s0 + 255 : p.T - 1;
