@@ -129,6 +129,35 @@ struct RmLoad {
   }
 };
 
+// Gathered rows: row r of the operand is row rid[r] of a row-major table E
+// ([nrows_e][ld], nrows_e*ld*2 < 2^31 bytes); rows r >= nvalid, and rows whose
+// id falls outside [0, nrows_e), read zero.
+template <int ROWS, int NW>
+struct RmGather {
+  static constexpr int WR = ROWS / NW, N = WR / 8;
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t vo[N];
+  __device__ __forceinline__ void init(const bf16_t *E, int ld, int nrows_e, const int32_t *rid, int nvalid, int w,
+                                       int lane) {
+    rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t *>(E), (short)0, (int)((long long)nrows_e * ld * 2),
+                                           kBufferFlags);
+    const int lr = lane >> 3;
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      const int row = w * WR + 8 * n + lr;
+      const int id = row < nvalid ? rid[row] : -1;
+      vo[n] = (id >= 0 && id < nrows_e) ? (uint32_t)id * (uint32_t)ld * 2u + (uint32_t)(((lane & 7) ^ swz(row)) << 4)
+                                        : kOutOfRange;
+    }
+  }
+  struct Pre {};
+  __device__ __forceinline__ Pre prep(int) const { return Pre{}; }
+  __device__ __forceinline__ void issue(const Pre &, bf16_t *tile, int sl, int w, int, int n) const {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(tile + (w * WR + 8 * n) * SK), 16, vo[n], sl * SK * 2, 0,
+                                             0);
+  }
+};
+
 // K-blocked operand: element (r, k) at base[(k/64)*kblk + r*64 + k%64], base
 // at the tile's first row in block 0; every row of the tile is valid. The
 // descriptor follows the slab's block. The swizzle depends on n only through
@@ -928,16 +957,22 @@ __global__ __launch_bounds__(NT_W, 1) void k_out(OutArgs p) {
 // rowpart[b][u][wr][s % 256] (wr = w - first t-tile that can share a chunk
 // with the s-tile). Summing a chunk's rows over every wr gives its squared
 // norm; the sums run in a fixed order, so results are deterministic.
+// GATHER: V's rows are read from the target table through the ids (V[p] =
+// E[ids[b][p+1]], zero for p >= T or an id outside [0, vocab)) instead of
+// from a row-major copy.
 // grid: B * (T_pad/256) * wspan workgroups of 256 threads
 struct GramArgs {
-  const bf16_t *Z;  // [B][T_pad][f]
-  const bf16_t *V;  // [B][T_pad][d], rows past T zero
-  float *rowpart;   // [B][T_pad/256][wspan][256]
-  int T, T_pad, C, d, f, wspan;
+  const bf16_t *Z;     // [B][T_pad][f]
+  const bf16_t *V;     // [B][T_pad][d], rows past T zero (without GATHER)
+  const bf16_t *E;     // [vocab][d] (GATHER)
+  const int32_t *ids;  // [B][T+1] (GATHER)
+  float *rowpart;      // [B][T_pad/256][wspan][256]
+  int T, T_pad, C, d, f, wspan, vocab;
 };
 
 constexpr int GR_P = 129;  // fp32 pitch of the [256][128] product tile in LDS (conflict-free row sums)
 
+template <bool GATHER>
 __global__ __launch_bounds__(NT_U, 1) void k_chunk_gram(GramArgs p) {
   __shared__ __attribute__((aligned(16))) Slab<WN_U, NBJ_U> ring[NSL_U];
   static_assert(sizeof(ring) >= sizeof(float) * 256 * GR_P, "the product tile reuses the ring");
@@ -958,7 +993,7 @@ __global__ __launch_bounds__(NT_U, 1) void k_chunk_gram(GramArgs p) {
   }
   const int t0 = w * 128;
   const bf16_t *Zb = p.Z + (long long)b * p.T_pad * p.f;
-  const bf16_t *Vb = p.V + (long long)b * p.T_pad * p.d;
+  const bf16_t *Vb = GATHER ? nullptr : p.V + (long long)b * p.T_pad * p.d;
   Acc<NBJ_U> az, av;
   acc_zero(az);
   acc_zero(av);
@@ -970,7 +1005,13 @@ __global__ __launch_bounds__(NT_U, 1) void k_chunk_gram(GramArgs p) {
     gemm_k<WN_U, NBJ_U, NSL_U, false>(az, ring, ld, p.f / BK);
   }
   __syncthreads();  // the second pass refills the ring
-  {
+  if constexpr (GATHER) {
+    SlabLoads<RmGather<BM, 2 * WN_U>, RmGather<32 * WN_U * NBJ_U, 2 * WN_U>> ld;
+    const int32_t *tg = p.ids + (long long)b * (p.T + 1) + 1;  // target id of slot p at tg[p]
+    ld.a.init(p.E, p.d, p.vocab, tg + s0, p.T - s0, wg, lg);
+    ld.b.init(p.E, p.d, p.vocab, tg + t0, p.T - t0, wg, lg);
+    gemm_k<WN_U, NBJ_U, NSL_U, false>(av, ring, ld, p.d / BK);
+  } else {
     SlabLoads<RmLoad<BM, 2 * WN_U>, RmLoad<32 * WN_U * NBJ_U, 2 * WN_U>> ld;
     ld.a.init(Vb + (long long)s0 * p.d, p.d, p.T_pad - s0, p.d, wg, lg);
     ld.b.init(Vb + (long long)t0 * p.d, p.d, p.T_pad - t0, p.d, wg, lg);
@@ -1003,9 +1044,12 @@ __global__ __launch_bounds__(NT_U, 1) void k_chunk_gram(GramArgs p) {
 // A 64-slot x 64-feature tile passes through LDS so both the row reads of E and
 // the writes (one contiguous 8 KB block) are 16 B per lane. With Vrow non-null
 // the rows are also written row-major, Vrow[b][p][a] (used by update clipping).
+// With cfac non-null, slot p is scaled by the clipping factor cfac[b][p/C]
+// (bf16 -> fp32, times the factor, rounded to bf16).
 // grid: (T_pad/64, d/64, B)
 __global__ __launch_bounds__(256) void k_gather_vt(const int32_t *ids, const bf16_t *E, int vocab, bf16_t *VT,
-                                                   bf16_t *Vrow, int T, int T_pad, int d) {
+                                                   bf16_t *Vrow, const float *cfac, int C, int nchunks, int T,
+                                                   int T_pad, int d) {
   __shared__ __attribute__((aligned(16))) bf16_t tile[64][72];
   const int p0 = blockIdx.x * 64, a0 = blockIdx.y * 64, b = blockIdx.z;
   const int tid = threadIdx.x, seg = tid & 7;
@@ -1017,6 +1061,12 @@ __global__ __launch_bounds__(256) void k_gather_vt(const int32_t *ids, const bf1
     if (pos < T) id = ids[(long long)b * (T + 1) + pos + 1];
     uint4 v = make_uint4(0u, 0u, 0u, 0u);
     if (id >= 0 && id < vocab) v = *reinterpret_cast<const uint4 *>(E + (long long)id * d + a0 + seg * 8);
+    if (cfac && pos < T) {
+      const float c = cfac[(long long)b * nchunks + pos / C];
+      bf16_t *e = reinterpret_cast<bf16_t *>(&v);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) e[k] = f32_to_bf16(bf16_to_f32(e[k]) * c);
+    }
     *reinterpret_cast<uint4 *>(&tile[pl][seg * 8]) = v;
     if (Vrow) *reinterpret_cast<uint4 *>(Vrow + ((long long)b * T_pad + pos) * d + a0 + seg * 8) = v;
   }
@@ -1036,18 +1086,24 @@ __global__ __launch_bounds__(256) void k_gather_vt(const int32_t *ids, const bf1
 }  // namespace
 
 hipError_t launch_gather_vt_bf16(const int32_t *ids, const bf16_t *E, int vocab, bf16_t *VT, bf16_t *Vrow,
-                                 const Layout &lay, hipStream_t s) {
+                                 const float *cfac, const Layout &lay, hipStream_t s) {
   dim3 grid(lay.T_pad / 64, lay.d / 64, lay.B);
-  hipLaunchKernelGGL(k_gather_vt, grid, dim3(256), 0, s, ids, E, vocab, VT, Vrow, lay.T, lay.T_pad, lay.d);
+  const int nchunks = (int)((lay.T + (long long)lay.C - 1) / lay.C);
+  hipLaunchKernelGGL(k_gather_vt, grid, dim3(256), 0, s, ids, E, vocab, VT, Vrow, cfac, lay.C, nchunks, lay.T,
+                     lay.T_pad, lay.d);
   return hipGetLastError();
 }
 
-hipError_t launch_chunk_gram_bf16(const bf16_t *Z, const bf16_t *Vrow, float *rowpart, int wspan, const Layout &lay,
-                                  hipStream_t s) {
+hipError_t launch_chunk_gram_bf16(const bf16_t *Z, const bf16_t *Vrow, const bf16_t *E, const int32_t *ids, int vocab,
+                                  float *rowpart, int wspan, const Layout &lay, hipStream_t s) {
   const long long n = (long long)lay.B * (lay.T_pad / 256) * wspan;
   if (n >= (1LL << 31)) return hipErrorInvalidConfiguration;
-  GramArgs p{Z, Vrow, rowpart, lay.T, lay.T_pad, lay.C, lay.d, lay.f, wspan};
-  hipLaunchKernelGGL(k_chunk_gram, dim3((unsigned)n), dim3(NT_U), 0, s, p);
+  if (!Vrow && (long long)vocab * lay.d * 2 >= (1LL << 31)) return hipErrorInvalidValue;
+  GramArgs p{Z, Vrow, E, ids, rowpart, lay.T, lay.T_pad, lay.C, lay.d, lay.f, wspan, vocab};
+  if (Vrow)
+    hipLaunchKernelGGL(k_chunk_gram<false>, dim3((unsigned)n), dim3(NT_U), 0, s, p);
+  else
+    hipLaunchKernelGGL(k_chunk_gram<true>, dim3((unsigned)n), dim3(NT_U), 0, s, p);
   return hipGetLastError();
 }
 

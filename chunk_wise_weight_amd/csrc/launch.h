@@ -5,9 +5,10 @@
 
 // ---- bf16 path: MFMA kernels (kernels_bf16.hip) ----
 // V^T[b][a][p] = E[ids[b][p+1]][a] for p < T and a valid id, else 0; K-blocked [B][T_pad/64][d][64].
-// Vrow (nullable): the same rows row-major, [B][T_pad][d].
+// Vrow (nullable): the same rows row-major, [B][T_pad][d]. cfac (nullable): clipping factors
+// [B][ceil(T/C)]; slot p is scaled by cfac[b][p/C].
 hipError_t launch_gather_vt_bf16(const int32_t *ids, const bf16_t *E, int vocab, bf16_t *VT, bf16_t *Vrow,
-                                 const Layout &lay, hipStream_t s);
+                                 const float *cfac, const Layout &lay, hipStream_t s);
 // Z = SiLU(x W_gate^T) * (x W_up^T) -> Z [B][T_pad][f] and ZT = eta*Z^T in planes of 8 tokens [B][T_pad/8][f][8].
 // Wug: [2f][d], rows interleaved in blocks of 32 (32 up rows, then the matching 32 gate rows).
 hipError_t launch_a1_bf16(const bf16_t *x, const bf16_t *Wug, bf16_t *Z, bf16_t *ZT, float eta, int write_zt,
@@ -23,9 +24,10 @@ hipError_t launch_state_to_snap_bf16(const float *state, bf16_t *snap, int d, in
 // y[b][gL+t] = Z[gL+t] snap[b][g]^T + sum_s P[b][g][t][s] V[gL+s].
 hipError_t launch_out_bf16(const bf16_t *Z, const bf16_t *P, const bf16_t *snap, const bf16_t *VT, bf16_t *y,
                            const Layout &lay, hipStream_t s);
-// Per-row chunk Gram sums for clipping: rowpart [B][T_pad/256][wspan][256] fp32.
-hipError_t launch_chunk_gram_bf16(const bf16_t *Z, const bf16_t *Vrow, float *rowpart, int wspan, const Layout &lay,
-                                  hipStream_t s);
+// Per-row chunk Gram sums for clipping: rowpart [B][T_pad/256][wspan][256] fp32. V's rows come from
+// Vrow [B][T_pad][d] or, with Vrow null, from E [vocab][d] through ids [B][T+1] (vocab*d*2 < 2^31).
+hipError_t launch_chunk_gram_bf16(const bf16_t *Z, const bf16_t *Vrow, const bf16_t *E, const int32_t *ids, int vocab,
+                                  float *rowpart, int wspan, const Layout &lay, hipStream_t s);
 
 // ---- fp32 path: FMA kernels (kernels_f32.hip), same buffers and meaning in fp32 ----
 hipError_t launch_gather_vt_f32(const int32_t *ids, const float *E, int vocab, float *VT, float *Vrow,

@@ -178,14 +178,14 @@ bool misaligned(const void *p) { return ((uintptr_t)p & 15) != 0; }
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 Scratch scratch_layout(const ttt_handle *h, int B, const Plan &pl, bool need_zt, bool need_p, bool clip,
-                       int wspan, bool conv) {
+                       bool need_vrow, int wspan, bool conv) {
   const size_t es = h->dt == TTT_BF16 ? 2 : 4;
   const size_t vt = align256(es * (size_t)B * h->d * pl.T_pad);
   const size_t z = align256(es * (size_t)B * pl.T_pad * h->f);
   const size_t zt = need_zt ? z : 0;
   const size_t sn = align256(es * (size_t)B * pl.ngroups * h->d * h->f);
   const size_t pp = need_p ? align256(es * (size_t)B * pl.ngroups * pl.L * pl.L) : 0;
-  const size_t vr = clip ? align256(es * (size_t)B * pl.T_pad * h->d) : 0;
+  const size_t vr = need_vrow ? align256(es * (size_t)B * pl.T_pad * h->d) : 0;
   const size_t rp = clip ? align256(4 * (size_t)B * (pl.T_pad / 256) * wspan * 256) : 0;
   const size_t cf = clip ? align256(4 * (size_t)B * ((pl.T_pad + pl.C - 1) / pl.C)) : 0;
   const size_t uu = conv ? align256(es * (size_t)B * pl.T_pad * h->d) : 0;
@@ -252,7 +252,13 @@ int forward_impl(ttt_handle *h, const void *x, const int32_t *ids, const void *E
   Layout lay{B, T, pl.T_pad, pl.C, pl.L, pl.ngroups, h->d, h->f, learn ? pl.intra : 0};
   const int wspan = clip_wspan(lay, h->dt == TTT_BF16);
   const bool conv = h->conv_K > 0 && (learn || lay.intra);
-  Scratch sc = scratch_layout(h, B, pl, learn, learn && pl.intra, clip, wspan, conv);
+  // With clipping on the plain bf16 target, the Gram kernel reads the target
+  // rows from E through the ids, and the gather runs after the clipping
+  // factors and writes V^T already scaled: no row-major copy of V, no
+  // scaling pass.
+  const bool gram_e =
+      clip && !conv && h->dt == TTT_BF16 && (long long)vocab * h->d * 2 < (1LL << 31);
+  Scratch sc = scratch_layout(h, B, pl, learn, learn && pl.intra, clip, clip && !gram_e, wspan, conv);
   if (sc.total > h->ws_bytes) {
     HIP_TRY(hipStreamSynchronize(s));
     HIP_TRY(hipDeviceSynchronize());
@@ -267,7 +273,7 @@ int forward_impl(ttt_handle *h, const void *x, const int32_t *ids, const void *E
   }
   void *VT = at(h->ws, sc.VT), *Z = at(h->ws, sc.Z), *ZT = at(h->ws, sc.ZT), *snap = at(h->ws, sc.snap),
        *P = at(h->ws, sc.P);
-  void *Vrow = clip ? at(h->ws, sc.Vrow) : nullptr;
+  void *Vrow = clip && !gram_e ? at(h->ws, sc.Vrow) : nullptr;
   float *rowpart = (float *)at(h->ws, sc.rowpart), *cfac = (float *)at(h->ws, sc.cfac);
   void *U = at(h->ws, sc.U);
 
@@ -275,17 +281,21 @@ int forward_impl(ttt_handle *h, const void *x, const int32_t *ids, const void *E
     if (conv) {
       HIP_TRY(launch_conv_taps_bf16(ids, (const bf16_t *)E_tgt, vocab, h->conv_w, h->conv_K, (bf16_t *)U, lay, s));
       HIP_TRY(launch_target_gemm_bf16((const bf16_t *)U, (const bf16_t *)h->Wt, (bf16_t *)VT, (bf16_t *)Vrow, lay, s));
-    } else if (learn || lay.intra) {
-      HIP_TRY(launch_gather_vt_bf16(ids, (const bf16_t *)E_tgt, vocab, (bf16_t *)VT, (bf16_t *)Vrow, lay, s));
+    } else if ((learn || lay.intra) && !gram_e) {
+      HIP_TRY(launch_gather_vt_bf16(ids, (const bf16_t *)E_tgt, vocab, (bf16_t *)VT, (bf16_t *)Vrow, nullptr, lay, s));
     }
     if (prof) HIP_TRY(hipEventRecord(h->ev[1], s));
     HIP_TRY(launch_a1_bf16((const bf16_t *)x, (const bf16_t *)h->Wug, (bf16_t *)Z, (bf16_t *)ZT, h->eta,
                            learn ? 1 : 0, lay, s));
     if (prof) HIP_TRY(hipEventRecord(h->ev[2], s));
     if (clip) {
-      HIP_TRY(launch_chunk_gram_bf16((const bf16_t *)Z, (const bf16_t *)Vrow, rowpart, wspan, lay, s));
+      HIP_TRY(launch_chunk_gram_bf16((const bf16_t *)Z, (const bf16_t *)Vrow, (const bf16_t *)E_tgt, ids, vocab, rowpart,
+                                     wspan, lay, s));
       HIP_TRY(launch_chunk_factors(rowpart, cfac, wspan, h->eta, h->clip_tau, lay, s));
-      HIP_TRY(launch_scale_vt_bf16((bf16_t *)VT, cfac, lay, s));
+      if (gram_e)
+        HIP_TRY(launch_gather_vt_bf16(ids, (const bf16_t *)E_tgt, vocab, (bf16_t *)VT, nullptr, cfac, lay, s));
+      else
+        HIP_TRY(launch_scale_vt_bf16((bf16_t *)VT, cfac, lay, s));
     }
     if (prof) HIP_TRY(hipEventRecord(h->ev[3], s));
     if (learn) {

@@ -202,8 +202,10 @@ int ttt_set_target_conv(ttt_handle *h, const void *conv_w, int K, const void *W_
  * state and in the outputs of later chunks alike. tau = 0 or +inf turns it
  * off (the default); tau < 0 or NaN returns TTT_E_ARG. The norm is taken from
  * the chunk Grams, ||V_i^T Z_i||_F^2 = sum_{s,t in chunk i} <v_s,v_t><z_s,z_t>,
- * in fp32. Applies to later ttt_forward_chunked calls; needs extra scratch
- * ([B][T][d] target rows in the handle's dtype plus small fp32 buffers).
+ * in fp32. Applies to later ttt_forward_chunked calls; needs extra scratch:
+ * small fp32 buffers, plus [B][T][d] target rows in the handle's dtype on an
+ * fp32 handle or with the general target (a bf16 handle with the plain
+ * target reads the rows from E_tgt through the ids when vocab*d*2 < 2^31).
  */
 int ttt_set_clip(ttt_handle *h, float tau);
 
@@ -212,7 +214,9 @@ int ttt_set_clip(ttt_handle *h, float tau);
  * recent ttt_forward_chunked, from HIP events recorded on its stream.
  * Phases: 0 target gather, 1 up/gate GEMM + SwiGLU, 2 clipping factors
  * (0 when clipping is off), 3 state update with snapshots, 4 within-group
- * scores, 5 output GEMM, 6 final-state copy.
+ * scores, 5 output GEMM, 6 final-state copy. With clipping on a bf16 handle
+ * and the plain target, the gather runs after the factors (it applies them)
+ * and counts in phase 2.
  * ttt_phase_times waits for the last event and writes `n` (<= 7)
  * milliseconds to ms[]; phases that did not run read 0.
  */
