@@ -950,32 +950,36 @@ __global__ __launch_bounds__(NT_W, 1) void k_out(OutArgs p) {
 
 // ---------------------------------------------------------------------------
 // Chunk Gram products for update clipping: ||V_i^T Z_i||_F^2 equals the sum of
-// (V_i V_i^T) * (Z_i Z_i^T) over the chunk's token pairs. For s-tile u (256
-// tokens) and t-tile w (128 tokens) of one sequence, G_Z = Z_s Z_t^T (K = f)
-// and G_V = V_s V_t^T (K = d) go into two sets of accumulators; the entries
-// with s and t in the same chunk contribute G_V * G_Z, summed per row s into
-// rowpart[b][u][wr][s % 256] (wr = w - first t-tile that can share a chunk
-// with the s-tile). Summing a chunk's rows over every wr gives its squared
-// norm; the sums run in a fixed order, so results are deterministic.
+// (V_i V_i^T) * (Z_i Z_i^T) over the chunk's token pairs. For s-tile u and
+// t-tile w (256 tokens each) of one sequence, G_V = V_s V_t^T (K = d) is formed
+// first and parked in a lane-private scratch (each lane later reads back only
+// what it wrote), then G_Z = Z_s Z_t^T (K = f) in the same accumulators; the
+// entries with s and t in the same chunk contribute G_V * G_Z, summed per row
+// s (first over t 0..127, then 128..255) into rowpart[b][u][wr][s % 256]
+// (wr = w - first t-tile that can share a chunk with the s-tile). Summing a
+// chunk's rows over every wr gives its squared norm; the sums run in a fixed
+// order, so results are deterministic.
 // GATHER: V's rows are read from the target table through the ids (V[p] =
 // E[ids[b][p+1]], zero for p >= T or an id outside [0, vocab)) instead of
 // from a row-major copy.
-// grid: B * (T_pad/256) * wspan workgroups of 256 threads
+// grid: B * (T_pad/256) * wspan workgroups of 512 threads
 struct GramArgs {
   const bf16_t *Z;     // [B][T_pad][f]
   const bf16_t *V;     // [B][T_pad][d], rows past T zero (without GATHER)
   const bf16_t *E;     // [vocab][d] (GATHER)
   const int32_t *ids;  // [B][T+1] (GATHER)
+  float *gv;           // scratch: 256 KB per workgroup of the grid
   float *rowpart;      // [B][T_pad/256][wspan][256]
   int T, T_pad, C, d, f, wspan, vocab;
 };
 
-constexpr int GR_P = 129;  // fp32 pitch of the [256][128] product tile in LDS (conflict-free row sums)
+constexpr int GR_P = 129;  // fp32 pitch of a [256][128] product tile in LDS (conflict-free row sums)
+constexpr int kSmemGram = cmax(kRingBytes, 256 * GR_P * 4);
 
 template <bool GATHER>
-__global__ __launch_bounds__(NT_U, 1) void k_chunk_gram(GramArgs p) {
-  __shared__ __attribute__((aligned(16))) Slab<WN_U, NBJ_U> ring[NSL_U];
-  static_assert(sizeof(ring) >= sizeof(float) * 256 * GR_P, "the product tile reuses the ring");
+__global__ __launch_bounds__(NT_W, 1) void k_chunk_gram(GramArgs p) {
+  __shared__ __attribute__((aligned(16))) char smem[kSmemGram];
+  Slab<WN_W, NBJ_W> *ring = reinterpret_cast<Slab<WN_W, NBJ_W> *>(smem);
   const int nu = p.T_pad / 256;
   const int id = xcd_tile(blockIdx.x, gridDim.x);  // the t-tiles of an s-tile share an XCD
   const int wr = id % p.wspan;
@@ -984,59 +988,97 @@ __global__ __launch_bounds__(NT_U, 1) void k_chunk_gram(GramArgs p) {
   const int s0 = u * 256;
   float *out = p.rowpart + (((long long)b * nu + u) * p.wspan + wr) * 256;
   const int s_last = (s0 + 255 < p.T - 1) ? s0 + 255 : p.T - 1;
-  const int w = (int)((long long)(s0 / p.C) * p.C / 128) + wr;
-  const long long w_end = (((long long)(s_last / p.C) + 1) * p.C - 1) / 128;
-  const int w_hi = (int)(w_end < p.T_pad / 128 - 1 ? w_end : p.T_pad / 128 - 1);
+  const int w = (int)((long long)(s0 / p.C) * p.C / 256) + wr;
+  const long long w_end = (((long long)(s_last / p.C) + 1) * p.C - 1) / 256;
+  const int w_hi = (int)(w_end < p.T_pad / 256 - 1 ? w_end : p.T_pad / 256 - 1);
   if (s0 >= p.T || w > w_hi) {  // no token pair of this tile shares a chunk
-    out[threadIdx.x] = 0.f;
+    if (threadIdx.x < 256) out[threadIdx.x] = 0.f;
     return;
   }
-  const int t0 = w * 128;
-  const bf16_t *Zb = p.Z + (long long)b * p.T_pad * p.f;
-  const bf16_t *Vb = GATHER ? nullptr : p.V + (long long)b * p.T_pad * p.d;
-  Acc<NBJ_U> az, av;
-  acc_zero(az);
-  acc_zero(av);
-  const int wg = wave_id(), lg = threadIdx.x & 63;
-  {
-    SlabLoads<RmLoad<BM, 2 * WN_U>, RmLoad<32 * WN_U * NBJ_U, 2 * WN_U>> ld;
-    ld.a.init(Zb + (long long)s0 * p.f, p.f, p.T_pad - s0, p.f, wg, lg);
-    ld.b.init(Zb + (long long)t0 * p.f, p.f, p.T_pad - t0, p.f, wg, lg);
-    gemm_k<WN_U, NBJ_U, NSL_U, false>(az, ring, ld, p.f / BK);
-  }
-  __syncthreads();  // the second pass refills the ring
-  if constexpr (GATHER) {
-    SlabLoads<RmGather<BM, 2 * WN_U>, RmGather<32 * WN_U * NBJ_U, 2 * WN_U>> ld;
-    const int32_t *tg = p.ids + (long long)b * (p.T + 1) + 1;  // target id of slot p at tg[p]
-    ld.a.init(p.E, p.d, p.vocab, tg + s0, p.T - s0, wg, lg);
-    ld.b.init(p.E, p.d, p.vocab, tg + t0, p.T - t0, wg, lg);
-    gemm_k<WN_U, NBJ_U, NSL_U, false>(av, ring, ld, p.d / BK);
-  } else {
-    SlabLoads<RmLoad<BM, 2 * WN_U>, RmLoad<32 * WN_U * NBJ_U, 2 * WN_U>> ld;
-    ld.a.init(Vb + (long long)s0 * p.d, p.d, p.T_pad - s0, p.d, wg, lg);
-    ld.b.init(Vb + (long long)t0 * p.d, p.d, p.T_pad - t0, p.d, wg, lg);
-    gemm_k<WN_U, NBJ_U, NSL_U, false>(av, ring, ld, p.d / BK);
-  }
-  __syncthreads();  // the product tile reuses the ring
-  float *tile = reinterpret_cast<float *>(ring);
+  const int t0 = w * 256;
   const int lane = threadIdx.x & 63, wv = wave_id(), wm = wv & 1, wn = wv >> 1;
-#pragma unroll
-  for (int bj = 0; bj < NBJ_U; ++bj) {
-    const int tl = wn * 32 * NBJ_U + bj * 32 + (lane & 31);
-    const int ct = (t0 + tl) / p.C;
-#pragma unroll
-    for (int bi = 0; bi < 4; ++bi)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int sl = wm * 128 + bi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const bool same = (s0 + sl) / p.C == ct;
-        tile[sl * GR_P + tl] = same ? az.v[bi][bj][r] * av.v[bi][bj][r] : 0.f;
-      }
+  Acc<NBJ_W> acc;
+  acc_zero(acc);
+  if constexpr (GATHER) {
+    SlabLoads<RmGather<BM, 2 * WN_W>, RmGather<BM, 2 * WN_W>> ld;
+    const int32_t *tg = p.ids + (long long)b * (p.T + 1) + 1;  // target id of slot p at tg[p]
+    ld.a.init(p.E, p.d, p.vocab, tg + s0, p.T - s0, wv, lane);
+    ld.b.init(p.E, p.d, p.vocab, tg + t0, p.T - t0, wv, lane);
+    gemm_k<WN_W, NBJ_W, NSL_W, false>(acc, ring, ld, p.d / BK);
+  } else {
+    const bf16_t *Vb = p.V + (long long)b * p.T_pad * p.d;
+    SlabLoads<RmW, RmW> ld;
+    ld.a.init(Vb + (long long)s0 * p.d, p.d, p.T_pad - s0, p.d, wv, lane);
+    ld.b.init(Vb + (long long)t0 * p.d, p.d, p.T_pad - t0, p.d, wv, lane);
+    gemm_k<WN_W, NBJ_W, NSL_W, false>(acc, ring, ld, p.d / BK);
   }
-  __syncthreads();
+  // G_V to this lane's scratch: register group k (4 registers) at [k][lane]
+  float4 *gv = reinterpret_cast<float4 *>(p.gv) + ((long long)id * 8 + wv) * (32 * 64) + lane;
+#pragma unroll
+  for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < NBJ_W; ++bj)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        gv[((bi * NBJ_W + bj) * 4 + q) * 64] = make_float4(acc.v[bi][bj][4 * q], acc.v[bi][bj][4 * q + 1],
+                                                           acc.v[bi][bj][4 * q + 2], acc.v[bi][bj][4 * q + 3]);
+  __syncthreads();  // the second pass refills the ring
+  acc_zero(acc);
+  {
+    const bf16_t *Zb = p.Z + (long long)b * p.T_pad * p.f;
+    SlabLoads<RmW, RmW> ld;
+    ld.a.init(Zb + (long long)s0 * p.f, p.f, p.T_pad - s0, p.f, wv, lane);
+    ld.b.init(Zb + (long long)t0 * p.f, p.f, p.T_pad - t0, p.f, wv, lane);
+    gemm_k<WN_W, NBJ_W, NSL_W, false>(acc, ring, ld, p.f / BK);
+  }
+  // products of same-chunk pairs, in place of G_Z: row s0 + sl shares column
+  // t's chunk when lo <= sl < lo + C (lo: the chunk's start less s0); one
+  // 16-register group at a time, so few reloaded values are live at once
+#pragma unroll
+  for (int bj = 0; bj < NBJ_W; ++bj) {
+    const int lo = (t0 + wn * WC_W + bj * 32 + (lane & 31)) / p.C * p.C - s0;
+#pragma unroll
+    for (int bi = 0; bi < 4; ++bi) {
+      pin();
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 g = gv[((bi * NBJ_W + bj) * 4 + q) * 64];
+        const float gq[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int sl = wm * 128 + bi * 32 + 8 * q + 4 * (lane >> 5) + r;
+          const float e = acc.v[bi][bj][4 * q + r];
+          acc.v[bi][bj][4 * q + r] = (sl >= lo && sl < lo + p.C) ? e * gq[r] : 0.f;
+        }
+      }
+    }
+  }
+  pin();
+  // row sums through LDS, one 128-column half at a time
+  float *tile = reinterpret_cast<float *>(smem);
   float sum = 0.f;
-  for (int t = 0; t < 128; ++t) sum += tile[threadIdx.x * GR_P + t];
-  out[threadIdx.x] = sum;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    __syncthreads();  // the ring, or the first half's tile, is no longer read
+    if ((wn >> 1) == half) {
+#pragma unroll
+      for (int bj = 0; bj < NBJ_W; ++bj) {
+        const int tl = (wn & 1) * WC_W + bj * 32 + (lane & 31);
+#pragma unroll
+        for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            tile[(wm * 128 + bi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * GR_P + tl] = acc.v[bi][bj][r];
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x < 256) {
+      float part = 0.f;
+      for (int t = 0; t < 128; ++t) part += tile[threadIdx.x * GR_P + t];
+      sum = half == 0 ? part : sum + part;
+    }
+  }
+  if (threadIdx.x < 256) out[threadIdx.x] = sum;
 }
 
 // ---------------------------------------------------------------------------
@@ -1095,15 +1137,15 @@ hipError_t launch_gather_vt_bf16(const int32_t *ids, const bf16_t *E, int vocab,
 }
 
 hipError_t launch_chunk_gram_bf16(const bf16_t *Z, const bf16_t *Vrow, const bf16_t *E, const int32_t *ids, int vocab,
-                                  float *rowpart, int wspan, const Layout &lay, hipStream_t s) {
+                                  float *gv, float *rowpart, int wspan, const Layout &lay, hipStream_t s) {
   const long long n = (long long)lay.B * (lay.T_pad / 256) * wspan;
-  if (n >= (1LL << 31)) return hipErrorInvalidConfiguration;
+  if (n >= (1LL << 31) / 8) return hipErrorInvalidConfiguration;
   if (!Vrow && (long long)vocab * lay.d * 2 >= (1LL << 31)) return hipErrorInvalidValue;
-  GramArgs p{Z, Vrow, E, ids, rowpart, lay.T, lay.T_pad, lay.C, lay.d, lay.f, wspan, vocab};
+  GramArgs p{Z, Vrow, E, ids, gv, rowpart, lay.T, lay.T_pad, lay.C, lay.d, lay.f, wspan, vocab};
   if (Vrow)
-    hipLaunchKernelGGL(k_chunk_gram<false>, dim3((unsigned)n), dim3(NT_U), 0, s, p);
+    hipLaunchKernelGGL(k_chunk_gram<false>, dim3((unsigned)n), dim3(NT_W), 0, s, p);
   else
-    hipLaunchKernelGGL(k_chunk_gram<true>, dim3((unsigned)n), dim3(NT_U), 0, s, p);
+    hipLaunchKernelGGL(k_chunk_gram<true>, dim3((unsigned)n), dim3(NT_W), 0, s, p);
   return hipGetLastError();
 }
 

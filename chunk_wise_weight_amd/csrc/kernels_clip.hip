@@ -112,22 +112,26 @@ unsigned grid_for(long long n) {
 
 }  // namespace
 
-// The most 128-token t-tiles that hold a token sharing a chunk with some token
+// The most 256-token t-tiles that hold a token sharing a chunk with some token
 // of one 256-token s-tile, over the s-tiles of the stream: the bf16 Gram
 // kernel's t-tiles per s-tile, so its grid has no slot without work when every
 // s-tile needs as many (chunk sizes dividing 256, or multiples of it).
 int clip_wspan(const Layout &lay, bool bf16) {
   if (!bf16) return 1;
-  const long long C = lay.C, T = lay.T, nw = lay.T_pad / 128;
+  const long long C = lay.C, T = lay.T, nw = lay.T_pad / 256;
   long long best = 1;
   for (long long s0 = 0; s0 < T; s0 += 256) {
     const long long s_last = s0 + 255 < T - 1 ? s0 + 255 : T - 1;
-    const long long w_lo = (s0 / C) * C / 128;
-    long long w_hi = ((s_last / C + 1) * C - 1) / 128;
+    const long long w_lo = (s0 / C) * C / 256;
+    long long w_hi = ((s_last / C + 1) * C - 1) / 256;
     if (w_hi > nw - 1) w_hi = nw - 1;
     if (w_hi - w_lo + 1 > best) best = w_hi - w_lo + 1;
   }
   return (int)best;
+}
+
+size_t clip_gram_scratch_bytes(const Layout &lay, int wspan) {
+  return (size_t)lay.B * (lay.T_pad / 256) * wspan * (256 * 256 * 4);
 }
 
 int clip_chunks(const Layout &lay) { return (int)((lay.T + (long long)lay.C - 1) / lay.C); }

@@ -26,8 +26,9 @@ hipError_t launch_out_bf16(const bf16_t *Z, const bf16_t *P, const bf16_t *snap,
                            const Layout &lay, hipStream_t s);
 // Per-row chunk Gram sums for clipping: rowpart [B][T_pad/256][wspan][256] fp32. V's rows come from
 // Vrow [B][T_pad][d] or, with Vrow null, from E [vocab][d] through ids [B][T+1] (vocab*d*2 < 2^31).
+// gv: scratch of clip_gram_scratch_bytes(lay, wspan) bytes.
 hipError_t launch_chunk_gram_bf16(const bf16_t *Z, const bf16_t *Vrow, const bf16_t *E, const int32_t *ids, int vocab,
-                                  float *rowpart, int wspan, const Layout &lay, hipStream_t s);
+                                  float *gv, float *rowpart, int wspan, const Layout &lay, hipStream_t s);
 
 // ---- fp32 path: FMA kernels (kernels_f32.hip), same buffers and meaning in fp32 ----
 hipError_t launch_gather_vt_f32(const int32_t *ids, const float *E, int vocab, float *VT, float *Vrow,
@@ -44,6 +45,8 @@ hipError_t launch_out_f32(const float *Z, const float *P, const float *snap, con
 // ---- update clipping (kernels_clip.hip) ----
 // t-tiles per s-tile in rowpart (1 on the fp32 path) and chunks per sequence of a call.
 int clip_wspan(const Layout &lay, bool bf16);
+// bytes of the bf16 Gram kernel's scratch: 256 KB per workgroup of its grid
+size_t clip_gram_scratch_bytes(const Layout &lay, int wspan);
 int clip_chunks(const Layout &lay);
 // fp32 path: rowpart [B][T_pad] (wspan 1).
 hipError_t launch_chunk_gram_f32(const float *Z, const float *Vrow, float *rowpart, const Layout &lay, hipStream_t s);

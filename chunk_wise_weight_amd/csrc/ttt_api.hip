@@ -168,7 +168,7 @@ void free_handle(ttt_handle *h) {
 }
 
 struct Scratch {
-  void *VT, *Z, *ZT, *snap, *P, *Vrow, *rowpart, *cfac, *U;
+  void *VT, *Z, *ZT, *snap, *P, *Vrow, *rowpart, *cfac, *U, *gv;
   size_t total;
 };
 
@@ -189,6 +189,8 @@ Scratch scratch_layout(const ttt_handle *h, int B, const Plan &pl, bool need_zt,
   const size_t rp = clip ? align256(4 * (size_t)B * (pl.T_pad / 256) * wspan * 256) : 0;
   const size_t cf = clip ? align256(4 * (size_t)B * ((pl.T_pad + pl.C - 1) / pl.C)) : 0;
   const size_t uu = conv ? align256(es * (size_t)B * pl.T_pad * h->d) : 0;
+  Layout lay{B, 0, pl.T_pad, pl.C, pl.L, pl.ngroups, h->d, h->f, 0};
+  const size_t gvb = clip && h->dt == TTT_BF16 ? align256(clip_gram_scratch_bytes(lay, wspan)) : 0;
   Scratch s;
   size_t off = 0;
   s.VT = (void *)off;
@@ -209,6 +211,8 @@ Scratch scratch_layout(const ttt_handle *h, int B, const Plan &pl, bool need_zt,
   off += cf;
   s.U = (void *)off;
   off += uu;
+  s.gv = (void *)off;
+  off += gvb;
   s.total = off;
   return s;
 }
@@ -275,6 +279,7 @@ int forward_impl(ttt_handle *h, const void *x, const int32_t *ids, const void *E
        *P = at(h->ws, sc.P);
   void *Vrow = clip && !gram_e ? at(h->ws, sc.Vrow) : nullptr;
   float *rowpart = (float *)at(h->ws, sc.rowpart), *cfac = (float *)at(h->ws, sc.cfac);
+  float *gv = (float *)at(h->ws, sc.gv);
   void *U = at(h->ws, sc.U);
 
   if (h->dt == TTT_BF16) {
@@ -289,8 +294,8 @@ int forward_impl(ttt_handle *h, const void *x, const int32_t *ids, const void *E
                            learn ? 1 : 0, lay, s));
     if (prof) HIP_TRY(hipEventRecord(h->ev[2], s));
     if (clip) {
-      HIP_TRY(launch_chunk_gram_bf16((const bf16_t *)Z, (const bf16_t *)Vrow, (const bf16_t *)E_tgt, ids, vocab, rowpart,
-                                     wspan, lay, s));
+      HIP_TRY(launch_chunk_gram_bf16((const bf16_t *)Z, (const bf16_t *)Vrow, (const bf16_t *)E_tgt, ids, vocab, gv,
+                                     rowpart, wspan, lay, s));
       HIP_TRY(launch_chunk_factors(rowpart, cfac, wspan, h->eta, h->clip_tau, lay, s));
       if (gram_e)
         HIP_TRY(launch_gather_vt_bf16(ids, (const bf16_t *)E_tgt, vocab, (bf16_t *)VT, nullptr, cfac, lay, s));
