@@ -21,9 +21,10 @@
 //
 // Operands are row-major (element (r, k) at r*ld + k), K-blocked by 64
 // (element (r, k) at (k/64)*kblk + r*64 + k%64), or held in planes of 8
-// columns (element (r, k) at (k/8)*pstride + r*8 + k%8). V^T is K-blocked, so
-// one slab is one contiguous block instead of rows strided by the whole stream
-// length. eta*Z^T and the snapshots are planes: the MFMA register layout holds
+// columns (element (r, k) at (k/8)*pstride + r*8 + k%8). V^T and Z are
+// K-blocked (Z's blocks hold every token slot, [f/64][T_pad][64]), so one slab
+// of a tile is one contiguous block instead of rows strided by the whole
+// stream length or by f. eta*Z^T and the snapshots are planes: the MFMA register layout holds
 // four consecutive k of one row per lane, so a store instruction of 32 rows x
 // 16 bytes is 512 contiguous bytes in a plane (in row-major or K-blocked form
 // it would touch 32 lines); a plane slab loads as 1 KB contiguous pieces into
@@ -126,6 +127,42 @@ struct RmLoad {
     }
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(tile + (w * WR + 8 * n) * SK), 16, v, sl * SK * 2, 0,
                                              0);
+  }
+};
+
+// Column-blocked operand [K/64][rows][64]: element (r, k) at
+// base[(k/64)*kblk + r*64 + k%64], base at the tile's first row in block 0.
+// Each slab is one contiguous block of 128-byte rows; its descriptor starts at
+// the slab's block and ends after nrows rows, so rows r >= nrows read zero
+// (the row offset is in the lane offset, which the range check covers).
+template <int ROWS, int NW>
+struct CbLoad {
+  static constexpr int WR = ROWS / NW, N = WR / 8;
+  const bf16_t *base;
+  long long kblk;
+  int bytes;
+  // a fixed bound: with vo[N] here, the host pass of hipcc rejects SlabLoads<PlLoad, CbLoad>
+  uint32_t vo[8];
+  static_assert(N <= 8, "lane offsets per wave");
+  __device__ __forceinline__ void init(const bf16_t *base_, long long kblk_, int nrows, int w, int lane) {
+    base = base_;
+    kblk = kblk_;
+    const long long by = (long long)(nrows > 0 ? nrows : 0) * 128;
+    bytes = (int)(by < 0x7fffffffLL ? by : 0x7fffffffLL);
+    const int lr = lane >> 3;
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      const int row = w * WR + 8 * n + lr;
+      vo[n] = (uint32_t)(row * 128 + (((lane & 7) ^ swz(row)) << 4));
+    }
+  }
+  using Pre = __amdgpu_buffer_rsrc_t;
+  __device__ __forceinline__ Pre prep(int sl) const {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t *>(base + (long long)sl * kblk), (short)0, bytes,
+                                             kBufferFlags);
+  }
+  __device__ __forceinline__ void issue(const Pre &rs, bf16_t *tile, int, int w, int, int n) const {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(tile + (w * WR + 8 * n) * SK), 16, vo[n], 0, 0, 0);
   }
 };
 
@@ -495,10 +532,11 @@ __device__ __forceinline__ void gemm_k(Acc<NBJ> &acc, Slab<WN, NBJ> *ring, const
 
 // The wide GEMMs' loaders: 8 waves, 256 x 256 tiles.
 using RmW = RmLoad<BM, 2 * WN_W>;
+using CbW = CbLoad<BM, 2 * WN_W>;
 
 // ---------------------------------------------------------------------------
 // Up/gate GEMM with SwiGLU epilogue. i = token slot, j = interleaved W_ug row.
-// Writes Z [B][T_pad][f] (row-major) and eta*Z^T in planes of 8 tokens [B][T_pad/8][f][8].
+// Writes Z column-blocked [B][f/64][T_pad][64] and eta*Z^T in planes of 8 tokens [B][T_pad/8][f][8].
 // grid: nx * ny workgroups, nx = 2f/256, ny = B*T_pad/256
 struct A1Args {
   const bf16_t *x;
@@ -544,9 +582,9 @@ __global__ __launch_bounds__(NT_W, 1) void k_a1(A1Args p) {
         if (p.write_zt)
           store_nt(ZTb + ((long long)(pos >> 3) * p.f + feat) * 8 + (pos & 7), pack_bf16x2(p.eta * z[0], p.eta * z[1]),
                    pack_bf16x2(p.eta * z[2], p.eta * z[3]));
-        bf16_t *zrow = p.Z + ((long long)b * p.T_pad + pos) * p.f + feat;
+        bf16_t *zrow = p.Z + (((long long)b * (p.f / 64) + feat / 64) * p.T_pad + pos) * 64 + feat % 64;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) store_nt(zrow + (long long)r * p.f, f32_to_bf16(z[r]));
+        for (int r = 0; r < 4; ++r) store_nt(zrow + r * 64, f32_to_bf16(z[r]));
       }
     }
   }
@@ -815,10 +853,11 @@ __global__ __launch_bounds__(NT_W, 1) void k_scores(ScoreArgs p) {
   // masked; the output GEMM never reads it (it stops before that chunk).
   const int jl = (j0 + 255 < Lg - 1) ? j0 + 255 : Lg - 1;
   if (i0 / p.C >= jl / p.C) return;
-  const bf16_t *Zg = p.Z + ((long long)b * p.T_pad + gs) * p.f;
-  SlabLoads<RmW, RmW> ld;
-  ld.a.init(Zg + (long long)i0 * p.f, p.f, (int)(p.T_pad - gs - i0), p.f, wave_id(), threadIdx.x & 63);
-  ld.b.init(Zg + (long long)j0 * p.f, p.f, (int)(p.T_pad - gs - j0), p.f, wave_id(), threadIdx.x & 63);
+  const bf16_t *Zg = p.Z + ((long long)b * (p.f / 64) * p.T_pad + gs) * 64;  // Z column-blocked [f/64][T_pad][64]
+  const long long zblk = (long long)p.T_pad * 64;
+  SlabLoads<CbW, CbW> ld;
+  ld.a.init(Zg + (long long)i0 * 64, zblk, (int)(p.T_pad - gs - i0), wave_id(), threadIdx.x & 63);
+  ld.b.init(Zg + (long long)j0 * 64, zblk, (int)(p.T_pad - gs - j0), wave_id(), threadIdx.x & 63);
   Acc<NBJ_W> acc;
   acc_zero(acc);
   gemm_k<WN_W, NBJ_W, NSL_W, false>(acc, ring, ld, p.f / BK);
@@ -896,9 +935,10 @@ __global__ __launch_bounds__(NT_W, 1) void k_out(OutArgs p) {
   Acc<NBJ_W> acc;
   acc_zero(acc);
   {  // segment 1: the group's snapshot ([f/8][d][8] planes) against Z, K = f
-    SlabLoads<PlLoad<2 * WN_W>, RmW> ld;
+    SlabLoads<PlLoad<2 * WN_W>, CbW> ld;
     ld.a.init(p.snap + ((long long)b * p.ngroups + g) * p.d * p.f + (long long)i0 * 8, (long long)p.d * 8, l8);
-    ld.b.init(p.Z + ((long long)b * p.T_pad + gs + j0) * p.f, p.f, (int)(p.T_pad - gs - j0), p.f, w8, l8);
+    ld.b.init(p.Z + ((long long)b * (p.f / 64) * p.T_pad + gs + j0) * 64, (long long)p.T_pad * 64,
+              (int)(p.T_pad - gs - j0), w8, l8);
     gemm_k<WN_W, NBJ_W, NSL_W, true>(acc, ring, ld, p.f / BK);
   }
   if (p.intra) {  // segment 2: V^T against P over the tokens before the last row's chunk
@@ -964,7 +1004,7 @@ __global__ __launch_bounds__(NT_W, 1) void k_out(OutArgs p) {
 // from a row-major copy.
 // grid: B * (T_pad/256) * wspan workgroups of 512 threads
 struct GramArgs {
-  const bf16_t *Z;     // [B][T_pad][f]
+  const bf16_t *Z;     // column-blocked [B][f/64][T_pad][64]
   const bf16_t *V;     // [B][T_pad][d], rows past T zero (without GATHER)
   const bf16_t *E;     // [vocab][d] (GATHER)
   const int32_t *ids;  // [B][T+1] (GATHER)
@@ -1025,10 +1065,10 @@ __global__ __launch_bounds__(NT_W, 1) void k_chunk_gram(GramArgs p) {
   __syncthreads();  // the second pass refills the ring
   acc_zero(acc);
   {
-    const bf16_t *Zb = p.Z + (long long)b * p.T_pad * p.f;
-    SlabLoads<RmW, RmW> ld;
-    ld.a.init(Zb + (long long)s0 * p.f, p.f, p.T_pad - s0, p.f, wv, lane);
-    ld.b.init(Zb + (long long)t0 * p.f, p.f, p.T_pad - t0, p.f, wv, lane);
+    const bf16_t *Zb = p.Z + (long long)b * (p.f / 64) * p.T_pad * 64;  // Z column-blocked [f/64][T_pad][64]
+    SlabLoads<CbW, CbW> ld;
+    ld.a.init(Zb + (long long)s0 * 64, (long long)p.T_pad * 64, p.T_pad - s0, wv, lane);
+    ld.b.init(Zb + (long long)t0 * 64, (long long)p.T_pad * 64, p.T_pad - t0, wv, lane);
     gemm_k<WN_W, NBJ_W, NSL_W, false>(acc, ring, ld, p.f / BK);
   }
   // products of same-chunk pairs, in place of G_Z: row s0 + sl shares column

@@ -9,7 +9,8 @@
 // [B][ceil(T/C)]; slot p is scaled by cfac[b][p/C].
 hipError_t launch_gather_vt_bf16(const int32_t *ids, const bf16_t *E, int vocab, bf16_t *VT, bf16_t *Vrow,
                                  const float *cfac, const Layout &lay, hipStream_t s);
-// Z = SiLU(x W_gate^T) * (x W_up^T) -> Z [B][T_pad][f] and ZT = eta*Z^T in planes of 8 tokens [B][T_pad/8][f][8].
+// Z = SiLU(x W_gate^T) * (x W_up^T) -> Z column-blocked [B][f/64][T_pad][64] (bf16 path) and ZT = eta*Z^T in
+// planes of 8 tokens [B][T_pad/8][f][8].
 // Wug: [2f][d], rows interleaved in blocks of 32 (32 up rows, then the matching 32 gate rows).
 hipError_t launch_a1_bf16(const bf16_t *x, const bf16_t *Wug, bf16_t *Z, bf16_t *ZT, float eta, int write_zt,
                           const Layout &lay, hipStream_t s);
