@@ -557,9 +557,9 @@ __global__ __launch_bounds__(NT_W, 1) void k_a1(A1Args p) {
   const int m0 = ty * BM;
   const int b = m0 / p.T_pad;
   const int pos0 = m0 - b * p.T_pad;
-  SlabLoads<RmW, RmW> ld;
+  SlabLoads<RmW, CbW> ld;
   ld.a.init(p.x + ((long long)b * p.T + pos0) * p.d, p.d, p.T - pos0, p.d, wave_id(), threadIdx.x & 63);
-  ld.b.init(p.Wug + (long long)n0 * p.d, p.d, 2 * p.f - n0, p.d, wave_id(), threadIdx.x & 63);
+  ld.b.init(p.Wug + (long long)n0 * 64, 2LL * p.f * 64, 2 * p.f - n0, wave_id(), threadIdx.x & 63);
   Acc<NBJ_W> acc;
   acc_zero(acc);
   gemm_k<WN_W, NBJ_W, NSL_W, false>(acc, ring, ld, p.d / BK);

@@ -8,9 +8,9 @@ __global__ __launch_bounds__(256) void k_interleave_ug(const bf16_t *Wu, const b
   const int r = blockIdx.x;
   const int blk = r >> 6, w = r & 63;
   const bf16_t *src = (w < 32 ? Wu : Wg) + (long long)(blk * 32 + (w & 31)) * d;
-  bf16_t *dst = Wug + (long long)r * d;
   for (int c = threadIdx.x * 8; c < d; c += 256 * 8)
-    *reinterpret_cast<uint4 *>(dst + c) = *reinterpret_cast<const uint4 *>(src + c);
+    *reinterpret_cast<uint4 *>(Wug + ((long long)(c / 64) * 2 * f + r) * 64 + c % 64) =
+        *reinterpret_cast<const uint4 *>(src + c);
 }
 
 __global__ __launch_bounds__(256) void k_bf16_to_f32(const bf16_t *src, float *dst, long long n) {

@@ -11,7 +11,8 @@ hipError_t launch_gather_vt_bf16(const int32_t *ids, const bf16_t *E, int vocab,
                                  const float *cfac, const Layout &lay, hipStream_t s);
 // Z = SiLU(x W_gate^T) * (x W_up^T) -> Z column-blocked [B][f/64][T_pad][64] (bf16 path) and ZT = eta*Z^T in
 // planes of 8 tokens [B][T_pad/8][f][8].
-// Wug: [2f][d], rows interleaved in blocks of 32 (32 up rows, then the matching 32 gate rows).
+// Wug: 2f rows of d, interleaved in blocks of 32 (32 up rows, then the matching 32 gate rows), held K-blocked
+// by 64 columns: [d/64][2f][64].
 hipError_t launch_a1_bf16(const bf16_t *x, const bf16_t *Wug, bf16_t *Z, bf16_t *ZT, float eta, int write_zt,
                           const Layout &lay, hipStream_t s);
 // state[b] += sum_p ZT[b][:, p] VT[b][:, p]^T (as W[a][b] layout), snapshots snap[b][g] = bf16(state at p = g*L).
@@ -74,6 +75,7 @@ hipError_t launch_transpose_bf16(const bf16_t *src, bf16_t *dst, int n, hipStrea
 hipError_t launch_copy_f32(const float *src, float *dst, long long n, hipStream_t s);
 
 // ---- layout helpers (kernels_misc.hip) ----
-// Wug[2f][d] from W_up[f][d], W_gate[f][d]: 32-row blocks, up block then gate block.
+// Wug (2f rows of d, K-blocked [d/64][2f][64]) from W_up[f][d], W_gate[f][d]: 32-row blocks, up block then gate
+// block.
 hipError_t launch_interleave_ug_bf16(const bf16_t *Wu, const bf16_t *Wg, bf16_t *Wug, int f, int d, hipStream_t s);
 hipError_t launch_bf16_to_f32(const bf16_t *src, float *dst, long long n, hipStream_t s);

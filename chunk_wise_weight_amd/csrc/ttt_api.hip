@@ -128,7 +128,7 @@ struct ttt_handle {
   float *conv_w = nullptr;  // [K][d] fp32 tap weights
   void *Wt = nullptr;       // bf16: W_target^T [d][d]; f32: W_target [d][d]
   ttt_dtype dt = TTT_BF16;
-  void *Wug = nullptr;      // bf16: [2f][d] interleaved; f32: [2][f][d]
+  void *Wug = nullptr;      // bf16: [d/64][2f][64] (rows interleaved); f32: [2][f][d]
   float *W0 = nullptr;      // [d][f] fp32 image of W_down0
   float *state = nullptr;   // [max_batch][d][f]
   void *ws = nullptr;       // scratch
