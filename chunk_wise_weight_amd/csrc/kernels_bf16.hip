@@ -657,33 +657,45 @@ __global__ __launch_bounds__(NT_W, 1) void k_target_gemm(TgtArgs p) {
 // of them (one per CU) run on the 8-wave configuration; a last partial round
 // of at most 128 tiles is split into 256 x 128 halves that run as one round
 // on the 4-wave configuration, so no CU idles for a whole round.
-// Tile loads of the update's whole rounds (8 waves, 256 x 256 tiles) with an
-// L2 prefetch. Every eta Z^T tile is read by one XCD only, so its slabs come
-// from HBM, one slab ahead of use without the prefetch. The workgroups that
-// share an operand tile split its prefetch: the 8 along a band of the tile
-// order take plane pa = ty % 8 of an eta Z^T slab (8 planes of 32 lines of
-// 128 bytes), the 4 along x take row quarter qb = tx % 4 of a V^T slab (256
-// rows of one line). Waves 0-3 touch 8 lines of the plane each, waves 4-7 16
-// lines of the quarter, with one 4-byte DMA per wave into a 256-byte LDS sink
-// that nothing reads. (In the half-tile round an eta Z^T tile has as few as 4
-// sharers, and the prefetch measured slower there.)
-struct UpdLoads : SlabLoads<PlLoad<8>, KbLoad<256, 8>> {
+// Tile loads of the update with an L2 prefetch. Every eta Z^T tile is read by
+// one XCD only, so its slabs come from HBM, one slab (two in the half-tile
+// round) ahead of use without the prefetch. The workgroups that share an
+// operand tile split its prefetch: the sa tiles (and halves) of a band of the
+// tile order split the 256 lines of 128 bytes of an eta Z^T slab (8 planes of
+// 32 lines), the sb tiles along x of an XCD's range split the BN rows (one
+// line each) of a V^T slab. Waves 0 .. WN-1 touch the first share, waves WN ..
+// 2WN-1 the second, each with one 4-byte DMA into a 256-byte LDS sink that
+// nothing reads; each lane's offset within the slab is fixed at the start.
+template <int WN, int BN>
+struct UpdLoads : SlabLoads<PlLoad<2 * WN>, KbLoad<BN, 2 * WN>> {
   static constexpr bool kPf = true;
   uint32_t *sink;
-  int pa, qb;
-  __device__ __forceinline__ void prefetch(int sl, int w, int lane) const {
-    __amdgpu_buffer_rsrc_t rs;
-    uint32_t vo;
-    if (w < 4) {
-      rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t *>(a.base + ((long long)sl * 8 + pa) * a.pstride),
-                                             (short)0, 0x7fffffff, kBufferFlags);
-      vo = (uint32_t)((8 * w + (lane & 7)) * 128);
+  uint32_t vp;  // this lane's byte offset in the slab (A: plane and line, B: row)
+  // sharer ka of sa takes lines [ka*256/sa, (ka+1)*256/sa) of the eta Z^T slab;
+  // sharer kb of sb takes rows [kb*BN/sb, (kb+1)*BN/sb) of the V^T slab
+  __device__ __forceinline__ void init_pf(uint32_t *sink_, int sa, int ka, int sb, int kb, int w, int lane) {
+    sink = sink_;
+    if (w < WN) {
+      const int lo = ka * 256 / sa, n = (ka + 1) * 256 / sa - lo;
+      const int per = (n + WN - 1) / WN < 64 ? (n + WN - 1) / WN : 64;
+      int line = lo + w * per + lane % per;
+      if (line > lo + n - 1) line = lo + n - 1;
+      vp = (uint32_t)((line >> 5) * this->a.pstride * 2 + (line & 31) * 128);
     } else {
-      rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t *>(b.base + (long long)sl * b.kblk), (short)0,
-                                             0x7fffffff, kBufferFlags);
-      vo = (uint32_t)((64 * qb + 16 * (w - 4) + (lane & 15)) * 128);
+      const int lo = kb * BN / sb, n = (kb + 1) * BN / sb - lo;
+      const int per = (n + WN - 1) / WN < 64 ? (n + WN - 1) / WN : 64;
+      int row = lo + (w - WN) * per + lane % per;
+      if (row > lo + n - 1) row = lo + n - 1;
+      vp = (uint32_t)(row * 128);
     }
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)sink, 4, vo, 0, 0, 0);
+  }
+  __device__ __forceinline__ void prefetch(int sl, int w, int lane) const {
+    const __amdgpu_buffer_rsrc_t rs =
+        w < WN ? __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t *>(this->a.base + (long long)sl * 8 * this->a.pstride),
+                                                   (short)0, 0x7fffffff, kBufferFlags)
+               : __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t *>(this->b.base + (long long)sl * this->b.kblk),
+                                                   (short)0, 0x7fffffff, kBufferFlags);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)sink, 4, vp, 0, 0, 0);
   }
 };
 
@@ -771,14 +783,16 @@ __global__ __launch_bounds__(128 * WN, 1) void k_update(UpdArgs p) {
   }
 
   // A: eta Z^T in planes of 8 tokens [T_pad/8][f][8]; B: V^T K-blocked [T_pad/64][d][64]
-  std::conditional_t<WN == 4, UpdLoads, SlabLoads<PlLoad<2 * WN>, KbLoad<BN, 2 * WN>>> ld;
-  if constexpr (WN == 4) {
-    ld.sink = lds.sink;
-    ld.pa = ty & 7;
-    ld.qb = tx & 3;
-  }
+  UpdLoads<WN, BN> ld;
   ld.a.init(p.ZT + (long long)b * p.f * p.T_pad + (long long)i0 * 8, (long long)p.f * 8, lane);
   ld.b.init(p.VT + (long long)b * p.d * p.T_pad + (long long)j0 * 64, (long long)p.d * 64, w, lane);
+  {
+    // eta Z^T tile tx is shared by the tiles of its band (h of them) and their halves;
+    // a V^T tile (or half) by the tiles along x of the XCD's range
+    const int full = ny / 8, band = ty / 8, h = band < full ? 8 : ny - full * 8;
+    const int halves = 256 / BN, half = n % halves;
+    ld.init_pf(lds.sink, h * halves, (ty - band * 8) * halves + half, 16 / WN, tx % (16 / WN), w, lane);
+  }
   const int nk = p.kend / BK;
   // Snapshot 0 is the entry state; group starts are multiples of the stage
   // depth, so snapshot g is written right after the last stage of group g-1,
