@@ -3,9 +3,10 @@
 // Every contraction is written as D[i][j] = sum_k A[i][k] * B[j][k] with both
 // operands K-contiguous ("NT" form). A block has 2 x WN waves; each wave
 // computes 128 x (32*NBJ) with v_mfma_f32_32x32x16_bf16 and fp32 accumulators
-// in AGPRs. The wide GEMMs use 8 waves (WN = 4, NBJ = 2: 256 x 256 tiles, two
-// waves per SIMD so one can issue MFMAs while the other waits); the state
-// update uses 4 waves (WN = 2, NBJ = 2: 256 x 128 tiles).
+// in AGPRs. Every GEMM uses 8 waves (WN = 4, NBJ = 2: 256 x 256 tiles, two
+// waves per SIMD so one can issue MFMAs while the other waits), except the
+// last, partial round of the state update, which runs 256 x 128 halves on 4
+// waves (WN = 2, NBJ = 2).
 //
 // Tiles go from HBM straight into LDS with 16-byte buffer loads (no register
 // staging) in slabs of 64 columns, so that every row contributes one whole
@@ -438,7 +439,7 @@ constexpr int WN_W = 4, NBJ_W = 2;  // wide GEMMs: 8 waves, 256 x 256 tiles
 constexpr int NSL_W = 2;             // 2 x 64 KB slabs
 constexpr int NT_W = 64 * 2 * WN_W;  // 512 threads
 constexpr int WC_W = 32 * NBJ_W;     // columns per wave
-constexpr int WN_U = 2, NBJ_U = 2;   // state update: 4 waves, 256 x 128 tiles
+constexpr int WN_U = 2, NBJ_U = 2;   // the state update's half-tile round: 4 waves, 256 x 128 tiles
 constexpr int NSL_U = 3;             // 3 x 48 KB slabs
 constexpr int NT_U = 64 * 2 * WN_U;  // 256 threads
 
@@ -657,6 +658,7 @@ __global__ __launch_bounds__(NT_W, 1) void k_target_gemm(TgtArgs p) {
 // of them (one per CU) run on the 8-wave configuration; a last partial round
 // of at most 128 tiles is split into 256 x 128 halves that run as one round
 // on the 4-wave configuration, so no CU idles for a whole round.
+
 // Tile loads of the update with an L2 prefetch. Every eta Z^T tile is read by
 // one XCD only, so its slabs come from HBM, one slab (two in the half-tile
 // round) ahead of use without the prefetch. The workgroups that share an
