@@ -845,21 +845,35 @@ __global__ __launch_bounds__(128 * WN, 1) void k_update(UpdArgs p) {
 // same group. i = s, j = t; only tiles with i-tile <= j-tile that hold an
 // unmasked entry are formed.
 // grid: B * ngroups * nt(nt+1)/2 workgroups, nt = ceil(L/256)
+constexpr int kMaxScorePairs = 136;  // the lower triangle of 16 x 16 tiles (L <= 4096)
+
 struct ScoreArgs {
   const bf16_t *Z;
   bf16_t *P;
   float eta;
   int T, T_pad, L, C, ngroups, f, nt;
+  // tiles (it, jt) of a full group that hold an unmasked entry; npairs = 0:
+  // every tile of the lower triangle gets a workgroup (long groups)
+  int npairs;
+  unsigned char pit[kMaxScorePairs], pjt[kMaxScorePairs];
 };
 
 __global__ __launch_bounds__(NT_W, 1) void k_scores(ScoreArgs p) {
   __shared__ __attribute__((aligned(16))) Slab<WN_W, NBJ_W> ring[NSL_W];
-  const int ntri = p.nt * (p.nt + 1) / 2;
   const int t = xcd_tile(blockIdx.x, gridDim.x);
-  const int bg = t / ntri;  // b * ngroups + g
-  int u = t - bg * ntri, jt = 0;
-  while (u > jt) u -= ++jt;  // u-th tile (it <= jt) of the lower triangle, jt-major
-  const int it = u;
+  int bg, it, jt;  // bg = b * ngroups + g
+  if (p.npairs > 0) {
+    bg = t / p.npairs;
+    it = p.pit[t - bg * p.npairs];
+    jt = p.pjt[t - bg * p.npairs];
+  } else {
+    const int ntri = p.nt * (p.nt + 1) / 2;
+    bg = t / ntri;
+    int u = t - bg * ntri;
+    jt = 0;
+    while (u > jt) u -= ++jt;  // u-th tile (it <= jt) of the lower triangle, jt-major
+    it = u;
+  }
   const int g = bg % p.ngroups, b = bg / p.ngroups;
   const long long gs = (long long)g * p.L;
   const int Lg = (int)((p.T - gs) < p.L ? (p.T - gs) : p.L);
@@ -1245,8 +1259,21 @@ hipError_t launch_update_bf16(const bf16_t *ZT, const bf16_t *VT, float *state, 
 
 hipError_t launch_scores_bf16(const bf16_t *Z, bf16_t *P, float eta, const Layout &lay, hipStream_t s) {
   const int nt = (lay.L + 255) / 256;
-  ScoreArgs p{Z, P, eta, lay.T, lay.T_pad, lay.L, lay.C, lay.ngroups, lay.f, nt};
-  const long long n = (long long)lay.B * lay.ngroups * (nt * (nt + 1) / 2);
+  ScoreArgs p{Z, P, eta, lay.T, lay.T_pad, lay.L, lay.C, lay.ngroups, lay.f, nt, 0, {}, {}};
+  if (nt * (nt + 1) / 2 <= kMaxScorePairs) {
+    // the tiles of a full group that the kernel would not skip, jt-major
+    for (int jt = 0; jt < nt; ++jt) {
+      const int jl = (jt * 256 + 255 < lay.L - 1) ? jt * 256 + 255 : lay.L - 1;
+      for (int it = 0; it <= jt; ++it)
+        if (it * 256 / lay.C < jl / lay.C) {
+          p.pit[p.npairs] = (unsigned char)it;
+          p.pjt[p.npairs] = (unsigned char)jt;
+          ++p.npairs;
+        }
+    }
+    if (p.npairs == 0) return hipSuccess;  // one chunk per group: no within-group term
+  }
+  const long long n = (long long)lay.B * lay.ngroups * (p.npairs > 0 ? p.npairs : nt * (nt + 1) / 2);
   if (n >= (1LL << 31)) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(k_scores, dim3((unsigned)n), dim3(NT_W), 0, s, p);
   return hipGetLastError();
