@@ -203,8 +203,10 @@ int ttt_set_target_conv(ttt_handle *h, const void *conv_w, int K, const void *W_
  * off (the default); tau < 0 or NaN returns TTT_E_ARG. The norm is taken from
  * the chunk Grams, ||V_i^T Z_i||_F^2 = sum_{s,t in chunk i} <v_s,v_t><z_s,z_t>,
  * in fp32. Applies to later ttt_forward_chunked calls; needs extra scratch:
- * small fp32 buffers, plus [B][T][d] target rows in the handle's dtype on an
- * fp32 handle or with the general target (a bf16 handle with the plain
+ * small fp32 buffers; on a bf16 handle 1 KB per token slot and per 256-token
+ * span of a chunk (the Gram kernel's fp32 partial products: 128 MB at
+ * T = 131072, C = 256); plus [B][T][d] target rows in the handle's dtype on
+ * an fp32 handle or with the general target (a bf16 handle with the plain
  * target reads the rows from E_tgt through the ids when vocab*d*2 < 2^31).
  */
 int ttt_set_clip(ttt_handle *h, float tau);
