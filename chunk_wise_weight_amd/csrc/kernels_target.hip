@@ -54,6 +54,62 @@ __global__ __launch_bounds__(256) void k_conv_taps(const int32_t *ids, const Tv 
   }
 }
 
+// The same sums for KT <= 8 taps, R consecutive slots per thread: the R+KT-1
+// rows the run touches are read once each (instead of KT times) and added,
+// in tap order, into every slot whose window holds them. Same arithmetic and
+// order per slot as k_conv_taps, so the same results.
+template <typename Tv, int KT>
+__global__ __launch_bounds__(256) void k_conv_taps_run(const int32_t *ids, const Tv *E, int vocab, const float *cw,
+                                                       Tv *U, int T, int T_pad, int C, int d, long long nthreads) {
+  constexpr int R = 8;
+  for (long long g = (long long)blockIdx.x * 256 + threadIdx.x; g < nthreads; g += (long long)gridDim.x * 256) {
+    const int a0 = (int)(g % (d / 8)) * 8;
+    const long long br = g / (d / 8);
+    const int t0 = (int)(br % (T_pad / R)) * R;
+    const int b = (int)(br / (T_pad / R));
+    float w[KT][8];
+#pragma unroll
+    for (int k = 0; k < KT; ++k)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) w[k][j] = cw[(long long)k * d + a0 + j];
+    int limit[R];  // last position slot t0+r may take a tap from (its chunk's end, at most T); -1 past T
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const long long chunk_end = ((long long)((t0 + r) / C) + 1) * C;
+      limit[r] = t0 + r < T ? (int)(chunk_end < T ? chunk_end : T) : -1;
+    }
+    float acc[R][8];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[r][j] = 0.f;
+#pragma unroll
+    for (int i = 0; i < R + KT - 1; ++i) {
+      const int p = t0 + 1 + i;  // position of window row i; slot t0+r takes it as tap i-r
+      if (p > T) break;
+      const int tok = ids[(long long)b * (T + 1) + p];
+      if (tok < 0 || tok >= vocab) continue;
+      const Tv *e = E + (long long)tok * d + a0;
+      float ev[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ev[j] = to_f32(e[j]);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int k = i - r;
+        if (k < 0 || k >= KT || p > limit[r]) continue;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[r][j] += w[k][j] * ev[j];
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      Tv *u = U + ((long long)b * T_pad + t0 + r) * d + a0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) store_out(u + j, acc[r][j]);
+    }
+  }
+}
+
 // fp32 path: VT[b][a][t] = sum_c U[b][t][c] W[c][a]; Vrow[b][t][a] the same value (optional).
 __global__ __launch_bounds__(256) void k_target_gemm_f32(const float *U, const float *W, float *VT, float *Vrow,
                                                          int T_pad, int d, long long n) {
@@ -88,22 +144,46 @@ unsigned grid_for(long long n) {
   return (unsigned)(g < 65536 ? (g > 0 ? g : 1) : 65536);
 }
 
-}  // namespace
-
-hipError_t launch_conv_taps_bf16(const int32_t *ids, const bf16_t *E, int vocab, const float *cw, int K, bf16_t *U,
-                                 const Layout &lay, hipStream_t s) {
-  const long long n = (long long)lay.B * lay.T_pad * (lay.d / 8);
-  hipLaunchKernelGGL((k_conv_taps<bf16_t>), dim3(grid_for(n)), dim3(256), 0, s, ids, E, vocab, cw, K, U, lay.T,
+template <typename Tv, int KT>
+hipError_t launch_conv_run(const int32_t *ids, const Tv *E, int vocab, const float *cw, Tv *U, const Layout &lay,
+                           hipStream_t s) {
+  const long long n = (long long)lay.B * (lay.T_pad / 8) * (lay.d / 8);
+  hipLaunchKernelGGL((k_conv_taps_run<Tv, KT>), dim3(grid_for(n)), dim3(256), 0, s, ids, E, vocab, cw, U, lay.T,
                      lay.T_pad, lay.C, lay.d, n);
   return hipGetLastError();
 }
 
-hipError_t launch_conv_taps_f32(const int32_t *ids, const float *E, int vocab, const float *cw, int K, float *U,
-                                const Layout &lay, hipStream_t s) {
+// Runs of 8 slots for up to 8 taps, one slot per thread beyond.
+template <typename Tv>
+hipError_t launch_conv_taps(const int32_t *ids, const Tv *E, int vocab, const float *cw, int K, Tv *U,
+                            const Layout &lay, hipStream_t s) {
+  switch (K) {
+    case 1: return launch_conv_run<Tv, 1>(ids, E, vocab, cw, U, lay, s);
+    case 2: return launch_conv_run<Tv, 2>(ids, E, vocab, cw, U, lay, s);
+    case 3: return launch_conv_run<Tv, 3>(ids, E, vocab, cw, U, lay, s);
+    case 4: return launch_conv_run<Tv, 4>(ids, E, vocab, cw, U, lay, s);
+    case 5: return launch_conv_run<Tv, 5>(ids, E, vocab, cw, U, lay, s);
+    case 6: return launch_conv_run<Tv, 6>(ids, E, vocab, cw, U, lay, s);
+    case 7: return launch_conv_run<Tv, 7>(ids, E, vocab, cw, U, lay, s);
+    case 8: return launch_conv_run<Tv, 8>(ids, E, vocab, cw, U, lay, s);
+    default: break;
+  }
   const long long n = (long long)lay.B * lay.T_pad * (lay.d / 8);
-  hipLaunchKernelGGL((k_conv_taps<float>), dim3(grid_for(n)), dim3(256), 0, s, ids, E, vocab, cw, K, U, lay.T,
+  hipLaunchKernelGGL((k_conv_taps<Tv>), dim3(grid_for(n)), dim3(256), 0, s, ids, E, vocab, cw, K, U, lay.T,
                      lay.T_pad, lay.C, lay.d, n);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_conv_taps_bf16(const int32_t *ids, const bf16_t *E, int vocab, const float *cw, int K, bf16_t *U,
+                                 const Layout &lay, hipStream_t s) {
+  return launch_conv_taps<bf16_t>(ids, E, vocab, cw, K, U, lay, s);
+}
+
+hipError_t launch_conv_taps_f32(const int32_t *ids, const float *E, int vocab, const float *cw, int K, float *U,
+                                const Layout &lay, hipStream_t s) {
+  return launch_conv_taps<float>(ids, E, vocab, cw, K, U, lay, s);
 }
 
 hipError_t launch_target_gemm_f32(const float *U, const float *W, float *VT, float *Vrow, const Layout &lay,
