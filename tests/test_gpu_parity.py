@@ -95,7 +95,8 @@ SHORT_4B_CASES = [  # (T, C, G, B) at d = 2560, f = 9728
     (64, 64, 0, 1),     # one slab
     (200, 64, 2, 1),    # odd stage count, groups of 128 tokens
     (333, 64, 1, 2),    # a snapshot every 64 tokens; 760 tiles, all on the 256 x 256 shape
-    (333, 100, 0, 1),   # 380 tiles: whole round and half-tile round
+    (333, 100, 0, 1),   # 380 tiles, one group: whole round and half-tile round
+    (1150, 64, 2, 1),   # 380 tiles, 9 groups of 128 tokens in both rounds, ragged tail
 ]
 
 
