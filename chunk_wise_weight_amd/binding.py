@@ -243,7 +243,8 @@ PHASES = ("gather", "up_gate_swiglu", "clip_factors", "update_snapshots", "group
 
 
 def ttt_phase_times(h: Handle) -> List[float]:
-    """Milliseconds per phase of the most recent profiled forward (waits for it)."""
+    """Milliseconds per phase, the mean per forward call over the profiled calls since the previous read
+    (waits for them; at most 16 launch sequences, a document of ttt_forward_docs counting as one)."""
     buf = (ctypes.c_float * len(PHASES))()
     _check(lib().ttt_phase_times(h.ptr, buf, len(PHASES)), "ttt_phase_times")
     return list(buf)

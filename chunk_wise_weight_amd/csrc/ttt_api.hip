@@ -50,6 +50,8 @@ constexpr int kDefaultGroupTokens = 1024;
 constexpr int kGroupAlign = 64;  // a group starts on a 64-token block of the K-blocked V^T
 // profiled phases: gather, up/gate, clip factors, update, scores, output, final copy
 constexpr int kPhases = 7;
+// event sets kept for ttt_phase_times: one per launch sequence (a forward call, or one document of it)
+constexpr int kEvRing = 16;
 constexpr int kMaxTaps = 64;
 
 int gcd_int(int a, int b) {
@@ -135,7 +137,11 @@ struct ttt_handle {
   size_t ws_bytes = 0;
   size_t fixed_bytes = 0;
   bool profiling = false, events_made = false, timed = false;
-  hipEvent_t ev[kPhases + 1] = {};
+  hipEvent_t ev[kEvRing][kPhases + 1] = {};
+  int ev_next = 0;        // the ring slot the next launch sequence records into
+  int ev_pending = 0;     // launch sequences recorded since the last ttt_phase_times
+  int calls_pending = 0;  // public forward calls among them
+  float ev_mean[kPhases] = {};
 };
 
 namespace {
@@ -163,7 +169,8 @@ void free_handle(ttt_handle *h) {
   if (h->Wt) (void)hipFree(h->Wt);
   if (h->ws) (void)hipFree(h->ws);
   if (h->events_made)
-    for (auto &e : h->ev) (void)hipEventDestroy(e);
+    for (auto &set : h->ev)
+      for (auto &e : set) (void)hipEventDestroy(e);
   delete h;
 }
 
@@ -241,11 +248,17 @@ int forward_impl(ttt_handle *h, const void *x, const int32_t *ids, const void *E
   if (dev != h->device) return fail(TTT_E_ARG, "current device differs from the handle's device");
   const size_t df = (size_t)h->d * h->f;
   const bool prof = h->profiling;
-  if (prof) HIP_TRY(hipEventRecord(h->ev[0], s));
+  hipEvent_t *ev = h->ev[h->ev_next];
+  auto close_events = [h]() {
+    h->ev_next = (h->ev_next + 1) % kEvRing;
+    ++h->ev_pending;
+    h->timed = true;
+  };
+  if (prof) HIP_TRY(hipEventRecord(ev[0], s));
   if (B == 0 || T == 0) {
     if (prof) {
-      for (int i = 1; i <= kPhases; ++i) HIP_TRY(hipEventRecord(h->ev[i], s));
-      h->timed = true;
+      for (int i = 1; i <= kPhases; ++i) HIP_TRY(hipEventRecord(ev[i], s));
+      close_events();
     }
     if (W_final && B > 0)
       HIP_TRY(hipMemcpyAsync(W_final, state, (size_t)B * df * 4, hipMemcpyDeviceToDevice, s));
@@ -289,10 +302,10 @@ int forward_impl(ttt_handle *h, const void *x, const int32_t *ids, const void *E
     } else if ((learn || lay.intra) && !gram_e) {
       HIP_TRY(launch_gather_vt_bf16(ids, (const bf16_t *)E_tgt, vocab, (bf16_t *)VT, (bf16_t *)Vrow, nullptr, lay, s));
     }
-    if (prof) HIP_TRY(hipEventRecord(h->ev[1], s));
+    if (prof) HIP_TRY(hipEventRecord(ev[1], s));
     HIP_TRY(launch_a1_bf16((const bf16_t *)x, (const bf16_t *)h->Wug, (bf16_t *)Z, (bf16_t *)ZT, h->eta,
                            learn ? 1 : 0, lay, s));
-    if (prof) HIP_TRY(hipEventRecord(h->ev[2], s));
+    if (prof) HIP_TRY(hipEventRecord(ev[2], s));
     if (clip) {
       HIP_TRY(launch_chunk_gram_bf16((const bf16_t *)Z, (const bf16_t *)Vrow, (const bf16_t *)E_tgt, ids, vocab, gv,
                                      rowpart, wspan, lay, s));
@@ -302,16 +315,16 @@ int forward_impl(ttt_handle *h, const void *x, const int32_t *ids, const void *E
       else
         HIP_TRY(launch_scale_vt_bf16((bf16_t *)VT, cfac, lay, s));
     }
-    if (prof) HIP_TRY(hipEventRecord(h->ev[3], s));
+    if (prof) HIP_TRY(hipEventRecord(ev[3], s));
     if (learn) {
       HIP_TRY(launch_update_bf16((const bf16_t *)ZT, (const bf16_t *)VT, state, (bf16_t *)snap, lay, s));
     } else {
       for (int b = 0; b < B; ++b)
         HIP_TRY(launch_state_to_snap_bf16(state + (size_t)b * df, (bf16_t *)snap + (size_t)b * df, h->d, h->f, s));
     }
-    if (prof) HIP_TRY(hipEventRecord(h->ev[4], s));
+    if (prof) HIP_TRY(hipEventRecord(ev[4], s));
     if (lay.intra) HIP_TRY(launch_scores_bf16((const bf16_t *)Z, (bf16_t *)P, h->eta, lay, s));
-    if (prof) HIP_TRY(hipEventRecord(h->ev[5], s));
+    if (prof) HIP_TRY(hipEventRecord(ev[5], s));
     HIP_TRY(launch_out_bf16((const bf16_t *)Z, (const bf16_t *)P, (const bf16_t *)snap, (const bf16_t *)VT,
                             (bf16_t *)y, lay, s));
   } else {
@@ -321,32 +334,32 @@ int forward_impl(ttt_handle *h, const void *x, const int32_t *ids, const void *E
     } else if (learn || lay.intra) {
       HIP_TRY(launch_gather_vt_f32(ids, (const float *)E_tgt, vocab, (float *)VT, (float *)Vrow, lay, s));
     }
-    if (prof) HIP_TRY(hipEventRecord(h->ev[1], s));
+    if (prof) HIP_TRY(hipEventRecord(ev[1], s));
     HIP_TRY(launch_a1_f32((const float *)x, (const float *)h->Wug, (float *)Z, (float *)ZT, h->eta, learn ? 1 : 0,
                           lay, s));
-    if (prof) HIP_TRY(hipEventRecord(h->ev[2], s));
+    if (prof) HIP_TRY(hipEventRecord(ev[2], s));
     if (clip) {
       HIP_TRY(launch_chunk_gram_f32((const float *)Z, (const float *)Vrow, rowpart, lay, s));
       HIP_TRY(launch_chunk_factors(rowpart, cfac, wspan, h->eta, h->clip_tau, lay, s));
       HIP_TRY(launch_scale_vt_f32((float *)VT, cfac, lay, s));
     }
-    if (prof) HIP_TRY(hipEventRecord(h->ev[3], s));
+    if (prof) HIP_TRY(hipEventRecord(ev[3], s));
     if (learn) {
       HIP_TRY(launch_update_f32((const float *)ZT, (const float *)VT, state, (float *)snap, lay, s));
     } else {
       HIP_TRY(hipMemcpyAsync(snap, state, (size_t)B * df * 4, hipMemcpyDeviceToDevice, s));
     }
-    if (prof) HIP_TRY(hipEventRecord(h->ev[4], s));
+    if (prof) HIP_TRY(hipEventRecord(ev[4], s));
     if (lay.intra) HIP_TRY(launch_scores_f32((const float *)Z, (float *)P, h->eta, lay, s));
-    if (prof) HIP_TRY(hipEventRecord(h->ev[5], s));
+    if (prof) HIP_TRY(hipEventRecord(ev[5], s));
     HIP_TRY(launch_out_f32((const float *)Z, (const float *)P, (const float *)snap, (const float *)VT, (float *)y,
                            lay, s));
   }
-  if (prof) HIP_TRY(hipEventRecord(h->ev[6], s));
+  if (prof) HIP_TRY(hipEventRecord(ev[6], s));
   if (W_final) HIP_TRY(hipMemcpyAsync(W_final, state, (size_t)B * df * 4, hipMemcpyDeviceToDevice, s));
   if (prof) {
-    HIP_TRY(hipEventRecord(h->ev[7], s));
-    h->timed = true;
+    HIP_TRY(hipEventRecord(ev[7], s));
+    close_events();
   }
   return TTT_OK;
 }
@@ -482,11 +495,13 @@ int ttt_set_target_conv(ttt_handle *h, const void *conv_w, int K, const void *W_
 int ttt_set_profiling(ttt_handle *h, int on) {
   if (!h) return fail(TTT_E_NULL, "handle is NULL");
   if (on && !h->events_made) {
-    for (auto &e : h->ev) HIP_TRY(hipEventCreate(&e));
+    for (auto &set : h->ev)
+      for (auto &e : set) HIP_TRY(hipEventCreate(&e));
     h->events_made = true;
   }
   h->profiling = on != 0;
   h->timed = false;
+  h->ev_pending = h->calls_pending = 0;
   return TTT_OK;
 }
 
@@ -494,12 +509,26 @@ int ttt_phase_times(ttt_handle *h, float *ms, int n) {
   if (!h || !ms) return fail(TTT_E_NULL, "handle or ms is NULL");
   if (n < 0 || n > kPhases) return fail(TTT_E_ARG, "n must be in [0, 7]");
   if (!h->timed) return fail(TTT_E_ARG, "no profiled forward call yet (enable ttt_set_profiling first)");
-  HIP_TRY(hipEventSynchronize(h->ev[kPhases]));
-  for (int i = 0; i < n; ++i) {
-    float t = 0.f;
-    HIP_TRY(hipEventElapsedTime(&t, h->ev[i], h->ev[i + 1]));
-    ms[i] = t;
+  if (h->ev_pending > kEvRing) {
+    h->ev_pending = h->calls_pending = 0;
+    return fail(TTT_E_ARG, "more than 16 profiled launch sequences since the last read; read more often");
   }
+  if (h->ev_pending > 0) {
+    double sum[kPhases] = {};
+    for (int k = 1; k <= h->ev_pending; ++k) {
+      hipEvent_t *e = h->ev[(h->ev_next - k + kEvRing) % kEvRing];
+      HIP_TRY(hipEventSynchronize(e[kPhases]));
+      for (int i = 0; i < kPhases; ++i) {
+        float t = 0.f;
+        HIP_TRY(hipEventElapsedTime(&t, e[i], e[i + 1]));
+        sum[i] += t;
+      }
+    }
+    const int calls = h->calls_pending > 0 ? h->calls_pending : 1;
+    for (int i = 0; i < kPhases; ++i) h->ev_mean[i] = (float)(sum[i] / calls);
+    h->ev_pending = h->calls_pending = 0;
+  }
+  for (int i = 0; i < n; ++i) ms[i] = h->ev_mean[i];
   return TTT_OK;
 }
 
@@ -531,7 +560,9 @@ int ttt_forward_chunked(ttt_handle *h, const void *x, const int32_t *ids, const 
   if (B > 0 && T > 0 && vocab < 1) return fail(TTT_E_SHAPE, "vocab must be >= 1");
   if (B > 0 && T > 0 && (misaligned(x) || misaligned(E_tgt) || misaligned(y)))
     return fail(TTT_E_ARG, "x, E_tgt and y must be 16-byte aligned");
-  return forward_impl(h, x, ids, E_tgt, vocab, B, T, y, h->state, W_final, (hipStream_t)hip_stream);
+  const int rc = forward_impl(h, x, ids, E_tgt, vocab, B, T, y, h->state, W_final, (hipStream_t)hip_stream);
+  if (rc == TTT_OK && h->profiling) ++h->calls_pending;
+  return rc;
 }
 
 int ttt_forward_docs(ttt_handle *h, const void *x, const int32_t *ids, const void *E_tgt, int vocab, int B, int T,
@@ -560,7 +591,11 @@ int ttt_forward_docs(ttt_handle *h, const void *x, const int32_t *ids, const voi
     }
   }
   hipStream_t s = (hipStream_t)hip_stream;
-  if (B == 0 || T == 0 || total == 0) return forward_impl(h, x, ids, E_tgt, vocab, B, T, y, h->state, W_final, s);
+  if (B == 0 || T == 0 || total == 0) {
+    const int rc = forward_impl(h, x, ids, E_tgt, vocab, B, T, y, h->state, W_final, s);
+    if (rc == TTT_OK && h->profiling) ++h->calls_pending;
+    return rc;
+  }
   const size_t es = h->dt == TTT_BF16 ? 2 : 4;
   const size_t df = (size_t)h->d * h->f;
   // Each document runs on its own slice: the state of sequence b returns to
@@ -582,6 +617,7 @@ int ttt_forward_docs(ttt_handle *h, const void *x, const int32_t *ids, const voi
     k += doc_counts[b];
   }
   if (W_final) HIP_TRY(hipMemcpyAsync(W_final, h->state, (size_t)B * df * 4, hipMemcpyDeviceToDevice, s));
+  if (h->profiling) ++h->calls_pending;
   return TTT_OK;
 }
 

@@ -127,8 +127,8 @@ int ttt_forward_chunked(ttt_handle *h, const void *x, const int32_t *ids, const 
  * last chunk, whose update the reset discards, so no target crosses a
  * document end. The final state is the last document's, kept in the handle as
  * usual. Documents run one after the other on the stream (B = 1 launches per
- * document); with profiling on, ttt_phase_times reports the last document's
- * phases. Other arguments, ownership and errors as ttt_forward_chunked.
+ * document); with profiling on, ttt_phase_times sums a call's documents.
+ * Other arguments, ownership and errors as ttt_forward_chunked.
  */
 int ttt_forward_docs(ttt_handle *h, const void *x, const int32_t *ids, const void *E_tgt, int vocab, int B, int T,
                      const int32_t *doc_starts, const int32_t *doc_counts, void *y, float *W_final,
@@ -212,15 +212,24 @@ int ttt_set_target_conv(ttt_handle *h, const void *conv_w, int K, const void *W_
 int ttt_set_clip(ttt_handle *h, float tau);
 
 /*
- * ttt_set_profiling / ttt_phase_times — per-phase device timing of the most
- * recent ttt_forward_chunked, from HIP events recorded on its stream.
+ * ttt_set_profiling / ttt_phase_times — per-phase device timing of the
+ * forward calls, from HIP events recorded on their streams.
  * Phases: 0 target gather, 1 up/gate GEMM + SwiGLU, 2 clipping factors
  * (0 when clipping is off), 3 state update with snapshots, 4 within-group
  * scores, 5 output GEMM, 6 final-state copy. With clipping on a bf16 handle
  * and the plain target, the gather runs after the factors (it applies them)
  * and counts in phase 2.
- * ttt_phase_times waits for the last event and writes `n` (<= 7)
- * milliseconds to ms[]; phases that did not run read 0.
+ * Each launch sequence (a ttt_forward_chunked call, or one document of a
+ * ttt_forward_docs call) records one set of events in a ring of 16 sets, so
+ * calls need not wait for each other. ttt_phase_times waits for the sets
+ * recorded since the previous read and writes `n` (<= 7) milliseconds per
+ * phase to ms[]: the sum over those sets divided by the number of forward
+ * calls among them (the mean per call; a call with documents sums them).
+ * With no call since the previous read it writes the previous figures again.
+ * A phase that did not run reads only the spacing of its two events (a few
+ * microseconds). More than 16 launch sequences between two
+ * reads is TTT_E_ARG (the oldest sets were overwritten) and starts a new
+ * window. ttt_set_profiling resets the window.
  */
 int ttt_set_profiling(ttt_handle *h, int on);
 int ttt_phase_times(ttt_handle *h, float *ms, int n);
