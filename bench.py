@@ -358,6 +358,24 @@ def main():
         r5 = run_gpu(w, a.chunk, a.steps, a.warmup, a.group_chunks, doc_starts=starts)
         ms5 = r5["event_ms"] / a.steps
         out["docs_leg"] = {"documents_per_sequence": 4, "tokens_per_s": tokens / (ms5 * 1e-3), "ms_per_step": ms5}
+        # One GPU's share of the layer split over 8 GPUs (the split itself is not built): a d_ff slice of
+        # 1280 (9728 is 38 tiles of 256, cut 5,5,5,5,5,5,4,4), whose y is a partial sum that a reduce-scatter
+        # would finish; and a context-parallel span of T/8 tokens of the whole layer, whose ids end with the
+        # next span's first token.
+        import dataclasses
+        fs, ts = 1280, w.T // 8
+        legs = {f"dff_slice_{fs}": dataclasses.replace(w, f=fs, W_up=w.W_up[:fs], W_gate=w.W_gate[:fs],
+                                                        W_down0=w.W_down0[:, :fs]),
+                f"cp_span_{ts}": dataclasses.replace(w, T=ts, x=w.x[:, :ts], ids=w.ids[:, :ts + 1])}
+        out["shard_legs"] = {}
+        for key, ws in legs.items():
+            r6 = run_gpu(ws, a.chunk, a.steps, a.warmup, a.group_chunks)
+            ms6 = r6["event_ms"] / a.steps
+            fl6 = 8.0 * ws.d * ws.f * ws.B * ws.T
+            out["shard_legs"][key] = {"d_ff": ws.f, "seq_len": ws.T, "ms_per_step": ms6,
+                                      "tokens_per_s": ws.B * ws.T / (ms6 * 1e-3),
+                                      "mfma_frac_layer": fl6 / (ms6 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                                      "phase_ms": dict(zip(names, r6["phase_ms"]))}
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, a.chunk, a.cpu_seconds)
     print(json.dumps(out), flush=True)
