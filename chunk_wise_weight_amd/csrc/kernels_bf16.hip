@@ -1179,7 +1179,10 @@ __global__ __launch_bounds__(256) void k_gather_vt(const int32_t *ids, const bf1
 #pragma unroll
       for (int k = 0; k < 8; ++k) e[k] = f32_to_bf16(bf16_to_f32(e[k]) * c);
     }
-    *reinterpret_cast<uint4 *>(&tile[pl][seg * 8]) = v;
+    // 16-byte column groups XOR-swizzled by (row / 8) % 8: the transposing
+    // reads below take one column from rows 8 apart, which the plain layout
+    // puts in the same banks
+    *reinterpret_cast<uint4 *>(&tile[pl][(seg ^ ((pl >> 3) & 7)) * 8]) = v;
     if (Vrow) *reinterpret_cast<uint4 *>(Vrow + ((long long)b * T_pad + pos) * d + a0 + seg * 8) = v;
   }
   __syncthreads();
@@ -1187,10 +1190,11 @@ __global__ __launch_bounds__(256) void k_gather_vt(const int32_t *ids, const bf1
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
     const int al = pass * 32 + (tid >> 3);
+    const int ax = al ^ (seg << 3);  // rows seg*8 .. seg*8+7 carry the swizzle seg
     uint32_t wv[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      wv[e] = (uint32_t)tile[seg * 8 + 2 * e][al] | ((uint32_t)tile[seg * 8 + 2 * e + 1][al] << 16);
+      wv[e] = (uint32_t)tile[seg * 8 + 2 * e][ax] | ((uint32_t)tile[seg * 8 + 2 * e + 1][ax] << 16);
     *reinterpret_cast<uint4 *>(blk + (long long)(a0 + al) * 64 + seg * 8) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
   }
 }
