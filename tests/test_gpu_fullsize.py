@@ -52,6 +52,12 @@ def test_c3_4b_32k():
     _check(make_config("c3_4b_32k"), 256)
 
 
+@pytest.mark.parametrize("layer", [0, 35])
+def test_c5_stack_layer(layer):
+    # one layer of the 36-layer stack (B = 2 sequences of 16384 tokens), drawn with its own seed
+    _check(make_config("c5_4b_stack36", seed=(5, layer)), 256)
+
+
 @pytest.fixture(scope="module")
 def c4_inputs():
     return make_config("c4_4b_128k")
