@@ -133,43 +133,28 @@ def run_gpu(w, C, steps, warmup, G, clip_tau=0.0, target_conv=None, doc_starts=N
         ttt.ttt_reset(h)
         forward()
     torch.cuda.synchronize()
-    if warmup:
-        ttt.ttt_phase_times(h)  # closes the warm-up calls' window
-    # The library keeps 16 event sets (one per forward, or per document), so
-    # the phases are read every `every` steps, without a wait in between.
-    seqs = 1 if doc_starts is None else sum(len(st) + 1 for st in doc_starts)
-    every = max(1, 16 // seqs)
-    phase_sum = [0.0] * len(ttt.PHASES)
-    since = 0
-
-    def read_phases():
-        ph = ttt.ttt_phase_times(h)  # the mean per call since the previous read
-        for i, v in enumerate(ph):
-            phase_sum[i] += v * since
-
+    # a new timing window for the timed steps; the library folds event sets
+    # beyond its ring of 16 into running sums, so the steps run back to back
+    # with one read at the end
+    ttt.ttt_set_profiling(h, True)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record()
-    for i in range(steps):
+    for _ in range(steps):
         ttt.ttt_reset(h)
         forward()
-        since += 1
-        if since == every and i < steps - 1:
-            read_phases()
-            since = 0
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ev_ms = ev0.elapsed_time(ev1)
-    if since:
-        read_phases()
+    phase_ms = list(ttt.ttt_phase_times(h))  # the mean per call over the timed steps
     plan = ttt.ttt_plan(w.T, C, G)
     ws = ttt.ttt_workspace_bytes(h)
     ttt.ttt_destroy(h)
     del x, E, ids, y
     torch.cuda.empty_cache()
-    return {"wall_s": wall, "event_ms": ev_ms, "phase_ms": [p / steps for p in phase_sum], "plan": plan,
+    return {"wall_s": wall, "event_ms": ev_ms, "phase_ms": phase_ms, "plan": plan,
             "workspace_bytes": ws}
 
 
@@ -181,9 +166,14 @@ def cpu_baseline(w, C, target_s):
 
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
-        threads = os.cpu_count() or 1
+        blas_threads = None
+    host_cpus = os.cpu_count() or 1
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except Exception:
+        affinity = host_cpus
 
     def run(S):
         ids = w.ids[0, :S + 1]
@@ -198,9 +188,13 @@ def cpu_baseline(w, C, target_s):
     t = run(S)
     S = max(S, min(w.T, int(S / t * target_s) // C * C))
     t = run(S)
-    return {"value": S / t, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    # the oracle's matmuls run on the BLAS pool; everything else is one thread
+    used = blas_threads if blas_threads else affinity
+    return {"value": S / t, "unit": "tokens/s", "cores": int(used), "kind": "oracle",
+            "dtype": "f64", "blas_threads": blas_threads, "host_cpus": host_cpus, "affinity_cpus": affinity,
             "sample": f"first {S} tokens of sequence 0 ({S // C} chunks of {C}), full layer shape "
-                      f"d={w.d} f={w.f}, fp64 NumPy oracle, target rows gathered to the ids used; {t:.1f} s"}
+                      f"d={w.d} f={w.f}; the fp64 NumPy oracle as it stands (not the fp32 variant), target rows "
+                      f"gathered to the ids used; {t:.1f} s; cores = the BLAS threads the oracle ran on"}
 
 
 def run_stack(a):
@@ -327,37 +321,61 @@ def main():
                      "traffic": measured_traffic(KERNEL_OF_PHASE[dom], a.chunk)},
         "workspace_gb": r["workspace_bytes"] / 1e9,
     }
-    if not a.no_sweep:
-        out["chunk_sweep"] = {}
+    def leg(key, fn):
+        """Runs one optional leg; a failure is recorded in the output instead of ending the run."""
+        t_leg = time.perf_counter()
+        try:
+            out[key] = fn()
+        except Exception as e:  # noqa: BLE001 - the headline must survive any leg
+            out[key] = {"error": f"{type(e).__name__}: {e}"}
+            import torch
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+        print(f"[bench] leg {key}: {time.perf_counter() - t_leg:.1f}s", file=sys.stderr, flush=True)
+
+    def chunk_sweep():
+        res = {}
         for Cs in (128, 512, 1024):
             if Cs == a.chunk:
                 continue
             w.C = Cs
-            r2 = run_gpu(w, Cs, a.steps, a.warmup, 0)
+            try:
+                r2 = run_gpu(w, Cs, a.steps, a.warmup, 0)
+            finally:
+                w.C = a.chunk
             ms2 = r2["event_ms"] / a.steps
-            out["chunk_sweep"][f"C{Cs}"] = {
+            res[f"C{Cs}"] = {
                 "tokens_per_s": tokens / (ms2 * 1e-3), "ms_per_step": ms2,
                 "mfma_frac_layer": total_flops / (ms2 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                 "group_tokens": r2["plan"]["L"], "phase_ms": dict(zip(names, r2["phase_ms"]))}
-        w.C = a.chunk
-    if not a.no_sweep:
+        return res
+
+    def clip_leg():
         # the pages' long-context setting: Frobenius clipping of each chunk update at 1e-5
         r3 = run_gpu(w, a.chunk, a.steps, a.warmup, a.group_chunks, clip_tau=1e-5)
         ms3 = r3["event_ms"] / a.steps
-        out["clip_leg"] = {"clip_tau": 1e-5, "tokens_per_s": tokens / (ms3 * 1e-3), "ms_per_step": ms3,
-                           "phase_ms": dict(zip(names, r3["phase_ms"]))}
+        return {"clip_tau": 1e-5, "tokens_per_s": tokens / (ms3 * 1e-3), "ms_per_step": ms3,
+                "phase_ms": dict(zip(names, r3["phase_ms"]))}
+
+    def target_conv_leg():
         # the general target Conv1D(X0) W_target with a kernel of 5 taps (E_tgt as X0)
         from synth import make_target_conv
         r4 = run_gpu(w, a.chunk, a.steps, a.warmup, a.group_chunks,
                      target_conv=make_target_conv(w.d, 5, "bf16", seed=4))
         ms4 = r4["event_ms"] / a.steps
-        out["target_conv_leg"] = {"K": 5, "tokens_per_s": tokens / (ms4 * 1e-3), "ms_per_step": ms4,
-                                  "phase_ms": dict(zip(names, r4["phase_ms"]))}
-        # packed documents: four documents of T/4 tokens, the state reset at each start
-        starts = [[w.T // 4 * k for k in (1, 2, 3)] for _ in range(w.B)]
+        return {"K": 5, "tokens_per_s": tokens / (ms4 * 1e-3), "ms_per_step": ms4,
+                "phase_ms": dict(zip(names, r4["phase_ms"]))}
+
+    def docs_leg(ndocs):
+        # packed documents: ndocs documents of T/ndocs tokens per sequence, the state reset at each start
+        starts = [[w.T // ndocs * k for k in range(1, ndocs)] for _ in range(w.B)]
         r5 = run_gpu(w, a.chunk, a.steps, a.warmup, a.group_chunks, doc_starts=starts)
         ms5 = r5["event_ms"] / a.steps
-        out["docs_leg"] = {"documents_per_sequence": 4, "tokens_per_s": tokens / (ms5 * 1e-3), "ms_per_step": ms5}
+        return {"documents_per_sequence": ndocs, "tokens_per_doc": w.T // ndocs,
+                "tokens_per_s": tokens / (ms5 * 1e-3), "ms_per_step": ms5,
+                "phase_ms": dict(zip(names, r5["phase_ms"]))}
+
+    def shard_legs():
         # One GPU's share of the layer split over 8 GPUs (the split itself is not built): a d_ff slice of
         # 1280 (9728 is 38 tiles of 256, cut 5,5,5,5,5,5,4,4), whose y is a partial sum that a reduce-scatter
         # would finish; and a context-parallel span of T/8 tokens of the whole layer, whose ids end with the
@@ -367,17 +385,26 @@ def main():
         legs = {f"dff_slice_{fs}": dataclasses.replace(w, f=fs, W_up=w.W_up[:fs], W_gate=w.W_gate[:fs],
                                                         W_down0=w.W_down0[:, :fs]),
                 f"cp_span_{ts}": dataclasses.replace(w, T=ts, x=w.x[:, :ts], ids=w.ids[:, :ts + 1])}
-        out["shard_legs"] = {}
+        res = {}
         for key, ws in legs.items():
             r6 = run_gpu(ws, a.chunk, a.steps, a.warmup, a.group_chunks)
             ms6 = r6["event_ms"] / a.steps
             fl6 = 8.0 * ws.d * ws.f * ws.B * ws.T
-            out["shard_legs"][key] = {"d_ff": ws.f, "seq_len": ws.T, "ms_per_step": ms6,
-                                      "tokens_per_s": ws.B * ws.T / (ms6 * 1e-3),
-                                      "mfma_frac_layer": fl6 / (ms6 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-                                      "phase_ms": dict(zip(names, r6["phase_ms"]))}
+            res[key] = {"d_ff": ws.f, "seq_len": ws.T, "ms_per_step": ms6,
+                        "tokens_per_s": ws.B * ws.T / (ms6 * 1e-3),
+                        "mfma_frac_layer": fl6 / (ms6 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                        "phase_ms": dict(zip(names, r6["phase_ms"]))}
+        return res
+
     if not a.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, a.chunk, a.cpu_seconds)
+        leg("cpu_baseline", lambda: cpu_baseline(w, a.chunk, a.cpu_seconds))
+    if not a.no_sweep:
+        leg("chunk_sweep", chunk_sweep)
+        leg("clip_leg", clip_leg)
+        leg("target_conv_leg", target_conv_leg)
+        leg("docs_leg", lambda: docs_leg(4))
+        leg("docs_leg_short", lambda: docs_leg(64))
+        leg("shard_legs", shard_legs)
     print(json.dumps(out), flush=True)
 
 

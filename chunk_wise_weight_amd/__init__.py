@@ -21,6 +21,7 @@ from .binding import (  # noqa: F401
     ttt_set_clip,
     ttt_set_target_conv,
     ttt_set_group_chunks,
+    ttt_set_output_f32,
     ttt_set_profiling,
     ttt_workspace_bytes,
 )

@@ -21,7 +21,7 @@ ERRORS = {-1: "TTT_E_NULL", -2: "TTT_E_SHAPE", -3: "TTT_E_DTYPE", -4: "TTT_E_NOM
           -6: "TTT_E_NODEV", -7: "TTT_E_ARG"}
 EXPORTS = ("ttt_init", "ttt_forward_chunked", "ttt_forward_docs", "ttt_reset", "ttt_destroy", "ttt_last_error",
            "ttt_set_group_chunks", "ttt_set_clip", "ttt_set_target_conv", "ttt_plan", "ttt_set_profiling", "ttt_phase_times",
-           "ttt_workspace_bytes")
+           "ttt_workspace_bytes", "ttt_set_output_f32")
 
 _lib = None
 
@@ -68,6 +68,8 @@ def lib() -> ctypes.CDLL:
     L.ttt_phase_times.restype = i32
     L.ttt_workspace_bytes.argtypes = [vp, ctypes.POINTER(ctypes.c_size_t)]
     L.ttt_workspace_bytes.restype = i32
+    L.ttt_set_output_f32.argtypes = [vp, i32]
+    L.ttt_set_output_f32.restype = i32
     _lib = L
     return L
 
@@ -107,6 +109,7 @@ class Handle:
                  max_batch: int):
         self._ptr = ptr
         self.d, self.f, self.C, self.eta, self.dtype, self.max_batch = d, f, C, eta, dtype, max_batch
+        self.y_dtype = dtype  # the dtype forward calls write y in
 
     @property
     def ptr(self) -> ctypes.c_void_p:
@@ -152,9 +155,9 @@ def _forward_args(h, x, ids, E_tgt, y, W_final, want_W_final):
     if tuple(ids.shape) != (B, T + 1) or d != h.d or E_tgt.shape[1] != h.d:
         raise ValueError("shape mismatch among x, ids, E_tgt and the handle")
     if y is None:
-        y = torch.empty((B, T, d), dtype=h.dtype, device=x.device)
+        y = torch.empty((B, T, d), dtype=h.y_dtype, device=x.device)
     else:
-        _dev(y, "y", h.dtype)
+        _dev(y, "y", h.y_dtype)
         if tuple(y.shape) != (B, T, d):
             raise ValueError("y must be [B][T][d]")
     if W_final is None and want_W_final:
@@ -235,6 +238,12 @@ def ttt_plan(T: int, C: int, G: int = 0) -> Dict[str, int]:
     return {"G": g.value, "L": L.value, "ngroups": n.value, "T_pad": tp.value}
 
 
+def ttt_set_output_f32(h: Handle, on: bool = True) -> None:
+    """On a bfloat16 handle, later forward calls write y as float32 (no final rounding to bf16)."""
+    _check(lib().ttt_set_output_f32(h.ptr, 1 if on else 0), "ttt_set_output_f32")
+    h.y_dtype = torch.float32 if (on or h.dtype == torch.float32) else h.dtype
+
+
 def ttt_set_profiling(h: Handle, on: bool = True) -> None:
     _check(lib().ttt_set_profiling(h.ptr, 1 if on else 0), "ttt_set_profiling")
 
@@ -244,7 +253,7 @@ PHASES = ("gather", "up_gate_swiglu", "clip_factors", "update_snapshots", "group
 
 def ttt_phase_times(h: Handle) -> List[float]:
     """Milliseconds per phase, the mean per forward call over the profiled calls since the previous read
-    (waits for them; at most 16 launch sequences, a document of ttt_forward_docs counting as one)."""
+    (waits for them)."""
     buf = (ctypes.c_float * len(PHASES))()
     _check(lib().ttt_phase_times(h.ptr, buf, len(PHASES)), "ttt_phase_times")
     return list(buf)

@@ -719,27 +719,99 @@ struct UpdArgs {
   int tile0;  // first 256 x 256 tile of this launch
 };
 
-// Write the accumulator tile as bf16 into a snapshot W[a][i], held as planes
-// of 8 columns ([f/8][d][8]: element (a, i) at ((i/8)*d + a)*8 + i%8). Lane l
-// holds, per group of 4 accumulator registers, four consecutive i of one a;
-// lanes l and l+32 hold the two halves of one 16-byte chunk, and the 32 lanes
-// of a half walk 32 consecutive a: each store instruction writes 512
-// contiguous bytes. `lane_ptr` points at this lane's element for (bi, bj, q) =
-// (0, 0, 0): a = j0 + wn*32*NBJ + l%32, i = i0 + wm*128 + 4*(l/32); tiles are
-// always full (d, f multiples of 256).
+// Snapshots W[a][i] are held as planes of 8 columns ([f/8][d][8]: element
+// (a, i) at ((i/8)*d + a)*8 + i%8). Lane l holds, per group of 4 accumulator
+// registers, four consecutive i of one a; lanes l and l+32 hold the two halves
+// of one 16-byte chunk, and the 32 lanes of a half walk 32 consecutive a: each
+// store instruction writes 512 contiguous bytes. A lane pointer points at this
+// lane's element for (bi, bj, q) = (0, 0, 0): a = j0 + wn*32*NBJ + l%32,
+// i = i0 + wm*128 + 4*(l/32); tiles are always full (d, f multiples of 256).
+__device__ __forceinline__ long long snap_off(int bi, int bj, int q, int d) {
+  return (long long)(bi * 4 + q) * 8 * d + bj * 256;
+}
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+
+// The entry state W_entry sits in the accumulators. Store Q = bf16(W_entry)
+// as snapshot 0 and keep only the exact remainder W_entry - Q (it has at most
+// 16 significant bits, so the subtraction does not round). The accumulators
+// then carry R = (W_entry - Q) + the updates so far, a quantity that starts
+// below half a bf16 ulp of W: every rank-16 MFMA increment is added to a small
+// number, and increments far below the fp32 resolution of W itself (as with
+// clipped updates) still accumulate with fp32 relative precision.
 template <int NBJ>
-__device__ __forceinline__ void dump_snapshot(const Acc<NBJ> &acc, bf16_t *lane_ptr, int d) {
+__device__ __forceinline__ void split_entry(Acc<NBJ> &acc, bf16_t *q_ptr, int d) {
 #pragma unroll
   for (int bj = 0; bj < NBJ; ++bj)
 #pragma unroll
     for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
+        f32x16 &v = acc.v[bi][bj];
         uint2 pk;
-        pk.x = pack_bf16x2(acc.v[bi][bj][4 * q + 0], acc.v[bi][bj][4 * q + 1]);
-        pk.y = pack_bf16x2(acc.v[bi][bj][4 * q + 2], acc.v[bi][bj][4 * q + 3]);
-        *reinterpret_cast<uint2 *>(lane_ptr + (long long)(bi * 4 + q) * 8 * d + bj * 256) = pk;
+        pk.x = pack_bf16x2(v[4 * q + 0], v[4 * q + 1]);
+        pk.y = pack_bf16x2(v[4 * q + 2], v[4 * q + 3]);
+        *reinterpret_cast<uint2 *>(q_ptr + snap_off(bi, bj, q, d)) = pk;
+        v[4 * q + 0] -= bf16_lo(pk.x);
+        v[4 * q + 1] -= bf16_hi(pk.x);
+        v[4 * q + 2] -= bf16_lo(pk.y);
+        v[4 * q + 3] -= bf16_hi(pk.y);
       }
+}
+
+// Q + R for the 8 accumulator groups (bi in [BI, BI+2), q = 0..3) of column
+// block bj, with Q read back from snapshot 0 at q_ptr (the same elements this
+// lane wrote there): 8 loads in flight at a time keep the live registers
+// within the budget of two waves per SIMD; the scheduling barriers around each
+// batch stop the compiler from hoisting the next batch's loads.
+// Snapshot 0 of this lane, for the readback: a buffer descriptor over the
+// sequence's snapshot 0 and the lane's byte offset in it, so that each load
+// is one instruction with a scalar offset (64-bit addresses per load would
+// cost two registers each).
+struct QRead {
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t vo;
+  int d;
+  __device__ __forceinline__ uint2 load(int bi, int bj, int q) const {
+    const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rs, vo, (int)(snap_off(bi, bj, q, d) * 2), 0);
+    return make_uint2(v.x, v.y);
+  }
+};
+
+template <int NBJ, int BI, class Fn>
+__device__ __forceinline__ void with_state8(const Acc<NBJ> &acc, const QRead &qr, int bj, Fn &&fn) {
+  uint2 qv[8];
+  pin();
+#pragma unroll
+  for (int k = 0; k < 8; ++k) qv[k] = qr.load(BI + k / 4, bj, k % 4);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int bi = BI + k / 4, q = k % 4;
+    const f32x16 &v = acc.v[bi][bj];
+    fn(bi, q, bf16_lo(qv[k].x) + v[4 * q + 0], bf16_hi(qv[k].x) + v[4 * q + 1], bf16_lo(qv[k].y) + v[4 * q + 2],
+       bf16_hi(qv[k].y) + v[4 * q + 3]);
+  }
+  pin();
+}
+
+template <int NBJ, class Fn>
+__device__ __forceinline__ void for_state(const Acc<NBJ> &acc, const QRead &qr, Fn &&fn) {
+#pragma unroll
+  for (int bj = 0; bj < NBJ; ++bj) {
+    with_state8<NBJ, 0>(acc, qr, bj, [&](int bi, int q, float a, float b, float c, float e) { fn(bi, bj, q, a, b, c, e); });
+    with_state8<NBJ, 2>(acc, qr, bj, [&](int bi, int q, float a, float b, float c, float e) { fn(bi, bj, q, a, b, c, e); });
+  }
+}
+
+// Snapshot of the state Q + R: bf16(Q + R) into the planes at lane_ptr.
+template <int NBJ>
+__device__ __forceinline__ void dump_snapshot(const Acc<NBJ> &acc, const QRead &qr, bf16_t *lane_ptr, int d) {
+  for_state(acc, qr, [&](int bi, int bj, int q, float s0, float s1, float s2, float s3) {
+    uint2 pk;
+    pk.x = pack_bf16x2(s0, s1);
+    pk.y = pack_bf16x2(s2, s3);
+    *reinterpret_cast<uint2 *>(lane_ptr + snap_off(bi, bj, q, d)) = pk;
+  });
 }
 
 // WN = 4: workgroup n of the launch is tile tile0 + n (a 256 x 256 tile);
@@ -796,10 +868,14 @@ __global__ __launch_bounds__(128 * WN, 1) void k_update(UpdArgs p) {
     ld.init_pf(lds.sink, h * halves, (ty - band * 8) * halves + half, 16 / WN, tx % (16 / WN), w, lane);
   }
   const int nk = p.kend / BK;
-  // Snapshot 0 is the entry state; group starts are multiples of the stage
-  // depth, so snapshot g is written right after the last stage of group g-1,
-  // while the following slabs are already in flight.
-  dump_snapshot(acc, snap0, p.d);
+  // Snapshot 0 is bf16 of the entry state; the accumulators keep the exact
+  // remainder. Group starts are multiples of the stage depth, so snapshot g is
+  // written right after the last stage of group g-1, while the following slabs
+  // are already in flight. Every later snapshot and the final state read Q
+  // back from snapshot 0; the wait makes its stores complete (vmcnt counts
+  // stores too) before any of those loads can be issued.
+  split_entry(acc, snap0, p.d);
+  __builtin_amdgcn_s_waitcnt(wait_imm(0));
   int g = 1;
   const int nsl = (nk + 1) >> 1;
   Frag<NBJ> cur, nxt;
@@ -812,8 +888,13 @@ __global__ __launch_bounds__(128 * WN, 1) void k_update(UpdArgs p) {
   // order among themselves, so while a load is outstanding every later load
   // is too, and the count exceeds the number allowed; a store in flight can
   // only make a wait last longer.
+  QRead qr;
+  qr.rs = __builtin_amdgcn_make_buffer_rsrc(p.snap + (long long)b * p.ngroups * df, (short)0, (int)(df * 2),
+                                           kBufferFlags);
+  qr.vo = (uint32_t)(lane_snap * 2);
+  qr.d = p.d;
   auto snapshot = [&](const Acc<NBJ> &a) {
-    dump_snapshot(a, snap0 + (long long)g * df, p.d);
+    dump_snapshot(a, qr, snap0 + (long long)g * df, p.d);
     ++g;
   };
   // Stages of group g-1 run plain; its last stage ends with snapshot g.
@@ -827,17 +908,10 @@ __global__ __launch_bounds__(128 * WN, 1) void k_update(UpdArgs p) {
     ++kt;
   }
   stage_run<WN, NBJ, NSL, true>(acc, ring, cur, nxt, kt, nk, nk, wm, wn, lane, w, ld);
-#pragma unroll
-  for (int bj = 0; bj < NBJ; ++bj) {
-    float *row = st + (long long)bj * 32 * p.f;
-#pragma unroll
-    for (int bi = 0; bi < 4; ++bi)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<float4 *>(row + bi * 32 + 8 * q) =
-            make_float4(acc.v[bi][bj][4 * q + 0], acc.v[bi][bj][4 * q + 1], acc.v[bi][bj][4 * q + 2],
-                        acc.v[bi][bj][4 * q + 3]);
-  }
+  // the final state Q + R in fp32
+  for_state(acc, qr, [&](int bi, int bj, int q, float s0, float s1, float s2, float s3) {
+    *reinterpret_cast<float4 *>(st + (long long)bj * 32 * p.f + bi * 32 + 8 * q) = make_float4(s0, s1, s2, s3);
+  });
 }
 
 // ---------------------------------------------------------------------------
@@ -944,9 +1018,13 @@ struct OutArgs {
   const bf16_t *P;
   const bf16_t *snap;
   const bf16_t *VT;
-  bf16_t *y;
+  void *y;    // bf16 [B][T][d], or fp32 with y_f32
   int T, T_pad, L, C, ngroups, d, f, intra;
+  int y_f32;
 };
+
+constexpr int LY_F = 260;  // [128 tokens][256 model dims + pad]: one half of an fp32 y tile
+static_assert(128 * LY_F * 4 <= kSmemOut, "the fp32 y half tile fits the output GEMM's LDS");
 
 __global__ __launch_bounds__(NT_W, 1) void k_out(OutArgs p) {
   __shared__ __attribute__((aligned(16))) bf16_t smem[kSmemOut / 2];
@@ -990,6 +1068,41 @@ __global__ __launch_bounds__(NT_W, 1) void k_out(OutArgs p) {
 
   // Epilogue through LDS ([token][model dim]) so y rows leave in whole lines.
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), wm = w & 1, wn = w >> 1;
+  if (p.y_f32) {
+    // fp32 y: two halves of 128 tokens (waves 0-3 hold tokens 0-127, waves 4-7 the rest), 1 KB rows
+    float *lf = reinterpret_cast<float *>(smem);
+    float *yb = static_cast<float *>(p.y) + ((long long)b * p.T + gs + j0) * p.d + i0;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      __syncthreads();  // the ring, or the first half's rows, are no longer read
+      if ((wn >> 1) == half) {
+#pragma unroll
+        for (int bj = 0; bj < NBJ_W; ++bj) {
+          const int tl = (wn & 1) * WC_W + bj * 32 + (lane & 31);
+#pragma unroll
+          for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int al = wm * 128 + bi * 32 + 8 * q + 4 * (lane >> 5);
+              *reinterpret_cast<float4 *>(lf + tl * LY_F + al) =
+                  make_float4(acc.v[bi][bj][4 * q + 0], acc.v[bi][bj][4 * q + 1], acc.v[bi][bj][4 * q + 2],
+                              acc.v[bi][bj][4 * q + 3]);
+            }
+        }
+      }
+      __syncthreads();
+      // 128 token rows x 1 KB; rows past the group's end are not written
+#pragma unroll
+      for (int it = 0; it < 8192 / NT_W; ++it) {
+        const int idx = it * NT_W + tid;
+        const int tr = idx >> 6, ch = idx & 63;
+        if (j0 + half * 128 + tr < Lg)
+          *reinterpret_cast<float4 *>(yb + (long long)(half * 128 + tr) * p.d + ch * 4) =
+              *reinterpret_cast<const float4 *>(lf + tr * LY_F + ch * 4);
+      }
+    }
+    return;
+  }
   bf16_t *ly = smem;
   __syncthreads();  // every wave is done with the ring
 #pragma unroll
@@ -1008,12 +1121,13 @@ __global__ __launch_bounds__(NT_W, 1) void k_out(OutArgs p) {
   }
   __syncthreads();
   // 256 token rows x 512 bytes; rows past the group's end are not written
+  bf16_t *yb = static_cast<bf16_t *>(p.y);
 #pragma unroll
   for (int it = 0; it < 8192 / NT_W; ++it) {
     const int idx = it * NT_W + tid;
     const int tr = idx >> 5, ch = idx & 31;
     if (j0 + tr < Lg)
-      *reinterpret_cast<uint4 *>(p.y + ((long long)b * p.T + gs + j0 + tr) * p.d + i0 + ch * 8) =
+      *reinterpret_cast<uint4 *>(yb + ((long long)b * p.T + gs + j0 + tr) * p.d + i0 + ch * 8) =
           *reinterpret_cast<const uint4 *>(ly + tr * LY_P + ch * 8);
   }
 }
@@ -1292,9 +1406,9 @@ hipError_t launch_state_to_snap_bf16(const float *state, bf16_t *snap, int d, in
   return hipGetLastError();
 }
 
-hipError_t launch_out_bf16(const bf16_t *Z, const bf16_t *P, const bf16_t *snap, const bf16_t *VT, bf16_t *y,
-                           const Layout &lay, hipStream_t s) {
-  OutArgs p{Z, P, snap, VT, y, lay.T, lay.T_pad, lay.L, lay.C, lay.ngroups, lay.d, lay.f, lay.intra};
+hipError_t launch_out_bf16(const bf16_t *Z, const bf16_t *P, const bf16_t *snap, const bf16_t *VT, void *y,
+                           int y_f32, const Layout &lay, hipStream_t s) {
+  OutArgs p{Z, P, snap, VT, y, lay.T, lay.T_pad, lay.L, lay.C, lay.ngroups, lay.d, lay.f, lay.intra, y_f32};
   const long long n = (long long)lay.B * lay.ngroups * (lay.d / BM) * ((lay.L + 255) / 256);
   if (n >= (1LL << 31)) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(k_out, dim3((unsigned)n), dim3(NT_W), 0, s, p);

@@ -114,17 +114,23 @@ __global__ __launch_bounds__(NT) void k_update_f32(const float *ZT, const float 
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
   float *st = state + (long long)b * d * f;
   float *sn = snap + (long long)b * ngroups * d * f;
-  AccF acc;
+  // The accumulators carry the change since the entry state, which starts at
+  // zero: increments far below the fp32 resolution of W itself (as with
+  // clipped updates) still accumulate with fp32 relative precision. The entry
+  // state stays in registers and is added back for each snapshot and at the end.
+  AccF acc, w0;
   const int i = i0 + tx * 4;
 #pragma unroll
   for (int y = 0; y < 4; ++y) {
     const int a = j0 + ty * 4 + y;
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     if (a < d && i < f) v = *reinterpret_cast<const float4 *>(st + (long long)a * f + i);
-    acc.v[y][0] = v.x;
-    acc.v[y][1] = v.y;
-    acc.v[y][2] = v.z;
-    acc.v[y][3] = v.w;
+    w0.v[y][0] = v.x;
+    w0.v[y][1] = v.y;
+    w0.v[y][2] = v.z;
+    w0.v[y][3] = v.w;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) acc.v[y][x] = 0.f;
   }
   auto dump = [&](int g) {
 #pragma unroll
@@ -132,7 +138,8 @@ __global__ __launch_bounds__(NT) void k_update_f32(const float *ZT, const float 
       const int a = j0 + ty * 4 + y;
       if (a < d && i < f)
         *reinterpret_cast<float4 *>(sn + ((long long)g * d + a) * f + i) =
-            make_float4(acc.v[y][0], acc.v[y][1], acc.v[y][2], acc.v[y][3]);
+            make_float4(w0.v[y][0] + acc.v[y][0], w0.v[y][1] + acc.v[y][1], w0.v[y][2] + acc.v[y][2],
+                        w0.v[y][3] + acc.v[y][3]);
     }
   };
   Seg<float> sa{ZT + (long long)b * f * T_pad, T_pad, f, T_pad};
@@ -154,7 +161,8 @@ __global__ __launch_bounds__(NT) void k_update_f32(const float *ZT, const float 
     const int a = j0 + ty * 4 + y;
     if (a < d && i < f)
       *reinterpret_cast<float4 *>(st + (long long)a * f + i) =
-          make_float4(acc.v[y][0], acc.v[y][1], acc.v[y][2], acc.v[y][3]);
+          make_float4(w0.v[y][0] + acc.v[y][0], w0.v[y][1] + acc.v[y][1], w0.v[y][2] + acc.v[y][2],
+                      w0.v[y][3] + acc.v[y][3]);
   }
 }
 

@@ -127,6 +127,7 @@ struct ttt_handle {
   float eta = 0.f;
   float clip_tau = 0.f;     // > 0: Frobenius clipping of each chunk update
   int conv_K = 0;           // > 0: general target with K taps
+  int y_f32 = 0;            // bf16 handle: y written as fp32
   float *conv_w = nullptr;  // [K][d] fp32 tap weights
   void *Wt = nullptr;       // bf16: W_target^T [d][d]; f32: W_target [d][d]
   ttt_dtype dt = TTT_BF16;
@@ -139,8 +140,9 @@ struct ttt_handle {
   bool profiling = false, events_made = false, timed = false;
   hipEvent_t ev[kEvRing][kPhases + 1] = {};
   int ev_next = 0;        // the ring slot the next launch sequence records into
-  int ev_pending = 0;     // launch sequences recorded since the last ttt_phase_times
-  int calls_pending = 0;  // public forward calls among them
+  int ev_pending = 0;     // launch sequences recorded since the last ttt_phase_times, still in the ring
+  int calls_pending = 0;  // public forward calls since the last ttt_phase_times
+  double ev_fold[kPhases] = {};  // phase sums of the sets folded out of the ring since the last read
   float ev_mean[kPhases] = {};
 };
 
@@ -230,6 +232,30 @@ void *at(void *base, void *off) { return (char *)base + (size_t)off; }
 
 namespace {
 
+// Adds the phase times of ring slot k (a recorded set) to sum[]; waits for the set to complete.
+int add_set_times(ttt_handle *h, int k, double *sum) {
+  hipEvent_t *e = h->ev[k];
+  HIP_TRY(hipEventSynchronize(e[kPhases]));
+  for (int i = 0; i < kPhases; ++i) {
+    float t = 0.f;
+    HIP_TRY(hipEventElapsedTime(&t, e[i], e[i + 1]));
+    sum[i] += t;
+  }
+  return TTT_OK;
+}
+
+// Before a launch sequence records into the ring: when every slot still holds
+// a set not yet read, the oldest one (the slot about to be reused) is folded
+// into running sums first. This waits for that set, recorded 16 launch
+// sequences earlier, to finish.
+int ring_make_room(ttt_handle *h) {
+  if (h->ev_pending < kEvRing) return TTT_OK;
+  const int rc = add_set_times(h, h->ev_next, h->ev_fold);
+  if (rc) return rc;
+  --h->ev_pending;
+  return TTT_OK;
+}
+
 // One forward over B sequences of T tokens whose states are state[0 .. B).
 int forward_impl(ttt_handle *h, const void *x, const int32_t *ids, const void *E_tgt, int vocab, int B, int T,
                  void *y, float *state, float *W_final, hipStream_t s_in) {
@@ -248,6 +274,10 @@ int forward_impl(ttt_handle *h, const void *x, const int32_t *ids, const void *E
   if (dev != h->device) return fail(TTT_E_ARG, "current device differs from the handle's device");
   const size_t df = (size_t)h->d * h->f;
   const bool prof = h->profiling;
+  if (prof) {
+    rc = ring_make_room(h);
+    if (rc) return rc;
+  }
   hipEvent_t *ev = h->ev[h->ev_next];
   auto close_events = [h]() {
     h->ev_next = (h->ev_next + 1) % kEvRing;
@@ -325,8 +355,8 @@ int forward_impl(ttt_handle *h, const void *x, const int32_t *ids, const void *E
     if (prof) HIP_TRY(hipEventRecord(ev[4], s));
     if (lay.intra) HIP_TRY(launch_scores_bf16((const bf16_t *)Z, (bf16_t *)P, h->eta, lay, s));
     if (prof) HIP_TRY(hipEventRecord(ev[5], s));
-    HIP_TRY(launch_out_bf16((const bf16_t *)Z, (const bf16_t *)P, (const bf16_t *)snap, (const bf16_t *)VT,
-                            (bf16_t *)y, lay, s));
+    HIP_TRY(launch_out_bf16((const bf16_t *)Z, (const bf16_t *)P, (const bf16_t *)snap, (const bf16_t *)VT, y,
+                            h->y_f32, lay, s));
   } else {
     if (conv) {
       HIP_TRY(launch_conv_taps_f32(ids, (const float *)E_tgt, vocab, h->conv_w, h->conv_K, (float *)U, lay, s));
@@ -492,6 +522,12 @@ int ttt_set_target_conv(ttt_handle *h, const void *conv_w, int K, const void *W_
   return TTT_OK;
 }
 
+int ttt_set_output_f32(ttt_handle *h, int on) {
+  if (!h) return fail(TTT_E_NULL, "handle is NULL");
+  h->y_f32 = (on != 0 && h->dt == TTT_BF16) ? 1 : 0;
+  return TTT_OK;
+}
+
 int ttt_set_profiling(ttt_handle *h, int on) {
   if (!h) return fail(TTT_E_NULL, "handle is NULL");
   if (on && !h->events_made) {
@@ -502,6 +538,7 @@ int ttt_set_profiling(ttt_handle *h, int on) {
   h->profiling = on != 0;
   h->timed = false;
   h->ev_pending = h->calls_pending = 0;
+  for (double &v : h->ev_fold) v = 0.0;
   return TTT_OK;
 }
 
@@ -509,24 +546,17 @@ int ttt_phase_times(ttt_handle *h, float *ms, int n) {
   if (!h || !ms) return fail(TTT_E_NULL, "handle or ms is NULL");
   if (n < 0 || n > kPhases) return fail(TTT_E_ARG, "n must be in [0, 7]");
   if (!h->timed) return fail(TTT_E_ARG, "no profiled forward call yet (enable ttt_set_profiling first)");
-  if (h->ev_pending > kEvRing) {
-    h->ev_pending = h->calls_pending = 0;
-    return fail(TTT_E_ARG, "more than 16 profiled launch sequences since the last read; read more often");
-  }
-  if (h->ev_pending > 0) {
-    double sum[kPhases] = {};
+  if (h->ev_pending > 0 || h->calls_pending > 0) {
+    double sum[kPhases];
+    for (int i = 0; i < kPhases; ++i) sum[i] = h->ev_fold[i];
     for (int k = 1; k <= h->ev_pending; ++k) {
-      hipEvent_t *e = h->ev[(h->ev_next - k + kEvRing) % kEvRing];
-      HIP_TRY(hipEventSynchronize(e[kPhases]));
-      for (int i = 0; i < kPhases; ++i) {
-        float t = 0.f;
-        HIP_TRY(hipEventElapsedTime(&t, e[i], e[i + 1]));
-        sum[i] += t;
-      }
+      const int rc = add_set_times(h, (h->ev_next - k + kEvRing) % kEvRing, sum);
+      if (rc) return rc;
     }
     const int calls = h->calls_pending > 0 ? h->calls_pending : 1;
     for (int i = 0; i < kPhases; ++i) h->ev_mean[i] = (float)(sum[i] / calls);
     h->ev_pending = h->calls_pending = 0;
+    for (double &v : h->ev_fold) v = 0.0;
   }
   for (int i = 0; i < n; ++i) ms[i] = h->ev_mean[i];
   return TTT_OK;
@@ -597,6 +627,7 @@ int ttt_forward_docs(ttt_handle *h, const void *x, const int32_t *ids, const voi
     return rc;
   }
   const size_t es = h->dt == TTT_BF16 ? 2 : 4;
+  const size_t ys = h->dt == TTT_BF16 && !h->y_f32 ? 2 : 4;  // bytes per element of y
   const size_t df = (size_t)h->d * h->f;
   // Each document runs on its own slice: the state of sequence b returns to
   // W_down0 at every document start, and chunking restarts there. The ids
@@ -608,9 +639,9 @@ int ttt_forward_docs(ttt_handle *h, const void *x, const int32_t *ids, const voi
     for (int j = 0; j <= doc_counts[b]; ++j) {
       const int s1 = j < doc_counts[b] ? doc_starts[k + j] : T;
       if (j > 0) HIP_TRY(hipMemcpyAsync(h->state + (size_t)b * df, h->W0, df * 4, hipMemcpyDeviceToDevice, s));
-      const size_t off = ((size_t)b * T + s0) * h->d * es;
-      const int rc = forward_impl(h, (const char *)x + off, ids + (size_t)b * (T + 1) + s0, E_tgt, vocab, 1, s1 - s0,
-                                  (char *)y + off, h->state + (size_t)b * df, nullptr, s);
+      const size_t row = ((size_t)b * T + s0) * h->d;
+      const int rc = forward_impl(h, (const char *)x + row * es, ids + (size_t)b * (T + 1) + s0, E_tgt, vocab, 1,
+                                  s1 - s0, (char *)y + row * ys, h->state + (size_t)b * df, nullptr, s);
       if (rc) return rc;
       s0 = s1;
     }

@@ -212,6 +212,18 @@ int ttt_set_target_conv(ttt_handle *h, const void *conv_w, int K, const void *W_
 int ttt_set_clip(ttt_handle *h, float tau);
 
 /*
+ * ttt_set_output_f32 — on a bf16 handle, later forward calls write y as fp32
+ * ([B][T][d] float, 4 bytes per element) instead of bf16: the output GEMM's
+ * fp32 accumulators are stored without the final rounding to bf16. The
+ * fast-weight contribution to y is often a small fraction of y (a few percent
+ * on short streams), and bf16 rounding of y alone then blurs it by up to
+ * 2^-9 |y|; callers that keep a residual stream in fp32 avoid that rounding.
+ * on = 0 restores bf16 y. No effect on an fp32 handle (y is always fp32).
+ * Returns TTT_E_NULL for a NULL handle.
+ */
+int ttt_set_output_f32(ttt_handle *h, int on);
+
+/*
  * ttt_set_profiling / ttt_phase_times — per-phase device timing of the
  * forward calls, from HIP events recorded on their streams.
  * Phases: 0 target gather, 1 up/gate GEMM + SwiGLU, 2 clipping factors
@@ -227,9 +239,10 @@ int ttt_set_clip(ttt_handle *h, float tau);
  * calls among them (the mean per call; a call with documents sums them).
  * With no call since the previous read it writes the previous figures again.
  * A phase that did not run reads only the spacing of its two events (a few
- * microseconds). More than 16 launch sequences between two
- * reads is TTT_E_ARG (the oldest sets were overwritten) and starts a new
- * window. ttt_set_profiling resets the window.
+ * microseconds). When a launch sequence finds all 16 sets unread, the oldest
+ * is folded into running sums first (the host waits for that set, recorded
+ * 16 sequences earlier, to complete), so any number of calls or documents
+ * may come between two reads. ttt_set_profiling resets the window.
  */
 int ttt_set_profiling(ttt_handle *h, int on);
 int ttt_phase_times(ttt_handle *h, float *ms, int n);

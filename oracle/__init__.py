@@ -10,4 +10,5 @@ from .ttt_oracle import (  # noqa: F401
     ttt_forward,
     ttt_forward_docs,
     ttt_forward_one,
+    window_outputs,
 )

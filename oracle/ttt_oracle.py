@@ -266,3 +266,42 @@ def final_state_columns(x: np.ndarray, ids: np.ndarray, E_tgt: np.ndarray, W_up:
         S = S + eta * (V[s:e].T @ Zc[s:e])
     return S
 
+
+
+def window_outputs(x: np.ndarray, ids: np.ndarray, E_tgt: np.ndarray, W_up: np.ndarray, W_gate: np.ndarray,
+                   W_entry: np.ndarray, C: int, eta: float, t0: int, t1: int, block: int = 8192) -> np.ndarray:
+    """The outputs y[t0:t1] of one sequence (plain next-token target, no clipping).
+
+    The state that chunk i applies is the entry state plus the updates of
+    every earlier chunk, W_entry + eta * sum_{s < iC} v_s z_s^T (the exclusive
+    prefix of the chunk deltas, paperlayer App. B; iplexlaw sec. 6). With c0
+    the start of the chunk holding t0, that prefix is split at c0:
+      y_t = z_t (W_entry + D)^T + eta * sum_{c0 <= s < start of t's chunk} <z_t, z_s> v_s,
+      D   = eta * V[:c0]^T Z[:c0],
+    and D is summed over blocks of `block` tokens, so a window late in a long
+    stream is reached without holding all of Z. Exact up to fp64 rounding
+    order; it agrees with ttt_forward_one on y[t0:t1].
+
+    x [T][d], ids [T+1], W_entry [d][f]; returns [t1 - t0][d] in fp64.
+    """
+    x = np.asarray(x)
+    T = x.shape[0]
+    if not (0 <= t0 <= t1 <= T):
+        raise ValueError("need 0 <= t0 <= t1 <= T")
+    S = _f64(W_entry)
+    c0 = (t0 // C) * C
+    D = np.zeros_like(S)
+    for a in range(0, c0, block):
+        b = min(a + block, c0)
+        Zb = gated_activation(x[a:b], W_up, W_gate)
+        Vb = ntp_targets(ids[a:b + 1], E_tgt)
+        D += eta * (Vb.T @ Zb)
+    Zw = gated_activation(x[c0:t1], W_up, W_gate)      # tokens c0 .. t1-1
+    Vw = ntp_targets(ids[c0:t1 + 1], E_tgt)
+    y = Zw[t0 - c0:] @ (S + D).T
+    G = Zw[t0 - c0:] @ Zw.T                             # <z_t, z_s> for t in the window, s in [c0, t1)
+    for r, t in enumerate(range(t0, t1)):
+        n = (t // C) * C - c0                           # tokens of [c0, t1) in earlier chunks than t's
+        if n > 0:
+            y[r] += eta * (G[r, :n] @ Vw[:n])
+    return y

@@ -23,6 +23,33 @@ def test_final_state_columns_match_full_state():
     assert np.max(np.abs(Wc - W[0][:, cols])) <= 1e-12 * np.max(np.abs(ref))
 
 
+@pytest.mark.parametrize("T,C,t0,t1,block", [
+    (37, 4, 0, 37, 8), (37, 4, 13, 29, 5), (37, 5, 20, 20, 3), (40, 8, 32, 40, 7), (23, 1, 9, 17, 4),
+    (23, 30, 4, 11, 2), (50, 6, 49, 50, 16)])
+def test_window_outputs_match_sequential_and_closed_form(T, C, t0, t1, block):
+    # the window form against the sequential apply-then-update loop and against the block-causal closed form
+    # (linear attention with a block mask, written in tests/pins.py), at windows that start inside a chunk,
+    # on a chunk boundary, are empty, or hold the stream's last token
+    rng = np.random.default_rng(T * 100 + t0)
+    x, ids, E, Wu, Wg, W0 = pins.tiny_case(rng, d=7, f=12, B=1, T=T)
+    y_seq, _ = oracle.ttt_forward(x, ids, E, Wu, Wg, W0, C, 0.3)
+    y_cf = pins.block_causal_closed_form(x[0], ids[0], E, Wu, Wg, W0, C, 0.3)[0]
+    yw = oracle.window_outputs(x[0], ids[0], E, Wu, Wg, W0, C, 0.3, t0, t1, block=block)
+    assert yw.shape == (t1 - t0, 7)
+    scale = max(np.max(np.abs(y_seq)), 1e-300)
+    assert np.max(np.abs(yw - y_seq[0, t0:t1]), initial=0.0) <= 1e-12 * scale
+    assert np.max(np.abs(yw - y_cf[t0:t1]), initial=0.0) <= 1e-12 * scale
+
+
+def test_window_outputs_rejects_bad_window():
+    rng = np.random.default_rng(3)
+    x, ids, E, Wu, Wg, W0 = pins.tiny_case(rng, T=10)
+    with pytest.raises(ValueError):
+        oracle.window_outputs(x[0], ids[0], E, Wu, Wg, W0, 4, 0.3, 6, 5)
+    with pytest.raises(ValueError):
+        oracle.window_outputs(x[0], ids[0], E, Wu, Wg, W0, 4, 0.3, 0, 11)
+
+
 def test_chunk_ranges():
     assert oracle.chunk_ranges(0, 4) == []
     assert oracle.chunk_ranges(10, 4) == [(0, 4), (4, 8), (8, 10)]
