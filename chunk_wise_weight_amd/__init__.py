@@ -23,5 +23,6 @@ from .binding import (  # noqa: F401
     ttt_set_group_chunks,
     ttt_set_output_f32,
     ttt_set_profiling,
+    ttt_state_delta,
     ttt_workspace_bytes,
 )

@@ -21,7 +21,7 @@ ERRORS = {-1: "TTT_E_NULL", -2: "TTT_E_SHAPE", -3: "TTT_E_DTYPE", -4: "TTT_E_NOM
           -6: "TTT_E_NODEV", -7: "TTT_E_ARG"}
 EXPORTS = ("ttt_init", "ttt_forward_chunked", "ttt_forward_docs", "ttt_reset", "ttt_destroy", "ttt_last_error",
            "ttt_set_group_chunks", "ttt_set_clip", "ttt_set_target_conv", "ttt_plan", "ttt_set_profiling", "ttt_phase_times",
-           "ttt_workspace_bytes", "ttt_set_output_f32")
+           "ttt_workspace_bytes", "ttt_set_output_f32", "ttt_state_delta")
 
 _lib = None
 
@@ -70,6 +70,8 @@ def lib() -> ctypes.CDLL:
     L.ttt_workspace_bytes.restype = i32
     L.ttt_set_output_f32.argtypes = [vp, i32]
     L.ttt_set_output_f32.restype = i32
+    L.ttt_state_delta.argtypes = [vp, vp, i32, vp]
+    L.ttt_state_delta.restype = i32
     _lib = L
     return L
 
@@ -236,6 +238,19 @@ def ttt_plan(T: int, C: int, G: int = 0) -> Dict[str, int]:
     _check(lib().ttt_plan(int(T), int(C), int(G), ctypes.byref(g), ctypes.byref(L), ctypes.byref(n),
                           ctypes.byref(tp)), "ttt_plan")
     return {"G": g.value, "L": L.value, "ngroups": n.value, "T_pad": tp.value}
+
+
+def ttt_state_delta(h: Handle, B: Optional[int] = None, out: Optional[torch.Tensor] = None,
+                    stream=None) -> torch.Tensor:
+    """D = W - W_down0 of sequences 0 .. B-1 (the change since each last reset), [B][d][f] float32."""
+    B = h.max_batch if B is None else int(B)
+    if out is None:
+        out = torch.empty((B, h.d, h.f), dtype=torch.float32, device="cuda")
+    _dev(out, "out", torch.float32)
+    if tuple(out.shape) != (B, h.d, h.f):
+        raise ValueError("out must be [B][d][f]")
+    _check(lib().ttt_state_delta(h.ptr, _ptr(out), B, _stream(stream)), "ttt_state_delta")
+    return out
 
 
 def ttt_set_output_f32(h: Handle, on: bool = True) -> None:

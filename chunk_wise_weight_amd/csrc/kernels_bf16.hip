@@ -649,9 +649,14 @@ __global__ __launch_bounds__(NT_W, 1) void k_target_gemm(TgtArgs p) {
 
 // ---------------------------------------------------------------------------
 // State update with snapshots. i = hidden unit (ZT row), j = model dim (VT row),
-// k = token slot. The fp32 accumulators ARE the state W[a][i] of one tile and
-// stay in registers for the whole token stream; at each group start g*L the
-// tile is written out as a bf16 snapshot.
+// k = token slot. The state of a sequence is D = W - W0, the change of the
+// fast weight since its last reset, in fp32; the accumulators of one tile
+// hold it for the whole token stream. Because D starts at zero and stays
+// small next to W, every rank-16 MFMA increment is added to a small number:
+// increments far below the fp32 resolution of W itself (as with clipped
+// updates) still accumulate with fp32 relative precision, also across calls.
+// At each group start g*L the tile is written out as the bf16 snapshot
+// bf16(W0 + D), with W0 read from the initial weight's bf16 planes.
 //
 // The state is cut into 256 x 256 tiles (i x a), numbered per sequence in
 // bands of 8 along a (see band_tile) and then across sequences. Whole rounds
@@ -713,8 +718,9 @@ struct UpdLds {
 struct UpdArgs {
   const bf16_t *ZT;
   const bf16_t *VT;
-  float *state;
+  float *state;        // D [B][d][f]
   bf16_t *snap;
+  const bf16_t *W0p;   // W0 as planes [f/8][d][8]
   int T_pad, kend, L, ngroups, d, f;
   int tile0;  // first 256 x 256 tile of this launch
 };
@@ -732,40 +738,13 @@ __device__ __forceinline__ long long snap_off(int bi, int bj, int q, int d) {
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
 
-// The entry state W_entry sits in the accumulators. Store Q = bf16(W_entry)
-// as snapshot 0 and keep only the exact remainder W_entry - Q (it has at most
-// 16 significant bits, so the subtraction does not round). The accumulators
-// then carry R = (W_entry - Q) + the updates so far, a quantity that starts
-// below half a bf16 ulp of W: every rank-16 MFMA increment is added to a small
-// number, and increments far below the fp32 resolution of W itself (as with
-// clipped updates) still accumulate with fp32 relative precision.
-template <int NBJ>
-__device__ __forceinline__ void split_entry(Acc<NBJ> &acc, bf16_t *q_ptr, int d) {
-#pragma unroll
-  for (int bj = 0; bj < NBJ; ++bj)
-#pragma unroll
-    for (int bi = 0; bi < 4; ++bi)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        f32x16 &v = acc.v[bi][bj];
-        uint2 pk;
-        pk.x = pack_bf16x2(v[4 * q + 0], v[4 * q + 1]);
-        pk.y = pack_bf16x2(v[4 * q + 2], v[4 * q + 3]);
-        *reinterpret_cast<uint2 *>(q_ptr + snap_off(bi, bj, q, d)) = pk;
-        v[4 * q + 0] -= bf16_lo(pk.x);
-        v[4 * q + 1] -= bf16_hi(pk.x);
-        v[4 * q + 2] -= bf16_lo(pk.y);
-        v[4 * q + 3] -= bf16_hi(pk.y);
-      }
-}
-
-// Q + R for the 8 accumulator groups (bi in [BI, BI+2), q = 0..3) of column
-// block bj, with Q read back from snapshot 0 at q_ptr (the same elements this
-// lane wrote there): 8 loads in flight at a time keep the live registers
+// W0 + D for the 8 accumulator groups (bi in [BI, BI+2), q = 0..3) of column
+// block bj, with the accumulators holding D and W0 read from the initial
+// weight's bf16 planes: 8 loads in flight at a time keep the live registers
 // within the budget of two waves per SIMD; the scheduling barriers around each
 // batch stop the compiler from hoisting the next batch's loads.
-// Snapshot 0 of this lane, for the readback: a buffer descriptor over the
-// sequence's snapshot 0 and the lane's byte offset in it, so that each load
+// The initial weight W0 as bf16 planes ([f/8][d][8], the snapshot layout): a
+// buffer descriptor over them and this lane's byte offset, so that each load
 // is one instruction with a scalar offset (64-bit addresses per load would
 // cost two registers each).
 struct QRead {
@@ -803,7 +782,7 @@ __device__ __forceinline__ void for_state(const Acc<NBJ> &acc, const QRead &qr, 
   }
 }
 
-// Snapshot of the state Q + R: bf16(Q + R) into the planes at lane_ptr.
+// Snapshot of the weight W0 + D: bf16(W0 + D) into the planes at lane_ptr.
 template <int NBJ>
 __device__ __forceinline__ void dump_snapshot(const Acc<NBJ> &acc, const QRead &qr, bf16_t *lane_ptr, int d) {
   for_state(acc, qr, [&](int bi, int bj, int q, float s0, float s1, float s2, float s3) {
@@ -868,14 +847,14 @@ __global__ __launch_bounds__(128 * WN, 1) void k_update(UpdArgs p) {
     ld.init_pf(lds.sink, h * halves, (ty - band * 8) * halves + half, 16 / WN, tx % (16 / WN), w, lane);
   }
   const int nk = p.kend / BK;
-  // Snapshot 0 is bf16 of the entry state; the accumulators keep the exact
-  // remainder. Group starts are multiples of the stage depth, so snapshot g is
-  // written right after the last stage of group g-1, while the following slabs
-  // are already in flight. Every later snapshot and the final state read Q
-  // back from snapshot 0; the wait makes its stores complete (vmcnt counts
-  // stores too) before any of those loads can be issued.
-  split_entry(acc, snap0, p.d);
-  __builtin_amdgcn_s_waitcnt(wait_imm(0));
+  QRead qr;
+  qr.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t *>(p.W0p), (short)0, (int)(df * 2), kBufferFlags);
+  qr.vo = (uint32_t)(lane_snap * 2);
+  qr.d = p.d;
+  // Snapshot 0 is the entry weight. Group starts are multiples of the stage
+  // depth, so snapshot g is written right after the last stage of group g-1,
+  // while the following slabs are already in flight.
+  dump_snapshot(acc, qr, snap0, p.d);
   int g = 1;
   const int nsl = (nk + 1) >> 1;
   Frag<NBJ> cur, nxt;
@@ -888,11 +867,6 @@ __global__ __launch_bounds__(128 * WN, 1) void k_update(UpdArgs p) {
   // order among themselves, so while a load is outstanding every later load
   // is too, and the count exceeds the number allowed; a store in flight can
   // only make a wait last longer.
-  QRead qr;
-  qr.rs = __builtin_amdgcn_make_buffer_rsrc(p.snap + (long long)b * p.ngroups * df, (short)0, (int)(df * 2),
-                                           kBufferFlags);
-  qr.vo = (uint32_t)(lane_snap * 2);
-  qr.d = p.d;
   auto snapshot = [&](const Acc<NBJ> &a) {
     dump_snapshot(a, qr, snap0 + (long long)g * df, p.d);
     ++g;
@@ -908,10 +882,18 @@ __global__ __launch_bounds__(128 * WN, 1) void k_update(UpdArgs p) {
     ++kt;
   }
   stage_run<WN, NBJ, NSL, true>(acc, ring, cur, nxt, kt, nk, nk, wm, wn, lane, w, ld);
-  // the final state Q + R in fp32
-  for_state(acc, qr, [&](int bi, int bj, int q, float s0, float s1, float s2, float s3) {
-    *reinterpret_cast<float4 *>(st + (long long)bj * 32 * p.f + bi * 32 + 8 * q) = make_float4(s0, s1, s2, s3);
-  });
+  // the final state D in fp32
+#pragma unroll
+  for (int bj = 0; bj < NBJ; ++bj) {
+    float *row = st + (long long)bj * 32 * p.f;
+#pragma unroll
+    for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<float4 *>(row + bi * 32 + 8 * q) =
+            make_float4(acc.v[bi][bj][4 * q + 0], acc.v[bi][bj][4 * q + 1], acc.v[bi][bj][4 * q + 2],
+                        acc.v[bi][bj][4 * q + 3]);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -991,21 +973,33 @@ __global__ __launch_bounds__(NT_W, 1) void k_scores(ScoreArgs p) {
 }
 
 // ---------------------------------------------------------------------------
-// Snapshot from an fp32 state with no update: snap[((i/8)*d + a)*8 + i%8] =
-// bf16(state[a][i]). Thread (plane, a) converts one 8-column chunk.
-__global__ __launch_bounds__(256) void k_state_to_snap(const float *state, bf16_t *snap, int d, int f) {
+// Snapshot with no update: snap[((i/8)*d + a)*8 + i%8] = bf16(W0[a][i] + D[a][i])
+// (fp32 W0 and state D, [d][f] each). Thread (plane, a) converts one
+// 8-column chunk.
+__global__ __launch_bounds__(256) void k_state_to_snap(const float *W0, const float *D, bf16_t *snap, int d, int f) {
   const long long n = (long long)d * (f / 8);
   for (long long t = blockIdx.x * 256LL + threadIdx.x; t < n; t += (long long)gridDim.x * 256) {
     const int a = (int)(t % d);
     const long long pl = t / d;
-    const float4 lo = *reinterpret_cast<const float4 *>(state + (long long)a * f + pl * 8);
-    const float4 hi = *reinterpret_cast<const float4 *>(state + (long long)a * f + pl * 8 + 4);
+    const long long o = (long long)a * f + pl * 8;
+    const float4 w0 = *reinterpret_cast<const float4 *>(W0 + o), w1 = *reinterpret_cast<const float4 *>(W0 + o + 4);
+    const float4 d0 = *reinterpret_cast<const float4 *>(D + o), d1 = *reinterpret_cast<const float4 *>(D + o + 4);
     uint4 pk;
-    pk.x = pack_bf16x2(lo.x, lo.y);
-    pk.y = pack_bf16x2(lo.z, lo.w);
-    pk.z = pack_bf16x2(hi.x, hi.y);
-    pk.w = pack_bf16x2(hi.z, hi.w);
+    pk.x = pack_bf16x2(w0.x + d0.x, w0.y + d0.y);
+    pk.y = pack_bf16x2(w0.z + d0.z, w0.w + d0.w);
+    pk.z = pack_bf16x2(w1.x + d1.x, w1.y + d1.y);
+    pk.w = pack_bf16x2(w1.z + d1.z, w1.w + d1.w);
     *reinterpret_cast<uint4 *>(snap + t * 8) = pk;
+  }
+}
+
+// The initial weight as planes: dst[((i/8)*d + a)*8 + i%8] = src[a][i] (bf16, [d][f]).
+__global__ __launch_bounds__(256) void k_to_planes(const bf16_t *src, bf16_t *dst, int d, int f) {
+  const long long n = (long long)d * (f / 8);
+  for (long long t = blockIdx.x * 256LL + threadIdx.x; t < n; t += (long long)gridDim.x * 256) {
+    const int a = (int)(t % d);
+    const long long pl = t / d;
+    *reinterpret_cast<uint4 *>(dst + t * 8) = *reinterpret_cast<const uint4 *>(src + (long long)a * f + pl * 8);
   }
 }
 
@@ -1357,8 +1351,8 @@ hipError_t launch_target_gemm_bf16(const bf16_t *U, const bf16_t *WtT, bf16_t *V
   return hipGetLastError();
 }
 
-hipError_t launch_update_bf16(const bf16_t *ZT, const bf16_t *VT, float *state, bf16_t *snap, const Layout &lay,
-                              hipStream_t s) {
+hipError_t launch_update_bf16(const bf16_t *ZT, const bf16_t *VT, float *state, bf16_t *snap, const bf16_t *W0p,
+                              const Layout &lay, hipStream_t s) {
   const int kend = (int)round_up_ll(lay.T, BK);
   const long long tiles = (long long)lay.B * (lay.f / BM) * (lay.d / 256);
   if (tiles * 2 >= (1LL << 31)) return hipErrorInvalidConfiguration;
@@ -1366,7 +1360,7 @@ hipError_t launch_update_bf16(const bf16_t *ZT, const bf16_t *VT, float *state, 
   const int cus = 256;
   const long long rem = tiles % cus;
   const long long whole = rem <= cus / 2 ? tiles - rem : tiles;
-  UpdArgs p{ZT, VT, state, snap, lay.T_pad, kend, lay.L, lay.ngroups, lay.d, lay.f, 0};
+  UpdArgs p{ZT, VT, state, snap, W0p, lay.T_pad, kend, lay.L, lay.ngroups, lay.d, lay.f, 0};
   if (whole > 0) hipLaunchKernelGGL((k_update<WN_W, NBJ_W, NSL_W>), dim3((unsigned)whole), dim3(NT_W), 0, s, p);
   if (tiles > whole) {
     p.tile0 = (int)whole;
@@ -1397,12 +1391,20 @@ hipError_t launch_scores_bf16(const bf16_t *Z, bf16_t *P, float eta, const Layou
   return hipGetLastError();
 }
 
-hipError_t launch_state_to_snap_bf16(const float *state, bf16_t *snap, int d, int f, hipStream_t s) {
+hipError_t launch_state_to_snap_bf16(const float *W0, const float *D, bf16_t *snap, int d, int f, hipStream_t s) {
   if (d <= 0 || f <= 0 || f % 8) return hipErrorInvalidValue;
   const long long n = (long long)d * (f / 8);
   const long long blocks = (n + 255) / 256;
-  hipLaunchKernelGGL(k_state_to_snap, dim3((unsigned)(blocks < 65536 ? blocks : 65536)), dim3(256), 0, s, state, snap, d,
-                     f);
+  hipLaunchKernelGGL(k_state_to_snap, dim3((unsigned)(blocks < 65536 ? blocks : 65536)), dim3(256), 0, s, W0, D, snap,
+                     d, f);
+  return hipGetLastError();
+}
+
+hipError_t launch_to_planes_bf16(const bf16_t *src, bf16_t *dst, int d, int f, hipStream_t s) {
+  if (d <= 0 || f <= 0 || f % 8) return hipErrorInvalidValue;
+  const long long n = (long long)d * (f / 8);
+  const long long blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(k_to_planes, dim3((unsigned)(blocks < 65536 ? blocks : 65536)), dim3(256), 0, s, src, dst, d, f);
   return hipGetLastError();
 }
 

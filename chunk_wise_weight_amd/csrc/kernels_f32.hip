@@ -107,30 +107,37 @@ __global__ __launch_bounds__(NT) void k_a1_f32(const float *x, const float *Wu, 
 
 // State update with fp32 snapshots at every group start. i = hidden unit, j = model dim.
 // grid (ceil(f/64), ceil(d/64), B)
+// The state is D = W - W0 (the change since the last reset); snapshots are W0 + D.
 __global__ __launch_bounds__(NT) void k_update_f32(const float *ZT, const float *VT, float *state, float *snap,
-                                                   int T_pad, int kend, int L, int ngroups, int d, int f) {
+                                                   const float *W0, int T_pad, int kend, int L, int ngroups, int d,
+                                                   int f) {
   __shared__ __attribute__((aligned(16))) Tile As, Bs;
   const int i0 = blockIdx.x * TM, j0 = blockIdx.y * TN, b = blockIdx.z;
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
   float *st = state + (long long)b * d * f;
   float *sn = snap + (long long)b * ngroups * d * f;
-  // The accumulators carry the change since the entry state, which starts at
-  // zero: increments far below the fp32 resolution of W itself (as with
-  // clipped updates) still accumulate with fp32 relative precision. The entry
-  // state stays in registers and is added back for each snapshot and at the end.
+  // The accumulators carry D, which starts at zero after a reset and stays
+  // small next to W: increments far below the fp32 resolution of W itself (as
+  // with clipped updates) still accumulate with fp32 relative precision. W0
+  // stays in registers and is added for each snapshot.
   AccF acc, w0;
   const int i = i0 + tx * 4;
 #pragma unroll
   for (int y = 0; y < 4; ++y) {
     const int a = j0 + ty * 4 + y;
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (a < d && i < f) v = *reinterpret_cast<const float4 *>(st + (long long)a * f + i);
-    w0.v[y][0] = v.x;
-    w0.v[y][1] = v.y;
-    w0.v[y][2] = v.z;
-    w0.v[y][3] = v.w;
-#pragma unroll
-    for (int x = 0; x < 4; ++x) acc.v[y][x] = 0.f;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f), u = v;
+    if (a < d && i < f) {
+      v = *reinterpret_cast<const float4 *>(st + (long long)a * f + i);
+      u = *reinterpret_cast<const float4 *>(W0 + (long long)a * f + i);
+    }
+    acc.v[y][0] = v.x;
+    acc.v[y][1] = v.y;
+    acc.v[y][2] = v.z;
+    acc.v[y][3] = v.w;
+    w0.v[y][0] = u.x;
+    w0.v[y][1] = u.y;
+    w0.v[y][2] = u.z;
+    w0.v[y][3] = u.w;
   }
   auto dump = [&](int g) {
 #pragma unroll
@@ -161,8 +168,7 @@ __global__ __launch_bounds__(NT) void k_update_f32(const float *ZT, const float 
     const int a = j0 + ty * 4 + y;
     if (a < d && i < f)
       *reinterpret_cast<float4 *>(st + (long long)a * f + i) =
-          make_float4(w0.v[y][0] + acc.v[y][0], w0.v[y][1] + acc.v[y][1], w0.v[y][2] + acc.v[y][2],
-                      w0.v[y][3] + acc.v[y][3]);
+          make_float4(acc.v[y][0], acc.v[y][1], acc.v[y][2], acc.v[y][3]);
   }
 }
 
@@ -273,11 +279,12 @@ hipError_t launch_a1_f32(const float *x, const float *Wug, float *Z, float *ZT, 
   return hipGetLastError();
 }
 
-hipError_t launch_update_f32(const float *ZT, const float *VT, float *state, float *snap, const Layout &lay,
+hipError_t launch_update_f32(const float *ZT, const float *VT, float *state, float *snap, const float *W0,
+                             const Layout &lay,
                              hipStream_t s) {
   const int kend = (int)round_up_ll(lay.T, TK);
   dim3 grid((lay.f + TM - 1) / TM, (lay.d + TN - 1) / TN, lay.B);
-  hipLaunchKernelGGL(k_update_f32, grid, dim3(NT), 0, s, ZT, VT, state, snap, lay.T_pad, kend, lay.L, lay.ngroups,
+  hipLaunchKernelGGL(k_update_f32, grid, dim3(NT), 0, s, ZT, VT, state, snap, W0, lay.T_pad, kend, lay.L, lay.ngroups,
                      lay.d, lay.f);
   return hipGetLastError();
 }

@@ -15,14 +15,17 @@ hipError_t launch_gather_vt_bf16(const int32_t *ids, const bf16_t *E, int vocab,
 // by 64 columns: [d/64][2f][64].
 hipError_t launch_a1_bf16(const bf16_t *x, const bf16_t *Wug, bf16_t *Z, bf16_t *ZT, float eta, int write_zt,
                           const Layout &lay, hipStream_t s);
-// state[b] += sum_p ZT[b][:, p] VT[b][:, p]^T (as W[a][b] layout), snapshots snap[b][g] = bf16(state at p = g*L).
+// state[b] += sum_p ZT[b][:, p] VT[b][:, p]^T (as W[a][i] layout; the state is D = W - W0), snapshots
+// snap[b][g] = bf16(W0 + state at p = g*L), with W0 from its bf16 planes W0p [f/8][d][8].
 // Snapshots are held as planes of 8 columns: [B][ngroups][f/8][d][8].
-hipError_t launch_update_bf16(const bf16_t *ZT, const bf16_t *VT, float *state, bf16_t *snap, const Layout &lay,
-                              hipStream_t s);
+hipError_t launch_update_bf16(const bf16_t *ZT, const bf16_t *VT, float *state, bf16_t *snap, const bf16_t *W0p,
+                              const Layout &lay, hipStream_t s);
 // P[b][g][t][s] = eta * <Z[gL+t], Z[gL+s]> if s/C < t/C else 0, for t, s < L.
 hipError_t launch_scores_bf16(const bf16_t *Z, bf16_t *P, float eta, const Layout &lay, hipStream_t s);
-// One snapshot [f/8][d][8] = bf16 of one fp32 state [d][f] (no update).
-hipError_t launch_state_to_snap_bf16(const float *state, bf16_t *snap, int d, int f, hipStream_t s);
+// One snapshot [f/8][d][8] = bf16(W0 + D) of fp32 W0 and state D, [d][f] each (no update).
+hipError_t launch_state_to_snap_bf16(const float *W0, const float *D, bf16_t *snap, int d, int f, hipStream_t s);
+// bf16 [d][f] -> planes [f/8][d][8].
+hipError_t launch_to_planes_bf16(const bf16_t *src, bf16_t *dst, int d, int f, hipStream_t s);
 // y[b][gL+t] = Z[gL+t] snap[b][g]^T + sum_s P[b][g][t][s] V[gL+s]; y is bf16, or fp32 with y_f32.
 hipError_t launch_out_bf16(const bf16_t *Z, const bf16_t *P, const bf16_t *snap, const bf16_t *VT, void *y,
                            int y_f32, const Layout &lay, hipStream_t s);
@@ -38,8 +41,9 @@ hipError_t launch_gather_vt_f32(const int32_t *ids, const float *E, int vocab, f
 // Wug: [2][f][d] (W_up then W_gate).
 hipError_t launch_a1_f32(const float *x, const float *Wug, float *Z, float *ZT, float eta, int write_zt,
                          const Layout &lay, hipStream_t s);
-hipError_t launch_update_f32(const float *ZT, const float *VT, float *state, float *snap, const Layout &lay,
-                             hipStream_t s);
+// state = D = W - W0; snapshots W0 + D ([B][ngroups][d][f]).
+hipError_t launch_update_f32(const float *ZT, const float *VT, float *state, float *snap, const float *W0,
+                             const Layout &lay, hipStream_t s);
 hipError_t launch_scores_f32(const float *Z, float *P, float eta, const Layout &lay, hipStream_t s);
 hipError_t launch_out_f32(const float *Z, const float *P, const float *snap, const float *VT, float *y,
                           const Layout &lay, hipStream_t s);
@@ -79,3 +83,7 @@ hipError_t launch_copy_f32(const float *src, float *dst, long long n, hipStream_
 // block.
 hipError_t launch_interleave_ug_bf16(const bf16_t *Wu, const bf16_t *Wg, bf16_t *Wug, int f, int d, hipStream_t s);
 hipError_t launch_bf16_to_f32(const bf16_t *src, float *dst, long long n, hipStream_t s);
+// dst[i] = v for i < n (fp32).
+hipError_t launch_fill_f32(float *dst, float v, long long n, hipStream_t s);
+// out[b][k] = W0[k] + D[b][k] for b < B, k < n (fp32): the weights of B sequences from their states.
+hipError_t launch_add_state_f32(const float *W0, const float *D, float *out, int B, long long n, hipStream_t s);

@@ -13,7 +13,8 @@
 //                         snapshot of W at the start of every group of G chunks
 //   4. group scores       P = eta * (Z Z^T) masked to earlier chunks of the group
 //   5. output GEMM        y = Z snapshot^T + P V
-//   6. optional copy of the final states to W_final
+//   6. optional W_final = W_down0 + D (the handle keeps each sequence's state as
+//                         D, the change since its last reset)
 // Steps 3-5 are the exclusive prefix over chunk updates (iplexlaw.co.kr sec. 6;
 // paperlayer.ai App. B) taken at two levels: across groups through the
 // snapshots, inside a group through the block-causal term. The result equals
@@ -133,7 +134,8 @@ struct ttt_handle {
   ttt_dtype dt = TTT_BF16;
   void *Wug = nullptr;      // bf16: [d/64][2f][64] (rows interleaved); f32: [2][f][d]
   float *W0 = nullptr;      // [d][f] fp32 image of W_down0
-  float *state = nullptr;   // [max_batch][d][f]
+  void *W0p = nullptr;      // bf16: W_down0 as planes [f/8][d][8] (the snapshot layout)
+  float *state = nullptr;   // [max_batch][d][f]: D = W - W_down0, the change since the last reset
   void *ws = nullptr;       // scratch
   size_t ws_bytes = 0;
   size_t fixed_bytes = 0;
@@ -166,6 +168,7 @@ void free_handle(ttt_handle *h) {
   (void)hipDeviceSynchronize();
   if (h->Wug) (void)hipFree(h->Wug);
   if (h->W0) (void)hipFree(h->W0);
+  if (h->W0p) (void)hipFree(h->W0p);
   if (h->state) (void)hipFree(h->state);
   if (h->conv_w) (void)hipFree(h->conv_w);
   if (h->Wt) (void)hipFree(h->Wt);
@@ -290,8 +293,7 @@ int forward_impl(ttt_handle *h, const void *x, const int32_t *ids, const void *E
       for (int i = 1; i <= kPhases; ++i) HIP_TRY(hipEventRecord(ev[i], s));
       close_events();
     }
-    if (W_final && B > 0)
-      HIP_TRY(hipMemcpyAsync(W_final, state, (size_t)B * df * 4, hipMemcpyDeviceToDevice, s));
+    if (W_final && B > 0) HIP_TRY(launch_add_state_f32(h->W0, state, W_final, B, (long long)df, s));
     return TTT_OK;
   }
 
@@ -347,10 +349,12 @@ int forward_impl(ttt_handle *h, const void *x, const int32_t *ids, const void *E
     }
     if (prof) HIP_TRY(hipEventRecord(ev[3], s));
     if (learn) {
-      HIP_TRY(launch_update_bf16((const bf16_t *)ZT, (const bf16_t *)VT, state, (bf16_t *)snap, lay, s));
+      HIP_TRY(launch_update_bf16((const bf16_t *)ZT, (const bf16_t *)VT, state, (bf16_t *)snap,
+                                 (const bf16_t *)h->W0p, lay, s));
     } else {
       for (int b = 0; b < B; ++b)
-        HIP_TRY(launch_state_to_snap_bf16(state + (size_t)b * df, (bf16_t *)snap + (size_t)b * df, h->d, h->f, s));
+        HIP_TRY(launch_state_to_snap_bf16(h->W0, state + (size_t)b * df, (bf16_t *)snap + (size_t)b * df, h->d,
+                                          h->f, s));
     }
     if (prof) HIP_TRY(hipEventRecord(ev[4], s));
     if (lay.intra) HIP_TRY(launch_scores_bf16((const bf16_t *)Z, (bf16_t *)P, h->eta, lay, s));
@@ -375,9 +379,9 @@ int forward_impl(ttt_handle *h, const void *x, const int32_t *ids, const void *E
     }
     if (prof) HIP_TRY(hipEventRecord(ev[3], s));
     if (learn) {
-      HIP_TRY(launch_update_f32((const float *)ZT, (const float *)VT, state, (float *)snap, lay, s));
+      HIP_TRY(launch_update_f32((const float *)ZT, (const float *)VT, state, (float *)snap, h->W0, lay, s));
     } else {
-      HIP_TRY(hipMemcpyAsync(snap, state, (size_t)B * df * 4, hipMemcpyDeviceToDevice, s));
+      HIP_TRY(launch_add_state_f32(h->W0, state, (float *)snap, B, (long long)df, s));
     }
     if (prof) HIP_TRY(hipEventRecord(ev[4], s));
     if (lay.intra) HIP_TRY(launch_scores_f32((const float *)Z, (float *)P, h->eta, lay, s));
@@ -386,7 +390,7 @@ int forward_impl(ttt_handle *h, const void *x, const int32_t *ids, const void *E
                            lay, s));
   }
   if (prof) HIP_TRY(hipEventRecord(ev[6], s));
-  if (W_final) HIP_TRY(hipMemcpyAsync(W_final, state, (size_t)B * df * 4, hipMemcpyDeviceToDevice, s));
+  if (W_final) HIP_TRY(launch_add_state_f32(h->W0, state, W_final, B, (long long)df, s));
   if (prof) {
     HIP_TRY(hipEventRecord(ev[7], s));
     close_events();
@@ -450,19 +454,20 @@ int ttt_init(ttt_handle **out, const void *W_up, const void *W_gate, const void 
   if (hipMalloc((void **)&h->W0, df * 4) != hipSuccess) return bail(TTT_E_NOMEM, "allocating W_down0 image");
   if (hipMalloc((void **)&h->state, df * 4 * max_batch) != hipSuccess)
     return bail(TTT_E_NOMEM, "allocating fast-weight states");
-  h->fixed_bytes = 2 * df * es + df * 4 + df * 4 * max_batch;
+  if (dt == TTT_BF16 && hipMalloc(&h->W0p, df * 2) != hipSuccess) return bail(TTT_E_NOMEM, "allocating W_down0 planes");
+  h->fixed_bytes = 2 * df * es + df * 4 + df * 4 * max_batch + (dt == TTT_BF16 ? df * 2 : 0);
   hipError_t e = hipSuccess;
   if (dt == TTT_BF16) {
     e = launch_interleave_ug_bf16((const bf16_t *)W_up, (const bf16_t *)W_gate, (bf16_t *)h->Wug, f, d, s);
     if (e == hipSuccess) e = launch_bf16_to_f32((const bf16_t *)W_down0, h->W0, (long long)df, s);
+    if (e == hipSuccess) e = launch_to_planes_bf16((const bf16_t *)W_down0, (bf16_t *)h->W0p, d, f, s);
   } else {
     e = hipMemcpyAsync(h->Wug, W_up, df * 4, hipMemcpyDeviceToDevice, s);
     if (e == hipSuccess)
       e = hipMemcpyAsync((float *)h->Wug + df, W_gate, df * 4, hipMemcpyDeviceToDevice, s);
     if (e == hipSuccess) e = hipMemcpyAsync(h->W0, W_down0, df * 4, hipMemcpyDeviceToDevice, s);
   }
-  for (int b = 0; b < max_batch && e == hipSuccess; ++b)
-    e = hipMemcpyAsync(h->state + (size_t)b * df, h->W0, df * 4, hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess) e = launch_fill_f32(h->state, 0.f, (long long)df * max_batch, s);
   if (e != hipSuccess) return bail(TTT_E_HIP, std::string("init copies: ") + hipGetErrorString(e));
   *out = h;
   return TTT_OK;
@@ -574,8 +579,7 @@ int ttt_reset(ttt_handle *h, int b, void *hip_stream) {
   hipStream_t s = (hipStream_t)hip_stream;
   const size_t df = (size_t)h->d * h->f;
   const int lo = b < 0 ? 0 : b, hi = b < 0 ? h->max_batch : b + 1;
-  for (int i = lo; i < hi; ++i)
-    HIP_TRY(hipMemcpyAsync(h->state + (size_t)i * df, h->W0, df * 4, hipMemcpyDeviceToDevice, s));
+  HIP_TRY(launch_fill_f32(h->state + (size_t)lo * df, 0.f, (long long)df * (hi - lo), s));
   return TTT_OK;
 }
 
@@ -638,7 +642,7 @@ int ttt_forward_docs(ttt_handle *h, const void *x, const int32_t *ids, const voi
     int s0 = 0;
     for (int j = 0; j <= doc_counts[b]; ++j) {
       const int s1 = j < doc_counts[b] ? doc_starts[k + j] : T;
-      if (j > 0) HIP_TRY(hipMemcpyAsync(h->state + (size_t)b * df, h->W0, df * 4, hipMemcpyDeviceToDevice, s));
+      if (j > 0) HIP_TRY(launch_fill_f32(h->state + (size_t)b * df, 0.f, (long long)df, s));
       const size_t row = ((size_t)b * T + s0) * h->d;
       const int rc = forward_impl(h, (const char *)x + row * es, ids + (size_t)b * (T + 1) + s0, E_tgt, vocab, 1,
                                   s1 - s0, (char *)y + row * ys, h->state + (size_t)b * df, nullptr, s);
@@ -647,8 +651,19 @@ int ttt_forward_docs(ttt_handle *h, const void *x, const int32_t *ids, const voi
     }
     k += doc_counts[b];
   }
-  if (W_final) HIP_TRY(hipMemcpyAsync(W_final, h->state, (size_t)B * df * 4, hipMemcpyDeviceToDevice, s));
+  if (W_final) HIP_TRY(launch_add_state_f32(h->W0, h->state, W_final, B, (long long)df, s));
   if (h->profiling) ++h->calls_pending;
+  return TTT_OK;
+}
+
+int ttt_state_delta(ttt_handle *h, float *dW, int B, void *hip_stream) {
+  if (!h) return fail(TTT_E_NULL, "handle is NULL");
+  if (B < 0 || B > h->max_batch) return fail(TTT_E_SHAPE, "B must be in [0, max_batch]");
+  if (B > 0 && !dW) return fail(TTT_E_NULL, "dW must be non-NULL");
+  if (B > 0 && misaligned(dW)) return fail(TTT_E_ARG, "dW must be 16-byte aligned");
+  const size_t df = (size_t)h->d * h->f;
+  if (B > 0)
+    HIP_TRY(hipMemcpyAsync(dW, h->state, (size_t)B * df * 4, hipMemcpyDeviceToDevice, (hipStream_t)hip_stream));
   return TTT_OK;
 }
 

@@ -44,6 +44,11 @@ extern "C" {
 typedef struct ttt_handle ttt_handle; /* opaque, owned by the library */
 
 /* Activation/weight element type. The fast-weight state is always fp32.
+ * The handle keeps each sequence's fast weight as D = W - W_down0, the change
+ * since its last reset, in fp32 (W_down0 is kept beside it): the updates are
+ * small next to W, and held this way they accumulate with fp32 relative
+ * precision even when each one is far below the fp32 resolution of W itself
+ * (as with clipped updates), also across calls.
  * TTT_F32:  x, W_up, W_gate, W_down0, E_tgt and y are float.
  * TTT_BF16: they are bfloat16 (uint16 bit patterns); matrix products run on
  *           bf16 MFMA with fp32 accumulation. */
@@ -96,8 +101,9 @@ int ttt_init(ttt_handle **out, const void *W_up, const void *W_gate, const void 
  *   E_tgt   : [vocab][d] target-embedding table (dtype of the handle).
  *   B       : 0 .. max_batch. T: tokens per sequence, 0 .. 2^23.
  *   y       : [B][T][d] output (dtype of the handle), written in full.
- *   W_final : optional [B][d][f] fp32 output; receives each sequence's state
- *             after the block (NULL = not wanted).
+ *   W_final : optional [B][d][f] fp32 output; receives each sequence's fast
+ *             weight after the block, W_down0 + D rounded to fp32 (NULL = not
+ *             wanted). ttt_state_delta gives D itself.
  *
  * x, E_tgt and y must be 16-byte aligned (TTT_E_ARG otherwise).
  *
@@ -136,7 +142,7 @@ int ttt_forward_docs(ttt_handle *h, const void *x, const int32_t *ids, const voi
 
 /*
  * ttt_reset — restore the fast weight of sequence b (or of every sequence if
- * b == -1) to W_down0: the document-boundary reset (paperlayer App. B;
+ * b == -1) to W_down0 (D = 0): the document-boundary reset (paperlayer App. B;
  * iplexlaw sec. 6). Queued on `hip_stream`.
  */
 int ttt_reset(ttt_handle *h, int b, void *hip_stream);
@@ -210,6 +216,18 @@ int ttt_set_target_conv(ttt_handle *h, const void *conv_w, int K, const void *W_
  * target reads the rows from E_tgt through the ids when vocab*d*2 < 2^31).
  */
 int ttt_set_clip(ttt_handle *h, float tau);
+
+/*
+ * ttt_state_delta — copy D = W - W_down0 of sequences 0 .. B-1, the change of
+ * each fast weight since its last reset (or init), to dW ([B][d][f] fp32,
+ * device, 16-byte aligned), queued on `hip_stream` after the work already
+ * there. Where the updates are much smaller than W (clipped updates at the
+ * pages' tau = 1e-5 move each element by about 1e-9 against |W| ~ 1e-2), the
+ * fp32 W_final cannot resolve them (its rounding alone is about 3% of D
+ * there), while D carries them at fp32 relative precision. B in [0,
+ * max_batch] (TTT_E_SHAPE otherwise); dW NULL with B > 0 is TTT_E_NULL.
+ */
+int ttt_state_delta(ttt_handle *h, float *dW, int B, void *hip_stream);
 
 /*
  * ttt_set_output_f32 — on a bf16 handle, later forward calls write y as fp32

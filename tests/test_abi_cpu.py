@@ -125,5 +125,7 @@ def test_null_handle_paths():
     assert L.ttt_phase_times(None, buf, 6) == -1
     n = ctypes.c_size_t()
     assert L.ttt_workspace_bytes(None, ctypes.byref(n)) == -1
+    assert L.ttt_set_output_f32(None, 1) == -1
+    assert L.ttt_state_delta(None, None, 1, None) == -1
     L.ttt_destroy(None)  # no-op
     assert "NULL" in ttt.ttt_last_error()

@@ -136,15 +136,21 @@ def test_clip_pages_threshold_4b(dtype):
     raw = [abs(w.eta) * np.linalg.norm(V[s:e].T @ Z[s:e]) for (s, e) in oracle.chunk_ranges(w.T, C)]
     assert min(raw) > 100 * tau  # every chunk is clipped, by a large factor
     del Z, V
-    y, Wf = _run(w, C, 0, tau)
+    lay = Layer(w, C=C)
+    ttt.ttt_set_clip(lay.h, tau)
+    y, Wf = lay.forward_np()
+    D = ttt.ttt_state_delta(lay.h, w.B).double().cpu().numpy()
     y_ref, W_ref = oracle.ttt_forward(w.x, w.ids, w.E_tgt, w.W_up, w.W_gate, w.W_down0, C, w.eta, clip_tau=tau)
     W0 = w.W_down0.astype(np.float64)
     dn = np.linalg.norm(W_ref[0] - W0)
     assert dn <= len(raw) * tau * (1 + 1e-9)  # the applied updates have norm tau each
     metric, tol = (rel_fro, BF16_TOL) if dtype == "bf16" else (max_rel, F32_TOL)
-    e_y, e_w, e_d = metric(y, y_ref), metric(Wf, W_ref), metric(Wf - W0, W_ref - W0)
-    print(f"  |W_final - W0| = {dn:.3e}; y err {e_y:.2e}, W_final err {e_w:.2e}, W_final - W_entry err {e_d:.2e}",
-          flush=True)
+    e_y, e_w, e_d = metric(y, y_ref), metric(Wf, W_ref), metric(D, W_ref - W0)
+    # W_final itself is W0 + D rounded to fp32, which cannot hold an update this small to 3e-2: the rounding of
+    # the exact result alone is about that large
+    floor = rel_fro(W_ref.astype(np.float32).astype(np.float64) - W0, W_ref - W0)
+    print(f"  |W_final - W0| = {dn:.3e}; y err {e_y:.2e}, W_final err {e_w:.2e}, D err {e_d:.2e} "
+          f"(fp32 W_final - W0: {metric(Wf - W0, W_ref - W0):.2e}, its rounding floor {floor:.2e})", flush=True)
     assert e_y <= tol and e_w <= tol and e_d <= tol
 
 
