@@ -12,6 +12,7 @@ from .binding import (  # noqa: F401
     lib,
     ttt_destroy,
     ttt_forward_chunked,
+    ttt_forward_chunked_noalloc,
     ttt_forward_docs,
     ttt_init,
     ttt_last_error,

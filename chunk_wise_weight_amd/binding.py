@@ -21,7 +21,7 @@ ERRORS = {-1: "TTT_E_NULL", -2: "TTT_E_SHAPE", -3: "TTT_E_DTYPE", -4: "TTT_E_NOM
           -6: "TTT_E_NODEV", -7: "TTT_E_ARG"}
 EXPORTS = ("ttt_init", "ttt_forward_chunked", "ttt_forward_docs", "ttt_reset", "ttt_destroy", "ttt_last_error",
            "ttt_set_group_chunks", "ttt_set_clip", "ttt_set_target_conv", "ttt_plan", "ttt_set_profiling", "ttt_phase_times",
-           "ttt_workspace_bytes", "ttt_set_output_f32", "ttt_state_delta")
+           "ttt_workspace_bytes", "ttt_set_output_f32", "ttt_state_delta", "ttt_forward_chunked_noalloc")
 
 _lib = None
 
@@ -72,6 +72,8 @@ def lib() -> ctypes.CDLL:
     L.ttt_set_output_f32.restype = i32
     L.ttt_state_delta.argtypes = [vp, vp, i32, vp]
     L.ttt_state_delta.restype = i32
+    L.ttt_forward_chunked_noalloc.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, vp, vp]
+    L.ttt_forward_chunked_noalloc.restype = i32
     _lib = L
     return L
 
@@ -179,6 +181,23 @@ def ttt_forward_chunked(h: Handle, x: torch.Tensor, ids: torch.Tensor, E_tgt: to
     B, T, y, W_final = _forward_args(h, x, ids, E_tgt, y, W_final, want_W_final)
     _check(lib().ttt_forward_chunked(h.ptr, _ptr(x), _ptr(ids), _ptr(E_tgt), int(E_tgt.shape[0]), int(B), int(T),
                                      _ptr(y), _ptr(W_final), _stream(stream)), "ttt_forward_chunked")
+    return y, W_final
+
+
+NOALLOC_WORKSPACE_BYTES = 64 << 20  # TTT_NOALLOC_WORKSPACE_BYTES in include/ttt.h
+
+
+def ttt_forward_chunked_noalloc(h: Handle, x: torch.Tensor, ids: torch.Tensor, E_tgt: torch.Tensor,
+                                y: torch.Tensor, W_final: Optional[torch.Tensor] = None,
+                                stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """ttt_forward_chunked with the library's fixed workspace: the call allocates nothing on the device.
+    y (and W_final, if wanted) must be given."""
+    if y is None:
+        raise ValueError("y must be given (the call allocates nothing)")
+    B, T, y, W_final = _forward_args(h, x, ids, E_tgt, y, W_final, False)
+    _check(lib().ttt_forward_chunked_noalloc(h.ptr, _ptr(x), _ptr(ids), _ptr(E_tgt), int(E_tgt.shape[0]), int(B),
+                                             int(T), _ptr(y), _ptr(W_final), _stream(stream)),
+           "ttt_forward_chunked_noalloc")
     return y, W_final
 
 

@@ -23,6 +23,7 @@
 
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/ttt.h"
@@ -118,6 +119,35 @@ int make_plan(int T, int C, int G_override, Plan &p) {
     p.ngroups = (int)((T + L - 1) / L);
   }
   p.intra = G > 1 ? 1 : 0;
+  return TTT_OK;
+}
+
+// Workspace of ttt_forward_chunked_noalloc: a file-scope device array, so that
+// entry point never allocates. Every GPU the library runs on holds its own
+// copy, at its own address, until the process ends. In host code the name is
+// only a stand-in: the device address comes from hipGetSymbolAddress, taken
+// once per device with that device current (in ttt_init) and kept in
+// g_scratch_ptr.
+constexpr size_t kNoAllocScratchBytes = TTT_NOALLOC_WORKSPACE_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+constexpr int kMaxDevices = 64;
+void *g_scratch_ptr[kMaxDevices] = {};
+std::mutex g_scratch_mu;
+
+// The device address of this device's `scratch` (dev current). Taken once per device.
+int scratch_ptr_for(int dev, void **out) {
+  if (dev < 0 || dev >= kMaxDevices) return fail(TTT_E_NODEV, "device index beyond the library's table");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return fail(TTT_E_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
   return TTT_OK;
 }
 
@@ -260,8 +290,11 @@ int ring_make_room(ttt_handle *h) {
 }
 
 // One forward over B sequences of T tokens whose states are state[0 .. B).
+// ext_ws: a caller-provided workspace of ext_cap bytes used instead of the
+// handle's scratch (NULL: the handle's, grown with hipMalloc when needed).
 int forward_impl(ttt_handle *h, const void *x, const int32_t *ids, const void *E_tgt, int vocab, int B, int T,
-                 void *y, float *state, float *W_final, hipStream_t s_in) {
+                 void *y, float *state, float *W_final, hipStream_t s_in, void *ext_ws = nullptr,
+                 size_t ext_cap = 0) {
   const bool learn = h->eta != 0.f;
   Plan pl;
   int rc = make_plan(T, h->C, learn ? h->G_override : 0, pl);
@@ -276,6 +309,24 @@ int forward_impl(ttt_handle *h, const void *x, const int32_t *ids, const void *E
   HIP_TRY(hipGetDevice(&dev));
   if (dev != h->device) return fail(TTT_E_ARG, "current device differs from the handle's device");
   const size_t df = (size_t)h->d * h->f;
+  const bool empty = B == 0 || T == 0;
+
+  const bool clip = learn && h->clip_tau > 0.f;
+  Layout lay{B, T, pl.T_pad, pl.C, pl.L, pl.ngroups, h->d, h->f, learn ? pl.intra : 0};
+  const int wspan = empty ? 1 : clip_wspan(lay, h->dt == TTT_BF16);
+  const bool conv = h->conv_K > 0 && (learn || lay.intra);
+  // With clipping on the plain bf16 target, the Gram kernel reads the target
+  // rows from E through the ids, and the gather runs after the clipping
+  // factors and writes V^T already scaled: no row-major copy of V, no
+  // scaling pass.
+  const bool gram_e =
+      clip && !conv && h->dt == TTT_BF16 && (long long)vocab * h->d * 2 < (1LL << 31);
+  Scratch sc = empty ? Scratch{} : scratch_layout(h, B, pl, learn, learn && pl.intra, clip, clip && !gram_e, wspan,
+                                                  conv);
+  if (ext_ws && sc.total > ext_cap)
+    return fail(TTT_E_SHAPE, "the call needs " + std::to_string(sc.total) + " bytes of workspace, more than the " +
+                                 std::to_string(ext_cap) + " available");
+
   const bool prof = h->profiling;
   if (prof) {
     rc = ring_make_room(h);
@@ -288,7 +339,7 @@ int forward_impl(ttt_handle *h, const void *x, const int32_t *ids, const void *E
     h->timed = true;
   };
   if (prof) HIP_TRY(hipEventRecord(ev[0], s));
-  if (B == 0 || T == 0) {
+  if (empty) {
     if (prof) {
       for (int i = 1; i <= kPhases; ++i) HIP_TRY(hipEventRecord(ev[i], s));
       close_events();
@@ -297,18 +348,7 @@ int forward_impl(ttt_handle *h, const void *x, const int32_t *ids, const void *E
     return TTT_OK;
   }
 
-  const bool clip = learn && h->clip_tau > 0.f;
-  Layout lay{B, T, pl.T_pad, pl.C, pl.L, pl.ngroups, h->d, h->f, learn ? pl.intra : 0};
-  const int wspan = clip_wspan(lay, h->dt == TTT_BF16);
-  const bool conv = h->conv_K > 0 && (learn || lay.intra);
-  // With clipping on the plain bf16 target, the Gram kernel reads the target
-  // rows from E through the ids, and the gather runs after the clipping
-  // factors and writes V^T already scaled: no row-major copy of V, no
-  // scaling pass.
-  const bool gram_e =
-      clip && !conv && h->dt == TTT_BF16 && (long long)vocab * h->d * 2 < (1LL << 31);
-  Scratch sc = scratch_layout(h, B, pl, learn, learn && pl.intra, clip, clip && !gram_e, wspan, conv);
-  if (sc.total > h->ws_bytes) {
+  if (!ext_ws && sc.total > h->ws_bytes) {
     HIP_TRY(hipStreamSynchronize(s));
     HIP_TRY(hipDeviceSynchronize());
     if (h->ws) HIP_TRY(hipFree(h->ws));
@@ -320,12 +360,12 @@ int forward_impl(ttt_handle *h, const void *x, const int32_t *ids, const void *E
     }
     h->ws_bytes = sc.total;
   }
-  void *VT = at(h->ws, sc.VT), *Z = at(h->ws, sc.Z), *ZT = at(h->ws, sc.ZT), *snap = at(h->ws, sc.snap),
-       *P = at(h->ws, sc.P);
-  void *Vrow = clip && !gram_e ? at(h->ws, sc.Vrow) : nullptr;
-  float *rowpart = (float *)at(h->ws, sc.rowpart), *cfac = (float *)at(h->ws, sc.cfac);
-  float *gv = (float *)at(h->ws, sc.gv);
-  void *U = at(h->ws, sc.U);
+  void *ws = ext_ws ? ext_ws : h->ws;
+  void *VT = at(ws, sc.VT), *Z = at(ws, sc.Z), *ZT = at(ws, sc.ZT), *snap = at(ws, sc.snap), *P = at(ws, sc.P);
+  void *Vrow = clip && !gram_e ? at(ws, sc.Vrow) : nullptr;
+  float *rowpart = (float *)at(ws, sc.rowpart), *cfac = (float *)at(ws, sc.cfac);
+  float *gv = (float *)at(ws, sc.gv);
+  void *U = at(ws, sc.U);
 
   if (h->dt == TTT_BF16) {
     if (conv) {
@@ -433,6 +473,9 @@ int ttt_init(ttt_handle **out, const void *W_up, const void *W_gate, const void 
   if (max_batch < 1 || max_batch > kMaxBatch) return fail(TTT_E_SHAPE, "max_batch must be in [1, 4096]");
   int dev = 0;
   int rc = check_device(&dev);
+  if (rc) return rc;
+  void *sp = nullptr;  // set-up of ttt_forward_chunked_noalloc's workspace on this device
+  rc = scratch_ptr_for(dev, &sp);
   if (rc) return rc;
 
   hipStream_t s = (hipStream_t)hip_stream;
@@ -595,6 +638,24 @@ int ttt_forward_chunked(ttt_handle *h, const void *x, const int32_t *ids, const 
   if (B > 0 && T > 0 && (misaligned(x) || misaligned(E_tgt) || misaligned(y)))
     return fail(TTT_E_ARG, "x, E_tgt and y must be 16-byte aligned");
   const int rc = forward_impl(h, x, ids, E_tgt, vocab, B, T, y, h->state, W_final, (hipStream_t)hip_stream);
+  if (rc == TTT_OK && h->profiling) ++h->calls_pending;
+  return rc;
+}
+
+int ttt_forward_chunked_noalloc(ttt_handle *h, const void *x, const int32_t *ids, const void *E_tgt, int vocab,
+                                int B, int T, void *y, float *W_final, void *hip_stream) {
+  if (!h) return fail(TTT_E_NULL, "handle is NULL");
+  if (B < 0 || B > h->max_batch) return fail(TTT_E_SHAPE, "B must be in [0, max_batch]");
+  if (T < 0 || T > kMaxT) return fail(TTT_E_SHAPE, "T must be in [0, 2^23]");
+  if (B > 0 && T > 0 && (!x || !ids || !E_tgt || !y)) return fail(TTT_E_NULL, "x, ids, E_tgt and y must be non-NULL");
+  if (B > 0 && T > 0 && vocab < 1) return fail(TTT_E_SHAPE, "vocab must be >= 1");
+  if (B > 0 && T > 0 && (misaligned(x) || misaligned(E_tgt) || misaligned(y)))
+    return fail(TTT_E_ARG, "x, E_tgt and y must be 16-byte aligned");
+  void *sp = nullptr;
+  int rc = scratch_ptr_for(h->device, &sp);  // resolved in ttt_init; a table lookup here
+  if (rc) return rc;
+  rc = forward_impl(h, x, ids, E_tgt, vocab, B, T, y, h->state, W_final, (hipStream_t)hip_stream, sp,
+                    kNoAllocScratchBytes);
   if (rc == TTT_OK && h->profiling) ++h->calls_pending;
   return rc;
 }

@@ -118,6 +118,29 @@ int ttt_forward_chunked(ttt_handle *h, const void *x, const int32_t *ids, const 
                         int T, void *y, float *W_final, void *hip_stream);
 
 /*
+ * ttt_forward_chunked_noalloc — ttt_forward_chunked for callers that cannot
+ * allocate device memory during the call: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. Same arguments,
+ * layouts, semantics and results (bit for bit) as ttt_forward_chunked, but the
+ * scratch of the call (target rows, Z and eta*Z^T, snapshots, group scores,
+ * clipping partials) lives in a fixed workspace of
+ * TTT_NOALLOC_WORKSPACE_BYTES inside the library: a file-scope device array
+ * that each GPU the library runs on holds until the process ends, its address
+ * taken in ttt_init. The call performs no hipMalloc, hipFree or other
+ * allocation. A call whose scratch would exceed the workspace returns
+ * TTT_E_SHAPE before any device work, naming the bytes it needs (roughly
+ * B*T*(4f + 2d) bytes plus 2*d*f per group of the plan on the bf16 path, so
+ * small layers and short blocks; larger calls use ttt_forward_chunked).
+ * Every call on one GPU shares that GPU's workspace, whichever handle it
+ * comes from, and leaves its contents behind (each call writes every part it
+ * reads): calls that overlap in time on one GPU, e.g. on two streams, race
+ * and must be ordered by the caller.
+ */
+#define TTT_NOALLOC_WORKSPACE_BYTES ((size_t)64 << 20)
+int ttt_forward_chunked_noalloc(ttt_handle *h, const void *x, const int32_t *ids, const void *E_tgt, int vocab,
+                                int B, int T, void *y, float *W_final, void *hip_stream);
+
+/*
  * ttt_forward_docs — ttt_forward_chunked over streams that pack several
  * documents (paperlayer App. B; iplexlaw sec. 6: the fast weight returns to its
  * initial value at document boundaries, so no state crosses between

@@ -127,5 +127,13 @@ def test_null_handle_paths():
     assert L.ttt_workspace_bytes(None, ctypes.byref(n)) == -1
     assert L.ttt_set_output_f32(None, 1) == -1
     assert L.ttt_state_delta(None, None, 1, None) == -1
+    assert L.ttt_forward_chunked_noalloc(None, None, None, None, 1, 1, 1, None, None, None) == -1
     L.ttt_destroy(None)  # no-op
     assert "NULL" in ttt.ttt_last_error()
+
+
+def test_noalloc_workspace_size_matches_header():
+    src = open(HEADER).read()
+    m = re.search(r"#define TTT_NOALLOC_WORKSPACE_BYTES \(\(size_t\)(\d+) << (\d+)\)", src)
+    assert m, "TTT_NOALLOC_WORKSPACE_BYTES not found"
+    assert int(m.group(1)) << int(m.group(2)) == binding.NOALLOC_WORKSPACE_BYTES
