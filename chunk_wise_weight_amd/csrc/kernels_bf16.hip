@@ -537,8 +537,8 @@ using CbW = CbLoad<BM, 2 * WN_W>;
 
 // ---------------------------------------------------------------------------
 // Up/gate GEMM with SwiGLU epilogue. i = token slot, j = interleaved W_ug row.
-// Writes Z column-blocked [B][f/64][T_pad][64] and eta*Z^T in planes of 8 tokens [B][T_pad/8][f][8].
-// grid: nx * ny workgroups, nx = 2f/256, ny = B*T_pad/256
+// Writes Z column-blocked [f/64][S][64] and eta*Z^T in planes of 8 tokens [S/8][f][8] (S scratch slots in all).
+// grid: nx * ny workgroups, nx = 2f/256, ny = S/256
 struct A1Args {
   const bf16_t *x;
   const bf16_t *Wug;
@@ -546,8 +546,10 @@ struct A1Args {
   bf16_t *ZT;
   float eta;
   int write_zt;
-  int T, T_pad, d, f;
+  long long S;
+  int d, f;
   int nx, ny;  // tiles along W_ug rows and along token slots
+  Seqs sq;
 };
 
 __global__ __launch_bounds__(NT_W, 1) void k_a1(A1Args p) {
@@ -555,18 +557,17 @@ __global__ __launch_bounds__(NT_W, 1) void k_a1(A1Args p) {
   int tx, ty;  // W_ug tile, token tile
   band_tile(xcd_tile(blockIdx.x, gridDim.x), p.nx, p.ny, 8, tx, ty);
   const int n0 = tx * 256;
-  const int m0 = ty * BM;
-  const int b = m0 / p.T_pad;
-  const int pos0 = m0 - b * p.T_pad;
+  const long long m0 = (long long)ty * BM;  // first slot of the tile
+  const SeqInfo si = p.sq.at(p.sq.of_tile(ty));
+  const int pos0 = (int)(m0 - si.slot0);
   SlabLoads<RmW, CbW> ld;
-  ld.a.init(p.x + ((long long)b * p.T + pos0) * p.d, p.d, p.T - pos0, p.d, wave_id(), threadIdx.x & 63);
+  ld.a.init(p.x + (si.xrow0 + pos0) * p.d, p.d, si.len - pos0, p.d, wave_id(), threadIdx.x & 63);
   ld.b.init(p.Wug + (long long)n0 * 64, 2LL * p.f * 64, 2 * p.f - n0, wave_id(), threadIdx.x & 63);
   Acc<NBJ_W> acc;
   acc_zero(acc);
   gemm_k<WN_W, NBJ_W, NSL_W, false>(acc, ring, ld, p.d / BK);
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w & 1, wn = w >> 1;
-  bf16_t *ZTb = p.ZT + (long long)b * p.f * p.T_pad;
   // the wave's two 32-column blocks are a matching (up, gate) pair of W_ug rows
   const int feat = (n0 + wn * 64) / 2 + (lane & 31);
   if (feat < p.f) {
@@ -576,14 +577,14 @@ __global__ __launch_bounds__(NT_W, 1) void k_a1(A1Args p) {
       const f32x16 &g = acc.v[bi][1];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int pos = pos0 + wm * 128 + bi * 32 + 8 * q + 4 * (lane >> 5);
+        const long long slot = m0 + wm * 128 + bi * 32 + 8 * q + 4 * (lane >> 5);
         float z[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) z[r] = silu_fast(g[4 * q + r]) * u[4 * q + r];
         if (p.write_zt)
-          store_nt(ZTb + ((long long)(pos >> 3) * p.f + feat) * 8 + (pos & 7), pack_bf16x2(p.eta * z[0], p.eta * z[1]),
+          store_nt(p.ZT + ((slot >> 3) * p.f + feat) * 8 + (slot & 7), pack_bf16x2(p.eta * z[0], p.eta * z[1]),
                    pack_bf16x2(p.eta * z[2], p.eta * z[3]));
-        bf16_t *zrow = p.Z + (((long long)b * (p.f / 64) + feat / 64) * p.T_pad + pos) * 64 + feat % 64;
+        bf16_t *zrow = p.Z + ((long long)(feat / 64) * p.S + slot) * 64 + feat % 64;
 #pragma unroll
         for (int r = 0; r < 4; ++r) store_nt(zrow + r * 64, f32_to_bf16(z[r]));
       }
@@ -718,11 +719,13 @@ struct UpdLds {
 struct UpdArgs {
   const bf16_t *ZT;
   const bf16_t *VT;
-  float *state;        // D [B][d][f]
+  const float *state_in;  // D [..][d][f], indexed by SeqInfo::state_in
+  float *state_out;       // D [..][d][f], indexed by SeqInfo::state_out
   bf16_t *snap;
-  const bf16_t *W0p;   // W0 as planes [f/8][d][8]
-  int T_pad, kend, L, ngroups, d, f;
+  const bf16_t *W0p;      // W0 as planes [f/8][d][8]
+  int L, d, f;
   int tile0;  // first 256 x 256 tile of this launch
+  Seqs sq;
 };
 
 // Snapshots W[a][i] are held as planes of 8 columns ([f/8][d][8]: element
@@ -803,7 +806,8 @@ __global__ __launch_bounds__(128 * WN, 1) void k_update(UpdArgs p) {
   const int nx = p.f / BM, ny = p.d / 256;
   const int n = xcd_tile(blockIdx.x, gridDim.x);
   const int t = p.tile0 + n / (256 / BN);
-  const int b = t / (nx * ny);
+  const int b = t / (nx * ny);  // sequence
+  const SeqInfo si = p.sq.at(b);
   int tx, ty;
   band_tile(t - b * nx * ny, nx, ny, 8, tx, ty);
   const int i0 = tx * BM;
@@ -816,29 +820,36 @@ __global__ __launch_bounds__(128 * WN, 1) void k_update(UpdArgs p) {
       (long long)(j0 + wn * 32 * NBJ + (lane & 31)) * p.f + i0 + wm * 128 + 4 * (lane >> 5);
   const long long lane_snap =
       (long long)((i0 + wm * 128) / 8) * 8 * p.d + (j0 + wn * 32 * NBJ + (lane & 31)) * 8 + 4 * (lane >> 5);
-  float *st = p.state + b * df + lane_off;
-  bf16_t *snap0 = p.snap + (long long)b * p.ngroups * df + lane_snap;
+  bf16_t *snap0 = p.snap + (long long)si.grp0 * df + lane_snap;
+  const int ngroups = si.len > p.L ? (si.len + p.L - 1) / p.L : 1;
+  // where this lane's part of the final state goes (null: nowhere)
+  float *st_out = si.state_out >= 0 ? p.state_out + si.state_out * df + lane_off : nullptr;
 
   Acc<NBJ> acc;
+  if (si.state_in >= 0) {
+    const float *st = p.state_in + si.state_in * df + lane_off;
 #pragma unroll
-  for (int bj = 0; bj < NBJ; ++bj) {
-    const float *row = st + (long long)bj * 32 * p.f;
+    for (int bj = 0; bj < NBJ; ++bj) {
+      const float *row = st + (long long)bj * 32 * p.f;
 #pragma unroll
-    for (int bi = 0; bi < 4; ++bi)
+      for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 v = *reinterpret_cast<const float4 *>(row + bi * 32 + 8 * q);
-        acc.v[bi][bj][4 * q + 0] = v.x;
-        acc.v[bi][bj][4 * q + 1] = v.y;
-        acc.v[bi][bj][4 * q + 2] = v.z;
-        acc.v[bi][bj][4 * q + 3] = v.w;
-      }
+        for (int q = 0; q < 4; ++q) {
+          const float4 v = *reinterpret_cast<const float4 *>(row + bi * 32 + 8 * q);
+          acc.v[bi][bj][4 * q + 0] = v.x;
+          acc.v[bi][bj][4 * q + 1] = v.y;
+          acc.v[bi][bj][4 * q + 2] = v.z;
+          acc.v[bi][bj][4 * q + 3] = v.w;
+        }
+    }
+  } else {
+    acc_zero(acc);  // a document start: W = W0
   }
 
-  // A: eta Z^T in planes of 8 tokens [T_pad/8][f][8]; B: V^T K-blocked [T_pad/64][d][64]
+  // A: eta Z^T in planes of 8 tokens [S/8][f][8]; B: V^T K-blocked [S/64][d][64]
   UpdLoads<WN, BN> ld;
-  ld.a.init(p.ZT + (long long)b * p.f * p.T_pad + (long long)i0 * 8, (long long)p.f * 8, lane);
-  ld.b.init(p.VT + (long long)b * p.d * p.T_pad + (long long)j0 * 64, (long long)p.d * 64, w, lane);
+  ld.a.init(p.ZT + (long long)si.slot0 * p.f + (long long)i0 * 8, (long long)p.f * 8, lane);
+  ld.b.init(p.VT + (long long)si.slot0 * p.d + (long long)j0 * 64, (long long)p.d * 64, w, lane);
   {
     // eta Z^T tile tx is shared by the tiles of its band (h of them) and their halves;
     // a V^T tile (or half) by the tiles along x of the XCD's range
@@ -846,7 +857,7 @@ __global__ __launch_bounds__(128 * WN, 1) void k_update(UpdArgs p) {
     const int halves = 256 / BN, half = n % halves;
     ld.init_pf(lds.sink, h * halves, (ty - band * 8) * halves + half, 16 / WN, tx % (16 / WN), w, lane);
   }
-  const int nk = p.kend / BK;
+  const int nk = (si.len + BK - 1) / BK;
   QRead qr;
   qr.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t *>(p.W0p), (short)0, (int)(df * 2), kBufferFlags);
   qr.vo = (uint32_t)(lane_snap * 2);
@@ -875,7 +886,7 @@ __global__ __launch_bounds__(128 * WN, 1) void k_update(UpdArgs p) {
   // A group spans L/BK stages, an even number (L is a multiple of 64), so
   // every group ends on an odd stage.
   int kt = 0;
-  for (; g < p.ngroups; ) {
+  for (; g < ngroups; ) {
     const int kt_last = g * (p.L / BK) - 1;  // last stage before group g starts
     stage_run<WN, NBJ, NSL, true>(acc, ring, cur, nxt, kt, kt_last, nk, wm, wn, lane, w, ld);
     pipelined_stage<WN, NBJ, NSL, true, true>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, w, ld, snapshot);
@@ -883,9 +894,10 @@ __global__ __launch_bounds__(128 * WN, 1) void k_update(UpdArgs p) {
   }
   stage_run<WN, NBJ, NSL, true>(acc, ring, cur, nxt, kt, nk, nk, wm, wn, lane, w, ld);
   // the final state D in fp32
+  if (!st_out) return;
 #pragma unroll
   for (int bj = 0; bj < NBJ; ++bj) {
-    float *row = st + (long long)bj * 32 * p.f;
+    float *row = st_out + (long long)bj * 32 * p.f;
 #pragma unroll
     for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
@@ -907,7 +919,9 @@ struct ScoreArgs {
   const bf16_t *Z;
   bf16_t *P;
   float eta;
-  int T, T_pad, L, C, ngroups, f, nt;
+  long long S;  // scratch slots in all (Z's block stride is S*64)
+  int L, C, f, nt;
+  Seqs sq;
   // tiles (it, jt) of a full group that hold an unmasked entry; npairs = 0:
   // every tile of the lower triangle gets a workgroup (long groups)
   int npairs;
@@ -930,26 +944,28 @@ __global__ __launch_bounds__(NT_W, 1) void k_scores(ScoreArgs p) {
     while (u > jt) u -= ++jt;  // u-th tile (it <= jt) of the lower triangle, jt-major
     it = u;
   }
-  const int g = bg % p.ngroups, b = bg / p.ngroups;
-  const long long gs = (long long)g * p.L;
-  const int Lg = (int)((p.T - gs) < p.L ? (p.T - gs) : p.L);
+  // bg: the group across all sequences
+  const SeqInfo si = p.sq.at(p.sq.of_group(bg));
+  const int gs = (bg - si.grp0) * p.L;       // first token of the group in its sequence
+  const int Lg = si.len - gs < p.L ? si.len - gs : p.L;
+  const int tp = (si.len + 255) & ~255;      // the sequence's slots
   const int i0 = it * BM, j0 = jt * 256;
   if (j0 >= Lg) return;
   // A tile whose every s lies in the chunk of its last t or later is all
   // masked; the output GEMM never reads it (it stops before that chunk).
   const int jl = (j0 + 255 < Lg - 1) ? j0 + 255 : Lg - 1;
   if (i0 / p.C >= jl / p.C) return;
-  const bf16_t *Zg = p.Z + ((long long)b * (p.f / 64) * p.T_pad + gs) * 64;  // Z column-blocked [f/64][T_pad][64]
-  const long long zblk = (long long)p.T_pad * 64;
+  const bf16_t *Zg = p.Z + ((long long)si.slot0 + gs) * 64;  // Z column-blocked [f/64][S][64]
+  const long long zblk = p.S * 64;
   SlabLoads<CbW, CbW> ld;
-  ld.a.init(Zg + (long long)i0 * 64, zblk, (int)(p.T_pad - gs - i0), wave_id(), threadIdx.x & 63);
-  ld.b.init(Zg + (long long)j0 * 64, zblk, (int)(p.T_pad - gs - j0), wave_id(), threadIdx.x & 63);
+  ld.a.init(Zg + (long long)i0 * 64, zblk, tp - gs - i0, wave_id(), threadIdx.x & 63);
+  ld.b.init(Zg + (long long)j0 * 64, zblk, tp - gs - j0, wave_id(), threadIdx.x & 63);
   Acc<NBJ_W> acc;
   acc_zero(acc);
   gemm_k<WN_W, NBJ_W, NSL_W, false>(acc, ring, ld, p.f / BK);
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w & 1, wn = w >> 1;
-  bf16_t *Pg = p.P + ((long long)b * p.ngroups + g) * p.L * p.L;
+  bf16_t *Pg = p.P + (long long)bg * p.L * p.L;
 #pragma unroll
   for (int bj = 0; bj < NBJ_W; ++bj) {
     const int t = j0 + wn * WC_W + bj * 32 + (lane & 31);
@@ -1012,9 +1028,11 @@ struct OutArgs {
   const bf16_t *P;
   const bf16_t *snap;
   const bf16_t *VT;
-  void *y;    // bf16 [B][T][d], or fp32 with y_f32
-  int T, T_pad, L, C, ngroups, d, f, intra;
+  void *y;    // bf16 rows of d, or fp32 with y_f32
+  long long S;  // scratch slots in all
+  int L, C, d, f, intra;
   int y_f32;
+  Seqs sq;
 };
 
 constexpr int LY_F = 260;  // [128 tokens][256 model dims + pad]: one half of an fp32 y tile
@@ -1026,21 +1044,21 @@ __global__ __launch_bounds__(NT_W, 1) void k_out(OutArgs p) {
   // one group's tiles are consecutive, token tiles fastest
   const int nx = p.d / BM, ny = (p.L + 255) / 256;
   const int t = xcd_tile(blockIdx.x, gridDim.x);
-  const int bg = t / (nx * ny), r = t - bg * nx * ny;
+  const int bg = t / (nx * ny), r = t - bg * nx * ny;  // bg: the group across all sequences
   const int i0 = (r / ny) * BM;
   const int j0 = (r % ny) * 256;
-  const int b = bg / p.ngroups, g = bg % p.ngroups;
-  const long long gs = (long long)g * p.L;
-  const int Lg = (int)((p.T - gs) < p.L ? (p.T - gs) : p.L);
+  const SeqInfo si = p.sq.at(p.sq.of_group(bg));
+  const int gs = (bg - si.grp0) * p.L;  // first token of the group in its sequence
+  const int Lg = si.len - gs < p.L ? si.len - gs : p.L;
+  const int tp = (si.len + 255) & ~255;
   if (j0 >= Lg) return;
   const int w8 = wave_id(), l8 = threadIdx.x & 63;
   Acc<NBJ_W> acc;
   acc_zero(acc);
   {  // segment 1: the group's snapshot ([f/8][d][8] planes) against Z, K = f
     SlabLoads<PlLoad<2 * WN_W>, CbW> ld;
-    ld.a.init(p.snap + ((long long)b * p.ngroups + g) * p.d * p.f + (long long)i0 * 8, (long long)p.d * 8, l8);
-    ld.b.init(p.Z + ((long long)b * (p.f / 64) * p.T_pad + gs + j0) * 64, (long long)p.T_pad * 64,
-              (int)(p.T_pad - gs - j0), w8, l8);
+    ld.a.init(p.snap + (long long)bg * p.d * p.f + (long long)i0 * 8, (long long)p.d * 8, l8);
+    ld.b.init(p.Z + ((long long)si.slot0 + gs + j0) * 64, p.S * 64, tp - gs - j0, w8, l8);
     gemm_k<WN_W, NBJ_W, NSL_W, true>(acc, ring, ld, p.f / BK);
   }
   if (p.intra) {  // segment 2: V^T against P over the tokens before the last row's chunk
@@ -1052,9 +1070,8 @@ __global__ __launch_bounds__(NT_W, 1) void k_out(OutArgs p) {
       // gs is a multiple of 64 (the plan's group length is), so V^T's slabs are whole blocks; columns of P
       // at or past kv read zero, so the V^T columns they meet contribute nothing
       SlabLoads<KbLoad<BM, 2 * WN_W>, RmLoad<BM, 2 * WN_W, true>> ld;
-      ld.a.init(p.VT + (long long)b * p.d * p.T_pad + (gs >> 6) * ((long long)p.d * 64) + (long long)i0 * 64,
-                (long long)p.d * 64, w8, l8);
-      ld.b.init(p.P + ((long long)b * p.ngroups + g) * p.L * p.L + (long long)j0 * p.L, p.L, p.L - j0, kv, w8, l8);
+      ld.a.init(p.VT + ((long long)si.slot0 + gs) * p.d + (long long)i0 * 64, (long long)p.d * 64, w8, l8);
+      ld.b.init(p.P + (long long)bg * p.L * p.L + (long long)j0 * p.L, p.L, p.L - j0, kv, w8, l8);
       __syncthreads();  // every wave is done reading the ring before it is refilled
       gemm_k<WN_W, NBJ_W, NSL_W, false>(acc, ring, ld, nk2);
     }
@@ -1065,7 +1082,7 @@ __global__ __launch_bounds__(NT_W, 1) void k_out(OutArgs p) {
   if (p.y_f32) {
     // fp32 y: two halves of 128 tokens (waves 0-3 hold tokens 0-127, waves 4-7 the rest), 1 KB rows
     float *lf = reinterpret_cast<float *>(smem);
-    float *yb = static_cast<float *>(p.y) + ((long long)b * p.T + gs + j0) * p.d + i0;
+    float *yb = static_cast<float *>(p.y) + (si.xrow0 + gs + j0) * p.d + i0;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       __syncthreads();  // the ring, or the first half's rows, are no longer read
@@ -1121,7 +1138,7 @@ __global__ __launch_bounds__(NT_W, 1) void k_out(OutArgs p) {
     const int idx = it * NT_W + tid;
     const int tr = idx >> 5, ch = idx & 31;
     if (j0 + tr < Lg)
-      *reinterpret_cast<uint4 *>(yb + ((long long)b * p.T + gs + j0 + tr) * p.d + i0 + ch * 8) =
+      *reinterpret_cast<uint4 *>(yb + (si.xrow0 + gs + j0 + tr) * p.d + i0 + ch * 8) =
           *reinterpret_cast<const uint4 *>(ly + tr * LY_P + ch * 8);
   }
 }
@@ -1149,6 +1166,7 @@ struct GramArgs {
   float *gv;           // scratch: 256 KB per workgroup of the grid
   float *rowpart;      // [B][T_pad/256][wspan][256]
   int T, T_pad, C, d, f, wspan, vocab;
+  long long S;         // B*T_pad: Z's block stride is S*64
 };
 
 constexpr int GR_P = 129;  // fp32 pitch of a [256][128] product tile in LDS (conflict-free row sums)
@@ -1203,10 +1221,10 @@ __global__ __launch_bounds__(NT_W, 1) void k_chunk_gram(GramArgs p) {
   __syncthreads();  // the second pass refills the ring
   acc_zero(acc);
   {
-    const bf16_t *Zb = p.Z + (long long)b * (p.f / 64) * p.T_pad * 64;  // Z column-blocked [f/64][T_pad][64]
+    const bf16_t *Zb = p.Z + (long long)b * p.T_pad * 64;  // Z column-blocked [f/64][S][64]
     SlabLoads<CbW, CbW> ld;
-    ld.a.init(Zb + (long long)s0 * 64, (long long)p.T_pad * 64, p.T_pad - s0, wv, lane);
-    ld.b.init(Zb + (long long)t0 * 64, (long long)p.T_pad * 64, p.T_pad - t0, wv, lane);
+    ld.a.init(Zb + (long long)s0 * 64, p.S * 64, p.T_pad - s0, wv, lane);
+    ld.b.init(Zb + (long long)t0 * 64, p.S * 64, p.T_pad - t0, wv, lane);
     gemm_k<WN_W, NBJ_W, NSL_W, false>(acc, ring, ld, p.f / BK);
   }
   // products of same-chunk pairs, in place of G_Z: row s0 + sl shares column
@@ -1260,28 +1278,32 @@ __global__ __launch_bounds__(NT_W, 1) void k_chunk_gram(GramArgs p) {
 }
 
 // ---------------------------------------------------------------------------
-// Target gather, transposed and K-blocked: V^T[b][p/64][a][p%64] = E[ids[b][p+1]][a].
-// A 64-slot x 64-feature tile passes through LDS so both the row reads of E and
+// Target gather, transposed and K-blocked: V^T[p/64][a][p%64] = E[ids of slot p's next token][a] (slots
+// across all sequences). A 64-slot x 64-feature tile passes through LDS so both the row reads of E and
 // the writes (one contiguous 8 KB block) are 16 B per lane. With Vrow non-null
-// the rows are also written row-major, Vrow[b][p][a] (used by update clipping).
-// With cfac non-null, slot p is scaled by the clipping factor cfac[b][p/C]
+// the rows are also written row-major, Vrow[p][a] (used by update clipping).
+// With cfac non-null, position t of sequence b is scaled by the clipping factor cfac[b][t/C]
 // (bf16 -> fp32, times the factor, rounded to bf16).
-// grid: (T_pad/64, d/64, B)
+// grid: (S/64, d/64)
 __global__ __launch_bounds__(256) void k_gather_vt(const int32_t *ids, const bf16_t *E, int vocab, bf16_t *VT,
-                                                   bf16_t *Vrow, const float *cfac, int C, int nchunks, int T,
-                                                   int T_pad, int d) {
+                                                   bf16_t *Vrow, const float *cfac, int C, int nchunks, int d,
+                                                   Seqs sq) {
   __shared__ __attribute__((aligned(16))) bf16_t tile[64][72];
-  const int p0 = blockIdx.x * 64, a0 = blockIdx.y * 64, b = blockIdx.z;
+  const long long p0 = (long long)blockIdx.x * 64;
+  const int a0 = blockIdx.y * 64;
+  const int b = sq.of_tile((int)(p0 / 256));
+  const SeqInfo si = sq.at(b);
+  const int q0 = (int)(p0 - si.slot0);  // position of the block's first slot in its sequence
   const int tid = threadIdx.x, seg = tid & 7;
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
     const int pl = pass * 32 + (tid >> 3);
-    const int pos = p0 + pl;
+    const int pos = q0 + pl;
     int id = -1;
-    if (pos < T) id = ids[(long long)b * (T + 1) + pos + 1];
+    if (pos < si.len) id = ids[si.id0 + pos + 1];
     uint4 v = make_uint4(0u, 0u, 0u, 0u);
     if (id >= 0 && id < vocab) v = *reinterpret_cast<const uint4 *>(E + (long long)id * d + a0 + seg * 8);
-    if (cfac && pos < T) {
+    if (cfac && pos < si.len) {
       const float c = cfac[(long long)b * nchunks + pos / C];
       bf16_t *e = reinterpret_cast<bf16_t *>(&v);
 #pragma unroll
@@ -1291,10 +1313,10 @@ __global__ __launch_bounds__(256) void k_gather_vt(const int32_t *ids, const bf1
     // reads below take one column from rows 8 apart, which the plain layout
     // puts in the same banks
     *reinterpret_cast<uint4 *>(&tile[pl][(seg ^ ((pl >> 3) & 7)) * 8]) = v;
-    if (Vrow) *reinterpret_cast<uint4 *>(Vrow + ((long long)b * T_pad + pos) * d + a0 + seg * 8) = v;
+    if (Vrow) *reinterpret_cast<uint4 *>(Vrow + (p0 + pl) * d + a0 + seg * 8) = v;
   }
   __syncthreads();
-  bf16_t *blk = VT + ((long long)b * (T_pad / 64) + blockIdx.x) * d * 64;
+  bf16_t *blk = VT + (long long)blockIdx.x * d * 64;
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
     const int al = pass * 32 + (tid >> 3);
@@ -1311,10 +1333,11 @@ __global__ __launch_bounds__(256) void k_gather_vt(const int32_t *ids, const bf1
 
 hipError_t launch_gather_vt_bf16(const int32_t *ids, const bf16_t *E, int vocab, bf16_t *VT, bf16_t *Vrow,
                                  const float *cfac, const Layout &lay, hipStream_t s) {
-  dim3 grid(lay.T_pad / 64, lay.d / 64, lay.B);
+  if (lay.n_slots() / 64 >= (1LL << 31)) return hipErrorInvalidConfiguration;
+  dim3 grid((unsigned)(lay.n_slots() / 64), lay.d / 64, 1);
   const int nchunks = (int)((lay.T + (long long)lay.C - 1) / lay.C);
-  hipLaunchKernelGGL(k_gather_vt, grid, dim3(256), 0, s, ids, E, vocab, VT, Vrow, cfac, lay.C, nchunks, lay.T,
-                     lay.T_pad, lay.d);
+  hipLaunchKernelGGL(k_gather_vt, grid, dim3(256), 0, s, ids, E, vocab, VT, Vrow, cfac, lay.C, nchunks, lay.d,
+                     lay.seqs());
   return hipGetLastError();
 }
 
@@ -1323,7 +1346,8 @@ hipError_t launch_chunk_gram_bf16(const bf16_t *Z, const bf16_t *Vrow, const bf1
   const long long n = (long long)lay.B * (lay.T_pad / 256) * wspan;
   if (n >= (1LL << 31) / 8) return hipErrorInvalidConfiguration;
   if (!Vrow && (long long)vocab * lay.d * 2 >= (1LL << 31)) return hipErrorInvalidValue;
-  GramArgs p{Z, Vrow, E, ids, gv, rowpart, lay.T, lay.T_pad, lay.C, lay.d, lay.f, wspan, vocab};
+  GramArgs p{Z, Vrow, E, ids, gv, rowpart, lay.T, lay.T_pad, lay.C, lay.d, lay.f, wspan, vocab,
+             (long long)lay.B * lay.T_pad};
   if (Vrow)
     hipLaunchKernelGGL(k_chunk_gram<false>, dim3((unsigned)n), dim3(NT_W), 0, s, p);
   else
@@ -1334,9 +1358,9 @@ hipError_t launch_chunk_gram_bf16(const bf16_t *Z, const bf16_t *Vrow, const bf1
 hipError_t launch_a1_bf16(const bf16_t *x, const bf16_t *Wug, bf16_t *Z, bf16_t *ZT, float eta, int write_zt,
                           const Layout &lay, hipStream_t s) {
   const int nx = (2 * lay.f + 255) / 256;
-  const long long ny = (long long)lay.B * lay.T_pad / BM;
+  const long long ny = lay.n_slots() / BM;
   if (nx * ny >= (1LL << 31)) return hipErrorInvalidConfiguration;
-  A1Args p{x, Wug, Z, ZT, eta, write_zt, lay.T, lay.T_pad, lay.d, lay.f, nx, (int)ny};
+  A1Args p{x, Wug, Z, ZT, eta, write_zt, lay.n_slots(), lay.d, lay.f, nx, (int)ny, lay.seqs()};
   hipLaunchKernelGGL(k_a1, dim3((unsigned)(nx * ny)), dim3(NT_W), 0, s, p);
   return hipGetLastError();
 }
@@ -1351,16 +1375,15 @@ hipError_t launch_target_gemm_bf16(const bf16_t *U, const bf16_t *WtT, bf16_t *V
   return hipGetLastError();
 }
 
-hipError_t launch_update_bf16(const bf16_t *ZT, const bf16_t *VT, float *state, bf16_t *snap, const bf16_t *W0p,
-                              const Layout &lay, hipStream_t s) {
-  const int kend = (int)round_up_ll(lay.T, BK);
-  const long long tiles = (long long)lay.B * (lay.f / BM) * (lay.d / 256);
+hipError_t launch_update_bf16(const bf16_t *ZT, const bf16_t *VT, const float *state_in, float *state_out,
+                              bf16_t *snap, const bf16_t *W0p, const Layout &lay, int cus, hipStream_t s) {
+  const long long tiles = (long long)lay.n_seq() * (lay.f / BM) * (lay.d / 256);
   if (tiles * 2 >= (1LL << 31)) return hipErrorInvalidConfiguration;
-  // whole rounds on the wide configuration, a last round of <= 128 tiles as halves
-  const int cus = 256;
+  // whole rounds on the wide configuration, a last round of <= cus/2 tiles as halves
+  if (cus < 2) cus = 2;
   const long long rem = tiles % cus;
   const long long whole = rem <= cus / 2 ? tiles - rem : tiles;
-  UpdArgs p{ZT, VT, state, snap, W0p, lay.T_pad, kend, lay.L, lay.ngroups, lay.d, lay.f, 0};
+  UpdArgs p{ZT, VT, state_in, state_out, snap, W0p, lay.L, lay.d, lay.f, 0, lay.seqs()};
   if (whole > 0) hipLaunchKernelGGL((k_update<WN_W, NBJ_W, NSL_W>), dim3((unsigned)whole), dim3(NT_W), 0, s, p);
   if (tiles > whole) {
     p.tile0 = (int)whole;
@@ -1371,7 +1394,7 @@ hipError_t launch_update_bf16(const bf16_t *ZT, const bf16_t *VT, float *state, 
 
 hipError_t launch_scores_bf16(const bf16_t *Z, bf16_t *P, float eta, const Layout &lay, hipStream_t s) {
   const int nt = (lay.L + 255) / 256;
-  ScoreArgs p{Z, P, eta, lay.T, lay.T_pad, lay.L, lay.C, lay.ngroups, lay.f, nt, 0, {}, {}};
+  ScoreArgs p{Z, P, eta, lay.n_slots(), lay.L, lay.C, lay.f, nt, lay.seqs(), 0, {}, {}};
   if (nt * (nt + 1) / 2 <= kMaxScorePairs) {
     // the tiles of a full group that the kernel would not skip, jt-major
     for (int jt = 0; jt < nt; ++jt) {
@@ -1385,7 +1408,7 @@ hipError_t launch_scores_bf16(const bf16_t *Z, bf16_t *P, float eta, const Layou
     }
     if (p.npairs == 0) return hipSuccess;  // one chunk per group: no within-group term
   }
-  const long long n = (long long)lay.B * lay.ngroups * (p.npairs > 0 ? p.npairs : nt * (nt + 1) / 2);
+  const long long n = lay.n_groups() * (p.npairs > 0 ? p.npairs : nt * (nt + 1) / 2);
   if (n >= (1LL << 31)) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(k_scores, dim3((unsigned)n), dim3(NT_W), 0, s, p);
   return hipGetLastError();
@@ -1410,8 +1433,8 @@ hipError_t launch_to_planes_bf16(const bf16_t *src, bf16_t *dst, int d, int f, h
 
 hipError_t launch_out_bf16(const bf16_t *Z, const bf16_t *P, const bf16_t *snap, const bf16_t *VT, void *y,
                            int y_f32, const Layout &lay, hipStream_t s) {
-  OutArgs p{Z, P, snap, VT, y, lay.T, lay.T_pad, lay.L, lay.C, lay.ngroups, lay.d, lay.f, lay.intra, y_f32};
-  const long long n = (long long)lay.B * lay.ngroups * (lay.d / BM) * ((lay.L + 255) / 256);
+  OutArgs p{Z, P, snap, VT, y, lay.n_slots(), lay.L, lay.C, lay.d, lay.f, lay.intra, y_f32, lay.seqs()};
+  const long long n = lay.n_groups() * (lay.d / BM) * ((lay.L + 255) / 256);
   if (n >= (1LL << 31)) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(k_out, dim3((unsigned)n), dim3(NT_W), 0, s, p);
   return hipGetLastError();

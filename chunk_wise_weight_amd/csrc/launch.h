@@ -4,22 +4,24 @@
 #include "common.h"
 
 // ---- bf16 path: MFMA kernels (kernels_bf16.hip) ----
-// V^T[b][a][p] = E[ids[b][p+1]][a] for p < T and a valid id, else 0; K-blocked [B][T_pad/64][d][64].
-// Vrow (nullable): the same rows row-major, [B][T_pad][d]. cfac (nullable): clipping factors
-// [B][ceil(T/C)]; slot p is scaled by cfac[b][p/C].
+// V^T over the scratch slots of all sequences: slot p (position t of sequence b) holds E[ids[b][t+1]] for
+// t < T and a valid id, else 0; K-blocked [S/64][d][64]. Vrow (nullable): the same rows row-major, [S][d].
+// cfac (nullable; batch layout only): clipping factors [B][ceil(T/C)]; position t is scaled by cfac[b][t/C].
 hipError_t launch_gather_vt_bf16(const int32_t *ids, const bf16_t *E, int vocab, bf16_t *VT, bf16_t *Vrow,
                                  const float *cfac, const Layout &lay, hipStream_t s);
-// Z = SiLU(x W_gate^T) * (x W_up^T) -> Z column-blocked [B][f/64][T_pad][64] (bf16 path) and ZT = eta*Z^T in
-// planes of 8 tokens [B][T_pad/8][f][8].
+// Z = SiLU(x W_gate^T) * (x W_up^T) -> Z column-blocked [f/64][S][64] (bf16 path; S scratch slots in all) and
+// ZT = eta*Z^T in planes of 8 tokens [S/8][f][8].
 // Wug: 2f rows of d, interleaved in blocks of 32 (32 up rows, then the matching 32 gate rows), held K-blocked
 // by 64 columns: [d/64][2f][64].
 hipError_t launch_a1_bf16(const bf16_t *x, const bf16_t *Wug, bf16_t *Z, bf16_t *ZT, float eta, int write_zt,
                           const Layout &lay, hipStream_t s);
-// state[b] += sum_p ZT[b][:, p] VT[b][:, p]^T (as W[a][i] layout; the state is D = W - W0), snapshots
-// snap[b][g] = bf16(W0 + state at p = g*L), with W0 from its bf16 planes W0p [f/8][d][8].
-// Snapshots are held as planes of 8 columns: [B][ngroups][f/8][d][8].
-hipError_t launch_update_bf16(const bf16_t *ZT, const bf16_t *VT, float *state, bf16_t *snap, const bf16_t *W0p,
-                              const Layout &lay, hipStream_t s);
+// For each sequence (of the batch, or document): D += sum_p ZT[:, p] VT[:, p]^T over its slots (W[a][i]
+// layout; the state is D = W - W0), from state_in[state_in index] or zero, into state_out[state_out index];
+// snapshot k of a sequence = bf16(W0 + D at its token k*L), with W0 from its bf16 planes W0p [f/8][d][8].
+// Snapshots are planes of 8 columns, [groups in all][f/8][d][8]. cus: compute units of the device (a last
+// partial round of at most cus/2 tiles runs as half tiles).
+hipError_t launch_update_bf16(const bf16_t *ZT, const bf16_t *VT, const float *state_in, float *state_out,
+                              bf16_t *snap, const bf16_t *W0p, const Layout &lay, int cus, hipStream_t s);
 // P[b][g][t][s] = eta * <Z[gL+t], Z[gL+s]> if s/C < t/C else 0, for t, s < L.
 hipError_t launch_scores_bf16(const bf16_t *Z, bf16_t *P, float eta, const Layout &lay, hipStream_t s);
 // One snapshot [f/8][d][8] = bf16(W0 + D) of fp32 W0 and state D, [d][f] each (no update).

@@ -25,6 +25,7 @@
 #include <cstring>
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include "../../include/ttt.h"
 #include "launch.h"
@@ -159,6 +160,11 @@ struct ttt_handle {
   float clip_tau = 0.f;     // > 0: Frobenius clipping of each chunk update
   int conv_K = 0;           // > 0: general target with K taps
   int y_f32 = 0;            // bf16 handle: y written as fp32
+  int cus = 256;            // compute units of the device
+  void *pin = nullptr;      // pinned host staging of the packed-documents tables
+  size_t pin_bytes = 0;
+  hipEvent_t pin_ev = nullptr;  // recorded after the last copy out of `pin`
+  bool pin_used = false;
   float *conv_w = nullptr;  // [K][d] fp32 tap weights
   void *Wt = nullptr;       // bf16: W_target^T [d][d]; f32: W_target [d][d]
   ttt_dtype dt = TTT_BF16;
@@ -203,6 +209,8 @@ void free_handle(ttt_handle *h) {
   if (h->conv_w) (void)hipFree(h->conv_w);
   if (h->Wt) (void)hipFree(h->Wt);
   if (h->ws) (void)hipFree(h->ws);
+  if (h->pin) (void)hipHostFree(h->pin);
+  if (h->pin_ev) (void)hipEventDestroy(h->pin_ev);
   if (h->events_made)
     for (auto &set : h->ev)
       for (auto &e : set) (void)hipEventDestroy(e);
@@ -210,7 +218,7 @@ void free_handle(ttt_handle *h) {
 }
 
 struct Scratch {
-  void *VT, *Z, *ZT, *snap, *P, *Vrow, *rowpart, *cfac, *U, *gv;
+  void *VT, *Z, *ZT, *snap, *P, *Vrow, *rowpart, *cfac, *U, *gv, *tabs, *state_tmp;
   size_t total;
 };
 
@@ -219,45 +227,54 @@ bool misaligned(const void *p) { return ((uintptr_t)p & 15) != 0; }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-Scratch scratch_layout(const ttt_handle *h, int B, const Plan &pl, bool need_zt, bool need_p, bool clip,
-                       bool need_vrow, int wspan, bool conv) {
+// Scratch of one call over S slots and G snapshot groups of L tokens (lay), for B caller sequences.
+// tab_bytes: the packed-documents tables (0 otherwise), followed by B fp32 states for their final values.
+Scratch scratch_layout(const ttt_handle *h, const Layout &lay, bool need_zt, bool need_p, bool clip,
+                       bool need_vrow, int wspan, bool conv, size_t tab_bytes) {
   const size_t es = h->dt == TTT_BF16 ? 2 : 4;
-  const size_t vt = align256(es * (size_t)B * h->d * pl.T_pad);
-  const size_t z = align256(es * (size_t)B * pl.T_pad * h->f);
+  const size_t S = (size_t)lay.n_slots(), G = (size_t)lay.n_groups();
+  const size_t vt = align256(es * S * h->d);
+  const size_t z = align256(es * S * h->f);
   const size_t zt = need_zt ? z : 0;
-  const size_t sn = align256(es * (size_t)B * pl.ngroups * h->d * h->f);
-  const size_t pp = need_p ? align256(es * (size_t)B * pl.ngroups * pl.L * pl.L) : 0;
-  const size_t vr = need_vrow ? align256(es * (size_t)B * pl.T_pad * h->d) : 0;
-  const size_t rp = clip ? align256(4 * (size_t)B * (pl.T_pad / 256) * wspan * 256) : 0;
-  const size_t cf = clip ? align256(4 * (size_t)B * ((pl.T_pad + pl.C - 1) / pl.C)) : 0;
-  const size_t uu = conv ? align256(es * (size_t)B * pl.T_pad * h->d) : 0;
-  Layout lay{B, 0, pl.T_pad, pl.C, pl.L, pl.ngroups, h->d, h->f, 0};
+  const size_t sn = align256(es * G * h->d * h->f);
+  const size_t pp = need_p ? align256(es * G * lay.L * lay.L) : 0;
+  const size_t vr = need_vrow ? align256(es * S * h->d) : 0;
+  const size_t rp = clip ? align256(4 * S * wspan) : 0;
+  const size_t cf = clip ? align256(4 * (size_t)lay.B * ((lay.T_pad + lay.C - 1) / lay.C)) : 0;
+  const size_t uu = conv ? align256(es * S * h->d) : 0;
   const size_t gvb = clip && h->dt == TTT_BF16 ? align256(clip_gram_scratch_bytes(lay, wspan)) : 0;
+  const size_t tb = align256(tab_bytes);
+  const size_t stt = tab_bytes ? align256((size_t)lay.B * h->d * h->f * 4) : 0;
   Scratch s;
   size_t off = 0;
-  s.VT = (void *)off;
-  off += vt;
-  s.Z = (void *)off;
-  off += z;
-  s.ZT = (void *)off;
-  off += zt;
-  s.snap = (void *)off;
-  off += sn;
-  s.P = (void *)off;
-  off += pp;
-  s.Vrow = (void *)off;
-  off += vr;
-  s.rowpart = (void *)off;
-  off += rp;
-  s.cfac = (void *)off;
-  off += cf;
-  s.U = (void *)off;
-  off += uu;
-  s.gv = (void *)off;
-  off += gvb;
+  auto take = [&](void *&ptr, size_t n) {
+    ptr = (void *)off;
+    off += n;
+  };
+  take(s.VT, vt);
+  take(s.Z, z);
+  take(s.ZT, zt);
+  take(s.snap, sn);
+  take(s.P, pp);
+  take(s.Vrow, vr);
+  take(s.rowpart, rp);
+  take(s.cfac, cf);
+  take(s.U, uu);
+  take(s.gv, gvb);
+  take(s.tabs, tb);
+  take(s.state_tmp, stt);
   s.total = off;
   return s;
 }
+
+// Packed documents as sequences of their own (bf16 path): the host tables.
+struct DocPlan {
+  std::vector<SeqInfo> seqs;
+  std::vector<int> tile_seq, group_seq;
+  long long S = 0;  // slots
+  long long G = 0;  // groups
+  size_t bytes() const { return seqs.size() * sizeof(SeqInfo) + (tile_seq.size() + group_seq.size()) * 4; }
+};
 
 void *at(void *base, void *off) { return (char *)base + (size_t)off; }
 
@@ -292,12 +309,18 @@ int ring_make_room(ttt_handle *h) {
 // One forward over B sequences of T tokens whose states are state[0 .. B).
 // ext_ws: a caller-provided workspace of ext_cap bytes used instead of the
 // handle's scratch (NULL: the handle's, grown with hipMalloc when needed).
+// dp: packed documents run as sequences of their own (bf16 path, eta != 0, no
+// clipping, plain target), with the plan dpl shared by every document.
 int forward_impl(ttt_handle *h, const void *x, const int32_t *ids, const void *E_tgt, int vocab, int B, int T,
                  void *y, float *state, float *W_final, hipStream_t s_in, void *ext_ws = nullptr,
-                 size_t ext_cap = 0) {
+                 size_t ext_cap = 0, const DocPlan *dp = nullptr, const Plan *dpl = nullptr) {
   const bool learn = h->eta != 0.f;
   Plan pl;
-  int rc = make_plan(T, h->C, learn ? h->G_override : 0, pl);
+  int rc = TTT_OK;
+  if (dp)
+    pl = *dpl;
+  else
+    rc = make_plan(T, h->C, learn ? h->G_override : 0, pl);
   if (rc) return rc;
   if (!learn && pl.ngroups > 0) {  // no updates: one group, the entry state serves every chunk
     pl.ngroups = 1;
@@ -313,6 +336,12 @@ int forward_impl(ttt_handle *h, const void *x, const int32_t *ids, const void *E
 
   const bool clip = learn && h->clip_tau > 0.f;
   Layout lay{B, T, pl.T_pad, pl.C, pl.L, pl.ngroups, h->d, h->f, learn ? pl.intra : 0};
+  if (dp) {
+    lay.nseq = (int)dp->seqs.size();
+    lay.S = (int)dp->S;
+    lay.G = (int)dp->G;
+    lay.tab = true;  // the table pointers are set to its device copy below
+  }
   const int wspan = empty ? 1 : clip_wspan(lay, h->dt == TTT_BF16);
   const bool conv = h->conv_K > 0 && (learn || lay.intra);
   // With clipping on the plain bf16 target, the Gram kernel reads the target
@@ -321,8 +350,8 @@ int forward_impl(ttt_handle *h, const void *x, const int32_t *ids, const void *E
   // scaling pass.
   const bool gram_e =
       clip && !conv && h->dt == TTT_BF16 && (long long)vocab * h->d * 2 < (1LL << 31);
-  Scratch sc = empty ? Scratch{} : scratch_layout(h, B, pl, learn, learn && pl.intra, clip, clip && !gram_e, wspan,
-                                                  conv);
+  Scratch sc = empty ? Scratch{} : scratch_layout(h, lay, learn, learn && pl.intra, clip, clip && !gram_e, wspan,
+                                                  conv, dp ? dp->bytes() : 0);
   if (ext_ws && sc.total > ext_cap)
     return fail(TTT_E_SHAPE, "the call needs " + std::to_string(sc.total) + " bytes of workspace, more than the " +
                                  std::to_string(ext_cap) + " available");
@@ -366,6 +395,37 @@ int forward_impl(ttt_handle *h, const void *x, const int32_t *ids, const void *E
   float *rowpart = (float *)at(ws, sc.rowpart), *cfac = (float *)at(ws, sc.cfac);
   float *gv = (float *)at(ws, sc.gv);
   void *U = at(ws, sc.U);
+  float *state_out = state;
+  if (dp) {
+    // the tables, through pinned staging (the previous call's copy out of it must have finished)
+    const size_t nb = dp->bytes();
+    if (h->pin_used) HIP_TRY(hipEventSynchronize(h->pin_ev));
+    if (nb > h->pin_bytes) {
+      if (h->pin) HIP_TRY(hipHostFree(h->pin));
+      h->pin = nullptr;
+      h->pin_bytes = 0;
+      if (hipHostMalloc(&h->pin, nb) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(TTT_E_NOMEM, "allocating pinned staging for the document tables");
+      }
+      h->pin_bytes = nb;
+    }
+    if (!h->pin_ev) HIP_TRY(hipEventCreateWithFlags(&h->pin_ev, hipEventDisableTiming));
+    char *hp = (char *)h->pin;
+    const size_t b0 = dp->seqs.size() * sizeof(SeqInfo), b1 = dp->tile_seq.size() * 4;
+    std::memcpy(hp, dp->seqs.data(), b0);
+    std::memcpy(hp + b0, dp->tile_seq.data(), b1);
+    std::memcpy(hp + b0 + b1, dp->group_seq.data(), dp->group_seq.size() * 4);
+    char *dt = (char *)at(ws, sc.tabs);
+    HIP_TRY(hipMemcpyAsync(dt, hp, nb, hipMemcpyHostToDevice, s));
+    HIP_TRY(hipEventRecord(h->pin_ev, s));
+    h->pin_used = true;
+    lay.info = reinterpret_cast<const SeqInfo *>(dt);
+    lay.tile_seq = reinterpret_cast<const int *>(dt + b0);
+    lay.group_seq = reinterpret_cast<const int *>(dt + b0 + b1);
+    // final states go to a copy: the first document of a sequence reads the state its last one writes
+    state_out = (float *)at(ws, sc.state_tmp);
+  }
 
   if (h->dt == TTT_BF16) {
     if (conv) {
@@ -389,8 +449,10 @@ int forward_impl(ttt_handle *h, const void *x, const int32_t *ids, const void *E
     }
     if (prof) HIP_TRY(hipEventRecord(ev[3], s));
     if (learn) {
-      HIP_TRY(launch_update_bf16((const bf16_t *)ZT, (const bf16_t *)VT, state, (bf16_t *)snap,
-                                 (const bf16_t *)h->W0p, lay, s));
+      HIP_TRY(launch_update_bf16((const bf16_t *)ZT, (const bf16_t *)VT, state, state_out, (bf16_t *)snap,
+                                 (const bf16_t *)h->W0p, lay, h->cus, s));
+      if (state_out != state)
+        HIP_TRY(hipMemcpyAsync(state, state_out, (size_t)B * df * 4, hipMemcpyDeviceToDevice, s));
     } else {
       for (int b = 0; b < B; ++b)
         HIP_TRY(launch_state_to_snap_bf16(h->W0, state + (size_t)b * df, (bf16_t *)snap + (size_t)b * df, h->d,
@@ -480,6 +542,11 @@ int ttt_init(ttt_handle **out, const void *W_up, const void *W_gate, const void 
 
   hipStream_t s = (hipStream_t)hip_stream;
   ttt_handle *h = new ttt_handle();
+  {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) == hipSuccess && prop.multiProcessorCount > 0)
+      h->cus = prop.multiProcessorCount;
+  }
   h->d = d;
   h->f = f;
   h->C = C;
@@ -694,7 +761,59 @@ int ttt_forward_docs(ttt_handle *h, const void *x, const int32_t *ids, const voi
   const size_t es = h->dt == TTT_BF16 ? 2 : 4;
   const size_t ys = h->dt == TTT_BF16 && !h->y_f32 ? 2 : 4;  // bytes per element of y
   const size_t df = (size_t)h->d * h->f;
-  // Each document runs on its own slice: the state of sequence b returns to
+  if (h->dt == TTT_BF16 && h->eta != 0.f && h->clip_tau == 0.f && h->conv_K == 0) {
+    // One launch sequence: every document is a sequence of its own in the scan kernels, with its own
+    // scratch slots (padded to 256) and snapshot groups; the first document of sequence b continues
+    // its state, every later one starts from W_down0, and the last one's final state is kept. Chunks
+    // and groups count from each document's first token. One plan serves every document: that of
+    // the longest one (a shorter document just has fewer groups).
+    DocPlan dp;
+    int maxlen = 0;
+    for (int b = 0, k = 0; b < B; ++b) {
+      int s0 = 0;
+      for (int j = 0; j <= doc_counts[b]; ++j) {
+        const int s1 = j < doc_counts[b] ? doc_starts[k + j] : T;
+        maxlen = s1 - s0 > maxlen ? s1 - s0 : maxlen;
+        s0 = s1;
+      }
+      k += doc_counts[b];
+    }
+    Plan pl;
+    int rc = make_plan(maxlen, h->C, h->G_override, pl);
+    if (rc) return rc;
+    for (int b = 0, k = 0; b < B; ++b) {
+      int s0 = 0;
+      for (int j = 0; j <= doc_counts[b]; ++j) {
+        const int s1 = j < doc_counts[b] ? doc_starts[k + j] : T;
+        const int len = s1 - s0;
+        SeqInfo si;
+        si.xrow0 = (long long)b * T + s0;
+        si.id0 = (long long)b * (T + 1) + s0;
+        si.slot0 = (int)dp.S;
+        si.len = len;
+        si.grp0 = (int)dp.G;
+        si.state_in = j == 0 ? b : -1;
+        si.state_out = j == doc_counts[b] ? b : -1;
+        si.pad_ = 0;
+        const int seq = (int)dp.seqs.size();
+        dp.seqs.push_back(si);
+        const long long tp = round_up_ll(len, 256), ng = len > pl.L ? (len + pl.L - 1) / pl.L : 1;
+        for (long long t = 0; t < tp / 256; ++t) dp.tile_seq.push_back(seq);
+        for (long long g = 0; g < ng; ++g) dp.group_seq.push_back(seq);
+        dp.S += tp;
+        dp.G += ng;
+        s0 = s1;
+      }
+      k += doc_counts[b];
+    }
+    if (dp.S < (1LL << 30) && dp.G < (1LL << 30)) {
+      rc = forward_impl(h, x, ids, E_tgt, vocab, B, T, y, h->state, W_final, s, nullptr, 0, &dp, &pl);
+      if (rc == TTT_OK && h->profiling) ++h->calls_pending;
+      return rc;
+    }
+  }
+  // Otherwise (fp32 handle, eta = 0, clipping or the general target): each
+  // document runs on its own slice: the state of sequence b returns to
   // W_down0 at every document start, and chunking restarts there. The ids
   // slice keeps the next document's first token as its look-ahead; that
   // target only enters the document's last chunk update, which the reset

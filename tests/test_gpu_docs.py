@@ -92,3 +92,65 @@ def test_docs_without_boundaries_is_plain_forward_and_errors():
         with pytest.raises(ttt.TTTError) as e:
             ttt.ttt_forward_docs(lay.h, lay.x, lay.ids, lay.E, bad)
         assert e.value.code == -7
+
+
+def test_docs_many_documents_one_launch_sequence():
+    """64 documents of 2048 tokens across two sequences, at the 1k/4k layer width. On a bf16 handle (plain
+    target, no clipping) a packed call runs every document as a sequence of its own in one launch sequence;
+    each document then gives the same bits as a call of its own from a reset state, and matches the oracle."""
+    T, C, ndoc = 32 * 2048, 256, 32
+    w = make_inputs(d=1024, f=4096, B=2, T=T, C=C, eta=1e-3, dtype="bf16", vocab=4096, e_std=0.02, seed=140)
+    starts = [[2048 * k for k in range(1, ndoc)] for _ in range(2)]
+    print(f"[docs many] B=2 T={T} C={C}, {ndoc} documents of 2048 per sequence", flush=True)
+    lay = Layer(w)
+    ttt.ttt_set_profiling(lay.h, True)
+    y, Wf = ttt.ttt_forward_docs(lay.h, lay.x, lay.ids, lay.E, starts, want_W_final=True)
+    torch.cuda.synchronize()
+    ph = ttt.ttt_phase_times(lay.h)
+    assert all(v >= 0.0 for v in ph)
+    # documents 0, 1 and the last of sequence 1, each alone from a reset state (its look-ahead id kept)
+    for j in (0, 1, ndoc - 1):
+        s0 = 2048 * j
+        ttt.ttt_reset(lay.h)
+        xs = lay.x[1:2, s0:s0 + 2048].contiguous()
+        ids_s = lay.ids[1:2, s0:s0 + 2049].contiguous()
+        ys, Ws = ttt.ttt_forward_chunked(lay.h, xs, ids_s, lay.E, want_W_final=True)
+        torch.cuda.synchronize()
+        assert torch.equal(ys[0], y[1, s0:s0 + 2048]), f"document {j}"
+        if j == ndoc - 1:
+            assert torch.equal(Ws[0], Wf[1])
+    y_ref, W_ref = _ref(w, C, starts)
+    y, Wf = y.double().cpu().numpy(), Wf.double().cpu().numpy()
+    W0 = w.W_down0.astype(np.float64)
+    e = (rel_fro(y, y_ref), rel_fro(Wf, W_ref), rel_fro(Wf - W0, W_ref - W0))
+    print(f"  y err {e[0]:.2e}, W_final err {e[1]:.2e}, W_final - W0 err {e[2]:.2e}", flush=True)
+    assert max(e) <= BF16_TOL, e
+
+
+@pytest.mark.parametrize("y_f32", [False, True])
+def test_docs_ragged_lengths_after_a_plain_call(y_f32):
+    """Documents of 1, 255, 256, 257 ... tokens (each padded to whole 256-slot tiles inside the library), a
+    sequence with no document start, and a carried state from a plain call before the packed one."""
+    d, f, C, T1, T = 256, 512, 128, 700, 3000
+    w = make_inputs(d=d, f=f, B=3, T=T1 + T, C=C, eta=1e-3, dtype="bf16", vocab=151, e_std=1.0, seed=150)
+    lay = Layer(w)
+    ttt.ttt_set_output_f32(lay.h, y_f32)
+    x1, ids1 = lay.x[:, :T1].contiguous(), lay.ids[:, :T1 + 1].contiguous()
+    ttt.ttt_forward_chunked(lay.h, x1, ids1, lay.E)
+    _, W_mid = oracle.ttt_forward(w.x[:, :T1], w.ids[:, :T1 + 1], w.E_tgt, w.W_up, w.W_gate, w.W_down0, C, w.eta)
+    starts = [[1, 2, 257, 513, 770, 1000, 2999], [256], []]
+    print(f"[docs ragged] y_f32={y_f32} starts={starts}", flush=True)
+    x2, ids2 = lay.x[:, T1:].contiguous(), lay.ids[:, T1:].contiguous()
+    y, Wf = ttt.ttt_forward_docs(lay.h, x2, ids2, lay.E, starts, want_W_final=True)
+    torch.cuda.synchronize()
+    assert y.dtype == (torch.float32 if y_f32 else torch.bfloat16)
+    y_ref, W_ref = oracle.ttt_forward_docs(w.x[:, T1:], w.ids[:, T1:], w.E_tgt, w.W_up, w.W_gate, W_mid, w.W_down0,
+                                           C, w.eta, starts)
+    y, Wf = y.double().cpu().numpy(), Wf.double().cpu().numpy()
+    W0 = w.W_down0.astype(np.float64)
+    e = (rel_fro(y, y_ref), rel_fro(Wf, W_ref), rel_fro(Wf[2] - W_mid[2], W_ref[2] - W_mid[2]))
+    print(f"  y err {e[0]:.2e}, W_final err {e[1]:.2e}, carried sequence's update err {e[2]:.2e}", flush=True)
+    assert max(e) <= BF16_TOL, e
+    # the state left for the next call: sequence 2 continued its carried state; 0 and 1 end in a fresh document
+    D = ttt.ttt_state_delta(lay.h, 3).double().cpu().numpy()
+    assert rel_fro(D + W0, W_ref) <= BF16_TOL
