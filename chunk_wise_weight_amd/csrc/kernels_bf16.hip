@@ -25,7 +25,7 @@
 // columns (element (r, k) at (k/8)*pstride + r*8 + k%8). V^T and Z are
 // K-blocked (Z's blocks hold every token slot, [f/64][T_pad][64]), so one slab
 // of a tile is one contiguous block instead of rows strided by the whole
-// stream length or by f. eta*Z^T and the snapshots are planes: the MFMA register layout holds
+// stream length or by f. Z^T and the snapshots are planes: the MFMA register layout holds
 // four consecutive k of one row per lane, so a store instruction of 32 rows x
 // 16 bytes is 512 contiguous bytes in a plane (in row-major or K-blocked form
 // it would touch 32 lines); a plane slab loads as 1 KB contiguous pieces into
@@ -537,21 +537,21 @@ using CbW = CbLoad<BM, 2 * WN_W>;
 
 // ---------------------------------------------------------------------------
 // Up/gate GEMM with SwiGLU epilogue. i = token slot, j = interleaved W_ug row.
-// Writes Z column-blocked [f/64][S][64] and eta*Z^T in planes of 8 tokens [S/8][f][8] (S scratch slots in all).
+// Writes Z column-blocked [f/64][S][64] and Z^T in planes of 8 tokens [S/8][f][8] (S scratch slots in all), the
+// same bf16 values twice. (eta is carried by the target rows V^T, not by Z^T.)
 // grid: nx * ny workgroups, nx = 2f/256, ny = S/256
 struct A1Args {
   const bf16_t *x;
   const bf16_t *Wug;
   bf16_t *Z;
   bf16_t *ZT;
-  float eta;
-  int write_zt;
   long long S;
   int d, f;
   int nx, ny;  // tiles along W_ug rows and along token slots
   Seqs sq;
 };
 
+template <bool WRITE_ZT>
 __global__ __launch_bounds__(NT_W, 1) void k_a1(A1Args p) {
   __shared__ __attribute__((aligned(16))) Slab<WN_W, NBJ_W> ring[NSL_W];
   int tx, ty;  // W_ug tile, token tile
@@ -567,26 +567,41 @@ __global__ __launch_bounds__(NT_W, 1) void k_a1(A1Args p) {
   acc_zero(acc);
   gemm_k<WN_W, NBJ_W, NSL_W, false>(acc, ring, ld, p.d / BK);
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w & 1, wn = w >> 1;
-  // the wave's two 32-column blocks are a matching (up, gate) pair of W_ug rows
-  const int feat = (n0 + wn * 64) / 2 + (lane & 31);
-  if (feat < p.f) {
+  // Epilogue. The wave's two 32-column blocks are a matching (up, gate) pair
+  // of W_ug rows: features f0 + l%32 (f0 is a multiple of 32, so they lie in
+  // one 64-feature block of Z; f is a multiple of 256, so all are < f). Lane l
+  // holds slots s0 + bi*32 + 8q + 4(l/32) + r. Both outputs are written with
+  // buffer stores from one lane offset each; every other offset is a
+  // compile-time constant or wave-uniform, so no per-store address arithmetic.
+  const int lane = threadIdx.x & 63, w = wave_id(), wm = w & 1, wn = w >> 1;
+  const int f0 = n0 / 2 + wn * 32;
+  const long long s0 = m0 + wm * 128;
+  // Z [f/64][S][64]: (slot, feature) at ((feature/64)*S + slot)*64 + feature%64
+  const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
+      p.Z + ((long long)(f0 / 64) * p.S + s0) * 64 + f0 % 64, (short)0, 0x7fffffff, kBufferFlags);
+  const uint32_t vz = (uint32_t)((256 * (lane >> 5) + (lane & 31)) * 2);
+  // Z^T [S/8][f][8]: (slot, feature) at ((slot/8)*f + feature)*8 + slot%8
+  const __amdgpu_buffer_rsrc_t rzt = __builtin_amdgcn_make_buffer_rsrc(
+      p.ZT + ((s0 >> 3) * p.f + f0) * 8, (short)0, 0x7fffffff, kBufferFlags);
+  const uint32_t vzt = (uint32_t)((8 * (lane & 31) + 4 * (lane >> 5)) * 2);
+  constexpr int kNt = 2;  // cache policy of the stores: non-temporal
 #pragma unroll
-    for (int bi = 0; bi < 4; ++bi) {
-      const f32x16 &u = acc.v[bi][0];
-      const f32x16 &g = acc.v[bi][1];
+  for (int bi = 0; bi < 4; ++bi) {
+    const f32x16 &u = acc.v[bi][0];
+    const f32x16 &g = acc.v[bi][1];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const long long slot = m0 + wm * 128 + bi * 32 + 8 * q + 4 * (lane >> 5);
-        float z[4];
+    for (int q = 0; q < 4; ++q) {
+      float z[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) z[r] = silu_fast(g[4 * q + r]) * u[4 * q + r];
-        if (p.write_zt)
-          store_nt(p.ZT + ((slot >> 3) * p.f + feat) * 8 + (slot & 7), pack_bf16x2(p.eta * z[0], p.eta * z[1]),
-                   pack_bf16x2(p.eta * z[2], p.eta * z[3]));
-        bf16_t *zrow = p.Z + ((long long)(feat / 64) * p.S + slot) * 64 + feat % 64;
+      for (int r = 0; r < 4; ++r) z[r] = silu_fast(g[4 * q + r]) * u[4 * q + r];
+      // slots r = 0, 1 in the halves of pk.x, r = 2, 3 in those of pk.y
+      const u32x2_t pk{pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3])};
+      if (WRITE_ZT) __builtin_amdgcn_raw_buffer_store_b64(pk, rzt, vzt, (bi * 4 + q) * p.f * 16, kNt);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) store_nt(zrow + r * 64, f32_to_bf16(z[r]));
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t h2 = r < 2 ? pk.x : pk.y;
+        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)((r & 1) ? (h2 >> 16) : h2), rz, vz,
+                                              (bi * 32 + 8 * q + r) * 128, kNt);
       }
     }
   }
@@ -602,8 +617,9 @@ __global__ __launch_bounds__(NT_W, 1) void k_a1(A1Args p) {
 struct TgtArgs {
   const bf16_t *U;
   const bf16_t *WtT;
-  bf16_t *VT;
-  bf16_t *Vrow;
+  bf16_t *VT;    // eta * V
+  bf16_t *Vrow;  // V
+  float eta;
   int T_pad, d, nx, ny;
 };
 
@@ -636,8 +652,8 @@ __global__ __launch_bounds__(NT_W, 1) void k_target_gemm(TgtArgs p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) v[r] = acc.v[bi][bj][4 * q + r];
         uint2 pk;
-        pk.x = pack_bf16x2(v[0], v[1]);
-        pk.y = pack_bf16x2(v[2], v[3]);
+        pk.x = pack_bf16x2(p.eta * v[0], p.eta * v[1]);
+        pk.y = pack_bf16x2(p.eta * v[2], p.eta * v[3]);
         *reinterpret_cast<uint2 *>(VTb + ((long long)(pos >> 6) * p.d + a) * 64 + (pos & 63)) = pk;
         if (p.Vrow) {
           bf16_t *vr = p.Vrow + ((long long)b * p.T_pad + pos) * p.d + a;
@@ -665,11 +681,11 @@ __global__ __launch_bounds__(NT_W, 1) void k_target_gemm(TgtArgs p) {
 // of at most 128 tiles is split into 256 x 128 halves that run as one round
 // on the 4-wave configuration, so no CU idles for a whole round.
 
-// Tile loads of the update with an L2 prefetch. Every eta Z^T tile is read by
+// Tile loads of the update with an L2 prefetch. Every Z^T tile is read by
 // one XCD only, so its slabs come from HBM, one slab (two in the half-tile
 // round) ahead of use without the prefetch. The workgroups that share an
 // operand tile split its prefetch: the sa tiles (and halves) of a band of the
-// tile order split the 256 lines of 128 bytes of an eta Z^T slab (8 planes of
+// tile order split the 256 lines of 128 bytes of a Z^T slab (8 planes of
 // 32 lines), the sb tiles along x of an XCD's range split the BN rows (one
 // line each) of a V^T slab. Waves 0 .. WN-1 touch the first share, waves WN ..
 // 2WN-1 the second, each with one 4-byte DMA into a 256-byte LDS sink that
@@ -679,7 +695,7 @@ struct UpdLoads : SlabLoads<PlLoad<2 * WN>, KbLoad<BN, 2 * WN>> {
   static constexpr bool kPf = true;
   uint32_t *sink;
   uint32_t vp;  // this lane's byte offset in the slab (A: plane and line, B: row)
-  // sharer ka of sa takes lines [ka*256/sa, (ka+1)*256/sa) of the eta Z^T slab;
+  // sharer ka of sa takes lines [ka*256/sa, (ka+1)*256/sa) of the Z^T slab;
   // sharer kb of sb takes rows [kb*BN/sb, (kb+1)*BN/sb) of the V^T slab
   __device__ __forceinline__ void init_pf(uint32_t *sink_, int sa, int ka, int sb, int kb, int w, int lane) {
     sink = sink_;
@@ -846,12 +862,12 @@ __global__ __launch_bounds__(128 * WN, 1) void k_update(UpdArgs p) {
     acc_zero(acc);  // a document start: W = W0
   }
 
-  // A: eta Z^T in planes of 8 tokens [S/8][f][8]; B: V^T K-blocked [S/64][d][64]
+  // A: Z^T in planes of 8 tokens [S/8][f][8]; B: eta V^T K-blocked [S/64][d][64]
   UpdLoads<WN, BN> ld;
   ld.a.init(p.ZT + (long long)si.slot0 * p.f + (long long)i0 * 8, (long long)p.f * 8, lane);
   ld.b.init(p.VT + (long long)si.slot0 * p.d + (long long)j0 * 64, (long long)p.d * 64, w, lane);
   {
-    // eta Z^T tile tx is shared by the tiles of its band (h of them) and their halves;
+    // Z^T tile tx is shared by the tiles of its band (h of them) and their halves;
     // a V^T tile (or half) by the tiles along x of the XCD's range
     const int full = ny / 8, band = ty / 8, h = band < full ? 8 : ny - full * 8;
     const int halves = 256 / BN, half = n % halves;
@@ -909,7 +925,7 @@ __global__ __launch_bounds__(128 * WN, 1) void k_update(UpdArgs p) {
 }
 
 // ---------------------------------------------------------------------------
-// Within-group scores P[t][s] = eta <z_t, z_s> for s in an earlier chunk of the
+// Within-group scores P[t][s] = <z_t, z_s> for s in an earlier chunk of the
 // same group. i = s, j = t; only tiles with i-tile <= j-tile that hold an
 // unmasked entry are formed.
 // grid: B * ngroups * nt(nt+1)/2 workgroups, nt = ceil(L/256)
@@ -918,7 +934,6 @@ constexpr int kMaxScorePairs = 136;  // the lower triangle of 16 x 16 tiles (L <
 struct ScoreArgs {
   const bf16_t *Z;
   bf16_t *P;
-  float eta;
   long long S;  // scratch slots in all (Z's block stride is S*64)
   int L, C, f, nt;
   Seqs sq;
@@ -979,7 +994,7 @@ __global__ __launch_bounds__(NT_W, 1) void k_scores(ScoreArgs p) {
         if (sidx >= p.L) continue;
         float v[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = ((sidx + r) / p.C < ct) ? p.eta * acc.v[bi][bj][4 * q + r] : 0.f;
+        for (int r = 0; r < 4; ++r) v[r] = ((sidx + r) / p.C < ct) ? acc.v[bi][bj][4 * q + r] : 0.f;
         uint2 pk;
         pk.x = pack_bf16x2(v[0], v[1]);
         pk.y = pack_bf16x2(v[2], v[3]);
@@ -1278,16 +1293,16 @@ __global__ __launch_bounds__(NT_W, 1) void k_chunk_gram(GramArgs p) {
 }
 
 // ---------------------------------------------------------------------------
-// Target gather, transposed and K-blocked: V^T[p/64][a][p%64] = E[ids of slot p's next token][a] (slots
-// across all sequences). A 64-slot x 64-feature tile passes through LDS so both the row reads of E and
+// Target gather, transposed and K-blocked: V^T[p/64][a][p%64] = eta * E[ids of slot p's next token][a]
+// (slots across all sequences). A 64-slot x 64-feature tile passes through LDS so both the row reads of E and
 // the writes (one contiguous 8 KB block) are 16 B per lane. With Vrow non-null
 // the rows are also written row-major, Vrow[p][a] (used by update clipping).
-// With cfac non-null, position t of sequence b is scaled by the clipping factor cfac[b][t/C]
-// (bf16 -> fp32, times the factor, rounded to bf16).
+// With cfac non-null, position t of sequence b is also scaled by the clipping factor cfac[b][t/C]
+// (bf16 -> fp32, times eta and the factor, rounded to bf16). Vrow holds the unscaled rows.
 // grid: (S/64, d/64)
 __global__ __launch_bounds__(256) void k_gather_vt(const int32_t *ids, const bf16_t *E, int vocab, bf16_t *VT,
-                                                   bf16_t *Vrow, const float *cfac, int C, int nchunks, int d,
-                                                   Seqs sq) {
+                                                   bf16_t *Vrow, const float *cfac, float eta, int C, int nchunks,
+                                                   int d, Seqs sq) {
   __shared__ __attribute__((aligned(16))) bf16_t tile[64][72];
   const long long p0 = (long long)blockIdx.x * 64;
   const int a0 = blockIdx.y * 64;
@@ -1303,17 +1318,20 @@ __global__ __launch_bounds__(256) void k_gather_vt(const int32_t *ids, const bf1
     if (pos < si.len) id = ids[si.id0 + pos + 1];
     uint4 v = make_uint4(0u, 0u, 0u, 0u);
     if (id >= 0 && id < vocab) v = *reinterpret_cast<const uint4 *>(E + (long long)id * d + a0 + seg * 8);
-    if (cfac && pos < si.len) {
-      const float c = cfac[(long long)b * nchunks + pos / C];
-      bf16_t *e = reinterpret_cast<bf16_t *>(&v);
+    if (Vrow) *reinterpret_cast<uint4 *>(Vrow + (p0 + pl) * d + a0 + seg * 8) = v;  // unscaled
+    // V^T carries eta (and the clipping factor): bf16 -> fp32, scaled, rounded to bf16
+    const float c = eta * ((cfac && pos < si.len) ? cfac[(long long)b * nchunks + pos / C] : 1.f);
+    uint4 sv;
+    {
+      const bf16_t *e = reinterpret_cast<const bf16_t *>(&v);
+      uint32_t *o = reinterpret_cast<uint32_t *>(&sv);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) e[k] = f32_to_bf16(bf16_to_f32(e[k]) * c);
+      for (int k = 0; k < 4; ++k) o[k] = pack_bf16x2(bf16_to_f32(e[2 * k]) * c, bf16_to_f32(e[2 * k + 1]) * c);
     }
     // 16-byte column groups XOR-swizzled by (row / 8) % 8: the transposing
     // reads below take one column from rows 8 apart, which the plain layout
     // puts in the same banks
-    *reinterpret_cast<uint4 *>(&tile[pl][(seg ^ ((pl >> 3) & 7)) * 8]) = v;
-    if (Vrow) *reinterpret_cast<uint4 *>(Vrow + (p0 + pl) * d + a0 + seg * 8) = v;
+    *reinterpret_cast<uint4 *>(&tile[pl][(seg ^ ((pl >> 3) & 7)) * 8]) = sv;
   }
   __syncthreads();
   bf16_t *blk = VT + (long long)blockIdx.x * d * 64;
@@ -1332,11 +1350,11 @@ __global__ __launch_bounds__(256) void k_gather_vt(const int32_t *ids, const bf1
 }  // namespace
 
 hipError_t launch_gather_vt_bf16(const int32_t *ids, const bf16_t *E, int vocab, bf16_t *VT, bf16_t *Vrow,
-                                 const float *cfac, const Layout &lay, hipStream_t s) {
+                                 const float *cfac, float eta, const Layout &lay, hipStream_t s) {
   if (lay.n_slots() / 64 >= (1LL << 31)) return hipErrorInvalidConfiguration;
   dim3 grid((unsigned)(lay.n_slots() / 64), lay.d / 64, 1);
   const int nchunks = (int)((lay.T + (long long)lay.C - 1) / lay.C);
-  hipLaunchKernelGGL(k_gather_vt, grid, dim3(256), 0, s, ids, E, vocab, VT, Vrow, cfac, lay.C, nchunks, lay.d,
+  hipLaunchKernelGGL(k_gather_vt, grid, dim3(256), 0, s, ids, E, vocab, VT, Vrow, cfac, eta, lay.C, nchunks, lay.d,
                      lay.seqs());
   return hipGetLastError();
 }
@@ -1355,22 +1373,25 @@ hipError_t launch_chunk_gram_bf16(const bf16_t *Z, const bf16_t *Vrow, const bf1
   return hipGetLastError();
 }
 
-hipError_t launch_a1_bf16(const bf16_t *x, const bf16_t *Wug, bf16_t *Z, bf16_t *ZT, float eta, int write_zt,
+hipError_t launch_a1_bf16(const bf16_t *x, const bf16_t *Wug, bf16_t *Z, bf16_t *ZT, int write_zt,
                           const Layout &lay, hipStream_t s) {
   const int nx = (2 * lay.f + 255) / 256;
   const long long ny = lay.n_slots() / BM;
   if (nx * ny >= (1LL << 31)) return hipErrorInvalidConfiguration;
-  A1Args p{x, Wug, Z, ZT, eta, write_zt, lay.n_slots(), lay.d, lay.f, nx, (int)ny, lay.seqs()};
-  hipLaunchKernelGGL(k_a1, dim3((unsigned)(nx * ny)), dim3(NT_W), 0, s, p);
+  A1Args p{x, Wug, Z, ZT, lay.n_slots(), lay.d, lay.f, nx, (int)ny, lay.seqs()};
+  if (write_zt)
+    hipLaunchKernelGGL(k_a1<true>, dim3((unsigned)(nx * ny)), dim3(NT_W), 0, s, p);
+  else
+    hipLaunchKernelGGL(k_a1<false>, dim3((unsigned)(nx * ny)), dim3(NT_W), 0, s, p);
   return hipGetLastError();
 }
 
-hipError_t launch_target_gemm_bf16(const bf16_t *U, const bf16_t *WtT, bf16_t *VT, bf16_t *Vrow, const Layout &lay,
-                                  hipStream_t s) {
+hipError_t launch_target_gemm_bf16(const bf16_t *U, const bf16_t *WtT, bf16_t *VT, bf16_t *Vrow, float eta,
+                                  const Layout &lay, hipStream_t s) {
   const int nx = lay.d / 256;
   const long long ny = (long long)lay.B * lay.T_pad / BM;
   if (nx * ny >= (1LL << 31)) return hipErrorInvalidConfiguration;
-  TgtArgs p{U, WtT, VT, Vrow, lay.T_pad, lay.d, nx, (int)ny};
+  TgtArgs p{U, WtT, VT, Vrow, eta, lay.T_pad, lay.d, nx, (int)ny};
   hipLaunchKernelGGL(k_target_gemm, dim3((unsigned)(nx * ny)), dim3(NT_W), 0, s, p);
   return hipGetLastError();
 }
@@ -1392,9 +1413,9 @@ hipError_t launch_update_bf16(const bf16_t *ZT, const bf16_t *VT, const float *s
   return hipGetLastError();
 }
 
-hipError_t launch_scores_bf16(const bf16_t *Z, bf16_t *P, float eta, const Layout &lay, hipStream_t s) {
+hipError_t launch_scores_bf16(const bf16_t *Z, bf16_t *P, const Layout &lay, hipStream_t s) {
   const int nt = (lay.L + 255) / 256;
-  ScoreArgs p{Z, P, eta, lay.n_slots(), lay.L, lay.C, lay.f, nt, lay.seqs(), 0, {}, {}};
+  ScoreArgs p{Z, P, lay.n_slots(), lay.L, lay.C, lay.f, nt, lay.seqs(), 0, {}, {}};
   if (nt * (nt + 1) / 2 <= kMaxScorePairs) {
     // the tiles of a full group that the kernel would not skip, jt-major
     for (int jt = 0; jt < nt; ++jt) {

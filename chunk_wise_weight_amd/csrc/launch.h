@@ -4,26 +4,27 @@
 #include "common.h"
 
 // ---- bf16 path: MFMA kernels (kernels_bf16.hip) ----
-// V^T over the scratch slots of all sequences: slot p (position t of sequence b) holds E[ids[b][t+1]] for
-// t < T and a valid id, else 0; K-blocked [S/64][d][64]. Vrow (nullable): the same rows row-major, [S][d].
-// cfac (nullable; batch layout only): clipping factors [B][ceil(T/C)]; position t is scaled by cfac[b][t/C].
+// V^T over the scratch slots of all sequences: slot p (position t of sequence b) holds eta * E[ids[b][t+1]] for
+// t < T and a valid id, else 0; K-blocked [S/64][d][64]. Vrow (nullable): the same rows row-major and unscaled,
+// [S][d]. cfac (nullable; batch layout only): clipping factors [B][ceil(T/C)]; V^T's position t is also scaled
+// by cfac[b][t/C].
 hipError_t launch_gather_vt_bf16(const int32_t *ids, const bf16_t *E, int vocab, bf16_t *VT, bf16_t *Vrow,
-                                 const float *cfac, const Layout &lay, hipStream_t s);
+                                 const float *cfac, float eta, const Layout &lay, hipStream_t s);
 // Z = SiLU(x W_gate^T) * (x W_up^T) -> Z column-blocked [f/64][S][64] (bf16 path; S scratch slots in all) and
-// ZT = eta*Z^T in planes of 8 tokens [S/8][f][8].
+// (write_zt) ZT = Z^T in planes of 8 tokens [S/8][f][8].
 // Wug: 2f rows of d, interleaved in blocks of 32 (32 up rows, then the matching 32 gate rows), held K-blocked
 // by 64 columns: [d/64][2f][64].
-hipError_t launch_a1_bf16(const bf16_t *x, const bf16_t *Wug, bf16_t *Z, bf16_t *ZT, float eta, int write_zt,
+hipError_t launch_a1_bf16(const bf16_t *x, const bf16_t *Wug, bf16_t *Z, bf16_t *ZT, int write_zt,
                           const Layout &lay, hipStream_t s);
-// For each sequence (of the batch, or document): D += sum_p ZT[:, p] VT[:, p]^T over its slots (W[a][i]
+// For each sequence (of the batch, or document): D += sum_p ZT[:, p] VT[:, p]^T over its slots (VT carries eta; W[a][i]
 // layout; the state is D = W - W0), from state_in[state_in index] or zero, into state_out[state_out index];
 // snapshot k of a sequence = bf16(W0 + D at its token k*L), with W0 from its bf16 planes W0p [f/8][d][8].
 // Snapshots are planes of 8 columns, [groups in all][f/8][d][8]. cus: compute units of the device (a last
 // partial round of at most cus/2 tiles runs as half tiles).
 hipError_t launch_update_bf16(const bf16_t *ZT, const bf16_t *VT, const float *state_in, float *state_out,
                               bf16_t *snap, const bf16_t *W0p, const Layout &lay, int cus, hipStream_t s);
-// P[b][g][t][s] = eta * <Z[gL+t], Z[gL+s]> if s/C < t/C else 0, for t, s < L.
-hipError_t launch_scores_bf16(const bf16_t *Z, bf16_t *P, float eta, const Layout &lay, hipStream_t s);
+// P[group][t][s] = <Z[gL+t], Z[gL+s]> if s/C < t/C else 0, for t, s < L (eta is in V^T).
+hipError_t launch_scores_bf16(const bf16_t *Z, bf16_t *P, const Layout &lay, hipStream_t s);
 // One snapshot [f/8][d][8] = bf16(W0 + D) of fp32 W0 and state D, [d][f] each (no update).
 hipError_t launch_state_to_snap_bf16(const float *W0, const float *D, bf16_t *snap, int d, int f, hipStream_t s);
 // bf16 [d][f] -> planes [f/8][d][8].
@@ -71,10 +72,10 @@ hipError_t launch_conv_taps_bf16(const int32_t *ids, const bf16_t *E, int vocab,
                                  const Layout &lay, hipStream_t s);
 hipError_t launch_conv_taps_f32(const int32_t *ids, const float *E, int vocab, const float *cw, int K, float *U,
                                 const Layout &lay, hipStream_t s);
-// V = U W_target into V^T (K-blocked bf16 / row-major [B][d][T_pad] fp32) and, if Vrow, row-major V.
-// bf16 takes W_target^T [d][d]; fp32 takes W_target [d][d].
-hipError_t launch_target_gemm_bf16(const bf16_t *U, const bf16_t *WtT, bf16_t *VT, bf16_t *Vrow, const Layout &lay,
-                                   hipStream_t s);
+// V = U W_target into V^T (K-blocked bf16, as eta * V / row-major [B][d][T_pad] fp32, unscaled) and, if Vrow,
+// row-major V (unscaled). bf16 takes W_target^T [d][d]; fp32 takes W_target [d][d].
+hipError_t launch_target_gemm_bf16(const bf16_t *U, const bf16_t *WtT, bf16_t *VT, bf16_t *Vrow, float eta,
+                                   const Layout &lay, hipStream_t s);
 hipError_t launch_target_gemm_f32(const float *U, const float *W, float *VT, float *Vrow, const Layout &lay,
                                   hipStream_t s);
 hipError_t launch_transpose_bf16(const bf16_t *src, bf16_t *dst, int n, hipStream_t s);

@@ -2,16 +2,16 @@
 // token layout of a call, scratch management and the launch sequence.
 //
 // One call of ttt_forward_chunked runs, on the caller's stream:
-//   1. target gather      V^T = E_tgt[ids shifted by one]^T       (next-token target), or
-//                         the general target Conv1D(X0) W_target: tap sums of the
-//                         token embeddings, then one GEMM into V^T
-//   2. up/gate GEMM       Z = SiLU(x W_gate^T) * (x W_up^T), and eta*Z^T
+//   1. target gather      V^T = eta * E_tgt[ids shifted by one]^T (next-token target,
+//                         eta folded in), or the general target Conv1D(X0) W_target:
+//                         tap sums of the token embeddings, then one GEMM into V^T
+//   2. up/gate GEMM       Z = SiLU(x W_gate^T) * (x W_up^T), and Z^T
 //   2b. optional clipping per-chunk factors c_i = min(1, tau/||eta V_i^T Z_i||_F)
 //                         from chunk Grams; V^T's rows of chunk i scaled by c_i
-//   3. state update       W += (eta Z)^T-weighted rank-C updates over the whole
+//   3. state update       D += Z^T-weighted rank-C updates (eta V^T) over the whole
 //                         block, the fp32 state resident in registers; a
-//                         snapshot of W at the start of every group of G chunks
-//   4. group scores       P = eta * (Z Z^T) masked to earlier chunks of the group
+//                         snapshot of W_down0 + D at the start of every group of G chunks
+//   4. group scores       P = Z Z^T masked to earlier chunks of the group
 //   5. output GEMM        y = Z snapshot^T + P V
 //   6. optional W_final = W_down0 + D (the handle keeps each sequence's state as
 //                         D, the change since its last reset)
@@ -430,20 +430,22 @@ int forward_impl(ttt_handle *h, const void *x, const int32_t *ids, const void *E
   if (h->dt == TTT_BF16) {
     if (conv) {
       HIP_TRY(launch_conv_taps_bf16(ids, (const bf16_t *)E_tgt, vocab, h->conv_w, h->conv_K, (bf16_t *)U, lay, s));
-      HIP_TRY(launch_target_gemm_bf16((const bf16_t *)U, (const bf16_t *)h->Wt, (bf16_t *)VT, (bf16_t *)Vrow, lay, s));
+      HIP_TRY(launch_target_gemm_bf16((const bf16_t *)U, (const bf16_t *)h->Wt, (bf16_t *)VT, (bf16_t *)Vrow, h->eta,
+                                      lay, s));
     } else if ((learn || lay.intra) && !gram_e) {
-      HIP_TRY(launch_gather_vt_bf16(ids, (const bf16_t *)E_tgt, vocab, (bf16_t *)VT, (bf16_t *)Vrow, nullptr, lay, s));
+      HIP_TRY(launch_gather_vt_bf16(ids, (const bf16_t *)E_tgt, vocab, (bf16_t *)VT, (bf16_t *)Vrow, nullptr, h->eta,
+                                    lay, s));
     }
     if (prof) HIP_TRY(hipEventRecord(ev[1], s));
-    HIP_TRY(launch_a1_bf16((const bf16_t *)x, (const bf16_t *)h->Wug, (bf16_t *)Z, (bf16_t *)ZT, h->eta,
-                           learn ? 1 : 0, lay, s));
+    HIP_TRY(launch_a1_bf16((const bf16_t *)x, (const bf16_t *)h->Wug, (bf16_t *)Z, (bf16_t *)ZT, learn ? 1 : 0, lay,
+                           s));
     if (prof) HIP_TRY(hipEventRecord(ev[2], s));
     if (clip) {
       HIP_TRY(launch_chunk_gram_bf16((const bf16_t *)Z, (const bf16_t *)Vrow, (const bf16_t *)E_tgt, ids, vocab, gv,
                                      rowpart, wspan, lay, s));
       HIP_TRY(launch_chunk_factors(rowpart, cfac, wspan, h->eta, h->clip_tau, lay, s));
       if (gram_e)
-        HIP_TRY(launch_gather_vt_bf16(ids, (const bf16_t *)E_tgt, vocab, (bf16_t *)VT, nullptr, cfac, lay, s));
+        HIP_TRY(launch_gather_vt_bf16(ids, (const bf16_t *)E_tgt, vocab, (bf16_t *)VT, nullptr, cfac, h->eta, lay, s));
       else
         HIP_TRY(launch_scale_vt_bf16((bf16_t *)VT, cfac, lay, s));
     }
@@ -459,7 +461,7 @@ int forward_impl(ttt_handle *h, const void *x, const int32_t *ids, const void *E
                                           h->f, s));
     }
     if (prof) HIP_TRY(hipEventRecord(ev[4], s));
-    if (lay.intra) HIP_TRY(launch_scores_bf16((const bf16_t *)Z, (bf16_t *)P, h->eta, lay, s));
+    if (lay.intra) HIP_TRY(launch_scores_bf16((const bf16_t *)Z, (bf16_t *)P, lay, s));
     if (prof) HIP_TRY(hipEventRecord(ev[5], s));
     HIP_TRY(launch_out_bf16((const bf16_t *)Z, (const bf16_t *)P, (const bf16_t *)snap, (const bf16_t *)VT, y,
                             h->y_f32, lay, s));
