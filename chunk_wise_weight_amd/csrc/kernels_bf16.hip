@@ -365,7 +365,7 @@ __device__ __forceinline__ void issue_point(const SL &ld, const typename SL::Pre
 // here at run time).
 template <int WN, int NBJ, int NSL, bool AFTER, bool APLANE, int H, int REFILL, class SL, class AfterFn>
 __device__ __forceinline__ void stage_body(Acc<NBJ> &acc, Slab<WN, NBJ> *ring, Frag<NBJ> &cur, Frag<NBJ> &nxt,
-                                           int kt, int nk, int wm, int wn, int lane, int w, const SL &ld,
+                                           int kt, int &cb, int nk, int wm, int wn, int lane, int w, const SL &ld,
                                            AfterFn &&after_fn) {
   constexpr int LPS = loads_per_slab<WN, NBJ>();
   static_assert(SL::N == LPS, "the slab loads match the tile configuration");
@@ -373,7 +373,9 @@ __device__ __forceinline__ void stage_body(Acc<NBJ> &acc, Slab<WN, NBJ> *ring, F
   const int nsl = (nk + 1) >> 1;
   const int h = H >= 0 ? H : (kt & 1);
   const bool refill = REFILL >= 0 ? REFILL == 1 : (h == 1 && sl + NSL < nsl);
-  frag_read<WN, NBJ, APLANE>(nxt, ring[sl % NSL], h, 1, wm, wn, lane);
+  // cb: the ring buffer of slab sl (sl % NSL, carried by the caller); nb: that of stage kt+1
+  const int nb = h == 1 ? (cb + 1 == NSL ? 0 : cb + 1) : cb;
+  frag_read<WN, NBJ, APLANE>(nxt, ring[cb], h, 1, wm, wn, lane);
   pin();
   frag_mma<0, 1>(acc, cur);
   pin();
@@ -383,7 +385,7 @@ __device__ __forceinline__ void stage_body(Acc<NBJ> &acc, Slab<WN, NBJ> *ring, F
     slab_wait<LPS, NSL - 2, SL::kPf ? 1 : 0>(later);
   }
   const int rs = sl + NSL;
-  Slab<WN, NBJ> &dst = ring[sl % NSL];  // the buffer just finished refills with slab rs
+  Slab<WN, NBJ> &dst = ring[cb];  // the buffer just finished refills with slab rs
   typename SL::Pre pre{};
   if (refill) pre = ld.prep(rs);
   pin();
@@ -400,7 +402,7 @@ __device__ __forceinline__ void stage_body(Acc<NBJ> &acc, Slab<WN, NBJ> *ring, F
   pin();
   // unconditional (past the end it reads a stale buffer of the ring): no
   // branch, so the compiler can count the reads and wait for each exactly
-  if (!AFTER) frag_read<WN, NBJ, APLANE>(cur, ring[((kt + 1) >> 1) % NSL], (kt + 1) & 1, 0, wm, wn, lane);
+  if (!AFTER) frag_read<WN, NBJ, APLANE>(cur, ring[nb], (kt + 1) & 1, 0, wm, wn, lane);
   if (refill) issue_point<LPS, 3>(ld, pre, dst, rs, w, lane);
   pin();
   frag_mma<1, 2>(acc, nxt);
@@ -418,16 +420,17 @@ __device__ __forceinline__ void stage_body(Acc<NBJ> &acc, Slab<WN, NBJ> *ring, F
   pin();
   if (AFTER) {
     after_fn(acc);
-    frag_read<WN, NBJ, APLANE>(cur, ring[((kt + 1) >> 1) % NSL], (kt + 1) & 1, 0, wm, wn, lane);
+    frag_read<WN, NBJ, APLANE>(cur, ring[nb], (kt + 1) & 1, 0, wm, wn, lane);
     pin();
   }
+  cb = nb;
 }
 
 template <int WN, int NBJ, int NSL, bool AFTER, bool APLANE = false, class SL, class AfterFn>
 __device__ __forceinline__ void pipelined_stage(Acc<NBJ> &acc, Slab<WN, NBJ> *ring, Frag<NBJ> &cur, Frag<NBJ> &nxt,
-                                                int kt, int nk, int wm, int wn, int lane, int w, const SL &ld,
-                                                AfterFn &&after_fn) {
-  stage_body<WN, NBJ, NSL, AFTER, APLANE, -1, -1>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, w, ld, after_fn);
+                                                int kt, int &cb, int nk, int wm, int wn, int lane, int w,
+                                                const SL &ld, AfterFn &&after_fn) {
+  stage_body<WN, NBJ, NSL, AFTER, APLANE, -1, -1>(acc, ring, cur, nxt, kt, cb, nk, wm, wn, lane, w, ld, after_fn);
 }
 
 struct NoHook {
@@ -483,21 +486,21 @@ __device__ __forceinline__ void band_tile(int t, int nx, int ny, int H, int &x, 
 // count of stages ends on a lone even stage. Leaves kt = kt_end.
 template <int WN, int NBJ, int NSL, bool APLANE, class SL>
 __device__ __forceinline__ void stage_run(Acc<NBJ> &acc, Slab<WN, NBJ> *ring, Frag<NBJ> &cur, Frag<NBJ> &nxt,
-                                          int &kt, int kt_end, int nk, int wm, int wn, int lane, int w,
+                                          int &kt, int &cb, int kt_end, int nk, int wm, int wn, int lane, int w,
                                           const SL &ld) {
   const int nsl = (nk + 1) >> 1;
   const int kref = nsl > NSL ? 2 * (nsl - NSL) : 0;  // first stage past the refilling slabs
   const int k1 = kref < kt_end ? kref : kt_end;
   for (; kt + 1 < k1; kt += 2) {
-    stage_body<WN, NBJ, NSL, false, APLANE, 0, 0>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, w, ld, NoHook{});
-    stage_body<WN, NBJ, NSL, false, APLANE, 1, 1>(acc, ring, cur, nxt, kt + 1, nk, wm, wn, lane, w, ld, NoHook{});
+    stage_body<WN, NBJ, NSL, false, APLANE, 0, 0>(acc, ring, cur, nxt, kt, cb, nk, wm, wn, lane, w, ld, NoHook{});
+    stage_body<WN, NBJ, NSL, false, APLANE, 1, 1>(acc, ring, cur, nxt, kt + 1, cb, nk, wm, wn, lane, w, ld, NoHook{});
   }
   for (; kt + 1 < kt_end; kt += 2) {
-    stage_body<WN, NBJ, NSL, false, APLANE, 0, 0>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, w, ld, NoHook{});
-    stage_body<WN, NBJ, NSL, false, APLANE, 1, 0>(acc, ring, cur, nxt, kt + 1, nk, wm, wn, lane, w, ld, NoHook{});
+    stage_body<WN, NBJ, NSL, false, APLANE, 0, 0>(acc, ring, cur, nxt, kt, cb, nk, wm, wn, lane, w, ld, NoHook{});
+    stage_body<WN, NBJ, NSL, false, APLANE, 1, 0>(acc, ring, cur, nxt, kt + 1, cb, nk, wm, wn, lane, w, ld, NoHook{});
   }
   if (kt < kt_end) {
-    stage_body<WN, NBJ, NSL, false, APLANE, 0, 0>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, w, ld, NoHook{});
+    stage_body<WN, NBJ, NSL, false, APLANE, 0, 0>(acc, ring, cur, nxt, kt, cb, nk, wm, wn, lane, w, ld, NoHook{});
     ++kt;
   }
 }
@@ -527,8 +530,8 @@ __device__ __forceinline__ void gemm_k(Acc<NBJ> &acc, Slab<WN, NBJ> *ring, const
   ring_prologue<WN, NBJ, NSL>(ld, ring, nsl, w, lane);
   Frag<NBJ> cur, nxt;
   frag_read<WN, NBJ, APLANE>(cur, ring[0], 0, 0, wm, wn, lane);
-  int kt = 0;
-  stage_run<WN, NBJ, NSL, APLANE>(acc, ring, cur, nxt, kt, nk, nk, wm, wn, lane, w, ld);
+  int kt = 0, cb = 0;
+  stage_run<WN, NBJ, NSL, APLANE>(acc, ring, cur, nxt, kt, cb, nk, nk, wm, wn, lane, w, ld);
 }
 
 // The wide GEMMs' loaders: 8 waves, 256 x 256 tiles.
@@ -901,14 +904,14 @@ __global__ __launch_bounds__(128 * WN, 1) void k_update(UpdArgs p) {
   // Stages of group g-1 run plain; its last stage ends with snapshot g.
   // A group spans L/BK stages, an even number (L is a multiple of 64), so
   // every group ends on an odd stage.
-  int kt = 0;
+  int kt = 0, cb = 0;
   for (; g < ngroups; ) {
     const int kt_last = g * (p.L / BK) - 1;  // last stage before group g starts
-    stage_run<WN, NBJ, NSL, true>(acc, ring, cur, nxt, kt, kt_last, nk, wm, wn, lane, w, ld);
-    pipelined_stage<WN, NBJ, NSL, true, true>(acc, ring, cur, nxt, kt, nk, wm, wn, lane, w, ld, snapshot);
+    stage_run<WN, NBJ, NSL, true>(acc, ring, cur, nxt, kt, cb, kt_last, nk, wm, wn, lane, w, ld);
+    pipelined_stage<WN, NBJ, NSL, true, true>(acc, ring, cur, nxt, kt, cb, nk, wm, wn, lane, w, ld, snapshot);
     ++kt;
   }
-  stage_run<WN, NBJ, NSL, true>(acc, ring, cur, nxt, kt, nk, nk, wm, wn, lane, w, ld);
+  stage_run<WN, NBJ, NSL, true>(acc, ring, cur, nxt, kt, cb, nk, nk, wm, wn, lane, w, ld);
   // the final state D in fp32
   if (!st_out) return;
 #pragma unroll
