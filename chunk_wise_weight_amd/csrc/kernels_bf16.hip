@@ -751,20 +751,13 @@ struct UpdArgs {
 // (a, i) at ((i/8)*d + a)*8 + i%8). Lane l holds, per group of 4 accumulator
 // registers, four consecutive i of one a; lanes l and l+32 hold the two halves
 // of one 16-byte chunk, and the 32 lanes of a half walk 32 consecutive a: each
-// store instruction writes 512 contiguous bytes. A lane pointer points at this
+// store instruction writes 512 contiguous bytes. A lane offset locates this
 // lane's element for (bi, bj, q) = (0, 0, 0): a = j0 + wn*32*NBJ + l%32,
 // i = i0 + wm*128 + 4*(l/32); tiles are always full (d, f multiples of 256).
-__device__ __forceinline__ long long snap_off(int bi, int bj, int q, int d) {
-  return (long long)(bi * 4 + q) * 8 * d + bj * 256;
-}
+// Group (bi, bj, q) lies (bi*4 + q) planes and bj*32 rows of a further on.
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
 
-// W0 + D for the 8 accumulator groups (bi in [BI, BI+2), q = 0..3) of column
-// block bj, with the accumulators holding D and W0 read from the initial
-// weight's bf16 planes: 8 loads in flight at a time keep the live registers
-// within the budget of two waves per SIMD; the scheduling barriers around each
-// batch stop the compiler from hoisting the next batch's loads.
 // The initial weight W0 as bf16 planes ([f/8][d][8], the snapshot layout): a
 // buffer descriptor over them and this lane's byte offset, so that each load
 // is one instruction with a scalar offset (64-bit addresses per load would
@@ -773,45 +766,58 @@ struct QRead {
   __amdgpu_buffer_rsrc_t rs;
   uint32_t vo;
   int d;
+  // byte offsets of group (bi, bj, q): (bi*4 + q) planes of 8 columns in the
+  // scalar offset, bj*256 elements in the lane offset (an immediate)
+  __device__ __forceinline__ int soff(int bi, int q) const { return (bi * 4 + q) * 16 * d; }
   __device__ __forceinline__ uint2 load(int bi, int bj, int q) const {
-    const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rs, vo, (int)(snap_off(bi, bj, q, d) * 2), 0);
+    const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rs, vo + bj * 512, soff(bi, q), 0);
     return make_uint2(v.x, v.y);
   }
 };
 
-template <int NBJ, int BI, class Fn>
-__device__ __forceinline__ void with_state8(const Acc<NBJ> &acc, const QRead &qr, int bj, Fn &&fn) {
-  uint2 qv[8];
-  pin();
-#pragma unroll
-  for (int k = 0; k < 8; ++k) qv[k] = qr.load(BI + k / 4, bj, k % 4);
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const int bi = BI + k / 4, q = k % 4;
-    const f32x16 &v = acc.v[bi][bj];
-    fn(bi, q, bf16_lo(qv[k].x) + v[4 * q + 0], bf16_hi(qv[k].x) + v[4 * q + 1], bf16_lo(qv[k].y) + v[4 * q + 2],
-       bf16_hi(qv[k].y) + v[4 * q + 3]);
-  }
-  pin();
-}
-
-template <int NBJ, class Fn>
+// W0 + D for every accumulator group (bi, bj, q) of the tile, with the
+// accumulators holding D and W0 read from the initial weight's bf16 planes.
+// The loads go out in batches of KB, each batch one memory round trip; the
+// scheduling barriers around a batch stop the compiler from hoisting the next
+// batch's loads. The snapshot takes all of them in one batch: it runs between
+// stages, when the MFMA fragments are dead, and the 64 registers fit.
+template <int KB, int NBJ, class Fn>
 __device__ __forceinline__ void for_state(const Acc<NBJ> &acc, const QRead &qr, Fn &&fn) {
+  constexpr int NTOT = 16 * NBJ;
+  static_assert(NTOT % KB == 0, "whole batches");
 #pragma unroll
-  for (int bj = 0; bj < NBJ; ++bj) {
-    with_state8<NBJ, 0>(acc, qr, bj, [&](int bi, int q, float a, float b, float c, float e) { fn(bi, bj, q, a, b, c, e); });
-    with_state8<NBJ, 2>(acc, qr, bj, [&](int bi, int q, float a, float b, float c, float e) { fn(bi, bj, q, a, b, c, e); });
+  for (int k0 = 0; k0 < NTOT; k0 += KB) {
+    uint2 qv[KB];
+    pin();
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      const int e = k0 + k;
+      qv[k] = qr.load((e >> 2) & 3, e >> 4, e & 3);
+    }
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      const int e = k0 + k, bi = (e >> 2) & 3, bj = e >> 4, q = e & 3;
+      const f32x16 &v = acc.v[bi][bj];
+      fn(bi, bj, q, bf16_lo(qv[k].x) + v[4 * q + 0], bf16_hi(qv[k].x) + v[4 * q + 1],
+         bf16_lo(qv[k].y) + v[4 * q + 2], bf16_hi(qv[k].y) + v[4 * q + 3]);
+    }
+    pin();
   }
 }
 
-// Snapshot of the weight W0 + D: bf16(W0 + D) into the planes at lane_ptr.
+// Snapshot of the weight W0 + D: bf16(W0 + D) into the snapshot planes at
+// `snap` (one group's [f/8][d][8] planes), with the lane and scalar offsets of
+// the W0 reads (the two share their layout). The stores are non-temporal: no
+// kernel of the update reads them, and they would evict operand slabs that
+// other workgroups still read from L2.
 template <int NBJ>
-__device__ __forceinline__ void dump_snapshot(const Acc<NBJ> &acc, const QRead &qr, bf16_t *lane_ptr, int d) {
-  for_state(acc, qr, [&](int bi, int bj, int q, float s0, float s1, float s2, float s3) {
-    uint2 pk;
-    pk.x = pack_bf16x2(s0, s1);
-    pk.y = pack_bf16x2(s2, s3);
-    *reinterpret_cast<uint2 *>(lane_ptr + snap_off(bi, bj, q, d)) = pk;
+__device__ __forceinline__ void dump_snapshot(const Acc<NBJ> &acc, const QRead &qr, const bf16_t *snap) {
+  constexpr int kNt = 2;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t *>(snap), (short)0, 0x7fffffff, kBufferFlags);
+  for_state<16 * NBJ>(acc, qr, [&](int bi, int bj, int q, float s0, float s1, float s2, float s3) {
+    const u32x2_t pk{pack_bf16x2(s0, s1), pack_bf16x2(s2, s3)};
+    __builtin_amdgcn_raw_buffer_store_b64(pk, rs, qr.vo + bj * 512, qr.soff(bi, q), kNt);
   });
 }
 
@@ -839,7 +845,7 @@ __global__ __launch_bounds__(128 * WN, 1) void k_update(UpdArgs p) {
       (long long)(j0 + wn * 32 * NBJ + (lane & 31)) * p.f + i0 + wm * 128 + 4 * (lane >> 5);
   const long long lane_snap =
       (long long)((i0 + wm * 128) / 8) * 8 * p.d + (j0 + wn * 32 * NBJ + (lane & 31)) * 8 + 4 * (lane >> 5);
-  bf16_t *snap0 = p.snap + (long long)si.grp0 * df + lane_snap;
+  const bf16_t *snap0 = p.snap + (long long)si.grp0 * df;
   const int ngroups = si.len > p.L ? (si.len + p.L - 1) / p.L : 1;
   // where this lane's part of the final state goes (null: nowhere)
   float *st_out = si.state_out >= 0 ? p.state_out + si.state_out * df + lane_off : nullptr;
@@ -884,7 +890,7 @@ __global__ __launch_bounds__(128 * WN, 1) void k_update(UpdArgs p) {
   // Snapshot 0 is the entry weight. Group starts are multiples of the stage
   // depth, so snapshot g is written right after the last stage of group g-1,
   // while the following slabs are already in flight.
-  dump_snapshot(acc, qr, snap0, p.d);
+  dump_snapshot(acc, qr, snap0);
   int g = 1;
   const int nsl = (nk + 1) >> 1;
   Frag<NBJ> cur, nxt;
@@ -898,7 +904,7 @@ __global__ __launch_bounds__(128 * WN, 1) void k_update(UpdArgs p) {
   // is too, and the count exceeds the number allowed; a store in flight can
   // only make a wait last longer.
   auto snapshot = [&](const Acc<NBJ> &a) {
-    dump_snapshot(a, qr, snap0 + (long long)g * df, p.d);
+    dump_snapshot(a, qr, snap0 + (long long)g * df);
     ++g;
   };
   // Stages of group g-1 run plain; its last stage ends with snapshot g.
