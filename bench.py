@@ -84,8 +84,9 @@ def measured_traffic(kernel, C):
             fields.setdefault(parts[0], parts[1:])
     if fields.get("source_sha256", [None])[0] != sha or fields.get("chunk", [None])[0] != str(C):
         return None
-    row = fields.get("bytes_" + kernel)
-    return float(row[0]) if row else None
+    # the state update is two launches (whole rounds, then the half-tile round): one figure per call
+    rows = [v for k, v in fields.items() if k == "bytes_" + kernel or k.startswith("bytes_" + kernel + "_")]
+    return sum(float(r[0]) for r in rows) if rows else None
 
 
 def copy_calibration():
