@@ -23,13 +23,16 @@
 // Operands are row-major (element (r, k) at r*ld + k), K-blocked by 64
 // (element (r, k) at (k/64)*kblk + r*64 + k%64), or held in planes of 8
 // columns (element (r, k) at (k/8)*pstride + r*8 + k%8). V^T and Z are
-// K-blocked (Z's blocks hold every token slot, [f/64][T_pad][64]), so one slab
+// K-blocked (Z's blocks hold every token slot, [f/64][S][64]), so one slab
 // of a tile is one contiguous block instead of rows strided by the whole
-// stream length or by f. Z^T and the snapshots are planes: the MFMA register layout holds
-// four consecutive k of one row per lane, so a store instruction of 32 rows x
-// 16 bytes is 512 contiguous bytes in a plane (in row-major or K-blocked form
-// it would touch 32 lines); a plane slab loads as 1 KB contiguous pieces into
-// an LDS tile of [8][256][8], whose fragment reads need no swizzle.
+// stream length or by f. The state update, whose contraction runs over the
+// tokens, takes Z's blocks as they are and reads its fragments with
+// transposing LDS reads. The snapshots are planes: the MFMA register layout
+// holds four consecutive k of one row per lane, so a store instruction of 32
+// rows x 16 bytes is 512 contiguous bytes in a plane (in row-major or
+// K-blocked form it would touch 32 lines); a plane slab loads as 1 KB
+// contiguous pieces into an LDS tile of [8][256][8], whose fragment reads
+// need no swizzle.
 //
 // MFMA 32x32x16 register layout (lane l, accumulator register r):
 //   A operand: row i = l % 32, k = 8*(l/32) .. +7;  B operand: column j = l % 32, same k.
@@ -69,6 +72,15 @@ __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 // element offset of (row r, logical 16-byte chunk c) inside an N x 64 bf16 LDS tile
 __device__ __forceinline__ int lds_off(int r, int c) { return r * SK + ((c ^ swz(r)) << 3); }
 
+// Chunk swizzle of the kAZ tile (below): k row r holds logical chunk c at
+// c ^ zsw(r). A transposing read of one 16-lane group covers 4 consecutive k
+// rows (r%4 = 0..3) and 2 adjacent chunks in each; across the wave's 4 groups
+// that is 4 chunks of rows r0 .. r0+3 and of rows r0+8 .. r0+11. zsw(r) =
+// 2*(r%4) gives the four rows four disjoint chunk pairs and rows r0, r0+2
+// disjoint halves of the row, so the read is free of bank conflicts with 32
+// or with 64 banks.
+__device__ __forceinline__ int zsw(int r) { return (r & 3) << 1; }
+
 template <int NBJ>
 __device__ __forceinline__ void acc_zero(Acc<NBJ> &acc) {
 #pragma unroll
@@ -96,6 +108,26 @@ constexpr int loads_per_slab() { return loads_a<WN, NBJ>() + 32 * WN * NBJ / (2 
 // rate of half lines), and lane l fills physical chunk l%8, i.e. the logical
 // chunk (l%8) ^ swz(row). Load n of wave w (of NW) moves rows
 // w*ROWS/NW + 8n .. +8.
+
+// LDS DMA issued as an instruction the compiler does not track (the state
+// update's loads). The compiler treats a tracked LDS DMA as a pending write to
+// LDS, and before a transposing read (ds_read_b64_tr_b16) it cannot tell that
+// the read's buffer is not the one in flight, so it waits for every DMA: the
+// ring's lookahead would be lost once per slab. Untracked, the loads are
+// ordered by the kernel's own counted waits and barriers alone (slab_wait),
+// which is how the ring is built anyway. No register outputs: the data goes
+// to LDS at M0 + 16 (4) bytes per lane.
+__device__ __forceinline__ void dma16_untracked(__amdgpu_buffer_rsrc_t rs, void *lds, uint32_t voff, uint32_t soff) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)lds);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(m0), "v"(voff), "s"(rs),
+               "s"(soff)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4_untracked(__amdgpu_buffer_rsrc_t rs, void *lds, uint32_t voff, uint32_t soff) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)lds);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds" ::"s"(m0), "v"(voff), "s"(rs), "s"(soff)
+               : "memory", "m0");
+}
 
 // Row-major operand: element (r, k) at base[r*ld + k], base at the tile's
 // first row. Rows r >= nrows read zero: the lane offset holds the whole row
@@ -223,6 +255,10 @@ struct KbLoad {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(tile + (w * WR + 8 * n) * SK), 16, (n & 1) ? vd : ve,
                                              (w * WR + 8 * n) * 128, 0, 0);
   }
+  // the same load, untracked (dma16_untracked)
+  __device__ __forceinline__ void issue_untracked(const Pre &rs, bf16_t *tile, int w, int n) const {
+    dma16_untracked(rs, tile + (w * WR + 8 * n) * SK, (n & 1) ? vd : ve, (w * WR + 8 * n) * 128);
+  }
 };
 
 // Plane operand (planes of 8 columns): element (r, k) at base[(k/8)*pstride +
@@ -252,6 +288,40 @@ struct PlLoad {
     const int pl = w * (N / 4) + (n >> 2);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(tile + (pl * BM + (n & 3) * 64) * 8), 16, vl,
                                              (int)(pl * pstride * 2) + (n & 3) * 1024, 0, 0);
+  }
+};
+
+// Z blocks as the A tile of the state update (kAZ): tile rows i are 256
+// hidden units (4 blocks of 64 of Z, [f/64][S][64]), k the token slots. The
+// slab of block b is 64 slots x 128 bytes, contiguous in memory, and lands as
+// LDS rows k of [4][64][64] with chunk swizzle zsw. Wave w of NW loads 8N of
+// the 64 rows of block w/(NW/4), 8 rows (1 KB) per load; lane l fills row
+// 8n + l/8 of its share, physical chunk l%8 = logical chunk (l%8) ^ zsw(row),
+// and the rows' offsets mod 4 do not depend on n, so one lane offset serves
+// every load. Every slot of a slab exists in Z (slabs stay within the
+// sequence's padded slots).
+template <int NW>
+struct ZbLoad {
+  static constexpr int N = 32 / NW;  // loads per wave per slab
+  static constexpr int WB = NW / 4;  // waves per block
+  const bf16_t *base;                // this wave's block at the tile's first slot
+  int r0;                            // this wave's first row in its block
+  int blk;                           // this wave's block
+  uint32_t vl;
+  __device__ __forceinline__ void init(const bf16_t *Z, long long S, int i0, long long slot0, int w, int lane) {
+    blk = w / WB;
+    r0 = (w % WB) * 8 * N;
+    base = Z + ((long long)(i0 / 64 + blk) * S + slot0) * 64;
+    const int r = r0 + (lane >> 3);
+    vl = (uint32_t)(r * 128 + (((lane & 7) ^ zsw(r)) << 4));
+  }
+  using Pre = __amdgpu_buffer_rsrc_t;
+  __device__ __forceinline__ Pre prep(int sl) const {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t *>(base + (long long)sl * 64 * 64), (short)0,
+                                             0x7fffffff, kBufferFlags);
+  }
+  __device__ __forceinline__ void issue(const Pre &rs, bf16_t *tile, int, int, int, int n) const {
+    dma16_untracked(rs, tile + (blk * 64 + r0 + 8 * n) * 64, vl, n * 1024);
   }
 };
 
@@ -306,17 +376,53 @@ struct Frag {
   bf16x8 a[4], b[NBJ];
 };
 
+// How the A tile of a slab is held in LDS:
+//   kARows:   256 rows of 64 k, 16-byte chunks swizzled by swz (see lds_off);
+//   kAPlanes: 8 planes of [256 rows][8 k] (chunk c of row r at (c*256 + r)*8);
+//   kAZ:      Z blocks: [4][64 k][64 rows] (row i of the tile is column i%64
+//             of block i/64: the tile is held transposed), 16-byte chunks of
+//             each k row swizzled by zsw. The fragments come from transposing
+//             reads.
+constexpr int kARows = 0, kAPlanes = 1, kAZ = 2;
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// A fragment of a kAZ tile: rows i0 + l%32 (lane l), k 8c .. 8c+7 with c =
+// 4h + 2ks + l/32, from two transposing reads (ds_read_b64_tr_b16) of k rows
+// 8c + 4j .. +3 (j = 0, 1). In each 16-lane group, lane t addresses k row
+// t/4, columns 4(t%4) .. +3 of the group's 16 (one 8-byte piece), and
+// receives column t of the 4 rows. Lane t of group g covers tile row
+// 16(g%2) + t of the 32; this is its element offset for an even 32-row block
+// (bi) of the tile, and `^ 32` (the other half of the 64-column row) gives it
+// for an odd one.
+__device__ __forceinline__ int az_lane_off(int lane) {
+  const int t = lane & 15, g = lane >> 4;
+  const int chunk = ((g & 1) * 2 + ((t & 3) >> 1)) ^ zsw(t >> 2);
+  return (lane >> 5) * 512 + (t >> 2) * 64 + chunk * 8 + 4 * (t & 1);
+}
+
 // Read substep ks (0 or 1) of half h (0 or 1) of an LDS slab into registers.
-// APLANE: the A tile is held as 8 planes of [256 rows][8 columns] (column
-// chunk c of row r at (c*256 + r)*8) instead of swizzled 128-byte rows.
-template <int WN, int NBJ, bool APLANE = false>
+template <int WN, int NBJ, int AMODE = kARows>
 __device__ __forceinline__ void frag_read(Frag<NBJ> &fr, const Slab<WN, NBJ> &st, int h, int ks, int wm, int wn,
                                           int lane) {
   const int c = 4 * h + 2 * ks + (lane >> 5);
+  if constexpr (AMODE == kAZ) {
+    const int lo = az_lane_off(lane), kb = (4 * h + 2 * ks) * 512;
 #pragma unroll
-  for (int bi = 0; bi < 4; ++bi)
-    fr.a[bi] = *reinterpret_cast<const bf16x8 *>(
-        st.a + (APLANE ? (c * BM + wm * 128 + bi * 32 + (lane & 31)) * 8 : lds_off(wm * 128 + bi * 32 + (lane & 31), c)));
+    for (int bi = 0; bi < 4; ++bi) {
+      const bf16_t *pa = st.a + (wm * 2 + (bi >> 1)) * 4096 + kb + ((bi & 1) ? (lo ^ 32) : lo);
+      const bf16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(pa));
+      const bf16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(pa + 256));
+      fr.a[bi] = __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  } else {
+#pragma unroll
+    for (int bi = 0; bi < 4; ++bi)
+      fr.a[bi] = *reinterpret_cast<const bf16x8 *>(
+          st.a + (AMODE == kAPlanes ? (c * BM + wm * 128 + bi * 32 + (lane & 31)) * 8
+                                    : lds_off(wm * 128 + bi * 32 + (lane & 31), c)));
+  }
 #pragma unroll
   for (int bj = 0; bj < NBJ; ++bj)
     fr.b[bj] = *reinterpret_cast<const bf16x8 *>(st.b + lds_off(wn * 32 * NBJ + bj * 32 + (lane & 31), c));
@@ -363,19 +469,25 @@ __device__ __forceinline__ void issue_point(const SL &ld, const typename SL::Pre
 // H (= kt % 2) and REFILL (this stage refills the buffer it finished: 1/0)
 // are fixed at compile time where the caller knows them, else -1 (decided
 // here at run time).
-template <int WN, int NBJ, int NSL, bool AFTER, bool APLANE, int H, int REFILL, class SL, class AfterFn>
-__device__ __forceinline__ void stage_body(Acc<NBJ> &acc, Slab<WN, NBJ> *ring, Frag<NBJ> &cur, Frag<NBJ> &nxt,
-                                           int kt, int &cb, int nk, int wm, int wn, int lane, int w, const SL &ld,
-                                           AfterFn &&after_fn) {
+// sc is the ring buffer of slab kt/2, sn that of the slab after it.
+template <int WN, int NBJ, int NSL, bool AFTER, int AMODE, int H, int REFILL, class SL, class AfterFn>
+__device__ __forceinline__ void stage_body(Acc<NBJ> &acc, Slab<WN, NBJ> &sc, Slab<WN, NBJ> &sn, Frag<NBJ> &cur,
+                                           Frag<NBJ> &nxt, int kt, int nk, int wm, int wn, int lane, int w,
+                                           const SL &ld, AfterFn &&after_fn) {
   constexpr int LPS = loads_per_slab<WN, NBJ>();
   static_assert(SL::N == LPS, "the slab loads match the tile configuration");
   const int sl = kt >> 1;
   const int nsl = (nk + 1) >> 1;
   const int h = H >= 0 ? H : (kt & 1);
   const bool refill = REFILL >= 0 ? REFILL == 1 : (h == 1 && sl + NSL < nsl);
-  // cb: the ring buffer of slab sl (sl % NSL, carried by the caller); nb: that of stage kt+1
-  const int nb = h == 1 ? (cb + 1 == NSL ? 0 : cb + 1) : cb;
-  frag_read<WN, NBJ, APLANE>(nxt, ring[cb], h, 1, wm, wn, lane);
+  // substep 0 of stage kt+1: the next slab's buffer after an odd stage
+  auto read_next = [&]() {
+    if (h == 1)
+      frag_read<WN, NBJ, AMODE>(cur, sn, 0, 0, wm, wn, lane);
+    else
+      frag_read<WN, NBJ, AMODE>(cur, sc, 1, 0, wm, wn, lane);
+  };
+  frag_read<WN, NBJ, AMODE>(nxt, sc, h, 1, wm, wn, lane);
   pin();
   frag_mma<0, 1>(acc, cur);
   pin();
@@ -385,7 +497,7 @@ __device__ __forceinline__ void stage_body(Acc<NBJ> &acc, Slab<WN, NBJ> *ring, F
     slab_wait<LPS, NSL - 2, SL::kPf ? 1 : 0>(later);
   }
   const int rs = sl + NSL;
-  Slab<WN, NBJ> &dst = ring[cb];  // the buffer just finished refills with slab rs
+  Slab<WN, NBJ> &dst = sc;  // the buffer just finished refills with slab rs
   typename SL::Pre pre{};
   if (refill) pre = ld.prep(rs);
   pin();
@@ -402,7 +514,7 @@ __device__ __forceinline__ void stage_body(Acc<NBJ> &acc, Slab<WN, NBJ> *ring, F
   pin();
   // unconditional (past the end it reads a stale buffer of the ring): no
   // branch, so the compiler can count the reads and wait for each exactly
-  if (!AFTER) frag_read<WN, NBJ, APLANE>(cur, ring[nb], (kt + 1) & 1, 0, wm, wn, lane);
+  if (!AFTER) read_next();
   if (refill) issue_point<LPS, 3>(ld, pre, dst, rs, w, lane);
   pin();
   frag_mma<1, 2>(acc, nxt);
@@ -420,17 +532,9 @@ __device__ __forceinline__ void stage_body(Acc<NBJ> &acc, Slab<WN, NBJ> *ring, F
   pin();
   if (AFTER) {
     after_fn(acc);
-    frag_read<WN, NBJ, APLANE>(cur, ring[nb], (kt + 1) & 1, 0, wm, wn, lane);
+    read_next();
     pin();
   }
-  cb = nb;
-}
-
-template <int WN, int NBJ, int NSL, bool AFTER, bool APLANE = false, class SL, class AfterFn>
-__device__ __forceinline__ void pipelined_stage(Acc<NBJ> &acc, Slab<WN, NBJ> *ring, Frag<NBJ> &cur, Frag<NBJ> &nxt,
-                                                int kt, int &cb, int nk, int wm, int wn, int lane, int w,
-                                                const SL &ld, AfterFn &&after_fn) {
-  stage_body<WN, NBJ, NSL, AFTER, APLANE, -1, -1>(acc, ring, cur, nxt, kt, cb, nk, wm, wn, lane, w, ld, after_fn);
 }
 
 struct NoHook {
@@ -483,55 +587,74 @@ __device__ __forceinline__ void band_tile(int t, int nx, int ny, int H, int &x, 
 // Stages kt .. kt_end-1 of an nk-stage K loop without hooks (kt even), with
 // each stage's parity and refill fixed at compile time: the stages of slabs
 // 0 .. nsl-NSL-1 refill their buffer, the rest drain the ring, and an odd
-// count of stages ends on a lone even stage. Leaves kt = kt_end.
-template <int WN, int NBJ, int NSL, bool APLANE, class SL>
-__device__ __forceinline__ void stage_run(Acc<NBJ> &acc, Slab<WN, NBJ> *ring, Frag<NBJ> &cur, Frag<NBJ> &nxt,
-                                          int &kt, int &cb, int kt_end, int nk, int wm, int wn, int lane, int w,
-                                          const SL &ld) {
+// count of stages ends on a lone even stage. Leaves kt = kt_end. `pair(kt,
+// refill)` runs the two stages of slab kt/2 (refill: whether the second one
+// refills), `lone(kt)` a lone even stage.
+template <int NSL, class Pair, class Lone>
+__device__ __forceinline__ void stage_phases(int &kt, int kt_end, int nk, Pair &&pair, Lone &&lone) {
   const int nsl = (nk + 1) >> 1;
   const int kref = nsl > NSL ? 2 * (nsl - NSL) : 0;  // first stage past the refilling slabs
   const int k1 = kref < kt_end ? kref : kt_end;
-  for (; kt + 1 < k1; kt += 2) {
-    stage_body<WN, NBJ, NSL, false, APLANE, 0, 0>(acc, ring, cur, nxt, kt, cb, nk, wm, wn, lane, w, ld, NoHook{});
-    stage_body<WN, NBJ, NSL, false, APLANE, 1, 1>(acc, ring, cur, nxt, kt + 1, cb, nk, wm, wn, lane, w, ld, NoHook{});
-  }
-  for (; kt + 1 < kt_end; kt += 2) {
-    stage_body<WN, NBJ, NSL, false, APLANE, 0, 0>(acc, ring, cur, nxt, kt, cb, nk, wm, wn, lane, w, ld, NoHook{});
-    stage_body<WN, NBJ, NSL, false, APLANE, 1, 0>(acc, ring, cur, nxt, kt + 1, cb, nk, wm, wn, lane, w, ld, NoHook{});
-  }
+  for (; kt + 1 < k1; kt += 2) pair(kt, std::true_type{});
+  for (; kt + 1 < kt_end; kt += 2) pair(kt, std::false_type{});
   if (kt < kt_end) {
-    stage_body<WN, NBJ, NSL, false, APLANE, 0, 0>(acc, ring, cur, nxt, kt, cb, nk, wm, wn, lane, w, ld, NoHook{});
+    lone(kt);
     ++kt;
   }
 }
 
+// The ring as one LDS array: buffer cb (runtime) holds slab kt/2.
+template <int WN, int NBJ, int NSL, int AMODE, class SL>
+__device__ __forceinline__ void stage_run(Acc<NBJ> &acc, Slab<WN, NBJ> *ring, Frag<NBJ> &cur, Frag<NBJ> &nxt,
+                                          int &kt, int &cb, int kt_end, int nk, int wm, int wn, int lane, int w,
+                                          const SL &ld) {
+  stage_phases<NSL>(
+      kt, kt_end, nk,
+      [&](int k, auto refill) {
+        const int nb = cb + 1 == NSL ? 0 : cb + 1;
+        stage_body<WN, NBJ, NSL, false, AMODE, 0, 0>(acc, ring[cb], ring[nb], cur, nxt, k, nk, wm, wn, lane, w, ld,
+                                                     NoHook{});
+        stage_body<WN, NBJ, NSL, false, AMODE, 1, decltype(refill)::value ? 1 : 0>(
+            acc, ring[cb], ring[nb], cur, nxt, k + 1, nk, wm, wn, lane, w, ld, NoHook{});
+        cb = nb;
+      },
+      [&](int k) {
+        const int nb = cb + 1 == NSL ? 0 : cb + 1;
+        stage_body<WN, NBJ, NSL, false, AMODE, 0, 0>(acc, ring[cb], ring[nb], cur, nxt, k, nk, wm, wn, lane, w, ld,
+                                                     NoHook{});
+      });
+}
+
 // K loop of nk stages over the slab loads `ld` (tiles of 256 x 32*WN*NBJ,
-// NSL slabs in the ring). APLANE: the A tile is a plane operand.
+// NSL slabs in the ring). AMODE: how the A tile is held (kARows, kAPlanes, kAZ).
 // Start of a K loop of nsl >= 1 slabs: the loads of the first min(NSL, nsl)
 // slabs and, with a prefetch, the first prefetch (slab NSL + 1); then the
-// wait for slab 0.
-template <int WN, int NBJ, int NSL, class SL>
-__device__ __forceinline__ void ring_prologue(const SL &ld, Slab<WN, NBJ> *ring, int nsl, int w, int lane) {
-  for (int sl = 0; sl < NSL && sl < nsl; ++sl) {
-    const typename SL::Pre pre = ld.prep(sl);
+// wait for slab 0. buf(sl) is the ring buffer of slab sl < NSL.
+template <int WN, int NBJ, int NSL, class SL, class Buf>
+__device__ __forceinline__ void ring_prologue(const SL &ld, Buf &&buf, int nsl, int w, int lane) {
 #pragma unroll
-    for (int j = 0; j < SL::N; ++j) ld.issue(pre, ring[sl], sl, w, lane, j);
+  for (int sl = 0; sl < NSL; ++sl) {
+    if (sl < nsl) {
+      const typename SL::Pre pre = ld.prep(sl);
+#pragma unroll
+      for (int j = 0; j < SL::N; ++j) ld.issue(pre, buf(sl), sl, w, lane, j);
+    }
   }
   if constexpr (SL::kPf) ld.prefetch((NSL + 1) < (nsl - 1) ? (NSL + 1) : (nsl - 1), w, lane);
   slab_wait<loads_per_slab<WN, NBJ>(), NSL - 1, SL::kPf ? 1 : 0>((nsl - 1) < (NSL - 1) ? (nsl - 1) : (NSL - 1));
 }
 
-template <int WN, int NBJ, int NSL, bool APLANE, class SL>
+template <int WN, int NBJ, int NSL, int AMODE, class SL>
 __device__ __forceinline__ void gemm_k(Acc<NBJ> &acc, Slab<WN, NBJ> *ring, const SL &ld, int nk) {
   const int lane = threadIdx.x & 63;
   const int w = wave_id(), wm = w & 1, wn = w >> 1;
   if (nk <= 0) return;
   const int nsl = (nk + 1) >> 1;
-  ring_prologue<WN, NBJ, NSL>(ld, ring, nsl, w, lane);
+  ring_prologue<WN, NBJ, NSL>(ld, [&](int sl) -> Slab<WN, NBJ> & { return ring[sl]; }, nsl, w, lane);
   Frag<NBJ> cur, nxt;
-  frag_read<WN, NBJ, APLANE>(cur, ring[0], 0, 0, wm, wn, lane);
+  frag_read<WN, NBJ, AMODE>(cur, ring[0], 0, 0, wm, wn, lane);
   int kt = 0, cb = 0;
-  stage_run<WN, NBJ, NSL, APLANE>(acc, ring, cur, nxt, kt, cb, nk, nk, wm, wn, lane, w, ld);
+  stage_run<WN, NBJ, NSL, AMODE>(acc, ring, cur, nxt, kt, cb, nk, nk, wm, wn, lane, w, ld);
 }
 
 // The wide GEMMs' loaders: 8 waves, 256 x 256 tiles.
@@ -540,21 +663,19 @@ using CbW = CbLoad<BM, 2 * WN_W>;
 
 // ---------------------------------------------------------------------------
 // Up/gate GEMM with SwiGLU epilogue. i = token slot, j = interleaved W_ug row.
-// Writes Z column-blocked [f/64][S][64] and Z^T in planes of 8 tokens [S/8][f][8] (S scratch slots in all), the
-// same bf16 values twice. (eta is carried by the target rows V^T, not by Z^T.)
+// Writes Z column-blocked [f/64][S][64] (S scratch slots in all); the state
+// update reads the same blocks transposed, so Z is written once.
 // grid: nx * ny workgroups, nx = 2f/256, ny = S/256
 struct A1Args {
   const bf16_t *x;
   const bf16_t *Wug;
   bf16_t *Z;
-  bf16_t *ZT;
   long long S;
   int d, f;
   int nx, ny;  // tiles along W_ug rows and along token slots
   Seqs sq;
 };
 
-template <bool WRITE_ZT>
 __global__ __launch_bounds__(NT_W, 1) void k_a1(A1Args p) {
   __shared__ __attribute__((aligned(16))) Slab<WN_W, NBJ_W> ring[NSL_W];
   int tx, ty;  // W_ug tile, token tile
@@ -568,14 +689,14 @@ __global__ __launch_bounds__(NT_W, 1) void k_a1(A1Args p) {
   ld.b.init(p.Wug + (long long)n0 * 64, 2LL * p.f * 64, 2 * p.f - n0, wave_id(), threadIdx.x & 63);
   Acc<NBJ_W> acc;
   acc_zero(acc);
-  gemm_k<WN_W, NBJ_W, NSL_W, false>(acc, ring, ld, p.d / BK);
+  gemm_k<WN_W, NBJ_W, NSL_W, kARows>(acc, ring, ld, p.d / BK);
 
   // Epilogue. The wave's two 32-column blocks are a matching (up, gate) pair
   // of W_ug rows: features f0 + l%32 (f0 is a multiple of 32, so they lie in
   // one 64-feature block of Z; f is a multiple of 256, so all are < f). Lane l
-  // holds slots s0 + bi*32 + 8q + 4(l/32) + r. Both outputs are written with
-  // buffer stores from one lane offset each; every other offset is a
-  // compile-time constant or wave-uniform, so no per-store address arithmetic.
+  // holds slots s0 + bi*32 + 8q + 4(l/32) + r. The stores are buffer stores
+  // from one lane offset; every other offset is a compile-time constant or
+  // wave-uniform, so no per-store address arithmetic.
   const int lane = threadIdx.x & 63, w = wave_id(), wm = w & 1, wn = w >> 1;
   const int f0 = n0 / 2 + wn * 32;
   const long long s0 = m0 + wm * 128;
@@ -583,10 +704,6 @@ __global__ __launch_bounds__(NT_W, 1) void k_a1(A1Args p) {
   const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
       p.Z + ((long long)(f0 / 64) * p.S + s0) * 64 + f0 % 64, (short)0, 0x7fffffff, kBufferFlags);
   const uint32_t vz = (uint32_t)((256 * (lane >> 5) + (lane & 31)) * 2);
-  // Z^T [S/8][f][8]: (slot, feature) at ((slot/8)*f + feature)*8 + slot%8
-  const __amdgpu_buffer_rsrc_t rzt = __builtin_amdgcn_make_buffer_rsrc(
-      p.ZT + ((s0 >> 3) * p.f + f0) * 8, (short)0, 0x7fffffff, kBufferFlags);
-  const uint32_t vzt = (uint32_t)((8 * (lane & 31) + 4 * (lane >> 5)) * 2);
   constexpr int kNt = 2;  // cache policy of the stores: non-temporal
 #pragma unroll
   for (int bi = 0; bi < 4; ++bi) {
@@ -599,7 +716,6 @@ __global__ __launch_bounds__(NT_W, 1) void k_a1(A1Args p) {
       for (int r = 0; r < 4; ++r) z[r] = silu_fast(g[4 * q + r]) * u[4 * q + r];
       // slots r = 0, 1 in the halves of pk.x, r = 2, 3 in those of pk.y
       const u32x2_t pk{pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3])};
-      if (WRITE_ZT) __builtin_amdgcn_raw_buffer_store_b64(pk, rzt, vzt, (bi * 4 + q) * p.f * 16, kNt);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const uint32_t h2 = r < 2 ? pk.x : pk.y;
@@ -639,7 +755,7 @@ __global__ __launch_bounds__(NT_W, 1) void k_target_gemm(TgtArgs p) {
   ld.b.init(p.WtT + (long long)n0 * p.d, p.d, 256, p.d, wave_id(), threadIdx.x & 63);
   Acc<NBJ_W> acc;
   acc_zero(acc);
-  gemm_k<WN_W, NBJ_W, NSL_W, false>(acc, ring, ld, p.d / BK);
+  gemm_k<WN_W, NBJ_W, NSL_W, kARows>(acc, ring, ld, p.d / BK);
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w & 1, wn = w >> 1;
   bf16_t *VTb = p.VT + (long long)b * p.d * p.T_pad;
@@ -668,7 +784,7 @@ __global__ __launch_bounds__(NT_W, 1) void k_target_gemm(TgtArgs p) {
 }
 
 // ---------------------------------------------------------------------------
-// State update with snapshots. i = hidden unit (ZT row), j = model dim (VT row),
+// State update with snapshots. i = hidden unit (Z column), j = model dim (VT row),
 // k = token slot. The state of a sequence is D = W - W0, the change of the
 // fast weight since its last reset, in fp32; the accumulators of one tile
 // hold it for the whole token stream. Because D starts at zero and stays
@@ -684,30 +800,46 @@ __global__ __launch_bounds__(NT_W, 1) void k_target_gemm(TgtArgs p) {
 // of at most 128 tiles is split into 256 x 128 halves that run as one round
 // on the 4-wave configuration, so no CU idles for a whole round.
 
-// Tile loads of the update with an L2 prefetch. Every Z^T tile is read by
-// one XCD only, so its slabs come from HBM, one slab (two in the half-tile
-// round) ahead of use without the prefetch. The workgroups that share an
-// operand tile split its prefetch: the sa tiles (and halves) of a band of the
-// tile order split the 256 lines of 128 bytes of a Z^T slab (8 planes of
-// 32 lines), the sb tiles along x of an XCD's range split the BN rows (one
-// line each) of a V^T slab. Waves 0 .. WN-1 touch the first share, waves WN ..
-// 2WN-1 the second, each with one 4-byte DMA into a 256-byte LDS sink that
-// nothing reads; each lane's offset within the slab is fixed at the start.
+// Tile loads of the update with an L2 prefetch. Every Z tile (a band of
+// 256 hidden units) is read by one XCD only, so its slabs come from HBM, one
+// slab (two in the half-tile round) ahead of use without the prefetch. The
+// workgroups that share an operand tile split its prefetch: the sa tiles (and
+// halves) of a band of the tile order split the 256 lines of 128 bytes of a Z
+// slab (4 blocks of 64 lines), the sb tiles along x of an XCD's range split
+// the BN rows (one line each) of a V^T slab. Waves 0 .. WN-1 touch the first
+// share, waves WN .. 2WN-1 the second, each with one 4-byte DMA into a
+// 256-byte LDS sink that nothing reads; each lane's offset within the slab is
+// fixed at the start. A wave's Z lines span at most two blocks (at most 64
+// lines), so its offsets, from the first block it touches, stay below
+// S*128 + 8 KB.
 template <int WN, int BN>
-struct UpdLoads : SlabLoads<PlLoad<2 * WN>, KbLoad<BN, 2 * WN>> {
+struct UpdLoads : SlabLoads<ZbLoad<2 * WN>, KbLoad<BN, 2 * WN>> {
   static constexpr bool kPf = true;
+  using Base = SlabLoads<ZbLoad<2 * WN>, KbLoad<BN, 2 * WN>>;
+  // every load untracked (see dma16_untracked): the A tile is read transposed
+  template <class S>
+  __device__ __forceinline__ void issue(const typename Base::Pre &p, S &slab, int sl, int w, int lane, int j) const {
+    if (j < ZbLoad<2 * WN>::N)
+      this->a.issue(p.a, slab.a, sl, w, lane, j);
+    else
+      this->b.issue_untracked(p.b, slab.b, w, j - ZbLoad<2 * WN>::N);
+  }
   uint32_t *sink;
-  uint32_t vp;  // this lane's byte offset in the slab (A: plane and line, B: row)
-  // sharer ka of sa takes lines [ka*256/sa, (ka+1)*256/sa) of the Z^T slab;
+  const bf16_t *pa;  // A sharers: the first Z block this wave touches, at the tile's first slot
+  uint32_t vp;       // this lane's byte offset in the slab (A: from block pa, B: row)
+  // sharer ka of sa takes lines [ka*256/sa, (ka+1)*256/sa) of the Z slab;
   // sharer kb of sb takes rows [kb*BN/sb, (kb+1)*BN/sb) of the V^T slab
-  __device__ __forceinline__ void init_pf(uint32_t *sink_, int sa, int ka, int sb, int kb, int w, int lane) {
+  __device__ __forceinline__ void init_pf(uint32_t *sink_, const bf16_t *Z, long long S, int i0, long long slot0,
+                                          int sa, int ka, int sb, int kb, int w, int lane) {
     sink = sink_;
     if (w < WN) {
       const int lo = ka * 256 / sa, n = (ka + 1) * 256 / sa - lo;
       const int per = (n + WN - 1) / WN < 64 ? (n + WN - 1) / WN : 64;
+      const int first = lo + w * per < lo + n - 1 ? lo + w * per : lo + n - 1;
       int line = lo + w * per + lane % per;
       if (line > lo + n - 1) line = lo + n - 1;
-      vp = (uint32_t)((line >> 5) * this->a.pstride * 2 + (line & 31) * 128);
+      pa = Z + ((long long)(i0 / 64 + (first >> 6)) * S + slot0) * 64;
+      vp = (uint32_t)(((line >> 6) - (first >> 6)) * S * 128 + (line & 63) * 128);
     } else {
       const int lo = kb * BN / sb, n = (kb + 1) * BN / sb - lo;
       const int per = (n + WN - 1) / WN < 64 ? (n + WN - 1) / WN : 64;
@@ -718,17 +850,15 @@ struct UpdLoads : SlabLoads<PlLoad<2 * WN>, KbLoad<BN, 2 * WN>> {
   }
   __device__ __forceinline__ void prefetch(int sl, int w, int lane) const {
     const __amdgpu_buffer_rsrc_t rs =
-        w < WN ? __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t *>(this->a.base + (long long)sl * 8 * this->a.pstride),
-                                                   (short)0, 0x7fffffff, kBufferFlags)
+        w < WN ? __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t *>(pa + (long long)sl * 64 * 64), (short)0,
+                                                   0x7fffffff, kBufferFlags)
                : __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t *>(this->b.base + (long long)sl * this->b.kblk),
                                                    (short)0, 0x7fffffff, kBufferFlags);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)sink, 4, vp, 0, 0, 0);
+    dma4_untracked(rs, sink, vp, 0);
   }
 };
 
-// LDS of the update: the ring and the prefetch sink in one object. (With the
-// sink in an object of its own, the compiler cannot tell the prefetch DMA from
-// the ring's, and waits for it before every fragment read.)
+// LDS of the update: the ring and the prefetch sink (256 bytes that nothing reads).
 template <int WN, int NBJ, int NSL>
 struct UpdLds {
   Slab<WN, NBJ> ring[NSL];
@@ -736,12 +866,13 @@ struct UpdLds {
 };
 
 struct UpdArgs {
-  const bf16_t *ZT;
+  const bf16_t *Z;        // Z [f/64][S][64]
   const bf16_t *VT;
   const float *state_in;  // D [..][d][f], indexed by SeqInfo::state_in
   float *state_out;       // D [..][d][f], indexed by SeqInfo::state_out
   bf16_t *snap;
   const bf16_t *W0p;      // W0 as planes [f/8][d][8]
+  long long S;            // scratch slots in all (Z's block stride is S*64)
   int L, d, f;
   int tile0;  // first 256 x 256 tile of this launch
   Seqs sq;
@@ -871,16 +1002,17 @@ __global__ __launch_bounds__(128 * WN, 1) void k_update(UpdArgs p) {
     acc_zero(acc);  // a document start: W = W0
   }
 
-  // A: Z^T in planes of 8 tokens [S/8][f][8]; B: eta V^T K-blocked [S/64][d][64]
+  // A: Z blocks [f/64][S][64], read transposed; B: eta V^T K-blocked [S/64][d][64]
   UpdLoads<WN, BN> ld;
-  ld.a.init(p.ZT + (long long)si.slot0 * p.f + (long long)i0 * 8, (long long)p.f * 8, lane);
+  ld.a.init(p.Z, p.S, i0, si.slot0, w, lane);
   ld.b.init(p.VT + (long long)si.slot0 * p.d + (long long)j0 * 64, (long long)p.d * 64, w, lane);
   {
-    // Z^T tile tx is shared by the tiles of its band (h of them) and their halves;
+    // Z tile tx is shared by the tiles of its band (h of them) and their halves;
     // a V^T tile (or half) by the tiles along x of the XCD's range
     const int full = ny / 8, band = ty / 8, h = band < full ? 8 : ny - full * 8;
     const int halves = 256 / BN, half = n % halves;
-    ld.init_pf(lds.sink, h * halves, (ty - band * 8) * halves + half, 16 / WN, tx % (16 / WN), w, lane);
+    ld.init_pf(lds.sink, p.Z, p.S, i0, si.slot0, h * halves, (ty - band * 8) * halves + half, 16 / WN, tx % (16 / WN),
+               w, lane);
   }
   const int nk = (si.len + BK - 1) / BK;
   QRead qr;
@@ -895,8 +1027,8 @@ __global__ __launch_bounds__(128 * WN, 1) void k_update(UpdArgs p) {
   const int nsl = (nk + 1) >> 1;
   Frag<NBJ> cur, nxt;
   if (nk > 0) {
-    ring_prologue<WN, NBJ, NSL>(ld, ring, nsl, w, lane);
-    frag_read<WN, NBJ, true>(cur, ring[0], 0, 0, wm, wn, lane);
+    ring_prologue<WN, NBJ, NSL>(ld, [&](int sl) -> Slab<WN, NBJ> & { return ring[sl]; }, nsl, w, lane);
+    frag_read<WN, NBJ, kAZ>(cur, ring[0], 0, 0, wm, wn, lane);
   }
   // The snapshot stores share the vector-memory counter with the tile loads.
   // The counted waits stay exact for the loads: loads complete in issue
@@ -910,14 +1042,17 @@ __global__ __launch_bounds__(128 * WN, 1) void k_update(UpdArgs p) {
   // Stages of group g-1 run plain; its last stage ends with snapshot g.
   // A group spans L/BK stages, an even number (L is a multiple of 64), so
   // every group ends on an odd stage.
-  int kt = 0, cb = 0;
+  int kt = 0, cb = 0;  // cb: the ring buffer of slab kt/2
   for (; g < ngroups; ) {
     const int kt_last = g * (p.L / BK) - 1;  // last stage before group g starts
-    stage_run<WN, NBJ, NSL, true>(acc, ring, cur, nxt, kt, cb, kt_last, nk, wm, wn, lane, w, ld);
-    pipelined_stage<WN, NBJ, NSL, true, true>(acc, ring, cur, nxt, kt, cb, nk, wm, wn, lane, w, ld, snapshot);
+    stage_run<WN, NBJ, NSL, kAZ>(acc, ring, cur, nxt, kt, cb, kt_last, nk, wm, wn, lane, w, ld);
+    const int nb = cb + 1 == NSL ? 0 : cb + 1;
+    stage_body<WN, NBJ, NSL, true, kAZ, 1, -1>(acc, ring[cb], ring[nb], cur, nxt, kt, nk, wm, wn, lane, w, ld,
+                                               snapshot);
+    cb = nb;
     ++kt;
   }
-  stage_run<WN, NBJ, NSL, true>(acc, ring, cur, nxt, kt, cb, nk, nk, wm, wn, lane, w, ld);
+  stage_run<WN, NBJ, NSL, kAZ>(acc, ring, cur, nxt, kt, cb, nk, nk, wm, wn, lane, w, ld);
   // the final state D in fp32
   if (!st_out) return;
 #pragma unroll
@@ -986,7 +1121,7 @@ __global__ __launch_bounds__(NT_W, 1) void k_scores(ScoreArgs p) {
   ld.b.init(Zg + (long long)j0 * 64, zblk, tp - gs - j0, wave_id(), threadIdx.x & 63);
   Acc<NBJ_W> acc;
   acc_zero(acc);
-  gemm_k<WN_W, NBJ_W, NSL_W, false>(acc, ring, ld, p.f / BK);
+  gemm_k<WN_W, NBJ_W, NSL_W, kARows>(acc, ring, ld, p.f / BK);
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w & 1, wn = w >> 1;
   bf16_t *Pg = p.P + (long long)bg * p.L * p.L;
@@ -1083,7 +1218,7 @@ __global__ __launch_bounds__(NT_W, 1) void k_out(OutArgs p) {
     SlabLoads<PlLoad<2 * WN_W>, CbW> ld;
     ld.a.init(p.snap + (long long)bg * p.d * p.f + (long long)i0 * 8, (long long)p.d * 8, l8);
     ld.b.init(p.Z + ((long long)si.slot0 + gs + j0) * 64, p.S * 64, tp - gs - j0, w8, l8);
-    gemm_k<WN_W, NBJ_W, NSL_W, true>(acc, ring, ld, p.f / BK);
+    gemm_k<WN_W, NBJ_W, NSL_W, kAPlanes>(acc, ring, ld, p.f / BK);
   }
   if (p.intra) {  // segment 2: V^T against P over the tokens before the last row's chunk
     const int jl = (j0 + 255 < Lg - 1) ? j0 + 255 : Lg - 1;
@@ -1097,7 +1232,7 @@ __global__ __launch_bounds__(NT_W, 1) void k_out(OutArgs p) {
       ld.a.init(p.VT + ((long long)si.slot0 + gs) * p.d + (long long)i0 * 64, (long long)p.d * 64, w8, l8);
       ld.b.init(p.P + (long long)bg * p.L * p.L + (long long)j0 * p.L, p.L, p.L - j0, kv, w8, l8);
       __syncthreads();  // every wave is done reading the ring before it is refilled
-      gemm_k<WN_W, NBJ_W, NSL_W, false>(acc, ring, ld, nk2);
+      gemm_k<WN_W, NBJ_W, NSL_W, kARows>(acc, ring, ld, nk2);
     }
   }
 
@@ -1224,13 +1359,13 @@ __global__ __launch_bounds__(NT_W, 1) void k_chunk_gram(GramArgs p) {
     const int32_t *tg = p.ids + (long long)b * (p.T + 1) + 1;  // target id of slot p at tg[p]
     ld.a.init(p.E, p.d, p.vocab, tg + s0, p.T - s0, wv, lane);
     ld.b.init(p.E, p.d, p.vocab, tg + t0, p.T - t0, wv, lane);
-    gemm_k<WN_W, NBJ_W, NSL_W, false>(acc, ring, ld, p.d / BK);
+    gemm_k<WN_W, NBJ_W, NSL_W, kARows>(acc, ring, ld, p.d / BK);
   } else {
     const bf16_t *Vb = p.V + (long long)b * p.T_pad * p.d;
     SlabLoads<RmW, RmW> ld;
     ld.a.init(Vb + (long long)s0 * p.d, p.d, p.T_pad - s0, p.d, wv, lane);
     ld.b.init(Vb + (long long)t0 * p.d, p.d, p.T_pad - t0, p.d, wv, lane);
-    gemm_k<WN_W, NBJ_W, NSL_W, false>(acc, ring, ld, p.d / BK);
+    gemm_k<WN_W, NBJ_W, NSL_W, kARows>(acc, ring, ld, p.d / BK);
   }
   // G_V to this lane's scratch: register group k (4 registers) at [k][lane]
   float4 *gv = reinterpret_cast<float4 *>(p.gv) + ((long long)id * 8 + wv) * (32 * 64) + lane;
@@ -1249,7 +1384,7 @@ __global__ __launch_bounds__(NT_W, 1) void k_chunk_gram(GramArgs p) {
     SlabLoads<CbW, CbW> ld;
     ld.a.init(Zb + (long long)s0 * 64, p.S * 64, p.T_pad - s0, wv, lane);
     ld.b.init(Zb + (long long)t0 * 64, p.S * 64, p.T_pad - t0, wv, lane);
-    gemm_k<WN_W, NBJ_W, NSL_W, false>(acc, ring, ld, p.f / BK);
+    gemm_k<WN_W, NBJ_W, NSL_W, kARows>(acc, ring, ld, p.f / BK);
   }
   // products of same-chunk pairs, in place of G_Z: row s0 + sl shares column
   // t's chunk when lo <= sl < lo + C (lo: the chunk's start less s0); one
@@ -1382,16 +1517,12 @@ hipError_t launch_chunk_gram_bf16(const bf16_t *Z, const bf16_t *Vrow, const bf1
   return hipGetLastError();
 }
 
-hipError_t launch_a1_bf16(const bf16_t *x, const bf16_t *Wug, bf16_t *Z, bf16_t *ZT, int write_zt,
-                          const Layout &lay, hipStream_t s) {
+hipError_t launch_a1_bf16(const bf16_t *x, const bf16_t *Wug, bf16_t *Z, const Layout &lay, hipStream_t s) {
   const int nx = (2 * lay.f + 255) / 256;
   const long long ny = lay.n_slots() / BM;
   if (nx * ny >= (1LL << 31)) return hipErrorInvalidConfiguration;
-  A1Args p{x, Wug, Z, ZT, lay.n_slots(), lay.d, lay.f, nx, (int)ny, lay.seqs()};
-  if (write_zt)
-    hipLaunchKernelGGL(k_a1<true>, dim3((unsigned)(nx * ny)), dim3(NT_W), 0, s, p);
-  else
-    hipLaunchKernelGGL(k_a1<false>, dim3((unsigned)(nx * ny)), dim3(NT_W), 0, s, p);
+  A1Args p{x, Wug, Z, lay.n_slots(), lay.d, lay.f, nx, (int)ny, lay.seqs()};
+  hipLaunchKernelGGL(k_a1, dim3((unsigned)(nx * ny)), dim3(NT_W), 0, s, p);
   return hipGetLastError();
 }
 
@@ -1405,15 +1536,17 @@ hipError_t launch_target_gemm_bf16(const bf16_t *U, const bf16_t *WtT, bf16_t *V
   return hipGetLastError();
 }
 
-hipError_t launch_update_bf16(const bf16_t *ZT, const bf16_t *VT, const float *state_in, float *state_out,
+hipError_t launch_update_bf16(const bf16_t *Z, const bf16_t *VT, const float *state_in, float *state_out,
                               bf16_t *snap, const bf16_t *W0p, const Layout &lay, int cus, hipStream_t s) {
   const long long tiles = (long long)lay.n_seq() * (lay.f / BM) * (lay.d / 256);
   if (tiles * 2 >= (1LL << 31)) return hipErrorInvalidConfiguration;
+  // the Z prefetch's lane offsets span one Z block (S*128 bytes) and a slab
+  if (lay.n_slots() * 128 + 8192 >= (1LL << 31)) return hipErrorInvalidConfiguration;
   // whole rounds on the wide configuration, a last round of <= cus/2 tiles as halves
   if (cus < 2) cus = 2;
   const long long rem = tiles % cus;
   const long long whole = rem <= cus / 2 ? tiles - rem : tiles;
-  UpdArgs p{ZT, VT, state_in, state_out, snap, W0p, lay.L, lay.d, lay.f, 0, lay.seqs()};
+  UpdArgs p{Z, VT, state_in, state_out, snap, W0p, lay.n_slots(), lay.L, lay.d, lay.f, 0, lay.seqs()};
   if (whole > 0) hipLaunchKernelGGL((k_update<WN_W, NBJ_W, NSL_W>), dim3((unsigned)whole), dim3(NT_W), 0, s, p);
   if (tiles > whole) {
     p.tile0 = (int)whole;

@@ -10,18 +10,17 @@
 // by cfac[b][t/C].
 hipError_t launch_gather_vt_bf16(const int32_t *ids, const bf16_t *E, int vocab, bf16_t *VT, bf16_t *Vrow,
                                  const float *cfac, float eta, const Layout &lay, hipStream_t s);
-// Z = SiLU(x W_gate^T) * (x W_up^T) -> Z column-blocked [f/64][S][64] (bf16 path; S scratch slots in all) and
-// (write_zt) ZT = Z^T in planes of 8 tokens [S/8][f][8].
+// Z = SiLU(x W_gate^T) * (x W_up^T) -> Z column-blocked [f/64][S][64] (bf16 path; S scratch slots in all).
 // Wug: 2f rows of d, interleaved in blocks of 32 (32 up rows, then the matching 32 gate rows), held K-blocked
 // by 64 columns: [d/64][2f][64].
-hipError_t launch_a1_bf16(const bf16_t *x, const bf16_t *Wug, bf16_t *Z, bf16_t *ZT, int write_zt,
-                          const Layout &lay, hipStream_t s);
-// For each sequence (of the batch, or document): D += sum_p ZT[:, p] VT[:, p]^T over its slots (VT carries eta; W[a][i]
-// layout; the state is D = W - W0), from state_in[state_in index] or zero, into state_out[state_out index];
+hipError_t launch_a1_bf16(const bf16_t *x, const bf16_t *Wug, bf16_t *Z, const Layout &lay, hipStream_t s);
+// For each sequence (of the batch, or document): D += sum_p Z[p]^T VT[:, p]^T over its slots (Z column-blocked
+// [f/64][S][64], as launch_a1_bf16 writes it; VT carries eta; W[a][i] layout; the state is D = W - W0), from
+// state_in[state_in index] or zero, into state_out[state_out index];
 // snapshot k of a sequence = bf16(W0 + D at its token k*L), with W0 from its bf16 planes W0p [f/8][d][8].
 // Snapshots are planes of 8 columns, [groups in all][f/8][d][8]. cus: compute units of the device (a last
 // partial round of at most cus/2 tiles runs as half tiles).
-hipError_t launch_update_bf16(const bf16_t *ZT, const bf16_t *VT, const float *state_in, float *state_out,
+hipError_t launch_update_bf16(const bf16_t *Z, const bf16_t *VT, const float *state_in, float *state_out,
                               bf16_t *snap, const bf16_t *W0p, const Layout &lay, int cus, hipStream_t s);
 // P[group][t][s] = <Z[gL+t], Z[gL+s]> if s/C < t/C else 0, for t, s < L (eta is in V^T).
 hipError_t launch_scores_bf16(const bf16_t *Z, bf16_t *P, const Layout &lay, hipStream_t s);

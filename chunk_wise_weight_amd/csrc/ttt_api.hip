@@ -5,10 +5,10 @@
 //   1. target gather      V^T = eta * E_tgt[ids shifted by one]^T (next-token target,
 //                         eta folded in), or the general target Conv1D(X0) W_target:
 //                         tap sums of the token embeddings, then one GEMM into V^T
-//   2. up/gate GEMM       Z = SiLU(x W_gate^T) * (x W_up^T), and Z^T
+//   2. up/gate GEMM       Z = SiLU(x W_gate^T) * (x W_up^T) (and, on the fp32 path, Z^T)
 //   2b. optional clipping per-chunk factors c_i = min(1, tau/||eta V_i^T Z_i||_F)
 //                         from chunk Grams; V^T's rows of chunk i scaled by c_i
-//   3. state update       D += Z^T-weighted rank-C updates (eta V^T) over the whole
+//   3. state update       D += rank-C updates eta V_i^T Z_i over the whole
 //                         block, the fp32 state resident in registers; a
 //                         snapshot of W_down0 + D at the start of every group of G chunks
 //   4. group scores       P = Z Z^T masked to earlier chunks of the group
@@ -350,8 +350,10 @@ int forward_impl(ttt_handle *h, const void *x, const int32_t *ids, const void *E
   // scaling pass.
   const bool gram_e =
       clip && !conv && h->dt == TTT_BF16 && (long long)vocab * h->d * 2 < (1LL << 31);
-  Scratch sc = empty ? Scratch{} : scratch_layout(h, lay, learn, learn && pl.intra, clip, clip && !gram_e, wspan,
-                                                  conv, dp ? dp->bytes() : 0);
+  // Z^T only on the fp32 path: the bf16 update reads Z's blocks transposed
+  Scratch sc = empty ? Scratch{}
+                     : scratch_layout(h, lay, learn && h->dt != TTT_BF16, learn && pl.intra, clip, clip && !gram_e,
+                                      wspan, conv, dp ? dp->bytes() : 0);
   if (ext_ws && sc.total > ext_cap)
     return fail(TTT_E_SHAPE, "the call needs " + std::to_string(sc.total) + " bytes of workspace, more than the " +
                                  std::to_string(ext_cap) + " available");
@@ -437,8 +439,7 @@ int forward_impl(ttt_handle *h, const void *x, const int32_t *ids, const void *E
                                     lay, s));
     }
     if (prof) HIP_TRY(hipEventRecord(ev[1], s));
-    HIP_TRY(launch_a1_bf16((const bf16_t *)x, (const bf16_t *)h->Wug, (bf16_t *)Z, (bf16_t *)ZT, learn ? 1 : 0, lay,
-                           s));
+    HIP_TRY(launch_a1_bf16((const bf16_t *)x, (const bf16_t *)h->Wug, (bf16_t *)Z, lay, s));
     if (prof) HIP_TRY(hipEventRecord(ev[2], s));
     if (clip) {
       HIP_TRY(launch_chunk_gram_bf16((const bf16_t *)Z, (const bf16_t *)Vrow, (const bf16_t *)E_tgt, ids, vocab, gv,
@@ -451,7 +452,7 @@ int forward_impl(ttt_handle *h, const void *x, const int32_t *ids, const void *E
     }
     if (prof) HIP_TRY(hipEventRecord(ev[3], s));
     if (learn) {
-      HIP_TRY(launch_update_bf16((const bf16_t *)ZT, (const bf16_t *)VT, state, state_out, (bf16_t *)snap,
+      HIP_TRY(launch_update_bf16((const bf16_t *)Z, (const bf16_t *)VT, state, state_out, (bf16_t *)snap,
                                  (const bf16_t *)h->W0p, lay, h->cus, s));
       if (state_out != state)
         HIP_TRY(hipMemcpyAsync(state, state_out, (size_t)B * df * 4, hipMemcpyDeviceToDevice, s));

@@ -122,7 +122,7 @@ int ttt_forward_chunked(ttt_handle *h, const void *x, const int32_t *ids, const 
  * allocate device memory during the call: code under HIP graph capture,
  * tight serving loops, harnesses that forbid hipMalloc. Same arguments,
  * layouts, semantics and results (bit for bit) as ttt_forward_chunked, but the
- * scratch of the call (target rows, Z and eta*Z^T, snapshots, group scores,
+ * scratch of the call (target rows, Z, snapshots, group scores,
  * clipping partials) lives in a fixed workspace of
  * TTT_NOALLOC_WORKSPACE_BYTES inside the library: a file-scope device array
  * that each GPU the library runs on holds until the process ends, its address
