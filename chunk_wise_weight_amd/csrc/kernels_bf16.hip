@@ -572,6 +572,19 @@ __device__ __forceinline__ int xcd_tile(int n, int N) {
   return xcd * q + (xcd < r ? xcd : r) + m;
 }
 
+// The same within each round of R workgroups (R: the workgroups resident at
+// once, one per CU, in launch order): round r's workgroups take logical tiles
+// r*R .. r*R + R - 1, XCD k a contiguous range of them. Where the logical order
+// keeps tiles that share operands together (the state update's tiles of one
+// sequence), the whole chip then works on one stretch of it at a time, and the
+// XCDs share the slabs of the stretch in the MALL; with xcd_tile alone, the 8
+// XCDs would walk 8 distant stretches (8 different documents of a packed call).
+__device__ __forceinline__ int xcd_tile_rounds(int n, int N, int R) {
+  const int r0 = n / R * R;
+  const int Rn = N - r0 < R ? N - r0 : R;
+  return r0 + xcd_tile(n - r0, Rn);
+}
+
 // Logical tile t of an nx x ny grid, in bands of H rows along y; inside a band
 // y runs fastest, so H consecutive tiles share one x and nx*H consecutive tiles
 // cover the band. The last band may be shorter.
@@ -875,6 +888,7 @@ struct UpdArgs {
   long long S;            // scratch slots in all (Z's block stride is S*64)
   int L, d, f;
   int tile0;  // first 256 x 256 tile of this launch
+  int round;  // workgroups resident at once (the compute units), a multiple of 8
   Seqs sq;
 };
 
@@ -960,7 +974,7 @@ __global__ __launch_bounds__(128 * WN, 1) void k_update(UpdArgs p) {
   Slab<WN, NBJ> *ring = lds.ring;
   constexpr int BN = 32 * WN * NBJ;  // columns of a per workgroup
   const int nx = p.f / BM, ny = p.d / 256;
-  const int n = xcd_tile(blockIdx.x, gridDim.x);
+  const int n = xcd_tile_rounds(blockIdx.x, gridDim.x, p.round);
   const int t = p.tile0 + n / (256 / BN);
   const int b = t / (nx * ny);  // sequence
   const SeqInfo si = p.sq.at(b);
@@ -1546,7 +1560,8 @@ hipError_t launch_update_bf16(const bf16_t *Z, const bf16_t *VT, const float *st
   if (cus < 2) cus = 2;
   const long long rem = tiles % cus;
   const long long whole = rem <= cus / 2 ? tiles - rem : tiles;
-  UpdArgs p{Z, VT, state_in, state_out, snap, W0p, lay.n_slots(), lay.L, lay.d, lay.f, 0, lay.seqs()};
+  UpdArgs p{Z, VT, state_in, state_out, snap, W0p, lay.n_slots(), lay.L, lay.d, lay.f, 0,
+            cus >= kXcds ? cus / kXcds * kXcds : kXcds, lay.seqs()};
   if (whole > 0) hipLaunchKernelGGL((k_update<WN_W, NBJ_W, NSL_W>), dim3((unsigned)whole), dim3(NT_W), 0, s, p);
   if (tiles > whole) {
     p.tile0 = (int)whole;
