@@ -20,6 +20,36 @@ __device__ __forceinline__ float to_f32<float>(float v) { return v; }
 template <>
 __device__ __forceinline__ float to_f32<bf16_t>(bf16_t v) { return bf16_to_f32(v); }
 
+// 8 consecutive elements of a row, loaded at once (16-byte aligned for bf16,
+// 32-byte aligned for fp32: a0 and d are multiples of 8); v(j) converts
+// element j as to_f32 does.
+template <typename Tv>
+struct Row;
+template <>
+struct Row<bf16_t> {
+  uint4 q;
+  __device__ __forceinline__ float v(int j) const {
+    const uint32_t w = (&q.x)[j >> 1];
+    return __uint_as_float((j & 1) ? (w & 0xffff0000u) : (w << 16));
+  }
+};
+template <>
+struct Row<float> {
+  float4 lo, hi;
+  __device__ __forceinline__ float v(int j) const { return j < 4 ? (&lo.x)[j] : (&hi.x)[j - 4]; }
+};
+__device__ __forceinline__ Row<bf16_t> load_row8(const bf16_t *p) {
+  Row<bf16_t> r;
+  r.q = *reinterpret_cast<const uint4 *>(p);
+  return r;
+}
+__device__ __forceinline__ Row<float> load_row8(const float *p) {
+  Row<float> r;
+  r.lo = *reinterpret_cast<const float4 *>(p);
+  r.hi = *reinterpret_cast<const float4 *>(p + 4);
+  return r;
+}
+
 __device__ __forceinline__ void store_out(float *p, float v) { *p = v; }
 __device__ __forceinline__ void store_out(bf16_t *p, float v) { *p = f32_to_bf16(v); }
 
@@ -83,22 +113,34 @@ __global__ __launch_bounds__(256) void k_conv_taps_run(const int32_t *ids, const
     for (int r = 0; r < R; ++r)
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[r][j] = 0.f;
+    // Window row i sits at position t0 + 1 + i; slot t0+r takes it as tap i-r.
+    // All ids are loaded first and then all rows, so the loads overlap
+    // instead of waiting one id and one row at a time; a row past T or with
+    // an id outside [0, vocab) is read from row 0 and left out of the sums.
+    constexpr int NW = R + KT - 1;
+    int tok[NW];
 #pragma unroll
-    for (int i = 0; i < R + KT - 1; ++i) {
-      const int p = t0 + 1 + i;  // position of window row i; slot t0+r takes it as tap i-r
-      if (p > T) break;
-      const int tok = ids[(long long)b * (T + 1) + p];
-      if (tok < 0 || tok >= vocab) continue;
-      const Tv *e = E + (long long)tok * d + a0;
-      float ev[8];
+    for (int i = 0; i < NW; ++i) {
+      const int p = t0 + 1 + i;
+      tok[i] = p <= T ? ids[(long long)b * (T + 1) + p] : -1;
+    }
+    bool ok[NW];
+    Row<Tv> ev[NW];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) ev[j] = to_f32(e[j]);
+    for (int i = 0; i < NW; ++i) {
+      ok[i] = tok[i] >= 0 && tok[i] < vocab;
+      ev[i] = load_row8(E + (long long)(ok[i] ? tok[i] : 0) * d + a0);
+    }
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      if (!ok[i]) continue;
+      const int p = t0 + 1 + i;
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const int k = i - r;
         if (k < 0 || k >= KT || p > limit[r]) continue;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[r][j] += w[k][j] * ev[j];
+        for (int j = 0; j < 8; ++j) acc[r][j] += w[k][j] * ev[i].v(j);
       }
     }
 #pragma unroll
