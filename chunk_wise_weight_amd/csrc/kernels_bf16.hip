@@ -1468,14 +1468,27 @@ __global__ __launch_bounds__(256) void k_gather_vt(const int32_t *ids, const bf1
   const SeqInfo si = sq.at(b);
   const int q0 = (int)(p0 - si.slot0);  // position of the block's first slot in its sequence
   const int tid = threadIdx.x, seg = tid & 7;
+  // both passes' ids, then both rows: the loads overlap instead of waiting in turn
+  int id[2];
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int pos = q0 + pass * 32 + (tid >> 3);
+    id[pass] = pos < si.len ? ids[si.id0 + pos + 1] : -1;
+  }
+  // unconditional loads (an id outside [0, vocab) reads row 0, then zero): a
+  // load behind a branch would wait for itself before the next one
+  uint4 row[2];
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const bool ok = id[pass] >= 0 && id[pass] < vocab;
+    const uint4 r = *reinterpret_cast<const uint4 *>(E + (long long)(ok ? id[pass] : 0) * d + a0 + seg * 8);
+    row[pass] = ok ? r : make_uint4(0u, 0u, 0u, 0u);
+  }
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
     const int pl = pass * 32 + (tid >> 3);
     const int pos = q0 + pl;
-    int id = -1;
-    if (pos < si.len) id = ids[si.id0 + pos + 1];
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (id >= 0 && id < vocab) v = *reinterpret_cast<const uint4 *>(E + (long long)id * d + a0 + seg * 8);
+    const uint4 v = row[pass];
     if (Vrow) *reinterpret_cast<uint4 *>(Vrow + (p0 + pl) * d + a0 + seg * 8) = v;  // unscaled
     // V^T carries eta (and the clipping factor): bf16 -> fp32, scaled, rounded to bf16
     const float c = eta * ((cfac && pos < si.len) ? cfac[(long long)b * nchunks + pos / C] : 1.f);
