@@ -742,17 +742,18 @@ __global__ __launch_bounds__(NT_W, 1) void k_a1(A1Args p) {
 // ---------------------------------------------------------------------------
 // General target rows V = U W_target (U: tap sums of the token embeddings),
 // written straight into the layouts the scan reads: V^T K-blocked
-// [B][T_pad/64][d][64] and, when clipping needs it, V row-major [B][T_pad][d].
-// i = token slot, j = model dim a; the B operand is W_target^T [d][d] (row a
-// holds column a of W_target). U rows past T are zero, so are those of V.
-// grid: nx * ny workgroups, nx = d/256, ny = B*T_pad/256
+// [S/64][d][64] and, when clipping needs it, V row-major [S][d] (S scratch
+// slots of all sequences). i = token slot, j = model dim a; the B operand is
+// W_target^T [d][d] (row a holds column a of W_target). U rows past each
+// sequence's length are zero, so are those of V.
+// grid: nx * ny workgroups, nx = d/256, ny = S/256
 struct TgtArgs {
   const bf16_t *U;
   const bf16_t *WtT;
   bf16_t *VT;    // eta * V
   bf16_t *Vrow;  // V
   float eta;
-  int T_pad, d, nx, ny;
+  int d, nx, ny;
 };
 
 __global__ __launch_bounds__(NT_W, 1) void k_target_gemm(TgtArgs p) {
@@ -760,9 +761,7 @@ __global__ __launch_bounds__(NT_W, 1) void k_target_gemm(TgtArgs p) {
   int tx, ty;  // model-dim tile, token tile
   band_tile(xcd_tile(blockIdx.x, gridDim.x), p.nx, p.ny, 8, tx, ty);
   const int n0 = tx * 256;
-  const int m0 = ty * BM;
-  const int b = m0 / p.T_pad;
-  const int pos0 = m0 - b * p.T_pad;
+  const long long m0 = (long long)ty * BM;  // first slot of the tile
   SlabLoads<RmW, RmW> ld;
   ld.a.init(p.U + (long long)m0 * p.d, p.d, BM, p.d, wave_id(), threadIdx.x & 63);
   ld.b.init(p.WtT + (long long)n0 * p.d, p.d, 256, p.d, wave_id(), threadIdx.x & 63);
@@ -771,7 +770,6 @@ __global__ __launch_bounds__(NT_W, 1) void k_target_gemm(TgtArgs p) {
   gemm_k<WN_W, NBJ_W, NSL_W, kARows>(acc, ring, ld, p.d / BK);
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w & 1, wn = w >> 1;
-  bf16_t *VTb = p.VT + (long long)b * p.d * p.T_pad;
 #pragma unroll
   for (int bj = 0; bj < NBJ_W; ++bj) {
     const int a = n0 + wn * WC_W + bj * 32 + (lane & 31);
@@ -779,16 +777,16 @@ __global__ __launch_bounds__(NT_W, 1) void k_target_gemm(TgtArgs p) {
     for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int pos = pos0 + wm * 128 + bi * 32 + 8 * q + 4 * (lane >> 5);
+        const long long pos = m0 + wm * 128 + bi * 32 + 8 * q + 4 * (lane >> 5);  // a slot
         float v[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) v[r] = acc.v[bi][bj][4 * q + r];
         uint2 pk;
         pk.x = pack_bf16x2(p.eta * v[0], p.eta * v[1]);
         pk.y = pack_bf16x2(p.eta * v[2], p.eta * v[3]);
-        *reinterpret_cast<uint2 *>(VTb + ((long long)(pos >> 6) * p.d + a) * 64 + (pos & 63)) = pk;
+        *reinterpret_cast<uint2 *>(p.VT + ((pos >> 6) * p.d + a) * 64 + (pos & 63)) = pk;
         if (p.Vrow) {
-          bf16_t *vr = p.Vrow + ((long long)b * p.T_pad + pos) * p.d + a;
+          bf16_t *vr = p.Vrow + pos * p.d + a;
 #pragma unroll
           for (int r = 0; r < 4; ++r) vr[(long long)r * p.d] = f32_to_bf16(v[r]);
         }
@@ -1332,14 +1330,15 @@ __global__ __launch_bounds__(NT_W, 1) void k_out(OutArgs p) {
 // from a row-major copy.
 // grid: B * (T_pad/256) * wspan workgroups of 512 threads
 struct GramArgs {
-  const bf16_t *Z;     // column-blocked [B][f/64][T_pad][64]
-  const bf16_t *V;     // [B][T_pad][d], rows past T zero (without GATHER)
+  const bf16_t *Z;     // column-blocked [f/64][S][64]
+  const bf16_t *V;     // [S][d], rows past each sequence's length zero (without GATHER)
   const bf16_t *E;     // [vocab][d] (GATHER)
-  const int32_t *ids;  // [B][T+1] (GATHER)
+  const int32_t *ids;  // the caller's ids, a sequence's at SeqInfo::id0 (GATHER)
   float *gv;           // scratch: 256 KB per workgroup of the grid
-  float *rowpart;      // [B][T_pad/256][wspan][256]
-  int T, T_pad, C, d, f, wspan, vocab;
-  long long S;         // B*T_pad: Z's block stride is S*64
+  float *rowpart;      // [S/256][wspan][256]
+  int C, d, f, wspan, vocab;
+  long long S;         // scratch slots in all: Z's block stride is S*64
+  Seqs sq;
 };
 
 constexpr int GR_P = 129;  // fp32 pitch of a [256][128] product tile in LDS (conflict-free row sums)
@@ -1349,18 +1348,18 @@ template <bool GATHER>
 __global__ __launch_bounds__(NT_W, 1) void k_chunk_gram(GramArgs p) {
   __shared__ __attribute__((aligned(16))) char smem[kSmemGram];
   Slab<WN_W, NBJ_W> *ring = reinterpret_cast<Slab<WN_W, NBJ_W> *>(smem);
-  const int nu = p.T_pad / 256;
   const int id = xcd_tile(blockIdx.x, gridDim.x);  // the t-tiles of an s-tile share an XCD
   const int wr = id % p.wspan;
-  const int u = (id / p.wspan) % nu;
-  const int b = id / (p.wspan * nu);
-  const int s0 = u * 256;
-  float *out = p.rowpart + (((long long)b * nu + u) * p.wspan + wr) * 256;
-  const int s_last = (s0 + 255 < p.T - 1) ? s0 + 255 : p.T - 1;
+  const int u = id / p.wspan;  // the s-tile: 256 slots of one sequence
+  const SeqInfo si = p.sq.at(p.sq.of_tile(u));
+  const int len = si.len, tp = (len + 255) & ~255;  // positions and slots of the sequence
+  const int s0 = (int)((long long)u * 256 - si.slot0);  // position of the s-tile in its sequence
+  float *out = p.rowpart + ((long long)u * p.wspan + wr) * 256;
+  const int s_last = (s0 + 255 < len - 1) ? s0 + 255 : len - 1;
   const int w = (int)((long long)(s0 / p.C) * p.C / 256) + wr;
   const long long w_end = (((long long)(s_last / p.C) + 1) * p.C - 1) / 256;
-  const int w_hi = (int)(w_end < p.T_pad / 256 - 1 ? w_end : p.T_pad / 256 - 1);
-  if (s0 >= p.T || w > w_hi) {  // no token pair of this tile shares a chunk
+  const int w_hi = (int)(w_end < tp / 256 - 1 ? w_end : tp / 256 - 1);
+  if (s0 >= len || w > w_hi) {  // no token pair of this tile shares a chunk
     if (threadIdx.x < 256) out[threadIdx.x] = 0.f;
     return;
   }
@@ -1370,15 +1369,15 @@ __global__ __launch_bounds__(NT_W, 1) void k_chunk_gram(GramArgs p) {
   acc_zero(acc);
   if constexpr (GATHER) {
     SlabLoads<RmGather<BM, 2 * WN_W>, RmGather<BM, 2 * WN_W>> ld;
-    const int32_t *tg = p.ids + (long long)b * (p.T + 1) + 1;  // target id of slot p at tg[p]
-    ld.a.init(p.E, p.d, p.vocab, tg + s0, p.T - s0, wv, lane);
-    ld.b.init(p.E, p.d, p.vocab, tg + t0, p.T - t0, wv, lane);
+    const int32_t *tg = p.ids + si.id0 + 1;  // target id of position q at tg[q]
+    ld.a.init(p.E, p.d, p.vocab, tg + s0, len - s0, wv, lane);
+    ld.b.init(p.E, p.d, p.vocab, tg + t0, len - t0, wv, lane);
     gemm_k<WN_W, NBJ_W, NSL_W, kARows>(acc, ring, ld, p.d / BK);
   } else {
-    const bf16_t *Vb = p.V + (long long)b * p.T_pad * p.d;
+    const bf16_t *Vb = p.V + (long long)si.slot0 * p.d;
     SlabLoads<RmW, RmW> ld;
-    ld.a.init(Vb + (long long)s0 * p.d, p.d, p.T_pad - s0, p.d, wv, lane);
-    ld.b.init(Vb + (long long)t0 * p.d, p.d, p.T_pad - t0, p.d, wv, lane);
+    ld.a.init(Vb + (long long)s0 * p.d, p.d, tp - s0, p.d, wv, lane);
+    ld.b.init(Vb + (long long)t0 * p.d, p.d, tp - t0, p.d, wv, lane);
     gemm_k<WN_W, NBJ_W, NSL_W, kARows>(acc, ring, ld, p.d / BK);
   }
   // G_V to this lane's scratch: register group k (4 registers) at [k][lane]
@@ -1394,10 +1393,10 @@ __global__ __launch_bounds__(NT_W, 1) void k_chunk_gram(GramArgs p) {
   __syncthreads();  // the second pass refills the ring
   acc_zero(acc);
   {
-    const bf16_t *Zb = p.Z + (long long)b * p.T_pad * 64;  // Z column-blocked [f/64][S][64]
+    const bf16_t *Zb = p.Z + (long long)si.slot0 * 64;  // Z column-blocked [f/64][S][64]
     SlabLoads<CbW, CbW> ld;
-    ld.a.init(Zb + (long long)s0 * 64, p.S * 64, p.T_pad - s0, wv, lane);
-    ld.b.init(Zb + (long long)t0 * 64, p.S * 64, p.T_pad - t0, wv, lane);
+    ld.a.init(Zb + (long long)s0 * 64, p.S * 64, tp - s0, wv, lane);
+    ld.b.init(Zb + (long long)t0 * 64, p.S * 64, tp - t0, wv, lane);
     gemm_k<WN_W, NBJ_W, NSL_W, kARows>(acc, ring, ld, p.f / BK);
   }
   // products of same-chunk pairs, in place of G_Z: row s0 + sl shares column
@@ -1532,11 +1531,10 @@ hipError_t launch_gather_vt_bf16(const int32_t *ids, const bf16_t *E, int vocab,
 
 hipError_t launch_chunk_gram_bf16(const bf16_t *Z, const bf16_t *Vrow, const bf16_t *E, const int32_t *ids, int vocab,
                                   float *gv, float *rowpart, int wspan, const Layout &lay, hipStream_t s) {
-  const long long n = (long long)lay.B * (lay.T_pad / 256) * wspan;
+  const long long n = lay.n_slots() / 256 * wspan;
   if (n >= (1LL << 31) / 8) return hipErrorInvalidConfiguration;
   if (!Vrow && (long long)vocab * lay.d * 2 >= (1LL << 31)) return hipErrorInvalidValue;
-  GramArgs p{Z, Vrow, E, ids, gv, rowpart, lay.T, lay.T_pad, lay.C, lay.d, lay.f, wspan, vocab,
-             (long long)lay.B * lay.T_pad};
+  GramArgs p{Z, Vrow, E, ids, gv, rowpart, lay.C, lay.d, lay.f, wspan, vocab, lay.n_slots(), lay.seqs()};
   if (Vrow)
     hipLaunchKernelGGL(k_chunk_gram<false>, dim3((unsigned)n), dim3(NT_W), 0, s, p);
   else
@@ -1556,9 +1554,9 @@ hipError_t launch_a1_bf16(const bf16_t *x, const bf16_t *Wug, bf16_t *Z, const L
 hipError_t launch_target_gemm_bf16(const bf16_t *U, const bf16_t *WtT, bf16_t *VT, bf16_t *Vrow, float eta,
                                   const Layout &lay, hipStream_t s) {
   const int nx = lay.d / 256;
-  const long long ny = (long long)lay.B * lay.T_pad / BM;
+  const long long ny = lay.n_slots() / BM;
   if (nx * ny >= (1LL << 31)) return hipErrorInvalidConfiguration;
-  TgtArgs p{U, WtT, VT, Vrow, eta, lay.T_pad, lay.d, nx, (int)ny};
+  TgtArgs p{U, WtT, VT, Vrow, eta, lay.d, nx, (int)ny};
   hipLaunchKernelGGL(k_target_gemm, dim3((unsigned)(nx * ny)), dim3(NT_W), 0, s, p);
   return hipGetLastError();
 }

@@ -14,18 +14,21 @@
 
 namespace {
 
-// rowpart[b][s/256][wr][s%256] summed over wr and the chunk's rows; one
-// workgroup per (chunk, sequence); c[b][i] = min(1, tau / (|eta| sqrt(sum))).
-__global__ __launch_bounds__(256) void k_chunk_factors(const float *rowpart, float *cfac, int T, int T_pad, int C,
-                                                       int wspan, int nchunks, float eta, float tau) {
+// rowpart[slot/256][wr][slot%256] summed over wr and the chunk's rows (slots
+// of sequence b: its own chunks, counted from its first position); one
+// workgroup per (chunk, sequence); c[b][i] = min(1, tau / (|eta| sqrt(sum))),
+// 1 for a chunk past the sequence's end.
+__global__ __launch_bounds__(256) void k_chunk_factors(const float *rowpart, float *cfac, Seqs sq, int C, int wspan,
+                                                       int nchunks, float eta, float tau) {
   __shared__ float red[256];
   const int i = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const SeqInfo si = sq.at(b);
   const long long c0 = (long long)i * C;
-  const long long c1 = (long long)(i + 1) * C < T ? (long long)(i + 1) * C : T;
-  const int nu = T_pad / 256;
+  const long long c1 = (long long)(i + 1) * C < si.len ? (long long)(i + 1) * C : si.len;
   float sum = 0.f;
   for (long long s = c0 + tid; s < c1; s += 256) {
-    const float *rp = rowpart + (((long long)b * nu + s / 256) * wspan) * 256 + s % 256;
+    const long long slot = si.slot0 + s;
+    const float *rp = rowpart + ((slot / 256) * wspan) * 256 + slot % 256;
     for (int wr = 0; wr < wspan; ++wr) sum += rp[wr * 256];
   }
   red[tid] = sum;
@@ -40,17 +43,17 @@ __global__ __launch_bounds__(256) void k_chunk_factors(const float *rowpart, flo
   }
 }
 
-// V^T K-blocked [B][T_pad/64][d][64] (bf16): slot p of sequence b scaled by
-// c[b][p / C]; slots past T are zero and stay so. 8 elements per thread.
-__global__ __launch_bounds__(256) void k_scale_vt_bf16(bf16_t *VT, const float *cfac, int T, int T_pad, int C, int d,
+// V^T K-blocked [S/64][d][64] (bf16): the slot at position p of sequence b
+// scaled by c[b][p / C]; slots past the sequence's length are zero and stay
+// so. 8 elements (8 slots of one model dim, one 64-slot block) per thread.
+__global__ __launch_bounds__(256) void k_scale_vt_bf16(bf16_t *VT, const float *cfac, Seqs sq, int C, int d,
                                                        int nchunks, long long n8) {
   for (long long g = (long long)blockIdx.x * 256 + threadIdx.x; g < n8; g += (long long)gridDim.x * 256) {
     const long long e = g * 8;
-    const long long per_b = (long long)T_pad * d;
-    const int b = (int)(e / per_b);
-    const long long rem = e - (long long)b * per_b;
-    const int blk = (int)(rem / ((long long)d * 64));
-    const int p0 = blk * 64 + (int)(rem % 64);
+    const long long slot = e / ((long long)d * 64) * 64 + e % 64;  // the first of the 8
+    const int b = sq.of_tile((int)(slot / 256));
+    const SeqInfo si = sq.at(b);
+    const int p0 = (int)(slot - si.slot0), T = si.len;
     if (p0 >= T) continue;
     uint4 raw = *reinterpret_cast<const uint4 *>(VT + e);
     bf16_t *v = reinterpret_cast<bf16_t *>(&raw);
@@ -131,22 +134,24 @@ int clip_wspan(const Layout &lay, bool bf16) {
 }
 
 size_t clip_gram_scratch_bytes(const Layout &lay, int wspan) {
-  return (size_t)lay.B * (lay.T_pad / 256) * wspan * (256 * 256 * 4);
+  return (size_t)(lay.n_slots() / 256) * wspan * (256 * 256 * 4);
 }
 
+// chunks per sequence in the factor table c[sequence][chunk]: those of the
+// caller's T (no sequence is longer)
 int clip_chunks(const Layout &lay) { return (int)((lay.T + (long long)lay.C - 1) / lay.C); }
 
 hipError_t launch_chunk_factors(const float *rowpart, float *cfac, int wspan, float eta, float tau, const Layout &lay,
                                 hipStream_t s) {
   const int nchunks = clip_chunks(lay);
-  hipLaunchKernelGGL(k_chunk_factors, dim3(nchunks, lay.B), dim3(256), 0, s, rowpart, cfac, lay.T, lay.T_pad, lay.C,
+  hipLaunchKernelGGL(k_chunk_factors, dim3(nchunks, lay.n_seq()), dim3(256), 0, s, rowpart, cfac, lay.seqs(), lay.C,
                      wspan, nchunks, eta, tau);
   return hipGetLastError();
 }
 
 hipError_t launch_scale_vt_bf16(bf16_t *VT, const float *cfac, const Layout &lay, hipStream_t s) {
-  const long long n8 = (long long)lay.B * lay.T_pad * lay.d / 8;
-  hipLaunchKernelGGL(k_scale_vt_bf16, dim3(grid_for(n8)), dim3(256), 0, s, VT, cfac, lay.T, lay.T_pad, lay.C, lay.d,
+  const long long n8 = lay.n_slots() * lay.d / 8;
+  hipLaunchKernelGGL(k_scale_vt_bf16, dim3(grid_for(n8)), dim3(256), 0, s, VT, cfac, lay.seqs(), lay.C, lay.d,
                      clip_chunks(lay), n8);
   return hipGetLastError();
 }

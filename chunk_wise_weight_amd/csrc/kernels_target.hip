@@ -53,16 +53,17 @@ __device__ __forceinline__ Row<float> load_row8(const float *p) {
 __device__ __forceinline__ void store_out(float *p, float v) { *p = v; }
 __device__ __forceinline__ void store_out(bf16_t *p, float v) { *p = f32_to_bf16(v); }
 
-// U[b][t][a] = sum_k cw[k][a] * E[ids[b][t+1+k]][a] (fp32 sums), rows t >= T zero.
-// One thread per (b, t, group of 8 model dims).
+// U[slot][a] = sum_k cw[k][a] * E[ids of position t+1+k][a] (fp32 sums) for
+// position t of the slot's sequence (its ids at SeqInfo::id0), rows past the
+// sequence's length zero. One thread per (slot, group of 8 model dims).
 template <typename Tv>
 __global__ __launch_bounds__(256) void k_conv_taps(const int32_t *ids, const Tv *E, int vocab, const float *cw, int K,
-                                                   Tv *U, int T, int T_pad, int C, int d, long long ngroups8) {
+                                                   Tv *U, Seqs sq, int C, int d, long long ngroups8) {
   for (long long g = (long long)blockIdx.x * 256 + threadIdx.x; g < ngroups8; g += (long long)gridDim.x * 256) {
     const int a0 = (int)(g % (d / 8)) * 8;
-    const long long bt = g / (d / 8);
-    const int t = (int)(bt % T_pad);
-    const int b = (int)(bt / T_pad);
+    const long long slot = g / (d / 8);
+    const SeqInfo si = sq.at(sq.of_tile((int)(slot / 256)));
+    const int t = (int)(slot - si.slot0), T = si.len;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (t < T) {
       const long long chunk_end = ((long long)(t / C) + 1) * C;
@@ -70,7 +71,7 @@ __global__ __launch_bounds__(256) void k_conv_taps(const int32_t *ids, const Tv 
       for (int k = 0; k < K; ++k) {
         const int p = t + 1 + k;
         if (p > limit) break;
-        const int tok = ids[(long long)b * (T + 1) + p];
+        const int tok = ids[si.id0 + p];
         if (tok < 0 || tok >= vocab) continue;
         const Tv *e = E + (long long)tok * d + a0;
         const float *w = cw + (long long)k * d + a0;
@@ -78,7 +79,7 @@ __global__ __launch_bounds__(256) void k_conv_taps(const int32_t *ids, const Tv 
         for (int j = 0; j < 8; ++j) acc[j] += w[j] * to_f32(e[j]);
       }
     }
-    Tv *u = U + ((long long)b * T_pad + t) * d + a0;
+    Tv *u = U + slot * d + a0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) store_out(u + j, acc[j]);
   }
@@ -90,13 +91,13 @@ __global__ __launch_bounds__(256) void k_conv_taps(const int32_t *ids, const Tv 
 // order per slot as k_conv_taps, so the same results.
 template <typename Tv, int KT>
 __global__ __launch_bounds__(256) void k_conv_taps_run(const int32_t *ids, const Tv *E, int vocab, const float *cw,
-                                                       Tv *U, int T, int T_pad, int C, int d, long long nthreads) {
+                                                       Tv *U, Seqs sq, int C, int d, long long nthreads) {
   constexpr int R = 8;
   for (long long g = (long long)blockIdx.x * 256 + threadIdx.x; g < nthreads; g += (long long)gridDim.x * 256) {
     const int a0 = (int)(g % (d / 8)) * 8;
-    const long long br = g / (d / 8);
-    const int t0 = (int)(br % (T_pad / R)) * R;
-    const int b = (int)(br / (T_pad / R));
+    const long long slot0 = g / (d / 8) * R;  // a run never straddles two sequences (their slots are 256-aligned)
+    const SeqInfo si = sq.at(sq.of_tile((int)(slot0 / 256)));
+    const int t0 = (int)(slot0 - si.slot0), T = si.len;
     float w[KT][8];
 #pragma unroll
     for (int k = 0; k < KT; ++k)
@@ -122,7 +123,7 @@ __global__ __launch_bounds__(256) void k_conv_taps_run(const int32_t *ids, const
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
       const int p = t0 + 1 + i;
-      tok[i] = p <= T ? ids[(long long)b * (T + 1) + p] : -1;
+      tok[i] = p <= T ? ids[si.id0 + p] : -1;
     }
     bool ok[NW];
     Row<Tv> ev[NW];
@@ -145,7 +146,7 @@ __global__ __launch_bounds__(256) void k_conv_taps_run(const int32_t *ids, const
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      Tv *u = U + ((long long)b * T_pad + t0 + r) * d + a0;
+      Tv *u = U + (slot0 + r) * d + a0;
 #pragma unroll
       for (int j = 0; j < 8; ++j) store_out(u + j, acc[r][j]);
     }
@@ -189,9 +190,9 @@ unsigned grid_for(long long n) {
 template <typename Tv, int KT>
 hipError_t launch_conv_run(const int32_t *ids, const Tv *E, int vocab, const float *cw, Tv *U, const Layout &lay,
                            hipStream_t s) {
-  const long long n = (long long)lay.B * (lay.T_pad / 8) * (lay.d / 8);
-  hipLaunchKernelGGL((k_conv_taps_run<Tv, KT>), dim3(grid_for(n)), dim3(256), 0, s, ids, E, vocab, cw, U, lay.T,
-                     lay.T_pad, lay.C, lay.d, n);
+  const long long n = lay.n_slots() / 8 * (lay.d / 8);
+  hipLaunchKernelGGL((k_conv_taps_run<Tv, KT>), dim3(grid_for(n)), dim3(256), 0, s, ids, E, vocab, cw, U, lay.seqs(),
+                     lay.C, lay.d, n);
   return hipGetLastError();
 }
 
@@ -210,9 +211,9 @@ hipError_t launch_conv_taps(const int32_t *ids, const Tv *E, int vocab, const fl
     case 8: return launch_conv_run<Tv, 8>(ids, E, vocab, cw, U, lay, s);
     default: break;
   }
-  const long long n = (long long)lay.B * lay.T_pad * (lay.d / 8);
-  hipLaunchKernelGGL((k_conv_taps<Tv>), dim3(grid_for(n)), dim3(256), 0, s, ids, E, vocab, cw, K, U, lay.T,
-                     lay.T_pad, lay.C, lay.d, n);
+  const long long n = lay.n_slots() * (lay.d / 8);
+  hipLaunchKernelGGL((k_conv_taps<Tv>), dim3(grid_for(n)), dim3(256), 0, s, ids, E, vocab, cw, K, U, lay.seqs(), lay.C,
+                     lay.d, n);
   return hipGetLastError();
 }
 

@@ -240,7 +240,7 @@ Scratch scratch_layout(const ttt_handle *h, const Layout &lay, bool need_zt, boo
   const size_t pp = need_p ? align256(es * G * lay.L * lay.L) : 0;
   const size_t vr = need_vrow ? align256(es * S * h->d) : 0;
   const size_t rp = clip ? align256(4 * S * wspan) : 0;
-  const size_t cf = clip ? align256(4 * (size_t)lay.B * ((lay.T_pad + lay.C - 1) / lay.C)) : 0;
+  const size_t cf = clip ? align256(4 * (size_t)lay.n_seq() * ((lay.T_pad + lay.C - 1) / lay.C)) : 0;
   const size_t uu = conv ? align256(es * S * h->d) : 0;
   const size_t gvb = clip && h->dt == TTT_BF16 ? align256(clip_gram_scratch_bytes(lay, wspan)) : 0;
   const size_t tb = align256(tab_bytes);
@@ -309,8 +309,9 @@ int ring_make_room(ttt_handle *h) {
 // One forward over B sequences of T tokens whose states are state[0 .. B).
 // ext_ws: a caller-provided workspace of ext_cap bytes used instead of the
 // handle's scratch (NULL: the handle's, grown with hipMalloc when needed).
-// dp: packed documents run as sequences of their own (bf16 path, eta != 0, no
-// clipping, plain target), with the plan dpl shared by every document.
+// dp: packed documents run as sequences of their own (bf16 path, eta != 0;
+// also with clipping and the general target), with the plan dpl shared by
+// every document.
 int forward_impl(ttt_handle *h, const void *x, const int32_t *ids, const void *E_tgt, int vocab, int B, int T,
                  void *y, float *state, float *W_final, hipStream_t s_in, void *ext_ws = nullptr,
                  size_t ext_cap = 0, const DocPlan *dp = nullptr, const Plan *dpl = nullptr) {
@@ -764,7 +765,7 @@ int ttt_forward_docs(ttt_handle *h, const void *x, const int32_t *ids, const voi
   const size_t es = h->dt == TTT_BF16 ? 2 : 4;
   const size_t ys = h->dt == TTT_BF16 && !h->y_f32 ? 2 : 4;  // bytes per element of y
   const size_t df = (size_t)h->d * h->f;
-  if (h->dt == TTT_BF16 && h->eta != 0.f && h->clip_tau == 0.f && h->conv_K == 0) {
+  if (h->dt == TTT_BF16 && h->eta != 0.f) {
     // One launch sequence: every document is a sequence of its own in the scan kernels, with its own
     // scratch slots (padded to 256) and snapshot groups; the first document of sequence b continues
     // its state, every later one starts from W_down0, and the last one's final state is kept. Chunks
@@ -815,8 +816,7 @@ int ttt_forward_docs(ttt_handle *h, const void *x, const int32_t *ids, const voi
       return rc;
     }
   }
-  // Otherwise (fp32 handle, eta = 0, clipping or the general target): each
-  // document runs on its own slice: the state of sequence b returns to
+  // Otherwise (fp32 handle, or eta = 0): each document runs on its own slice: the state of sequence b returns to
   // W_down0 at every document start, and chunking restarts there. The ids
   // slice keeps the next document's first token as its look-ahead; that
   // target only enters the document's last chunk update, which the reset

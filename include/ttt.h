@@ -155,8 +155,13 @@ int ttt_forward_chunked_noalloc(ttt_handle *h, const void *x, const int32_t *ids
  * chunking restarts from that token. A document's last target row lies in its
  * last chunk, whose update the reset discards, so no target crosses a
  * document end. The final state is the last document's, kept in the handle as
- * usual. Documents run one after the other on the stream (B = 1 launches per
- * document); with profiling on, ttt_phase_times sums a call's documents.
+ * usual. On a bf16 handle with eta != 0 (also with clipping and the general
+ * target) the call is one launch sequence in which every document is a
+ * sequence of its own, with its own scratch slots and snapshot groups, and
+ * the state a sequence's last document leaves is copied back once at the end.
+ * On an fp32 handle, or with eta = 0, documents run one after the other on
+ * the stream (B = 1 launches per document). With profiling on,
+ * ttt_phase_times sums a call's launch sequences.
  * Other arguments, ownership and errors as ttt_forward_chunked.
  */
 int ttt_forward_docs(ttt_handle *h, const void *x, const int32_t *ids, const void *E_tgt, int vocab, int B, int T,

@@ -154,3 +154,39 @@ def test_docs_ragged_lengths_after_a_plain_call(y_f32):
     # the state left for the next call: sequence 2 continued its carried state; 0 and 1 end in a fresh document
     D = ttt.ttt_state_delta(lay.h, 3).double().cpu().numpy()
     assert rel_fro(D + W0, W_ref) <= BF16_TOL
+
+
+@pytest.mark.parametrize("C", [100, 256])
+def test_docs_many_with_clip_and_target_one_launch_sequence(C):
+    """Ragged documents (1 to 700 tokens) across three sequences, with clipping and the general target
+    (K = 5) on a bf16 handle: a packed call is one launch sequence here too, its chunk Grams, factors and
+    target rows taken per document. C = 100 makes a chunk span two 256-slot tiles."""
+    d, f, T = 256, 512, 1800
+    w = make_inputs(d=d, f=f, B=3, T=T, C=C, eta=1e-3, dtype="bf16", vocab=211, e_std=1.0, seed=160 + C)
+    cw, Wt = make_target_conv(d, 5, "bf16", seed=16)
+    lay = Layer(w)
+    ttt.ttt_set_target_conv(lay.h, dev(cw, lay.dt), dev(Wt, lay.dt))
+    starts = [[1, 2, 100, 356, 700, 1400], [256, 512, 768, 1024, 1280, 1536], [700]]
+    # a threshold that clips some chunk updates and not others: from the oracle's first documents
+    _, W_probe = oracle.ttt_forward_docs(w.x[:, :700], w.ids[:, :701], w.E_tgt, w.W_up, w.W_gate, w.W_down0,
+                                         w.W_down0, C, w.eta, [[1, 2, 100, 356], [256, 512], []], conv_w=cw,
+                                         W_target=Wt)
+    tau = 0.05 * float(np.median([np.linalg.norm(W_probe[b] - w.W_down0) for b in range(3)]))
+    ttt.ttt_set_clip(lay.h, tau)
+    print(f"[docs clip+target] C={C} tau={tau:.3e} starts={starts}", flush=True)
+    y, Wf = ttt.ttt_forward_docs(lay.h, lay.x, lay.ids, lay.E, starts, want_W_final=True)
+    torch.cuda.synchronize()
+    y_ref, W_ref = _ref(w, C, starts, clip_tau=tau, conv_w=cw, W_target=Wt)
+    y, Wf = y.double().cpu().numpy(), Wf.double().cpu().numpy()
+    W0 = w.W_down0.astype(np.float64)
+    e = (rel_fro(y, y_ref), rel_fro(Wf, W_ref), rel_fro(Wf - W0, W_ref - W0))
+    print(f"  y err {e[0]:.2e}, W_final err {e[1]:.2e}, W_final - W0 err {e[2]:.2e}", flush=True)
+    assert max(e) <= BF16_TOL, e
+    # one document alone from a reset state gives the same bits (document 3 of sequence 1: positions 768 .. 1023)
+    ttt.ttt_reset(lay.h)
+    ys, _ = ttt.ttt_forward_chunked(lay.h, lay.x[1:2, 768:1024].contiguous(), lay.ids[1:2, 768:1025].contiguous(),
+                                    lay.E)
+    torch.cuda.synchronize()
+    y_dev, _ = ttt.ttt_forward_docs(lay.h, lay.x, lay.ids, lay.E, starts)
+    torch.cuda.synchronize()
+    assert torch.equal(ys[0], y_dev[1, 768:1024])
