@@ -367,14 +367,17 @@ def main():
         return {"K": 5, "tokens_per_s": tokens / (ms4 * 1e-3), "ms_per_step": ms4,
                 "phase_ms": dict(zip(names, r4["phase_ms"]))}
 
-    def docs_leg(ndocs):
+    def docs_leg(ndocs, clip_tau=0.0):
         # packed documents: ndocs documents of T/ndocs tokens per sequence, the state reset at each start
         starts = [[w.T // ndocs * k for k in range(1, ndocs)] for _ in range(w.B)]
-        r5 = run_gpu(w, a.chunk, a.steps, a.warmup, a.group_chunks, doc_starts=starts)
+        r5 = run_gpu(w, a.chunk, a.steps, a.warmup, a.group_chunks, doc_starts=starts, clip_tau=clip_tau)
         ms5 = r5["event_ms"] / a.steps
-        return {"documents_per_sequence": ndocs, "tokens_per_doc": w.T // ndocs,
-                "tokens_per_s": tokens / (ms5 * 1e-3), "ms_per_step": ms5,
-                "phase_ms": dict(zip(names, r5["phase_ms"]))}
+        res = {"documents_per_sequence": ndocs, "tokens_per_doc": w.T // ndocs,
+               "tokens_per_s": tokens / (ms5 * 1e-3), "ms_per_step": ms5,
+               "phase_ms": dict(zip(names, r5["phase_ms"]))}
+        if clip_tau:
+            res["clip_tau"] = clip_tau
+        return res
 
     def shard_legs():
         # One GPU's share of the layer split over 8 GPUs (the split itself is not built): a d_ff slice of
@@ -405,6 +408,7 @@ def main():
         leg("target_conv_leg", target_conv_leg)
         leg("docs_leg", lambda: docs_leg(4))
         leg("docs_leg_short", lambda: docs_leg(64))
+        leg("docs_leg_short_clip", lambda: docs_leg(64, clip_tau=1e-5))
         leg("shard_legs", shard_legs)
     print(json.dumps(out), flush=True)
 
