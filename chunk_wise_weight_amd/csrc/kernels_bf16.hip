@@ -116,17 +116,25 @@ constexpr int loads_per_slab() { return loads_a<WN, NBJ>() + 32 * WN * NBJ / (2 
 // ring's lookahead would be lost once per slab. Untracked, the loads are
 // ordered by the kernel's own counted waits and barriers alone (slab_wait),
 // which is how the ring is built anyway. No register outputs: the data goes
-// to LDS at M0 + 16 (4) bytes per lane.
+// to LDS at M0 + 16 (4) bytes per lane. M0 is the compiler's register: the
+// block saves it in a scalar register of its own and puts it back.
 __device__ __forceinline__ void dma16_untracked(__amdgpu_buffer_rsrc_t rs, void *lds, uint32_t voff, uint32_t soff) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)lds);
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(m0), "v"(voff), "s"(rs),
-               "s"(soff)
-               : "memory", "m0");
+  const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)lds);
+  uint32_t keep;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, %4 offen lds\n\ts_mov_b32 m0, %0"
+      : "=&s"(keep)
+      : "s"(base), "v"(voff), "s"(rs), "s"(soff)
+      : "memory");
 }
 __device__ __forceinline__ void dma4_untracked(__amdgpu_buffer_rsrc_t rs, void *lds, uint32_t voff, uint32_t soff) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)lds);
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds" ::"s"(m0), "v"(voff), "s"(rs), "s"(soff)
-               : "memory", "m0");
+  const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)lds);
+  uint32_t keep;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dword %2, %3, %4 offen lds\n\ts_mov_b32 m0, %0"
+      : "=&s"(keep)
+      : "s"(base), "v"(voff), "s"(rs), "s"(soff)
+      : "memory");
 }
 
 // Row-major operand: element (r, k) at base[r*ld + k], base at the tile's
@@ -527,7 +535,7 @@ __device__ __forceinline__ void stage_body(Acc<NBJ> &acc, Slab<WN, NBJ> &sc, Sla
   if (refill) issue_point<LPS, 6>(ld, pre, dst, rs, w, lane);
   // one prefetch per odd stage, always issued, so every slab wait counts one
   if constexpr (SL::kPf) {
-    if (h == 1) ld.prefetch((sl + NSL + 2) < (nsl - 1) ? (sl + NSL + 2) : (nsl - 1), w, lane);
+    if (h == 1) ld.prefetch((sl + NSL + 2) < (nsl - 1) ? (sl + NSL + 2) : (nsl - 1), w);
   }
   pin();
   if (AFTER) {
@@ -653,7 +661,7 @@ __device__ __forceinline__ void ring_prologue(const SL &ld, Buf &&buf, int nsl, 
       for (int j = 0; j < SL::N; ++j) ld.issue(pre, buf(sl), sl, w, lane, j);
     }
   }
-  if constexpr (SL::kPf) ld.prefetch((NSL + 1) < (nsl - 1) ? (NSL + 1) : (nsl - 1), w, lane);
+  if constexpr (SL::kPf) ld.prefetch((NSL + 1) < (nsl - 1) ? (NSL + 1) : (nsl - 1), w);
   slab_wait<loads_per_slab<WN, NBJ>(), NSL - 1, SL::kPf ? 1 : 0>((nsl - 1) < (NSL - 1) ? (nsl - 1) : (NSL - 1));
 }
 
@@ -859,7 +867,7 @@ struct UpdLoads : SlabLoads<ZbLoad<2 * WN>, KbLoad<BN, 2 * WN>> {
       vp = (uint32_t)(row * 128);
     }
   }
-  __device__ __forceinline__ void prefetch(int sl, int w, int lane) const {
+  __device__ __forceinline__ void prefetch(int sl, int w) const {
     const __amdgpu_buffer_rsrc_t rs =
         w < WN ? __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t *>(pa + (long long)sl * 64 * 64), (short)0,
                                                    0x7fffffff, kBufferFlags)
@@ -1055,7 +1063,7 @@ __global__ __launch_bounds__(128 * WN, 1) void k_update(UpdArgs p) {
   // A group spans L/BK stages, an even number (L is a multiple of 64), so
   // every group ends on an odd stage.
   int kt = 0, cb = 0;  // cb: the ring buffer of slab kt/2
-  for (; g < ngroups; ) {
+  while (g < ngroups) {  // the snapshot advances g
     const int kt_last = g * (p.L / BK) - 1;  // last stage before group g starts
     stage_run<WN, NBJ, NSL, kAZ>(acc, ring, cur, nxt, kt, cb, kt_last, nk, wm, wn, lane, w, ld);
     const int nb = cb + 1 == NSL ? 0 : cb + 1;
