@@ -2,8 +2,10 @@
 //
 // Every contraction is written as D[i][j] = sum_k A[i][k] * B[j][k] with both
 // operands K-contiguous ("NT" form). A block has 2 x WN waves; each wave
-// computes 128 x (32*NBJ) with v_mfma_f32_32x32x16_bf16 and fp32 accumulators
-// in AGPRs. Every GEMM uses 8 waves (WN = 4, NBJ = 2: 256 x 256 tiles, two
+// computes 128 x (32*NBJ) with v_mfma_f32_16x16x32_bf16 and fp32 accumulators.
+// Under the chip's power limit the 16x16x32 form runs at a higher clock than
+// the 32x32x16 one (measured with MFMAs alone on every CU: 2.0 against
+// 1.73 GHz), at the same work per cycle. Every GEMM uses 8 waves (WN = 4, NBJ = 2: 256 x 256 tiles, two
 // waves per SIMD so one can issue MFMAs while the other waits), except the
 // last, partial round of the state update, which runs 256 x 128 halves on 4
 // waves (WN = 2, NBJ = 2).
@@ -28,17 +30,19 @@
 // stream length or by f. The state update, whose contraction runs over the
 // tokens, takes Z's blocks as they are and reads its fragments with
 // transposing LDS reads. The snapshots are planes: the MFMA register layout
-// holds four consecutive k of one row per lane, so a store instruction of 32
-// rows x 16 bytes is 512 contiguous bytes in a plane (in row-major or
-// K-blocked form it would touch 32 lines); a plane slab loads as 1 KB
+// holds four consecutive i of one j per lane, so a store instruction of 16
+// columns x 16 bytes is 256 contiguous bytes in a plane (in row-major or
+// K-blocked form it would touch 16 lines); a plane slab loads as 1 KB
 // contiguous pieces into an LDS tile of [8][256][8], whose fragment reads
 // need no swizzle.
 //
-// MFMA 32x32x16 register layout (lane l, accumulator register r):
-//   A operand: row i = l % 32, k = 8*(l/32) .. +7;  B operand: column j = l % 32, same k.
-//   D: j = l % 32, i = 8*(r/4) + 4*(l/32) + r%4.
-// So each lane holds, per group of 4 registers, four consecutive i for one j:
-// epilogues store 4 consecutive elements along i.
+// MFMA 16x16x32 register layout (lane l, accumulator register r):
+//   A operand: row i = l % 16, k = 8*(l/16) .. +7;  B operand: column j = l % 16, same k.
+//   D: j = l % 16, i = 4*(l/16) + r.
+// So each lane holds, per accumulator (a group of 4 registers), four
+// consecutive i for one j: epilogues store 4 consecutive elements along i.
+// A wave's accumulator (gi, gj), gi < 8, gj < 2*NBJ, covers rows
+// 16 gi .. +15 and columns 16 gj .. +15 of its 128 x (32*NBJ) sub-tile.
 #include <type_traits>
 
 #include "launch.h"
@@ -53,7 +57,7 @@ constexpr uint32_t kOutOfRange = 0x80000000u;   // offset past num_records: the 
 
 template <int NBJ>
 struct Acc {
-  f32x16 v[4][NBJ];
+  f32x4 v[8][2 * NBJ];
 };
 
 // One LDS slab: the A tile (256 rows) and the B tile (32*WN*NBJ rows), 64 columns each.
@@ -73,22 +77,23 @@ __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int lds_off(int r, int c) { return r * SK + ((c ^ swz(r)) << 3); }
 
 // Chunk swizzle of the kAZ tile (below): k row r holds logical chunk c at
-// c ^ zsw(r). A transposing read of one 16-lane group covers 4 consecutive k
-// rows (r%4 = 0..3) and 2 adjacent chunks in each; across the wave's 4 groups
-// that is 4 chunks of rows r0 .. r0+3 and of rows r0+8 .. r0+11. zsw(r) =
-// 2*(r%4) gives the four rows four disjoint chunk pairs and rows r0, r0+2
-// disjoint halves of the row, so the read is free of bank conflicts with 32
-// or with 64 banks.
-__device__ __forceinline__ int zsw(int r) { return (r & 3) << 1; }
+// c ^ zsw(r). A transposing read of one 16-lane group g covers 4 consecutive
+// k rows r0 + 8g .. +3 and one pair of adjacent chunks in each; the LDS
+// serves 32 lanes (two groups, 8 rows apart) at a time. zsw(r) =
+// 2*((r%4) ^ (r/8 % 2)) gives the 4 rows of one parity (rows of a 128-byte
+// stride alternate between the two halves of the 64 banks) of the two groups
+// the four disjoint chunk pairs of that half, so the read is free of bank
+// conflicts.
+__device__ __forceinline__ int zsw(int r) { return ((r & 3) ^ ((r >> 3) & 1)) << 1; }
 
 template <int NBJ>
 __device__ __forceinline__ void acc_zero(Acc<NBJ> &acc) {
 #pragma unroll
-  for (int bi = 0; bi < 4; ++bi)
+  for (int gi = 0; gi < 8; ++gi)
 #pragma unroll
-    for (int bj = 0; bj < NBJ; ++bj)
+    for (int gj = 0; gj < 2 * NBJ; ++gj)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc.v[bi][bj][r] = 0.f;
+      for (int r = 0; r < 4; ++r) acc.v[gi][gj][r] = 0.f;
 }
 
 // buffer loads per wave per slab: A tile, then B tile
@@ -304,10 +309,10 @@ struct PlLoad {
 // slab of block b is 64 slots x 128 bytes, contiguous in memory, and lands as
 // LDS rows k of [4][64][64] with chunk swizzle zsw. Wave w of NW loads 8N of
 // the 64 rows of block w/(NW/4), 8 rows (1 KB) per load; lane l fills row
-// 8n + l/8 of its share, physical chunk l%8 = logical chunk (l%8) ^ zsw(row),
-// and the rows' offsets mod 4 do not depend on n, so one lane offset serves
-// every load. Every slot of a slab exists in Z (slabs stay within the
-// sequence's padded slots).
+// 8n + l/8 of its share, physical chunk l%8 = logical chunk (l%8) ^ zsw(row).
+// The swizzle depends on n only through its parity (the share starts at a
+// multiple of 8), so two lane offsets serve every load. Every slot of a slab
+// exists in Z (slabs stay within the sequence's padded slots).
 template <int NW>
 struct ZbLoad {
   static constexpr int N = 32 / NW;  // loads per wave per slab
@@ -315,13 +320,14 @@ struct ZbLoad {
   const bf16_t *base;                // this wave's block at the tile's first slot
   int r0;                            // this wave's first row in its block
   int blk;                           // this wave's block
-  uint32_t vl;
+  uint32_t ve, vd;                   // lane offsets for even / odd n
   __device__ __forceinline__ void init(const bf16_t *Z, long long S, int i0, long long slot0, int w, int lane) {
     blk = w / WB;
     r0 = (w % WB) * 8 * N;
     base = Z + ((long long)(i0 / 64 + blk) * S + slot0) * 64;
     const int r = r0 + (lane >> 3);
-    vl = (uint32_t)(r * 128 + (((lane & 7) ^ zsw(r)) << 4));
+    ve = (uint32_t)(r * 128 + (((lane & 7) ^ zsw(r)) << 4));
+    vd = (uint32_t)(r * 128 + (((lane & 7) ^ zsw(r + 8)) << 4));
   }
   using Pre = __amdgpu_buffer_rsrc_t;
   __device__ __forceinline__ Pre prep(int sl) const {
@@ -329,7 +335,7 @@ struct ZbLoad {
                                              0x7fffffff, kBufferFlags);
   }
   __device__ __forceinline__ void issue(const Pre &rs, bf16_t *tile, int, int, int, int n) const {
-    dma16_untracked(rs, tile + (blk * 64 + r0 + 8 * n) * 64, vl, n * 1024);
+    dma16_untracked(rs, tile + (blk * 64 + r0 + 8 * n) * 64, (n & 1) ? vd : ve, n * 1024);
   }
 };
 
@@ -377,11 +383,14 @@ __device__ __forceinline__ void slab_wait(int later) {
   asm volatile("s_barrier" ::: "memory");
 }
 
-// MFMA fragments of one 16-deep k-substep: 4 A fragments (rows) and NBJ B
-// fragments (columns) of this wave's sub-tile.
+// MFMA fragments of a 32-deep stage: the A fragments of the wave's rows
+// 0-63 (lo) and 64-127 (hi), 16 rows each, and two sets of B fragments (16
+// columns each), set s used by the stages of parity s, so that the next
+// stage's set can load while this stage's last MFMAs still read theirs.
 template <int NBJ>
 struct Frag {
-  bf16x8 a[4], b[NBJ];
+  bf16x8 lo[4], hi[4];
+  bf16x8 b[2][2 * NBJ];
 };
 
 // How the A tile of a slab is held in LDS:
@@ -396,54 +405,59 @@ constexpr int kARows = 0, kAPlanes = 1, kAZ = 2;
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
-// A fragment of a kAZ tile: rows i0 + l%32 (lane l), k 8c .. 8c+7 with c =
-// 4h + 2ks + l/32, from two transposing reads (ds_read_b64_tr_b16) of k rows
-// 8c + 4j .. +3 (j = 0, 1). In each 16-lane group, lane t addresses k row
-// t/4, columns 4(t%4) .. +3 of the group's 16 (one 8-byte piece), and
-// receives column t of the 4 rows. Lane t of group g covers tile row
-// 16(g%2) + t of the 32; this is its element offset for an even 32-row block
-// (bi) of the tile, and `^ 32` (the other half of the 64-column row) gives it
-// for an odd one.
+// A fragment of a kAZ tile: rows 16gi + l%16 of a 64-row block (lane l), k
+// 8(l/16) .. +7 of the stage, from two transposing reads (ds_read_b64_tr_b16)
+// of 4 k rows each. In each 16-lane group g, lane t addresses k row
+// 8g + t/4 (+4 for the second read), columns 4(t%4) .. +3 of the fragment's
+// 16 (one 8-byte piece), and receives column t of the 4 rows. This is lane
+// l's element offset for gi = 0; the chunk pair of fragment gi is gi
+// further on, which in the swizzled row is `^ (gi << 4)` (zsw is even, so
+// the XOR leaves the 8-byte half within the chunk alone).
 __device__ __forceinline__ int az_lane_off(int lane) {
   const int t = lane & 15, g = lane >> 4;
-  const int chunk = ((g & 1) * 2 + ((t & 3) >> 1)) ^ zsw(t >> 2);
-  return (lane >> 5) * 512 + (t >> 2) * 64 + chunk * 8 + 4 * (t & 1);
+  const int krow = 8 * g + (t >> 2);
+  const int chunk = ((t & 3) >> 1) ^ zsw(krow);
+  return krow * 64 + chunk * 8 + 4 * (t & 1);
 }
 
-// Read substep ks (0 or 1) of half h (0 or 1) of an LDS slab into registers.
+// The A fragments of rows 64hf .. 64hf+63 of the wave's 128 (hf = 0, 1) for
+// stage half h (0 or 1) of an LDS slab.
 template <int WN, int NBJ, int AMODE = kARows>
-__device__ __forceinline__ void frag_read(Frag<NBJ> &fr, const Slab<WN, NBJ> &st, int h, int ks, int wm, int wn,
-                                          int lane) {
-  const int c = 4 * h + 2 * ks + (lane >> 5);
+__device__ __forceinline__ void read_a(bf16x8 (&a)[4], const Slab<WN, NBJ> &st, int h, int hf, int wm, int lane) {
+  const int c = 4 * h + (lane >> 4);
   if constexpr (AMODE == kAZ) {
-    const int lo = az_lane_off(lane), kb = (4 * h + 2 * ks) * 512;
+    const int lo = az_lane_off(lane);
 #pragma unroll
-    for (int bi = 0; bi < 4; ++bi) {
-      const bf16_t *pa = st.a + (wm * 2 + (bi >> 1)) * 4096 + kb + ((bi & 1) ? (lo ^ 32) : lo);
+    for (int gi = 0; gi < 4; ++gi) {
+      const bf16_t *pa = st.a + (wm * 2 + hf) * 4096 + h * 2048 + (lo ^ (gi << 4));
       const bf16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(pa));
       const bf16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(pa + 256));
-      fr.a[bi] = __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7);
+      a[gi] = __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7);
     }
   } else {
 #pragma unroll
-    for (int bi = 0; bi < 4; ++bi)
-      fr.a[bi] = *reinterpret_cast<const bf16x8 *>(
-          st.a + (AMODE == kAPlanes ? (c * BM + wm * 128 + bi * 32 + (lane & 31)) * 8
-                                    : lds_off(wm * 128 + bi * 32 + (lane & 31), c)));
+    for (int gi = 0; gi < 4; ++gi) {
+      const int r = wm * 128 + hf * 64 + gi * 16 + (lane & 15);
+      a[gi] = *reinterpret_cast<const bf16x8 *>(st.a + (AMODE == kAPlanes ? (c * BM + r) * 8 : lds_off(r, c)));
+    }
   }
-#pragma unroll
-  for (int bj = 0; bj < NBJ; ++bj)
-    fr.b[bj] = *reinterpret_cast<const bf16x8 *>(st.b + lds_off(wn * 32 * NBJ + bj * 32 + (lane & 31), c));
 }
 
-// MFMAs of one k-substep for fragment rows bi in [BLO, BHI).
-template <int BLO, int BHI, int NBJ>
-__device__ __forceinline__ void frag_mma(Acc<NBJ> &acc, const Frag<NBJ> &fr) {
+// The B fragments of the wave's 32*NBJ columns for stage half h of a slab.
+template <int WN, int NBJ>
+__device__ __forceinline__ void read_b(bf16x8 (&b)[2 * NBJ], const Slab<WN, NBJ> &st, int h, int wn, int lane) {
+  const int c = 4 * h + (lane >> 4);
 #pragma unroll
-  for (int bi = BLO; bi < BHI; ++bi)
+  for (int gj = 0; gj < 2 * NBJ; ++gj)
+    b[gj] = *reinterpret_cast<const bf16x8 *>(st.b + lds_off(wn * 32 * NBJ + gj * 16 + (lane & 15), c));
+}
+
+// The MFMAs of row fragment GI (0..7) of a stage.
+template <int GI, int NBJ>
+__device__ __forceinline__ void frag_mma(Acc<NBJ> &acc, const bf16x8 &a, const bf16x8 (&b)[2 * NBJ]) {
 #pragma unroll
-    for (int bj = 0; bj < NBJ; ++bj)
-      acc.v[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.a[bi], fr.b[bj], acc.v[bi][bj], 0, 0, 0);
+  for (int gj = 0; gj < 2 * NBJ; ++gj)
+    acc.v[GI][gj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[gj], acc.v[GI][gj], 0, 0, 0);
 }
 
 // Keep the compiler from moving instructions across this point.
@@ -458,14 +472,15 @@ __device__ __forceinline__ void issue_point(const SL &ld, const typename SL::Pre
 }
 
 // The software pipeline of one 32-deep stage kt = half kt%2 of slab kt/2. On
-// entry `cur` holds (or is loading) substep 0 of stage kt; on exit it holds
-// substep 0 of stage kt+1. Every LDS read and tile-load issue sits behind
-// MFMAs already queued, so the matrix cores keep running while they wait:
-//   read substep 1 of kt -> nxt | MFMAs of row 0 on cur
+// entry fr.lo and fr.b[kt%2] hold (or are loading) stage kt's fragments of
+// rows 0-63 and of the columns; on exit fr.lo and fr.b[(kt+1)%2] hold those
+// of stage kt+1. Every LDS read and tile-load issue sits behind MFMAs already
+// queued, so the matrix cores keep running while they wait:
+//   read rows 64-127 of kt -> fr.hi | MFMAs of row fragment 0
 //   at the end of a slab: wait for the next slab + barrier
-//   MFMAs of rows 1-3 on cur and rows 0-3 on nxt, with this wave's loads of
-//   slab kt/2 + NSL (into the buffer just finished) issued between them, and
-//   substep 0 of kt+1 read into cur after nxt's first row.
+//   MFMAs of row fragments 1-7, with this wave's loads of slab kt/2 + NSL
+//   (into the buffer just finished) issued between them, and rows 0-63 and
+//   the columns of kt+1 read after fragment 4 (fr.lo is no longer read).
 // After the barrier no wave reads the finished slab's buffer again (all its
 // reads were issued before, and the wait includes lgkmcnt(0)), so it can be
 // refilled. Spreading the loads keeps a burst of them from stalling the MFMA
@@ -474,30 +489,35 @@ __device__ __forceinline__ void issue_point(const SL &ld, const typename SL::Pre
 // Loads with a prefetch (SL::kPf) also touch, in every odd stage, this
 // workgroup's share of slab kt/2 + NSL + 2, so that the slab's own loads two
 // stages later find it in L2.
-// H (= kt % 2) and REFILL (this stage refills the buffer it finished: 1/0)
-// are fixed at compile time where the caller knows them, else -1 (decided
-// here at run time).
+// H (= kt % 2) is fixed at compile time (it picks the B fragment set), and so
+// is REFILL (this stage refills the buffer it finished: 1/0) where the caller
+// knows it, else -1 (decided here at run time).
 // sc is the ring buffer of slab kt/2, sn that of the slab after it.
 template <int WN, int NBJ, int NSL, bool AFTER, int AMODE, int H, int REFILL, class SL, class AfterFn>
-__device__ __forceinline__ void stage_body(Acc<NBJ> &acc, Slab<WN, NBJ> &sc, Slab<WN, NBJ> &sn, Frag<NBJ> &cur,
-                                           Frag<NBJ> &nxt, int kt, int nk, int wm, int wn, int lane, int w,
-                                           const SL &ld, AfterFn &&after_fn) {
+__device__ __forceinline__ void stage_body(Acc<NBJ> &acc, Slab<WN, NBJ> &sc, Slab<WN, NBJ> &sn, Frag<NBJ> &fr, int kt,
+                                           int nk, int wm, int wn, int lane, int w, const SL &ld,
+                                           AfterFn &&after_fn) {
   constexpr int LPS = loads_per_slab<WN, NBJ>();
   static_assert(SL::N == LPS, "the slab loads match the tile configuration");
+  static_assert(H == 0 || H == 1, "the stage parity is known at compile time");
+  constexpr int h = H;
   const int sl = kt >> 1;
   const int nsl = (nk + 1) >> 1;
-  const int h = H >= 0 ? H : (kt & 1);
   const bool refill = REFILL >= 0 ? REFILL == 1 : (h == 1 && sl + NSL < nsl);
-  // substep 0 of stage kt+1: the next slab's buffer after an odd stage
+  const bf16x8(&b)[2 * NBJ] = fr.b[h];
+  // rows 0-63 and the columns of stage kt+1: the next slab's buffer after an odd stage
   auto read_next = [&]() {
-    if (h == 1)
-      frag_read<WN, NBJ, AMODE>(cur, sn, 0, 0, wm, wn, lane);
-    else
-      frag_read<WN, NBJ, AMODE>(cur, sc, 1, 0, wm, wn, lane);
+    if constexpr (h == 1) {
+      read_a<WN, NBJ, AMODE>(fr.lo, sn, 0, 0, wm, lane);
+      read_b<WN, NBJ>(fr.b[0], sn, 0, wn, lane);
+    } else {
+      read_a<WN, NBJ, AMODE>(fr.lo, sc, 1, 0, wm, lane);
+      read_b<WN, NBJ>(fr.b[1], sc, 1, wn, lane);
+    }
   };
-  frag_read<WN, NBJ, AMODE>(nxt, sc, h, 1, wm, wn, lane);
+  read_a<WN, NBJ, AMODE>(fr.hi, sc, h, 1, wm, lane);
   pin();
-  frag_mma<0, 1>(acc, cur);
+  frag_mma<0>(acc, fr.lo[0], b);
   pin();
   const bool more = kt + 1 < nk;  // always true when refilling
   if (h == 1 && (refill || more)) {
@@ -509,29 +529,29 @@ __device__ __forceinline__ void stage_body(Acc<NBJ> &acc, Slab<WN, NBJ> &sc, Sla
   typename SL::Pre pre{};
   if (refill) pre = ld.prep(rs);
   pin();
-  frag_mma<1, 2>(acc, cur);
+  frag_mma<1>(acc, fr.lo[1], b);
   if (refill) issue_point<LPS, 0>(ld, pre, dst, rs, w, lane);
   pin();
-  frag_mma<2, 3>(acc, cur);
+  frag_mma<2>(acc, fr.lo[2], b);
   if (refill) issue_point<LPS, 1>(ld, pre, dst, rs, w, lane);
   pin();
-  frag_mma<3, 4>(acc, cur);
+  frag_mma<3>(acc, fr.lo[3], b);
   if (refill) issue_point<LPS, 2>(ld, pre, dst, rs, w, lane);
   pin();
-  frag_mma<0, 1>(acc, nxt);
+  frag_mma<4>(acc, fr.hi[0], b);
   pin();
   // unconditional (past the end it reads a stale buffer of the ring): no
   // branch, so the compiler can count the reads and wait for each exactly
   if (!AFTER) read_next();
   if (refill) issue_point<LPS, 3>(ld, pre, dst, rs, w, lane);
   pin();
-  frag_mma<1, 2>(acc, nxt);
+  frag_mma<5>(acc, fr.hi[1], b);
   if (refill) issue_point<LPS, 4>(ld, pre, dst, rs, w, lane);
   pin();
-  frag_mma<2, 3>(acc, nxt);
+  frag_mma<6>(acc, fr.hi[2], b);
   if (refill) issue_point<LPS, 5>(ld, pre, dst, rs, w, lane);
   pin();
-  frag_mma<3, 4>(acc, nxt);
+  frag_mma<7>(acc, fr.hi[3], b);
   if (refill) issue_point<LPS, 6>(ld, pre, dst, rs, w, lane);
   // one prefetch per odd stage, always issued, so every slab wait counts one
   if constexpr (SL::kPf) {
@@ -626,22 +646,21 @@ __device__ __forceinline__ void stage_phases(int &kt, int kt_end, int nk, Pair &
 
 // The ring as one LDS array: buffer cb (runtime) holds slab kt/2.
 template <int WN, int NBJ, int NSL, int AMODE, class SL>
-__device__ __forceinline__ void stage_run(Acc<NBJ> &acc, Slab<WN, NBJ> *ring, Frag<NBJ> &cur, Frag<NBJ> &nxt,
-                                          int &kt, int &cb, int kt_end, int nk, int wm, int wn, int lane, int w,
-                                          const SL &ld) {
+__device__ __forceinline__ void stage_run(Acc<NBJ> &acc, Slab<WN, NBJ> *ring, Frag<NBJ> &fr, int &kt, int &cb,
+                                          int kt_end, int nk, int wm, int wn, int lane, int w, const SL &ld) {
   stage_phases<NSL>(
       kt, kt_end, nk,
       [&](int k, auto refill) {
         const int nb = cb + 1 == NSL ? 0 : cb + 1;
-        stage_body<WN, NBJ, NSL, false, AMODE, 0, 0>(acc, ring[cb], ring[nb], cur, nxt, k, nk, wm, wn, lane, w, ld,
+        stage_body<WN, NBJ, NSL, false, AMODE, 0, 0>(acc, ring[cb], ring[nb], fr, k, nk, wm, wn, lane, w, ld,
                                                      NoHook{});
         stage_body<WN, NBJ, NSL, false, AMODE, 1, decltype(refill)::value ? 1 : 0>(
-            acc, ring[cb], ring[nb], cur, nxt, k + 1, nk, wm, wn, lane, w, ld, NoHook{});
+            acc, ring[cb], ring[nb], fr, k + 1, nk, wm, wn, lane, w, ld, NoHook{});
         cb = nb;
       },
       [&](int k) {
         const int nb = cb + 1 == NSL ? 0 : cb + 1;
-        stage_body<WN, NBJ, NSL, false, AMODE, 0, 0>(acc, ring[cb], ring[nb], cur, nxt, k, nk, wm, wn, lane, w, ld,
+        stage_body<WN, NBJ, NSL, false, AMODE, 0, 0>(acc, ring[cb], ring[nb], fr, k, nk, wm, wn, lane, w, ld,
                                                      NoHook{});
       });
 }
@@ -672,10 +691,11 @@ __device__ __forceinline__ void gemm_k(Acc<NBJ> &acc, Slab<WN, NBJ> *ring, const
   if (nk <= 0) return;
   const int nsl = (nk + 1) >> 1;
   ring_prologue<WN, NBJ, NSL>(ld, [&](int sl) -> Slab<WN, NBJ> & { return ring[sl]; }, nsl, w, lane);
-  Frag<NBJ> cur, nxt;
-  frag_read<WN, NBJ, AMODE>(cur, ring[0], 0, 0, wm, wn, lane);
+  Frag<NBJ> fr;
+  read_a<WN, NBJ, AMODE>(fr.lo, ring[0], 0, 0, wm, lane);
+  read_b<WN, NBJ>(fr.b[0], ring[0], 0, wn, lane);
   int kt = 0, cb = 0;
-  stage_run<WN, NBJ, NSL, AMODE>(acc, ring, cur, nxt, kt, cb, nk, nk, wm, wn, lane, w, ld);
+  stage_run<WN, NBJ, NSL, AMODE>(acc, ring, fr, kt, cb, nk, nk, wm, wn, lane, w, ld);
 }
 
 // The wide GEMMs' loaders: 8 waves, 256 x 256 tiles.
@@ -683,9 +703,11 @@ using RmW = RmLoad<BM, 2 * WN_W>;
 using CbW = CbLoad<BM, 2 * WN_W>;
 
 // ---------------------------------------------------------------------------
-// Up/gate GEMM with SwiGLU epilogue. i = token slot, j = interleaved W_ug row.
-// Writes Z column-blocked [f/64][S][64] (S scratch slots in all); the state
-// update reads the same blocks transposed, so Z is written once.
+// Up/gate GEMM with SwiGLU epilogue. i = interleaved W_ug row, j = token slot
+// (the weight is the A operand, so each lane's four consecutive i are four
+// consecutive features of Z). Writes Z column-blocked [f/64][S][64] (S
+// scratch slots in all); the state update reads the same blocks transposed,
+// so Z is written once.
 // grid: nx * ny workgroups, nx = 2f/256, ny = S/256
 struct A1Args {
   const bf16_t *x;
@@ -705,44 +727,41 @@ __global__ __launch_bounds__(NT_W, 1) void k_a1(A1Args p) {
   const long long m0 = (long long)ty * BM;  // first slot of the tile
   const SeqInfo si = p.sq.at(p.sq.of_tile(ty));
   const int pos0 = (int)(m0 - si.slot0);
-  SlabLoads<RmW, CbW> ld;
-  ld.a.init(p.x + (si.xrow0 + pos0) * p.d, p.d, si.len - pos0, p.d, wave_id(), threadIdx.x & 63);
-  ld.b.init(p.Wug + (long long)n0 * 64, 2LL * p.f * 64, 2 * p.f - n0, wave_id(), threadIdx.x & 63);
+  SlabLoads<CbW, RmW> ld;
+  ld.a.init(p.Wug + (long long)n0 * 64, 2LL * p.f * 64, 2 * p.f - n0, wave_id(), threadIdx.x & 63);
+  ld.b.init(p.x + (si.xrow0 + pos0) * p.d, p.d, si.len - pos0, p.d, wave_id(), threadIdx.x & 63);
   Acc<NBJ_W> acc;
   acc_zero(acc);
   gemm_k<WN_W, NBJ_W, NSL_W, kARows>(acc, ring, ld, p.d / BK);
 
-  // Epilogue. The wave's two 32-column blocks are a matching (up, gate) pair
-  // of W_ug rows: features f0 + l%32 (f0 is a multiple of 32, so they lie in
-  // one 64-feature block of Z; f is a multiple of 256, so all are < f). Lane l
-  // holds slots s0 + bi*32 + 8q + 4(l/32) + r. The stores are buffer stores
-  // from one lane offset; every other offset is a compile-time constant or
-  // wave-uniform, so no per-store address arithmetic.
+  // Epilogue. The wave's 128 W_ug rows are two (up, gate) pairs of 32-row
+  // blocks: row fragments gi and gi + 2 (gi in 0, 1, 4, 5) hold matching up
+  // and gate rows, features f0 + 32(gi/4) + 16(gi%2) + 4(l/16) + r with
+  // f0 = n0/2 + 64 wm, a multiple of 64: all of the wave's features lie in
+  // one 64-feature block of Z (f is a multiple of 256, so all are < f). Lane
+  // l holds slots s0 + 16gj + l%16. Each lane stores its 4 features of a slot
+  // as one 8-byte buffer store from one lane offset; every other offset is a
+  // compile-time constant, so no per-store address arithmetic.
   const int lane = threadIdx.x & 63, w = wave_id(), wm = w & 1, wn = w >> 1;
-  const int f0 = n0 / 2 + wn * 32;
-  const long long s0 = m0 + wm * 128;
+  const int f0 = n0 / 2 + wm * 64;
+  const long long s0 = m0 + wn * 64;
   // Z [f/64][S][64]: (slot, feature) at ((feature/64)*S + slot)*64 + feature%64
   const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
-      p.Z + ((long long)(f0 / 64) * p.S + s0) * 64 + f0 % 64, (short)0, 0x7fffffff, kBufferFlags);
-  const uint32_t vz = (uint32_t)((256 * (lane >> 5) + (lane & 31)) * 2);
+      p.Z + ((long long)(f0 / 64) * p.S + s0) * 64, (short)0, 0x7fffffff, kBufferFlags);
+  const uint32_t vz = (uint32_t)(((lane & 15) * 64 + 4 * (lane >> 4)) * 2);
   constexpr int kNt = 2;  // cache policy of the stores: non-temporal
 #pragma unroll
-  for (int bi = 0; bi < 4; ++bi) {
-    const f32x16 &u = acc.v[bi][0];
-    const f32x16 &g = acc.v[bi][1];
+  for (int gp = 0; gp < 4; ++gp) {
+    const int gi = (gp >> 1) * 4 + (gp & 1);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int gj = 0; gj < 2 * NBJ_W; ++gj) {
+      const f32x4 &u = acc.v[gi][gj];
+      const f32x4 &g = acc.v[gi + 2][gj];
       float z[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) z[r] = silu_fast(g[4 * q + r]) * u[4 * q + r];
-      // slots r = 0, 1 in the halves of pk.x, r = 2, 3 in those of pk.y
+      for (int r = 0; r < 4; ++r) z[r] = silu_fast(g[r]) * u[r];
       const u32x2_t pk{pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3])};
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const uint32_t h2 = r < 2 ? pk.x : pk.y;
-        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)((r & 1) ? (h2 >> 16) : h2), rz, vz,
-                                              (bi * 32 + 8 * q + r) * 128, kNt);
-      }
+      __builtin_amdgcn_raw_buffer_store_b64(pk, rz, vz, (gj * 16 * 64 + (gi >> 2) * 32 + (gi & 1) * 16) * 2, kNt);
     }
   }
 }
@@ -779,16 +798,14 @@ __global__ __launch_bounds__(NT_W, 1) void k_target_gemm(TgtArgs p) {
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w & 1, wn = w >> 1;
 #pragma unroll
-  for (int bj = 0; bj < NBJ_W; ++bj) {
-    const int a = n0 + wn * WC_W + bj * 32 + (lane & 31);
+  for (int gj = 0; gj < 2 * NBJ_W; ++gj) {
+    const int a = n0 + wn * WC_W + gj * 16 + (lane & 15);
 #pragma unroll
-    for (int bi = 0; bi < 4; ++bi)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const long long pos = m0 + wm * 128 + bi * 32 + 8 * q + 4 * (lane >> 5);  // a slot
+    for (int gi = 0; gi < 8; ++gi) {
+        const long long pos = m0 + wm * 128 + gi * 16 + 4 * (lane >> 4);  // a slot
         float v[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = acc.v[bi][bj][4 * q + r];
+        for (int r = 0; r < 4; ++r) v[r] = acc.v[gi][gj][r];
         uint2 pk;
         pk.x = pack_bf16x2(p.eta * v[0], p.eta * v[1]);
         pk.y = pack_bf16x2(p.eta * v[2], p.eta * v[3]);
@@ -899,13 +916,14 @@ struct UpdArgs {
 };
 
 // Snapshots W[a][i] are held as planes of 8 columns ([f/8][d][8]: element
-// (a, i) at ((i/8)*d + a)*8 + i%8). Lane l holds, per group of 4 accumulator
-// registers, four consecutive i of one a; lanes l and l+32 hold the two halves
-// of one 16-byte chunk, and the 32 lanes of a half walk 32 consecutive a: each
-// store instruction writes 512 contiguous bytes. A lane offset locates this
-// lane's element for (bi, bj, q) = (0, 0, 0): a = j0 + wn*32*NBJ + l%32,
-// i = i0 + wm*128 + 4*(l/32); tiles are always full (d, f multiples of 256).
-// Group (bi, bj, q) lies (bi*4 + q) planes and bj*32 rows of a further on.
+// (a, i) at ((i/8)*d + a)*8 + i%8). Lane l holds, per accumulator, four
+// consecutive i of one a; lanes l and l+16 hold the two halves of one 16-byte
+// chunk, and the 16 lanes of a quarter walk 16 consecutive a: each store
+// instruction writes two runs of 256 contiguous bytes (lanes 32-63 in the
+// next plane). A lane offset locates this lane's element of accumulator
+// (gi, gj) = (0, 0): a = j0 + wn*32*NBJ + l%16, i = i0 + wm*128 + 4*(l/16);
+// tiles are always full (d, f multiples of 256). Accumulator (gi, gj) lies
+// 2gi planes and 16gj rows of a further on.
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
 
@@ -917,17 +935,17 @@ struct QRead {
   __amdgpu_buffer_rsrc_t rs;
   uint32_t vo;
   int d;
-  // byte offsets of group (bi, bj, q): (bi*4 + q) planes of 8 columns in the
-  // scalar offset, bj*256 elements in the lane offset (an immediate)
-  __device__ __forceinline__ int soff(int bi, int q) const { return (bi * 4 + q) * 16 * d; }
-  __device__ __forceinline__ uint2 load(int bi, int bj, int q) const {
-    const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rs, vo + bj * 512, soff(bi, q), 0);
+  // byte offsets of accumulator (gi, gj): 2gi planes of 8 columns in the
+  // scalar offset, 16gj rows (gj*128 elements) in the lane offset (an immediate)
+  __device__ __forceinline__ int soff(int gi) const { return gi * 32 * d; }
+  __device__ __forceinline__ uint2 load(int gi, int gj) const {
+    const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rs, vo + gj * 256, soff(gi), 0);
     return make_uint2(v.x, v.y);
   }
 };
 
-// W0 + D for every accumulator group (bi, bj, q) of the tile, with the
-// accumulators holding D and W0 read from the initial weight's bf16 planes.
+// W0 + D for every accumulator (gi, gj) of the tile, with the accumulators
+// holding D and W0 read from the initial weight's bf16 planes.
 // The loads go out in batches of KB, each batch one memory round trip; the
 // scheduling barriers around a batch stop the compiler from hoisting the next
 // batch's loads. The snapshot takes all of them in one batch: it runs between
@@ -943,14 +961,14 @@ __device__ __forceinline__ void for_state(const Acc<NBJ> &acc, const QRead &qr, 
 #pragma unroll
     for (int k = 0; k < KB; ++k) {
       const int e = k0 + k;
-      qv[k] = qr.load((e >> 2) & 3, e >> 4, e & 3);
+      qv[k] = qr.load(e & 7, e >> 3);
     }
 #pragma unroll
     for (int k = 0; k < KB; ++k) {
-      const int e = k0 + k, bi = (e >> 2) & 3, bj = e >> 4, q = e & 3;
-      const f32x16 &v = acc.v[bi][bj];
-      fn(bi, bj, q, bf16_lo(qv[k].x) + v[4 * q + 0], bf16_hi(qv[k].x) + v[4 * q + 1],
-         bf16_lo(qv[k].y) + v[4 * q + 2], bf16_hi(qv[k].y) + v[4 * q + 3]);
+      const int e = k0 + k, gi = e & 7, gj = e >> 3;
+      const f32x4 &v = acc.v[gi][gj];
+      fn(gi, gj, bf16_lo(qv[k].x) + v[0], bf16_hi(qv[k].x) + v[1], bf16_lo(qv[k].y) + v[2],
+         bf16_hi(qv[k].y) + v[3]);
     }
     pin();
   }
@@ -966,9 +984,9 @@ __device__ __forceinline__ void dump_snapshot(const Acc<NBJ> &acc, const QRead &
   constexpr int kNt = 2;
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t *>(snap), (short)0, 0x7fffffff, kBufferFlags);
-  for_state<16 * NBJ>(acc, qr, [&](int bi, int bj, int q, float s0, float s1, float s2, float s3) {
+  for_state<16 * NBJ>(acc, qr, [&](int gi, int gj, float s0, float s1, float s2, float s3) {
     const u32x2_t pk{pack_bf16x2(s0, s1), pack_bf16x2(s2, s3)};
-    __builtin_amdgcn_raw_buffer_store_b64(pk, rs, qr.vo + bj * 512, qr.soff(bi, q), kNt);
+    __builtin_amdgcn_raw_buffer_store_b64(pk, rs, qr.vo + gj * 256, qr.soff(gi), kNt);
   });
 }
 
@@ -993,9 +1011,9 @@ __global__ __launch_bounds__(128 * WN, 1) void k_update(UpdArgs p) {
   const long long df = (long long)p.d * p.f;
   // this lane's first element of the tile in the state ([d][f]) and in a snapshot ([f/8][d][8])
   const long long lane_off =
-      (long long)(j0 + wn * 32 * NBJ + (lane & 31)) * p.f + i0 + wm * 128 + 4 * (lane >> 5);
-  const long long lane_snap =
-      (long long)((i0 + wm * 128) / 8) * 8 * p.d + (j0 + wn * 32 * NBJ + (lane & 31)) * 8 + 4 * (lane >> 5);
+      (long long)(j0 + wn * 32 * NBJ + (lane & 15)) * p.f + i0 + wm * 128 + 4 * (lane >> 4);
+  const long long lane_snap = (long long)((i0 + wm * 128) / 8 + (lane >> 5)) * 8 * p.d +
+                              (j0 + wn * 32 * NBJ + (lane & 15)) * 8 + 4 * ((lane >> 4) & 1);
   const bf16_t *snap0 = p.snap + (long long)si.grp0 * df;
   const int ngroups = si.len > p.L ? (si.len + p.L - 1) / p.L : 1;
   // where this lane's part of the final state goes (null: nowhere)
@@ -1005,18 +1023,16 @@ __global__ __launch_bounds__(128 * WN, 1) void k_update(UpdArgs p) {
   if (si.state_in >= 0) {
     const float *st = p.state_in + si.state_in * df + lane_off;
 #pragma unroll
-    for (int bj = 0; bj < NBJ; ++bj) {
-      const float *row = st + (long long)bj * 32 * p.f;
+    for (int gj = 0; gj < 2 * NBJ; ++gj) {
+      const float *row = st + (long long)gj * 16 * p.f;
 #pragma unroll
-      for (int bi = 0; bi < 4; ++bi)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float4 v = *reinterpret_cast<const float4 *>(row + bi * 32 + 8 * q);
-          acc.v[bi][bj][4 * q + 0] = v.x;
-          acc.v[bi][bj][4 * q + 1] = v.y;
-          acc.v[bi][bj][4 * q + 2] = v.z;
-          acc.v[bi][bj][4 * q + 3] = v.w;
-        }
+      for (int gi = 0; gi < 8; ++gi) {
+        const float4 v = *reinterpret_cast<const float4 *>(row + gi * 16);
+        acc.v[gi][gj][0] = v.x;
+        acc.v[gi][gj][1] = v.y;
+        acc.v[gi][gj][2] = v.z;
+        acc.v[gi][gj][3] = v.w;
+      }
     }
   } else {
     acc_zero(acc);  // a document start: W = W0
@@ -1045,10 +1061,11 @@ __global__ __launch_bounds__(128 * WN, 1) void k_update(UpdArgs p) {
   dump_snapshot(acc, qr, snap0);
   int g = 1;
   const int nsl = (nk + 1) >> 1;
-  Frag<NBJ> cur, nxt;
+  Frag<NBJ> fr;
   if (nk > 0) {
     ring_prologue<WN, NBJ, NSL>(ld, [&](int sl) -> Slab<WN, NBJ> & { return ring[sl]; }, nsl, w, lane);
-    frag_read<WN, NBJ, kAZ>(cur, ring[0], 0, 0, wm, wn, lane);
+    read_a<WN, NBJ, kAZ>(fr.lo, ring[0], 0, 0, wm, lane);
+    read_b<WN, NBJ>(fr.b[0], ring[0], 0, wn, lane);
   }
   // The snapshot stores share the vector-memory counter with the tile loads.
   // The counted waits stay exact for the loads: loads complete in issue
@@ -1065,26 +1082,22 @@ __global__ __launch_bounds__(128 * WN, 1) void k_update(UpdArgs p) {
   int kt = 0, cb = 0;  // cb: the ring buffer of slab kt/2
   while (g < ngroups) {  // the snapshot advances g
     const int kt_last = g * (p.L / BK) - 1;  // last stage before group g starts
-    stage_run<WN, NBJ, NSL, kAZ>(acc, ring, cur, nxt, kt, cb, kt_last, nk, wm, wn, lane, w, ld);
+    stage_run<WN, NBJ, NSL, kAZ>(acc, ring, fr, kt, cb, kt_last, nk, wm, wn, lane, w, ld);
     const int nb = cb + 1 == NSL ? 0 : cb + 1;
-    stage_body<WN, NBJ, NSL, true, kAZ, 1, -1>(acc, ring[cb], ring[nb], cur, nxt, kt, nk, wm, wn, lane, w, ld,
-                                               snapshot);
+    stage_body<WN, NBJ, NSL, true, kAZ, 1, -1>(acc, ring[cb], ring[nb], fr, kt, nk, wm, wn, lane, w, ld, snapshot);
     cb = nb;
     ++kt;
   }
-  stage_run<WN, NBJ, NSL, kAZ>(acc, ring, cur, nxt, kt, cb, nk, nk, wm, wn, lane, w, ld);
+  stage_run<WN, NBJ, NSL, kAZ>(acc, ring, fr, kt, cb, nk, nk, wm, wn, lane, w, ld);
   // the final state D in fp32
   if (!st_out) return;
 #pragma unroll
-  for (int bj = 0; bj < NBJ; ++bj) {
-    float *row = st_out + (long long)bj * 32 * p.f;
+  for (int gj = 0; gj < 2 * NBJ; ++gj) {
+    float *row = st_out + (long long)gj * 16 * p.f;
 #pragma unroll
-    for (int bi = 0; bi < 4; ++bi)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<float4 *>(row + bi * 32 + 8 * q) =
-            make_float4(acc.v[bi][bj][4 * q + 0], acc.v[bi][bj][4 * q + 1], acc.v[bi][bj][4 * q + 2],
-                        acc.v[bi][bj][4 * q + 3]);
+    for (int gi = 0; gi < 8; ++gi)
+      *reinterpret_cast<float4 *>(row + gi * 16) =
+          make_float4(acc.v[gi][gj][0], acc.v[gi][gj][1], acc.v[gi][gj][2], acc.v[gi][gj][3]);
   }
 }
 
@@ -1146,19 +1159,17 @@ __global__ __launch_bounds__(NT_W, 1) void k_scores(ScoreArgs p) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w & 1, wn = w >> 1;
   bf16_t *Pg = p.P + (long long)bg * p.L * p.L;
 #pragma unroll
-  for (int bj = 0; bj < NBJ_W; ++bj) {
-    const int t = j0 + wn * WC_W + bj * 32 + (lane & 31);
+  for (int gj = 0; gj < 2 * NBJ_W; ++gj) {
+    const int t = j0 + wn * WC_W + gj * 16 + (lane & 15);
     if (t >= p.L) continue;
     const int ct = t / p.C;
 #pragma unroll
-    for (int bi = 0; bi < 4; ++bi)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int sidx = i0 + wm * 128 + bi * 32 + 8 * q + 4 * (lane >> 5);
+    for (int gi = 0; gi < 8; ++gi) {
+        const int sidx = i0 + wm * 128 + gi * 16 + 4 * (lane >> 4);
         if (sidx >= p.L) continue;
         float v[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = ((sidx + r) / p.C < ct) ? acc.v[bi][bj][4 * q + r] : 0.f;
+        for (int r = 0; r < 4; ++r) v[r] = ((sidx + r) / p.C < ct) ? acc.v[gi][gj][r] : 0.f;
         uint2 pk;
         pk.x = pack_bf16x2(v[0], v[1]);
         pk.y = pack_bf16x2(v[2], v[3]);
@@ -1267,17 +1278,14 @@ __global__ __launch_bounds__(NT_W, 1) void k_out(OutArgs p) {
       __syncthreads();  // the ring, or the first half's rows, are no longer read
       if ((wn >> 1) == half) {
 #pragma unroll
-        for (int bj = 0; bj < NBJ_W; ++bj) {
-          const int tl = (wn & 1) * WC_W + bj * 32 + (lane & 31);
+        for (int gj = 0; gj < 2 * NBJ_W; ++gj) {
+          const int tl = (wn & 1) * WC_W + gj * 16 + (lane & 15);
 #pragma unroll
-          for (int bi = 0; bi < 4; ++bi)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const int al = wm * 128 + bi * 32 + 8 * q + 4 * (lane >> 5);
-              *reinterpret_cast<float4 *>(lf + tl * LY_F + al) =
-                  make_float4(acc.v[bi][bj][4 * q + 0], acc.v[bi][bj][4 * q + 1], acc.v[bi][bj][4 * q + 2],
-                              acc.v[bi][bj][4 * q + 3]);
-            }
+          for (int gi = 0; gi < 8; ++gi) {
+            const int al = wm * 128 + gi * 16 + 4 * (lane >> 4);
+            *reinterpret_cast<float4 *>(lf + tl * LY_F + al) =
+                make_float4(acc.v[gi][gj][0], acc.v[gi][gj][1], acc.v[gi][gj][2], acc.v[gi][gj][3]);
+          }
         }
       }
       __syncthreads();
@@ -1296,18 +1304,16 @@ __global__ __launch_bounds__(NT_W, 1) void k_out(OutArgs p) {
   bf16_t *ly = smem;
   __syncthreads();  // every wave is done with the ring
 #pragma unroll
-  for (int bj = 0; bj < NBJ_W; ++bj) {
-    const int tl = wn * WC_W + bj * 32 + (lane & 31);
+  for (int gj = 0; gj < 2 * NBJ_W; ++gj) {
+    const int tl = wn * WC_W + gj * 16 + (lane & 15);
 #pragma unroll
-    for (int bi = 0; bi < 4; ++bi)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int al = wm * 128 + bi * 32 + 8 * q + 4 * (lane >> 5);
-        uint2 pk;
-        pk.x = pack_bf16x2(acc.v[bi][bj][4 * q + 0], acc.v[bi][bj][4 * q + 1]);
-        pk.y = pack_bf16x2(acc.v[bi][bj][4 * q + 2], acc.v[bi][bj][4 * q + 3]);
-        *reinterpret_cast<uint2 *>(ly + tl * LY_P + al) = pk;
-      }
+    for (int gi = 0; gi < 8; ++gi) {
+      const int al = wm * 128 + gi * 16 + 4 * (lane >> 4);
+      uint2 pk;
+      pk.x = pack_bf16x2(acc.v[gi][gj][0], acc.v[gi][gj][1]);
+      pk.y = pack_bf16x2(acc.v[gi][gj][2], acc.v[gi][gj][3]);
+      *reinterpret_cast<uint2 *>(ly + tl * LY_P + al) = pk;
+    }
   }
   __syncthreads();
   // 256 token rows x 512 bytes; rows past the group's end are not written
@@ -1388,16 +1394,14 @@ __global__ __launch_bounds__(NT_W, 1) void k_chunk_gram(GramArgs p) {
     ld.b.init(Vb + (long long)t0 * p.d, p.d, tp - t0, p.d, wv, lane);
     gemm_k<WN_W, NBJ_W, NSL_W, kARows>(acc, ring, ld, p.d / BK);
   }
-  // G_V to this lane's scratch: register group k (4 registers) at [k][lane]
+  // G_V to this lane's scratch: accumulator k = gi*2*NBJ + gj (4 registers) at [k][lane]
   float4 *gv = reinterpret_cast<float4 *>(p.gv) + ((long long)id * 8 + wv) * (32 * 64) + lane;
 #pragma unroll
-  for (int bi = 0; bi < 4; ++bi)
+  for (int gi = 0; gi < 8; ++gi)
 #pragma unroll
-    for (int bj = 0; bj < NBJ_W; ++bj)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        gv[((bi * NBJ_W + bj) * 4 + q) * 64] = make_float4(acc.v[bi][bj][4 * q], acc.v[bi][bj][4 * q + 1],
-                                                           acc.v[bi][bj][4 * q + 2], acc.v[bi][bj][4 * q + 3]);
+    for (int gj = 0; gj < 2 * NBJ_W; ++gj)
+      gv[(gi * 2 * NBJ_W + gj) * 64] =
+          make_float4(acc.v[gi][gj][0], acc.v[gi][gj][1], acc.v[gi][gj][2], acc.v[gi][gj][3]);
   __syncthreads();  // the second pass refills the ring
   acc_zero(acc);
   {
@@ -1408,23 +1412,23 @@ __global__ __launch_bounds__(NT_W, 1) void k_chunk_gram(GramArgs p) {
     gemm_k<WN_W, NBJ_W, NSL_W, kARows>(acc, ring, ld, p.f / BK);
   }
   // products of same-chunk pairs, in place of G_Z: row s0 + sl shares column
-  // t's chunk when lo <= sl < lo + C (lo: the chunk's start less s0); one
-  // 16-register group at a time, so few reloaded values are live at once
+  // t's chunk when lo <= sl < lo + C (lo: the chunk's start less s0); four
+  // accumulators at a time, so few reloaded values are live at once
 #pragma unroll
-  for (int bj = 0; bj < NBJ_W; ++bj) {
-    const int lo = (t0 + wn * WC_W + bj * 32 + (lane & 31)) / p.C * p.C - s0;
+  for (int gj = 0; gj < 2 * NBJ_W; ++gj) {
+    const int lo = (t0 + wn * WC_W + gj * 16 + (lane & 15)) / p.C * p.C - s0;
 #pragma unroll
-    for (int bi = 0; bi < 4; ++bi) {
+    for (int g4 = 0; g4 < 8; g4 += 4) {
       pin();
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 g = gv[((bi * NBJ_W + bj) * 4 + q) * 64];
+      for (int gi = g4; gi < g4 + 4; ++gi) {
+        const float4 g = gv[(gi * 2 * NBJ_W + gj) * 64];
         const float gq[4] = {g.x, g.y, g.z, g.w};
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int sl = wm * 128 + bi * 32 + 8 * q + 4 * (lane >> 5) + r;
-          const float e = acc.v[bi][bj][4 * q + r];
-          acc.v[bi][bj][4 * q + r] = (sl >= lo && sl < lo + p.C) ? e * gq[r] : 0.f;
+          const int sl = wm * 128 + gi * 16 + 4 * (lane >> 4) + r;
+          const float e = acc.v[gi][gj][r];
+          acc.v[gi][gj][r] = (sl >= lo && sl < lo + p.C) ? e * gq[r] : 0.f;
         }
       }
     }
@@ -1438,13 +1442,12 @@ __global__ __launch_bounds__(NT_W, 1) void k_chunk_gram(GramArgs p) {
     __syncthreads();  // the ring, or the first half's tile, is no longer read
     if ((wn >> 1) == half) {
 #pragma unroll
-      for (int bj = 0; bj < NBJ_W; ++bj) {
-        const int tl = (wn & 1) * WC_W + bj * 32 + (lane & 31);
+      for (int gj = 0; gj < 2 * NBJ_W; ++gj) {
+        const int tl = (wn & 1) * WC_W + gj * 16 + (lane & 15);
 #pragma unroll
-        for (int bi = 0; bi < 4; ++bi)
+        for (int gi = 0; gi < 8; ++gi)
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            tile[(wm * 128 + bi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * GR_P + tl] = acc.v[bi][bj][r];
+          for (int r = 0; r < 4; ++r) tile[(wm * 128 + gi * 16 + 4 * (lane >> 4) + r) * GR_P + tl] = acc.v[gi][gj][r];
       }
     }
     __syncthreads();
