@@ -26,6 +26,7 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float x) { return __builtin_bit_ca
 // the same kernel reads, so that they do not push the operand tiles other
 // workgroups are still reading out of L2.
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void store_nt(void *p, uint32_t lo, uint32_t hi) {
   __builtin_nontemporal_store(u32x2_t{lo, hi}, reinterpret_cast<u32x2_t *>(p));
 }
