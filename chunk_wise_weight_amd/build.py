@@ -16,6 +16,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libttt.so")
+# a standalone program: MFMA throughput and shader clock under the power limit (not part of the library)
+PROBE_SRC = os.path.join(PKG, "probes", "mfma_clock.hip")
+PROBE = os.path.join(PKG, "probes", "mfma_clock")
 SOURCES = ["ttt_api.hip", "kernels_bf16.hip", "kernels_f32.hip", "kernels_clip.hip", "kernels_target.hip", "kernels_misc.hip"]
 
 HIPCC_FLAGS = [
@@ -63,6 +66,13 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    cmd = [hipcc, *[f for f in HIPCC_FLAGS if f != "-fPIC"], "-o", PROBE + ".tmp", PROBE_SRC]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {PROBE_SRC}:\n{r.stdout}\n{r.stderr}")
+    os.replace(PROBE + ".tmp", PROBE)
     return LIB
 
 
