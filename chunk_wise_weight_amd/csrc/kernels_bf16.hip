@@ -745,15 +745,16 @@ __global__ __launch_bounds__(NT_W, 1) void k_a1(A1Args p) {
   // its 4 features of a slot (8 bytes), then reads back 16 bytes of a slot
   // row, and every store instruction writes 1 KB contiguous. Partial-line
   // stores (8-byte pieces, 32 contiguous bytes per slot row) measured 5%
-  // slower on this kernel. Row pitch 72 elements (144 bytes): the 16 rows a
-  // write instruction touches at one column fall in distinct banks.
-  constexpr int kPitch = 72;
-  static_assert(2 * WN_W * 64 * kPitch * 2 <= (int)sizeof(ring), "the staging tiles fit the ring");
+  // slower on this kernel. The staging tile is [64 slots][64 features] with
+  // the GEMM tiles' chunk swizzle (lds_off): the 16 rows one write
+  // instruction touches at one column, and the 2 rows of 16 lanes of a read,
+  // fall in distinct banks.
+  static_assert(2 * WN_W * 64 * SK * 2 <= (int)sizeof(ring), "the staging tiles fit the ring");
   const int lane = threadIdx.x & 63, w = wave_id(), wm = w & 1, wn = w >> 1;
   const int f0 = n0 / 2 + wm * 64;
   const long long s0 = m0 + wn * 64;
   __syncthreads();  // every wave is done reading the ring
-  bf16_t *stg = reinterpret_cast<bf16_t *>(ring) + w * 64 * kPitch;
+  bf16_t *stg = reinterpret_cast<bf16_t *>(ring) + w * 64 * SK;
 #pragma unroll
   for (int gp = 0; gp < 4; ++gp) {
     const int gi = (gp >> 1) * 4 + (gp & 1);
@@ -764,8 +765,9 @@ __global__ __launch_bounds__(NT_W, 1) void k_a1(A1Args p) {
       float z[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) z[r] = silu_fast(g[r]) * u[r];
-      *reinterpret_cast<u32x2_t *>(stg + (16 * gj + (lane & 15)) * kPitch + (gi >> 2) * 32 + (gi & 1) * 16 +
-                                   4 * (lane >> 4)) = u32x2_t{pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3])};
+      // features (gi/4)*32 + (gi%2)*16 + 4(l/16) .. +3: 16-byte chunk (gi/4)*4 + (gi%2)*2 + l/32, half (l/16)%2
+      *reinterpret_cast<u32x2_t *>(stg + lds_off(16 * gj + (lane & 15), (gi >> 2) * 4 + (gi & 1) * 2 + (lane >> 5)) +
+                                   4 * ((lane >> 4) & 1)) = u32x2_t{pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3])};
     }
   }
   // Z [f/64][S][64]: (slot, feature) at ((feature/64)*S + slot)*64 + feature%64; the wave's run starts at slot s0
@@ -775,7 +777,7 @@ __global__ __launch_bounds__(NT_W, 1) void k_a1(A1Args p) {
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     // slot row 8k + l/8, bytes 16(l%8) .. +15 of it: byte 1024k + 16l of the run
-    const u32x4_t v = *reinterpret_cast<const u32x4_t *>(stg + (8 * k + (lane >> 3)) * kPitch + (lane & 7) * 8);
+    const u32x4_t v = *reinterpret_cast<const u32x4_t *>(stg + lds_off(8 * k + (lane >> 3), lane & 7));
     __builtin_amdgcn_raw_buffer_store_b128(v, rz, (uint32_t)(lane * 16), k * 1024, kNt);
   }
 }
