@@ -15,9 +15,9 @@
 // 128-byte line: whole lines fill LDS at twice the rate of half lines. A ring
 // of NSL slabs keeps the next slabs in flight while one is multiplied, and
 // each wave waits only for the oldest slab it needs. The MFMAs run in stages
-// of 32 (two per slab); within a stage the fragment reads of the next
-// k-substep and the next stage are issued behind MFMAs already queued (a
-// software pipeline). The eight 16-byte chunks of each 128-byte LDS row are
+// of 32 (two per slab), one MFMA per 16 x 16 output tile; within a stage the
+// fragment reads of its second half of rows and of the next stage are issued
+// behind MFMAs already queued (a software pipeline). The eight 16-byte chunks of each 128-byte LDS row are
 // XOR-swizzled so that the fragment reads are free of bank conflicts. Rows or
 // columns outside an operand's valid range are fetched through an
 // out-of-range buffer offset, which the hardware returns as zero.
