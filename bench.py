@@ -317,6 +317,9 @@ def main():
         "mfma_frac_scan_gemms": (flops["update_snapshots"] + flops["output"]) / (scan_ms * 1e-3) / 1e12
         / PEAK_BF16_TFLOPS,
         "phase_ms": phases,
+        # algorithmic flops over each GEMM phase's live event time (the update phase includes its snapshots)
+        "phase_tflops": {k: flops[k] / (phases[k] * 1e-3) / 1e12 for k in ("up_gate_swiglu", "update_snapshots", "output")
+                         if phases[k] > 0},
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                      "traffic": measured_traffic(KERNEL_OF_PHASE[dom], a.chunk)},
