@@ -6,11 +6,11 @@ checks of the parity tests can miss when few elements are hit. Each mode runs
 the same call three times from a reset state, at d = 2560, f = 9728 and 4096
 tokens: 4.75 rounds of up/gate tiles, a whole round and a half-tile round of
 the update, 160 output tiles, and, with the general target or clipping, the
-target GEMM and the chunk Grams.
+target GEMM and the chunk Grams; packed documents of ragged lengths run as
+one launch sequence over a sequence table.
 """
 from __future__ import annotations
 
-import numpy as np
 import pytest
 import torch
 
@@ -26,7 +26,7 @@ def w4b():
     return make_inputs(d=2560, f=9728, B=1, T=4096, C=256, eta=1e-3, dtype="bf16", vocab=512, e_std=1.0, seed=123)
 
 
-@pytest.mark.parametrize("mode", ["plain", "target", "clip"])
+@pytest.mark.parametrize("mode", ["plain", "target", "clip", "docs"])
 def test_repeat_bitwise_4b_width(w4b, mode):
     lay = Layer(w4b)
     if mode == "target":
@@ -37,7 +37,11 @@ def test_repeat_bitwise_4b_width(w4b, mode):
     runs = []
     for _ in range(3):
         ttt.ttt_reset(lay.h)
-        y, Wf = lay.forward()
+        if mode == "docs":  # ragged packed documents: one launch sequence with a sequence table
+            y, Wf = ttt.ttt_forward_docs(lay.h, lay.x, lay.ids, lay.E, [[700, 1900, 2100, 3333]], want_W_final=True)
+            torch.cuda.synchronize()
+        else:
+            y, Wf = lay.forward()
         runs.append((y.clone(), Wf.clone()))
     y0, W0 = runs[0]
     assert torch.isfinite(y0.float()).all() and torch.isfinite(W0).all()
