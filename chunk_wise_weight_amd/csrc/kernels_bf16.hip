@@ -604,9 +604,11 @@ __device__ __forceinline__ int xcd_tile(int n, int N) {
 // once, one per CU, in launch order): round r's workgroups take logical tiles
 // r*R .. r*R + R - 1, XCD k a contiguous range of them. Where the logical order
 // keeps tiles that share operands together (the state update's tiles of one
-// sequence), the whole chip then works on one stretch of it at a time, and the
-// XCDs share the slabs of the stretch in the MALL; with xcd_tile alone, the 8
-// XCDs would walk 8 distant stretches (8 different documents of a packed call).
+// sequence, the output's and the scores' tiles of one group), the whole chip
+// then works on one stretch of it at a time, and the XCDs share the slabs of
+// the stretch in the MALL; with xcd_tile alone, the 8 XCDs would walk 8
+// distant stretches (8 different documents of a packed call, 8 groups 16
+// apart in the output of a 128-group stream).
 __device__ __forceinline__ int xcd_tile_rounds(int n, int N, int R) {
   const int r0 = n / R * R;
   const int Rn = N - r0 < R ? N - r0 : R;
@@ -1129,6 +1131,7 @@ struct ScoreArgs {
   bf16_t *P;
   long long S;  // scratch slots in all (Z's block stride is S*64)
   int L, C, f, nt;
+  int round;  // workgroups resident at once (the compute units), a multiple of 8
   Seqs sq;
   // tiles (it, jt) of a full group that hold an unmasked entry; npairs = 0:
   // every tile of the lower triangle gets a workgroup (long groups)
@@ -1138,7 +1141,7 @@ struct ScoreArgs {
 
 __global__ __launch_bounds__(NT_W, 1) void k_scores(ScoreArgs p) {
   __shared__ __attribute__((aligned(16))) Slab<WN_W, NBJ_W> ring[NSL_W];
-  const int t = xcd_tile(blockIdx.x, gridDim.x);
+  const int t = xcd_tile_rounds(blockIdx.x, gridDim.x, p.round);
   int bg, it, jt;  // bg = b * ngroups + g
   if (p.npairs > 0) {
     bg = t / p.npairs;
@@ -1238,6 +1241,7 @@ struct OutArgs {
   long long S;  // scratch slots in all
   int L, C, d, f, intra;
   int y_f32;
+  int round;  // workgroups resident at once (the compute units), a multiple of 8
   Seqs sq;
 };
 
@@ -1247,9 +1251,10 @@ static_assert(128 * LY_F * 4 <= kSmemOut, "the fp32 y half tile fits the output 
 __global__ __launch_bounds__(NT_W, 1) void k_out(OutArgs p) {
   __shared__ __attribute__((aligned(16))) bf16_t smem[kSmemOut / 2];
   Slab<WN_W, NBJ_W> *ring = reinterpret_cast<Slab<WN_W, NBJ_W> *>(smem);
-  // one group's tiles are consecutive, token tiles fastest
+  // one group's tiles are consecutive, token tiles fastest; the chip takes
+  // them in rounds, each XCD a contiguous range of a round
   const int nx = p.d / BM, ny = (p.L + 255) / 256;
-  const int t = xcd_tile(blockIdx.x, gridDim.x);
+  const int t = xcd_tile_rounds(blockIdx.x, gridDim.x, p.round);
   const int bg = t / (nx * ny), r = t - bg * nx * ny;  // bg: the group across all sequences
   const int i0 = (r / ny) * BM;
   const int j0 = (r % ny) * 256;
@@ -1588,6 +1593,10 @@ hipError_t launch_target_gemm_bf16(const bf16_t *U, const bf16_t *WtT, bf16_t *V
   return hipGetLastError();
 }
 
+// Workgroups of the one-per-CU kernels resident at once: the compute units,
+// rounded down to a multiple of the XCD count (at least one per XCD).
+static int launch_round(int cus) { return cus >= kXcds ? cus / kXcds * kXcds : kXcds; }
+
 hipError_t launch_update_bf16(const bf16_t *Z, const bf16_t *VT, const float *state_in, float *state_out,
                               bf16_t *snap, const bf16_t *W0p, const Layout &lay, int cus, hipStream_t s) {
   const long long tiles = (long long)lay.n_seq() * (lay.f / BM) * (lay.d / 256);
@@ -1598,8 +1607,8 @@ hipError_t launch_update_bf16(const bf16_t *Z, const bf16_t *VT, const float *st
   if (cus < 2) cus = 2;
   const long long rem = tiles % cus;
   const long long whole = rem <= cus / 2 ? tiles - rem : tiles;
-  UpdArgs p{Z, VT, state_in, state_out, snap, W0p, lay.n_slots(), lay.L, lay.d, lay.f, 0,
-            cus >= kXcds ? cus / kXcds * kXcds : kXcds, lay.seqs()};
+  UpdArgs p{Z, VT, state_in, state_out, snap, W0p, lay.n_slots(), lay.L, lay.d, lay.f, 0, launch_round(cus),
+            lay.seqs()};
   if (whole > 0) hipLaunchKernelGGL((k_update<WN_W, NBJ_W, NSL_W>), dim3((unsigned)whole), dim3(NT_W), 0, s, p);
   if (tiles > whole) {
     p.tile0 = (int)whole;
@@ -1608,9 +1617,9 @@ hipError_t launch_update_bf16(const bf16_t *Z, const bf16_t *VT, const float *st
   return hipGetLastError();
 }
 
-hipError_t launch_scores_bf16(const bf16_t *Z, bf16_t *P, const Layout &lay, hipStream_t s) {
+hipError_t launch_scores_bf16(const bf16_t *Z, bf16_t *P, const Layout &lay, int cus, hipStream_t s) {
   const int nt = (lay.L + 255) / 256;
-  ScoreArgs p{Z, P, lay.n_slots(), lay.L, lay.C, lay.f, nt, lay.seqs(), 0, {}, {}};
+  ScoreArgs p{Z, P, lay.n_slots(), lay.L, lay.C, lay.f, nt, launch_round(cus), lay.seqs(), 0, {}, {}};
   if (nt * (nt + 1) / 2 <= kMaxScorePairs) {
     // the tiles of a full group that the kernel would not skip, jt-major
     for (int jt = 0; jt < nt; ++jt) {
@@ -1648,8 +1657,9 @@ hipError_t launch_to_planes_bf16(const bf16_t *src, bf16_t *dst, int d, int f, h
 }
 
 hipError_t launch_out_bf16(const bf16_t *Z, const bf16_t *P, const bf16_t *snap, const bf16_t *VT, void *y,
-                           int y_f32, const Layout &lay, hipStream_t s) {
-  OutArgs p{Z, P, snap, VT, y, lay.n_slots(), lay.L, lay.C, lay.d, lay.f, lay.intra, y_f32, lay.seqs()};
+                           int y_f32, const Layout &lay, int cus, hipStream_t s) {
+  OutArgs p{Z, P, snap, VT, y, lay.n_slots(), lay.L, lay.C, lay.d, lay.f, lay.intra, y_f32, launch_round(cus),
+            lay.seqs()};
   const long long n = lay.n_groups() * (lay.d / BM) * ((lay.L + 255) / 256);
   if (n >= (1LL << 31)) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(k_out, dim3((unsigned)n), dim3(NT_W), 0, s, p);

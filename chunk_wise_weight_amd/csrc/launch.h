@@ -22,15 +22,17 @@ hipError_t launch_a1_bf16(const bf16_t *x, const bf16_t *Wug, bf16_t *Z, const L
 // partial round of at most cus/2 tiles runs as half tiles).
 hipError_t launch_update_bf16(const bf16_t *Z, const bf16_t *VT, const float *state_in, float *state_out,
                               bf16_t *snap, const bf16_t *W0p, const Layout &lay, int cus, hipStream_t s);
-// P[group][t][s] = <Z[gL+t], Z[gL+s]> if s/C < t/C else 0, for t, s < L (eta is in V^T).
-hipError_t launch_scores_bf16(const bf16_t *Z, bf16_t *P, const Layout &lay, hipStream_t s);
+// P[group][t][s] = <Z[gL+t], Z[gL+s]> if s/C < t/C else 0, for t, s < L (eta is in V^T). cus: compute units of
+// the device (the tiles run in rounds of one per CU).
+hipError_t launch_scores_bf16(const bf16_t *Z, bf16_t *P, const Layout &lay, int cus, hipStream_t s);
 // One snapshot [f/8][d][8] = bf16(W0 + D) of fp32 W0 and state D, [d][f] each (no update).
 hipError_t launch_state_to_snap_bf16(const float *W0, const float *D, bf16_t *snap, int d, int f, hipStream_t s);
 // bf16 [d][f] -> planes [f/8][d][8].
 hipError_t launch_to_planes_bf16(const bf16_t *src, bf16_t *dst, int d, int f, hipStream_t s);
-// y[b][gL+t] = Z[gL+t] snap[b][g]^T + sum_s P[b][g][t][s] V[gL+s]; y is bf16, or fp32 with y_f32.
+// y[b][gL+t] = Z[gL+t] snap[b][g]^T + sum_s P[b][g][t][s] V[gL+s]; y is bf16, or fp32 with y_f32. cus: compute
+// units of the device (the tiles run in rounds of one per CU).
 hipError_t launch_out_bf16(const bf16_t *Z, const bf16_t *P, const bf16_t *snap, const bf16_t *VT, void *y,
-                           int y_f32, const Layout &lay, hipStream_t s);
+                           int y_f32, const Layout &lay, int cus, hipStream_t s);
 // Per-row chunk Gram sums for clipping: rowpart [B][T_pad/256][wspan][256] fp32. V's rows come from
 // Vrow [B][T_pad][d] or, with Vrow null, from E [vocab][d] through ids [B][T+1] (vocab*d*2 < 2^31).
 // gv: scratch of clip_gram_scratch_bytes(lay, wspan) bytes.

@@ -463,10 +463,10 @@ int forward_impl(ttt_handle *h, const void *x, const int32_t *ids, const void *E
                                           h->f, s));
     }
     if (prof) HIP_TRY(hipEventRecord(ev[4], s));
-    if (lay.intra) HIP_TRY(launch_scores_bf16((const bf16_t *)Z, (bf16_t *)P, lay, s));
+    if (lay.intra) HIP_TRY(launch_scores_bf16((const bf16_t *)Z, (bf16_t *)P, lay, h->cus, s));
     if (prof) HIP_TRY(hipEventRecord(ev[5], s));
     HIP_TRY(launch_out_bf16((const bf16_t *)Z, (const bf16_t *)P, (const bf16_t *)snap, (const bf16_t *)VT, y,
-                            h->y_f32, lay, s));
+                            h->y_f32, lay, h->cus, s));
   } else {
     if (conv) {
       HIP_TRY(launch_conv_taps_f32(ids, (const float *)E_tgt, vocab, h->conv_w, h->conv_K, (float *)U, lay, s));
