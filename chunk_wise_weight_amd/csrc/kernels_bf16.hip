@@ -615,6 +615,10 @@ __device__ __forceinline__ int xcd_tile_rounds(int n, int N, int R) {
   return r0 + xcd_tile(n - r0, Rn);
 }
 
+// R for the kernels of one workgroup per CU: the compute units, rounded down
+// to a multiple of the XCD count (at least one per XCD).
+static int launch_round(int cus) { return cus >= kXcds ? cus / kXcds * kXcds : kXcds; }
+
 // Logical tile t of an nx x ny grid, in bands of H rows along y; inside a band
 // y runs fastest, so H consecutive tiles share one x and nx*H consecutive tiles
 // cover the band. The last band may be shorter.
@@ -799,12 +803,13 @@ struct TgtArgs {
   bf16_t *Vrow;  // V
   float eta;
   int d, nx, ny;
+  int round;  // workgroups resident at once (the compute units), a multiple of 8
 };
 
 __global__ __launch_bounds__(NT_W, 1) void k_target_gemm(TgtArgs p) {
   __shared__ __attribute__((aligned(16))) Slab<WN_W, NBJ_W> ring[NSL_W];
   int tx, ty;  // model-dim tile, token tile
-  band_tile(xcd_tile(blockIdx.x, gridDim.x), p.nx, p.ny, 8, tx, ty);
+  band_tile(xcd_tile_rounds(blockIdx.x, gridDim.x, p.round), p.nx, p.ny, 8, tx, ty);
   const int n0 = tx * 256;
   const long long m0 = (long long)ty * BM;  // first slot of the tile
   SlabLoads<RmW, RmW> ld;
@@ -1373,6 +1378,7 @@ struct GramArgs {
   float *rowpart;      // [S/256][wspan][256]
   int C, d, f, wspan, vocab;
   long long S;         // scratch slots in all: Z's block stride is S*64
+  int round;           // workgroups resident at once (the compute units), a multiple of 8
   Seqs sq;
 };
 
@@ -1383,7 +1389,7 @@ template <bool GATHER>
 __global__ __launch_bounds__(NT_W, 1) void k_chunk_gram(GramArgs p) {
   __shared__ __attribute__((aligned(16))) char smem[kSmemGram];
   Slab<WN_W, NBJ_W> *ring = reinterpret_cast<Slab<WN_W, NBJ_W> *>(smem);
-  const int id = xcd_tile(blockIdx.x, gridDim.x);  // the t-tiles of an s-tile share an XCD
+  const int id = xcd_tile_rounds(blockIdx.x, gridDim.x, p.round);  // the t-tiles of an s-tile share an XCD
   const int wr = id % p.wspan;
   const int u = id / p.wspan;  // the s-tile: 256 slots of one sequence
   const SeqInfo si = p.sq.at(p.sq.of_tile(u));
@@ -1562,11 +1568,12 @@ hipError_t launch_gather_vt_bf16(const int32_t *ids, const bf16_t *E, int vocab,
 }
 
 hipError_t launch_chunk_gram_bf16(const bf16_t *Z, const bf16_t *Vrow, const bf16_t *E, const int32_t *ids, int vocab,
-                                  float *gv, float *rowpart, int wspan, const Layout &lay, hipStream_t s) {
+                                  float *gv, float *rowpart, int wspan, const Layout &lay, int cus, hipStream_t s) {
   const long long n = lay.n_slots() / 256 * wspan;
   if (n >= (1LL << 31) / 8) return hipErrorInvalidConfiguration;
   if (!Vrow && (long long)vocab * lay.d * 2 >= (1LL << 31)) return hipErrorInvalidValue;
-  GramArgs p{Z, Vrow, E, ids, gv, rowpart, lay.C, lay.d, lay.f, wspan, vocab, lay.n_slots(), lay.seqs()};
+  GramArgs p{Z, Vrow, E, ids, gv, rowpart, lay.C, lay.d, lay.f, wspan, vocab, lay.n_slots(), launch_round(cus),
+             lay.seqs()};
   if (Vrow)
     hipLaunchKernelGGL(k_chunk_gram<false>, dim3((unsigned)n), dim3(NT_W), 0, s, p);
   else
@@ -1584,18 +1591,14 @@ hipError_t launch_a1_bf16(const bf16_t *x, const bf16_t *Wug, bf16_t *Z, const L
 }
 
 hipError_t launch_target_gemm_bf16(const bf16_t *U, const bf16_t *WtT, bf16_t *VT, bf16_t *Vrow, float eta,
-                                  const Layout &lay, hipStream_t s) {
+                                  const Layout &lay, int cus, hipStream_t s) {
   const int nx = lay.d / 256;
   const long long ny = lay.n_slots() / BM;
   if (nx * ny >= (1LL << 31)) return hipErrorInvalidConfiguration;
-  TgtArgs p{U, WtT, VT, Vrow, eta, lay.d, nx, (int)ny};
+  TgtArgs p{U, WtT, VT, Vrow, eta, lay.d, nx, (int)ny, launch_round(cus)};
   hipLaunchKernelGGL(k_target_gemm, dim3((unsigned)(nx * ny)), dim3(NT_W), 0, s, p);
   return hipGetLastError();
 }
-
-// Workgroups of the one-per-CU kernels resident at once: the compute units,
-// rounded down to a multiple of the XCD count (at least one per XCD).
-static int launch_round(int cus) { return cus >= kXcds ? cus / kXcds * kXcds : kXcds; }
 
 hipError_t launch_update_bf16(const bf16_t *Z, const bf16_t *VT, const float *state_in, float *state_out,
                               bf16_t *snap, const bf16_t *W0p, const Layout &lay, int cus, hipStream_t s) {

@@ -35,9 +35,10 @@ hipError_t launch_out_bf16(const bf16_t *Z, const bf16_t *P, const bf16_t *snap,
                            int y_f32, const Layout &lay, int cus, hipStream_t s);
 // Per-row chunk Gram sums for clipping: rowpart [B][T_pad/256][wspan][256] fp32. V's rows come from
 // Vrow [B][T_pad][d] or, with Vrow null, from E [vocab][d] through ids [B][T+1] (vocab*d*2 < 2^31).
-// gv: scratch of clip_gram_scratch_bytes(lay, wspan) bytes.
+// gv: scratch of clip_gram_scratch_bytes(lay, wspan) bytes. cus: compute units of the device (the tiles run in
+// rounds of one per CU).
 hipError_t launch_chunk_gram_bf16(const bf16_t *Z, const bf16_t *Vrow, const bf16_t *E, const int32_t *ids, int vocab,
-                                  float *gv, float *rowpart, int wspan, const Layout &lay, hipStream_t s);
+                                  float *gv, float *rowpart, int wspan, const Layout &lay, int cus, hipStream_t s);
 
 // ---- fp32 path: FMA kernels (kernels_f32.hip), same buffers and meaning in fp32 ----
 hipError_t launch_gather_vt_f32(const int32_t *ids, const float *E, int vocab, float *VT, float *Vrow,
@@ -74,9 +75,10 @@ hipError_t launch_conv_taps_bf16(const int32_t *ids, const bf16_t *E, int vocab,
 hipError_t launch_conv_taps_f32(const int32_t *ids, const float *E, int vocab, const float *cw, int K, float *U,
                                 const Layout &lay, hipStream_t s);
 // V = U W_target into V^T (K-blocked bf16, as eta * V / row-major [B][d][T_pad] fp32, unscaled) and, if Vrow,
-// row-major V (unscaled). bf16 takes W_target^T [d][d]; fp32 takes W_target [d][d].
+// row-major V (unscaled). bf16 takes W_target^T [d][d]; fp32 takes W_target [d][d]. cus (bf16): compute units
+// of the device (the tiles run in rounds of one per CU).
 hipError_t launch_target_gemm_bf16(const bf16_t *U, const bf16_t *WtT, bf16_t *VT, bf16_t *Vrow, float eta,
-                                   const Layout &lay, hipStream_t s);
+                                   const Layout &lay, int cus, hipStream_t s);
 hipError_t launch_target_gemm_f32(const float *U, const float *W, float *VT, float *Vrow, const Layout &lay,
                                   hipStream_t s);
 hipError_t launch_transpose_bf16(const bf16_t *src, bf16_t *dst, int n, hipStream_t s);

@@ -434,7 +434,7 @@ int forward_impl(ttt_handle *h, const void *x, const int32_t *ids, const void *E
     if (conv) {
       HIP_TRY(launch_conv_taps_bf16(ids, (const bf16_t *)E_tgt, vocab, h->conv_w, h->conv_K, (bf16_t *)U, lay, s));
       HIP_TRY(launch_target_gemm_bf16((const bf16_t *)U, (const bf16_t *)h->Wt, (bf16_t *)VT, (bf16_t *)Vrow, h->eta,
-                                      lay, s));
+                                      lay, h->cus, s));
     } else if ((learn || lay.intra) && !gram_e) {
       HIP_TRY(launch_gather_vt_bf16(ids, (const bf16_t *)E_tgt, vocab, (bf16_t *)VT, (bf16_t *)Vrow, nullptr, h->eta,
                                     lay, s));
@@ -444,7 +444,7 @@ int forward_impl(ttt_handle *h, const void *x, const int32_t *ids, const void *E
     if (prof) HIP_TRY(hipEventRecord(ev[2], s));
     if (clip) {
       HIP_TRY(launch_chunk_gram_bf16((const bf16_t *)Z, (const bf16_t *)Vrow, (const bf16_t *)E_tgt, ids, vocab, gv,
-                                     rowpart, wspan, lay, s));
+                                     rowpart, wspan, lay, h->cus, s));
       HIP_TRY(launch_chunk_factors(rowpart, cfac, wspan, h->eta, h->clip_tau, lay, s));
       if (gram_e)
         HIP_TRY(launch_gather_vt_bf16(ids, (const bf16_t *)E_tgt, vocab, (bf16_t *)VT, nullptr, cfac, h->eta, lay, s));
