@@ -939,78 +939,99 @@ struct UpdArgs {
 };
 
 // Snapshots W[a][i] are held as planes of 8 columns ([f/8][d][8]: element
-// (a, i) at ((i/8)*d + a)*8 + i%8). Lane l holds, per accumulator, four
-// consecutive i of one a; lanes l and l+16 hold the two halves of one 16-byte
-// chunk, and the 16 lanes of a quarter walk 16 consecutive a: each store
-// instruction writes two runs of 256 contiguous bytes (lanes 32-63 in the
-// next plane). A lane offset locates this lane's element of accumulator
-// (gi, gj) = (0, 0): a = j0 + wn*32*NBJ + l%16, i = i0 + wm*128 + 4*(l/16);
-// tiles are always full (d, f multiples of 256). Accumulator (gi, gj) lies
-// 2gi planes and 16gj rows of a further on.
+// (a, i) at ((i/8)*d + a)*8 + i%8). The MFMA accumulator layout gives lane l
+// four consecutive i of one a per accumulator: i = 4*(l/16) .. +3 of the
+// tile's 16, a = l%16. Snapshots are written, and the initial weight read
+// back, 16 bytes per lane in an exchanged layout: for the accumulators
+// (gi, 2gp) and (gi, 2gp+1), 16 a apart, lanes 0-15 hold the eight i 0-7 (one
+// 16-byte chunk of a plane) of the first, lanes 16-31 those of the second,
+// and lanes 32-63 the same for i 8-15, the next plane. One instruction then
+// covers 32 consecutive a of two planes: two runs of 512 contiguous bytes.
+// v_permlane16_swap trades the odd 16-lane rows of its first operand for the
+// even rows of its second; applied to the low and high halves of each lane's
+// chunk it turns the exchanged layout into the two accumulators' layout, and
+// back (it is its own inverse).
+// A lane offset locates this lane's chunk for (gi, gp) = (0, 0):
+// a = j0 + wn*32*NBJ + l%32, plane (i0 + wm*128)/8 + l/32; tiles are always
+// full (d, f multiples of 256). Pair (gi, gp) lies 2gi planes and 32gp rows
+// of a further on.
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
 
+// Swaps the odd 16-lane rows of a with the even rows of b.
+__device__ __forceinline__ void swap_rows16(uint32_t &a, uint32_t &b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+  a = r[0];
+  b = r[1];
+}
+
+// A VALU write to the data registers of a buffer store wider than 8 bytes
+// must come at least two wait states after the store, or the store may write
+// the new values. The compiler counts them for such stores with a constant
+// soffset but not with a register soffset (the snapshot stores take their
+// plane offset there), so they are explicit here.
+__device__ __forceinline__ void guard_wide_store() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 1");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // The initial weight W0 as bf16 planes ([f/8][d][8], the snapshot layout): a
-// buffer descriptor over them and this lane's byte offset, so that each load
-// is one instruction with a scalar offset (64-bit addresses per load would
-// cost two registers each).
+// buffer descriptor over them and this lane's byte offset in the exchanged
+// layout, so that each load is one instruction with a scalar offset (64-bit
+// addresses per load would cost two registers each).
 struct QRead {
   __amdgpu_buffer_rsrc_t rs;
   uint32_t vo;
   int d;
-  // byte offsets of accumulator (gi, gj): 2gi planes of 8 columns in the
-  // scalar offset, 16gj rows (gj*128 elements) in the lane offset (an immediate)
+  // byte offsets of pair (gi, gp): 2gi planes of 8 columns in the scalar
+  // offset, 32gp rows (gp*256 elements) in the lane offset (an immediate)
   __device__ __forceinline__ int soff(int gi) const { return gi * 32 * d; }
-  __device__ __forceinline__ uint2 load(int gi, int gj) const {
-    const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rs, vo + gj * 256, soff(gi), 0);
-    return make_uint2(v.x, v.y);
+  __device__ __forceinline__ u32x4_t load(int gi, int gp) const {
+    return __builtin_amdgcn_raw_buffer_load_b128(rs, vo + gp * 512, soff(gi), 0);
   }
 };
 
-// W0 + D for every accumulator (gi, gj) of the tile, with the accumulators
-// holding D and W0 read from the initial weight's bf16 planes.
-// The loads go out in batches of KB, each batch one memory round trip; the
-// scheduling barriers around a batch stop the compiler from hoisting the next
-// batch's loads. The snapshot takes all of them in one batch: it runs between
-// stages, when the MFMA fragments are dead, and the 64 registers fit.
-template <int KB, int NBJ, class Fn>
-__device__ __forceinline__ void for_state(const Acc<NBJ> &acc, const QRead &qr, Fn &&fn) {
-  constexpr int NTOT = 16 * NBJ;
-  static_assert(NTOT % KB == 0, "whole batches");
-#pragma unroll
-  for (int k0 = 0; k0 < NTOT; k0 += KB) {
-    uint2 qv[KB];
-    pin();
-#pragma unroll
-    for (int k = 0; k < KB; ++k) {
-      const int e = k0 + k;
-      qv[k] = qr.load(e & 7, e >> 3);
-    }
-#pragma unroll
-    for (int k = 0; k < KB; ++k) {
-      const int e = k0 + k, gi = e & 7, gj = e >> 3;
-      const f32x4 &v = acc.v[gi][gj];
-      fn(gi, gj, bf16_lo(qv[k].x) + v[0], bf16_hi(qv[k].x) + v[1], bf16_lo(qv[k].y) + v[2],
-         bf16_hi(qv[k].y) + v[3]);
-    }
-    pin();
-  }
-}
-
 // Snapshot of the weight W0 + D: bf16(W0 + D) into the snapshot planes at
-// `snap` (one group's [f/8][d][8] planes), with the lane and scalar offsets of
-// the W0 reads (the two share their layout). The stores are non-temporal: no
-// kernel of the update reads them, and they would evict operand slabs that
-// other workgroups still read from L2.
+// `snap` (one group's [f/8][d][8] planes), with the accumulators holding D
+// (read, not changed) and W0 read back from the initial weight's bf16 planes,
+// with the same lane and scalar offsets (the two share their layout). All
+// loads go out before the first add (one memory round trip); the scheduling
+// barriers keep the compiler from moving them. The snapshot runs between
+// stages, when the MFMA fragments are dead, so their 64 registers fit. The
+// stores are non-temporal: no kernel of the update reads them, and they would
+// evict operand slabs that other workgroups still read from L2.
 template <int NBJ>
 __device__ __forceinline__ void dump_snapshot(const Acc<NBJ> &acc, const QRead &qr, const bf16_t *snap) {
   constexpr int kNt = 2;
+  constexpr int NTOT = 8 * NBJ;  // 8 row fragments x NBJ pairs of column fragments
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t *>(snap), (short)0, 0x7fffffff, kBufferFlags);
-  for_state<16 * NBJ>(acc, qr, [&](int gi, int gj, float s0, float s1, float s2, float s3) {
-    const u32x2_t pk{pack_bf16x2(s0, s1), pack_bf16x2(s2, s3)};
-    __builtin_amdgcn_raw_buffer_store_b64(pk, rs, qr.vo + gj * 256, qr.soff(gi), kNt);
-  });
+  u32x4_t qv[NTOT];
+  pin();
+#pragma unroll
+  for (int k = 0; k < NTOT; ++k) qv[k] = qr.load(k & 7, k >> 3);
+#pragma unroll
+  for (int k = 0; k < NTOT; ++k) {
+    const int gi = k & 7, gp = k >> 3;
+    const f32x4 &u = acc.v[gi][2 * gp];
+    const f32x4 &v = acc.v[gi][2 * gp + 1];
+    // W0 in the accumulators' layout: the chunk's low half (i 0-3) becomes
+    // the first accumulator's four i, its high half the second's
+    uint32_t w0 = qv[k].x, w1 = qv[k].y, w2 = qv[k].z, w3 = qv[k].w;
+    swap_rows16(w0, w2);
+    swap_rows16(w1, w3);
+    uint32_t p0 = pack_bf16x2(u[0] + bf16_lo(w0), u[1] + bf16_hi(w0));
+    uint32_t p1 = pack_bf16x2(u[2] + bf16_lo(w1), u[3] + bf16_hi(w1));
+    uint32_t p2 = pack_bf16x2(v[0] + bf16_lo(w2), v[1] + bf16_hi(w2));
+    uint32_t p3 = pack_bf16x2(v[2] + bf16_lo(w3), v[3] + bf16_hi(w3));
+    // and back to the exchanged layout: eight consecutive i of one a per lane
+    swap_rows16(p0, p2);
+    swap_rows16(p1, p3);
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{p0, p1, p2, p3}, rs, qr.vo + gp * 512, qr.soff(gi), kNt);
+    guard_wide_store();
+  }
+  pin();
 }
 
 // WN = 4: workgroup n of the launch is tile tile0 + n (a 256 x 256 tile);
@@ -1032,11 +1053,12 @@ __global__ __launch_bounds__(128 * WN, 1) void k_update(UpdArgs p) {
   const int lane = threadIdx.x & 63;
   const int w = wave_id(), wm = w & 1, wn = w >> 1;
   const long long df = (long long)p.d * p.f;
-  // this lane's first element of the tile in the state ([d][f]) and in a snapshot ([f/8][d][8])
+  // this lane's first element of the tile in the state ([d][f]), and its first 16-byte chunk of a
+  // snapshot ([f/8][d][8]) in the exchanged layout of the snapshot accesses
   const long long lane_off =
       (long long)(j0 + wn * 32 * NBJ + (lane & 15)) * p.f + i0 + wm * 128 + 4 * (lane >> 4);
-  const long long lane_snap = (long long)((i0 + wm * 128) / 8 + (lane >> 5)) * 8 * p.d +
-                              (j0 + wn * 32 * NBJ + (lane & 15)) * 8 + 4 * ((lane >> 4) & 1);
+  const long long lane_snap =
+      (long long)((i0 + wm * 128) / 8 + (lane >> 5)) * 8 * p.d + (j0 + wn * 32 * NBJ + (lane & 31)) * 8;
   const bf16_t *snap0 = p.snap + (long long)si.grp0 * df;
   const int ngroups = si.len > p.L ? (si.len + p.L - 1) / p.L : 1;
   // where this lane's part of the final state goes (null: nowhere)
