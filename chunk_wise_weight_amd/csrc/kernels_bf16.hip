@@ -1016,8 +1016,8 @@ __device__ __forceinline__ void dump_snapshot(const Acc<NBJ> &acc, const QRead &
     const int gi = k & 7, gp = k >> 3;
     const f32x4 &u = acc.v[gi][2 * gp];
     const f32x4 &v = acc.v[gi][2 * gp + 1];
-    // W0 in the accumulators' layout: the chunk's low half (i 0-3) becomes
-    // the first accumulator's four i, its high half the second's
+    // W0 in the accumulators' layout: after the two swaps w0, w1 hold this
+    // lane's four i of accumulator (gi, 2gp) and w2, w3 those of (gi, 2gp+1)
     uint32_t w0 = qv[k].x, w1 = qv[k].y, w2 = qv[k].z, w3 = qv[k].w;
     swap_rows16(w0, w2);
     swap_rows16(w1, w3);
