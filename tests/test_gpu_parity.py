@@ -216,3 +216,30 @@ def test_out_of_range_ids_zero_targets():
     W0 = w.W_down0.astype(np.float64)
     assert rel_fro(y, y_ref) <= BF16_TOL
     assert rel_fro(Wf - W0, W_ref - W0) <= BF16_TOL
+
+
+TINY_CASES = [  # (T, C, B): streams shorter than one 8-token stage, a ragged 33 with chunks of 1, 4 and 16
+    (1, 1, 1),
+    (1, 256, 2),
+    (7, 4, 1),
+    (33, 1, 1),
+    (33, 4, 2),
+    (33, 16, 1),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T,C,B", TINY_CASES)
+def test_tiny_streams(dtype, T, C, B):
+    # A single token only updates the state (its output uses the entry weight); a few tokens exercise the
+    # ragged first slab of every kernel, the clamped L2 prefetch and the first snapshot alone.
+    d, f = (64, 128) if dtype == "f32" else (256, 512)
+    w = make_inputs(d=d, f=f, B=B, T=T, C=C, eta=0.05, dtype=dtype, vocab=31, e_std=1.0, seed=900 + 10 * T + C)
+    print(f"[tiny] {dtype} T={T} C={C} B={B}", flush=True)
+    y, Wf = Layer(w).forward_np()
+    y_ref, W_ref = _oracle(w)
+    W0 = w.W_down0.astype(np.float64)
+    metric, tol = (max_rel, F32_TOL) if dtype == "f32" else (rel_fro, BF16_TOL)
+    assert metric(y, y_ref) <= tol, metric(y, y_ref)
+    assert metric(Wf, W_ref) <= tol, metric(Wf, W_ref)
+    assert metric(Wf - W0, W_ref - W0) <= tol, metric(Wf - W0, W_ref - W0)
