@@ -181,6 +181,8 @@ struct RmLoad {
 // Each slab is one contiguous block of 128-byte rows; its descriptor starts at
 // the slab's block and ends after nrows rows, so rows r >= nrows read zero
 // (the row offset is in the lane offset, which the range check covers).
+// gap: tile rows 128 and up come from operand rows r + gap (two 128-row
+// pieces of one operand in one tile).
 template <int ROWS, int NW>
 struct CbLoad {
   static constexpr int WR = ROWS / NW, N = WR / 8;
@@ -190,7 +192,8 @@ struct CbLoad {
   // a fixed bound: with vo[N] here, the host pass of hipcc rejects SlabLoads<PlLoad, CbLoad>
   uint32_t vo[8];
   static_assert(N <= 8, "lane offsets per wave");
-  __device__ __forceinline__ void init(const bf16_t *base_, long long kblk_, int nrows, int w, int lane) {
+  __device__ __forceinline__ void init(const bf16_t *base_, long long kblk_, int nrows, int w, int lane,
+                                       int gap = 0) {
     base = base_;
     kblk = kblk_;
     const long long by = (long long)(nrows > 0 ? nrows : 0) * 128;
@@ -199,7 +202,7 @@ struct CbLoad {
 #pragma unroll
     for (int n = 0; n < N; ++n) {
       const int row = w * WR + 8 * n + lr;
-      vo[n] = (uint32_t)(row * 128 + (((lane & 7) ^ swz(row)) << 4));
+      vo[n] = (uint32_t)((row + (row >= 128 ? gap : 0)) * 128 + (((lane & 7) ^ swz(row)) << 4));
     }
   }
   using Pre = __amdgpu_buffer_rsrc_t;
@@ -1152,6 +1155,9 @@ __global__ __launch_bounds__(128 * WN, 1) void k_update(UpdArgs p) {
 // unmasked entry are formed.
 // grid: B * ngroups * nt(nt+1)/2 workgroups, nt = ceil(L/256)
 constexpr int kMaxScorePairs = 136;  // the lower triangle of 16 x 16 tiles (L <= 4096)
+// A pair entry (kPackedPair, a): with C = 128 the diagonal tiles a and a+1
+// of a group, each holding two chunks, share one workgroup (below).
+constexpr unsigned char kPackedPair = 0xff;
 
 struct ScoreArgs {
   const bf16_t *Z;
@@ -1160,8 +1166,9 @@ struct ScoreArgs {
   int L, C, f, nt;
   int round;  // workgroups resident at once (the compute units), a multiple of 8
   Seqs sq;
-  // tiles (it, jt) of a full group that hold an unmasked entry; npairs = 0:
-  // every tile of the lower triangle gets a workgroup (long groups)
+  // tiles (it, jt) of a full group that hold an unmasked entry, and packed
+  // diagonal pairs (kPackedPair, a); npairs = 0: every tile of the lower
+  // triangle gets a workgroup (long groups)
   int npairs;
   unsigned char pit[kMaxScorePairs], pjt[kMaxScorePairs];
 };
@@ -1187,23 +1194,53 @@ __global__ __launch_bounds__(NT_W, 1) void k_scores(ScoreArgs p) {
   const int gs = (bg - si.grp0) * p.L;       // first token of the group in its sequence
   const int Lg = si.len - gs < p.L ? si.len - gs : p.L;
   const int tp = (si.len + 255) & ~255;      // the sequence's slots
-  const int i0 = it * BM, j0 = jt * 256;
-  if (j0 >= Lg) return;
+  // A packed pair (C = 128): of diagonal tile k (tokens 256k .. 256k+255,
+  // chunks 2k and 2k+1) only s in chunk 2k against t in chunk 2k+1 is
+  // unmasked, and the output GEMM also reads the all-masked block of t and s
+  // in chunk 2k (as zeros). One workgroup takes tiles a and b = a+1: its rows
+  // are s in chunk 2a, then chunk 2b; its columns t in chunk 2a+1, then
+  // chunk 2b+1. The two diagonal quadrants are the unmasked blocks; the two
+  // cross quadrants write the zero blocks of a and b.
+  const bool packed = it == kPackedPair;
+  const int i0 = packed ? jt * 256 : it * BM, j0 = packed ? jt * 256 + 128 : jt * 256;
+  if (packed ? i0 >= Lg : j0 >= Lg) return;
   // A tile whose every s lies in the chunk of its last t or later is all
   // masked; the output GEMM never reads it (it stops before that chunk).
   const int jl = (j0 + 255 < Lg - 1) ? j0 + 255 : Lg - 1;
-  if (i0 / p.C >= jl / p.C) return;
+  if (!packed && i0 / p.C >= jl / p.C) return;
   const bf16_t *Zg = p.Z + ((long long)si.slot0 + gs) * 64;  // Z column-blocked [f/64][S][64]
   const long long zblk = p.S * 64;
   SlabLoads<CbW, CbW> ld;
-  ld.a.init(Zg + (long long)i0 * 64, zblk, tp - gs - i0, wave_id(), threadIdx.x & 63);
-  ld.b.init(Zg + (long long)j0 * 64, zblk, tp - gs - j0, wave_id(), threadIdx.x & 63);
+  const int gap = packed ? 128 : 0;
+  ld.a.init(Zg + (long long)i0 * 64, zblk, tp - gs - i0, wave_id(), threadIdx.x & 63, gap);
+  ld.b.init(Zg + (long long)j0 * 64, zblk, tp - gs - j0, wave_id(), threadIdx.x & 63, gap);
   Acc<NBJ_W> acc;
   acc_zero(acc);
   gemm_k<WN_W, NBJ_W, NSL_W, kARows>(acc, ring, ld, p.f / BK);
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w & 1, wn = w >> 1;
   bf16_t *Pg = p.P + (long long)bg * p.L * p.L;
+  if (packed) {
+    // wave rows are s of tile k = a + wm; columns of the same half are t of
+    // chunk 2k+1 (computed), of the other half t of chunk 2k (zeros)
+    const int k = jt + wm;
+#pragma unroll
+    for (int gj = 0; gj < 2 * NBJ_W; ++gj) {
+      const int c = wn * WC_W + gj * 16 + (lane & 15);
+      const bool diag = (c >> 7) == wm;
+      const int t = 256 * k + (diag ? 128 : 0) + (c & 127);
+      if (t >= p.L) continue;
+#pragma unroll
+      for (int gi = 0; gi < 8; ++gi) {
+        const int sidx = 256 * k + gi * 16 + 4 * (lane >> 4);
+        uint2 pk;
+        pk.x = diag ? pack_bf16x2(acc.v[gi][gj][0], acc.v[gi][gj][1]) : 0u;
+        pk.y = diag ? pack_bf16x2(acc.v[gi][gj][2], acc.v[gi][gj][3]) : 0u;
+        *reinterpret_cast<uint2 *>(Pg + (long long)t * p.L + sidx) = pk;
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int gj = 0; gj < 2 * NBJ_W; ++gj) {
     const int t = j0 + wn * WC_W + gj * 16 + (lane & 15);
@@ -1646,15 +1683,22 @@ hipError_t launch_scores_bf16(const bf16_t *Z, bf16_t *P, const Layout &lay, int
   const int nt = (lay.L + 255) / 256;
   ScoreArgs p{Z, P, lay.n_slots(), lay.L, lay.C, lay.f, nt, launch_round(cus), lay.seqs(), 0, {}, {}};
   if (nt * (nt + 1) / 2 <= kMaxScorePairs) {
+    // with C = 128 and an even number of tiles, the diagonal tiles go in packed pairs
+    const bool pack = lay.C == 128 && lay.L % 512 == 0;
     // the tiles of a full group that the kernel would not skip, jt-major
     for (int jt = 0; jt < nt; ++jt) {
       const int jl = (jt * 256 + 255 < lay.L - 1) ? jt * 256 + 255 : lay.L - 1;
       for (int it = 0; it <= jt; ++it)
-        if (it * 256 / lay.C < jl / lay.C) {
+        if (it * 256 / lay.C < jl / lay.C && !(pack && it == jt)) {
           p.pit[p.npairs] = (unsigned char)it;
           p.pjt[p.npairs] = (unsigned char)jt;
           ++p.npairs;
         }
+    }
+    for (int a = 0; pack && a < nt; a += 2) {
+      p.pit[p.npairs] = kPackedPair;
+      p.pjt[p.npairs] = (unsigned char)a;
+      ++p.npairs;
     }
     if (p.npairs == 0) return hipSuccess;  // one chunk per group: no within-group term
   }
