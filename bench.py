@@ -46,6 +46,8 @@ def parse():
                     help="measure the 36-layer stack (B=2 x 16384 tokens, C=256) instead of the single layer")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain device copy of COPY_BYTES (calibrates rocprofv3 FETCH_SIZE/WRITE_SIZE)")
+    ap.add_argument("--lib", default=None,
+                    help="time another build of libttt.so instead of the in-tree one (same-box A/B comparisons)")
     return ap.parse_args()
 
 
@@ -275,6 +277,10 @@ def main():
     from synth import make_config
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if a.lib:
+        import chunk_wise_weight_amd.binding as binding
+        binding.LIB_PATH = os.path.abspath(a.lib)
+        print(f"[bench] library {binding.LIB_PATH}", file=sys.stderr, flush=True)
     if a.stack:
         run_stack(a)
         return
