@@ -269,8 +269,9 @@ def run_stack(a):
 def main():
     a = parse()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build runs the fast-weight path on a single MI355X "
-              "(multi-GPU sharding is a design note, not built). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the library runs the fast-weight path on a single MI355X "
+              "(sharding across GPUs is described in the design notes, not implemented). Run with --gpus 1.",
+              file=sys.stderr)
         sys.exit(2)
     import torch
 
